@@ -1,0 +1,132 @@
+"""Oracle rejection sampler (test infrastructure; see package docstring).
+
+The steps, in the order of Algorithm 1 as printed on [P1 "What one iteration
+actually does"] and the rule on [P3 "Why the output doesn't change"]:
+
+1. p_i = softmax(logits_i / T) for the gamma+1 verify rows.
+2. Accept test for i = 1..gamma in order: reject iff r_i > p_i(x_i)/q_i(x_i)
+   [P1, Algorithm 1 "Determine the number of accepted guesses"].  Written
+   division-free as: accept iff u_i * q_i(x_i) <= p_i(x_i), evaluated in
+   float32 (the same precision on both sides, since it decides an integer).
+   q(x) = 0 therefore accepts.
+3. n = index of the first rejection (prefix truncation [P1 "Rejection is
+   prefix-truncating"]), or n_draft when all drafts pass.
+4. Corrected distribution for row j = n (0-based): if n < n_draft,
+   norm(max(0, p_j - q_j)) [P1 Algorithm 1 "Adjust the distribution";
+   P3 residual]; otherwise p_j itself (the bonus token [P2 "The
+   draft-then-verify loop", step 3]).  The subtraction is float32.  An
+   all-zero residual (p == q up to rounding) falls back to p_j.
+5. t ~ p' by a fixed-point inverse CDF: w_v = floor(r_v * 2**40) (exact),
+   S = sum w (exact in uint64), T = floor(k * S / 2**24) with k = u * 2**24,
+   t = smallest v whose inclusive prefix sum exceeds T.  The pages only say
+   "t ~ p'"; the normalisation of step 4 is carried by S.
+6. Emit [x_1 .. x_n, t]; the rest of the gamma+1 slots hold -1.
+
+All steps are vectorised over the batch with NumPy; nothing else is reordered.
+Valid for V < 2**23 (so that S < 2**63).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+TWO40 = float(1 << 40)
+TWO24 = 1 << 24
+
+
+def softmax(logits: np.ndarray, temperature: float = 1.0) -> np.ndarray:
+    """Row softmax in fp64 over the last axis of logits / T."""
+    x = np.asarray(logits, dtype=np.float64) / float(temperature)
+    x = x - x.max(axis=-1, keepdims=True)
+    e = np.exp(x)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def accept_flags(p_x, q_x, u) -> np.ndarray:
+    """Per-draft accept decision, float32: u * q(x) <= p(x)."""
+    p_x = np.asarray(p_x, dtype=np.float32)
+    q_x = np.asarray(q_x, dtype=np.float32)
+    u = np.asarray(u, dtype=np.float32)
+    return (u * q_x) <= p_x
+
+
+def accepted_length(ok: np.ndarray, n_draft: np.ndarray) -> np.ndarray:
+    """n = index of the first failed test among the first n_draft, else n_draft."""
+    B, g = ok.shape
+    n_draft = np.asarray(n_draft, dtype=np.int64)
+    valid = np.arange(g)[None, :] < n_draft[:, None]
+    fail = valid & ~ok
+    first = np.argmax(fail, axis=1) if g > 0 else np.zeros(B, dtype=np.int64)
+    return np.where(fail.any(axis=1) if g > 0 else np.zeros(B, bool), first, n_draft).astype(np.int64)
+
+
+def fixed_point_weights(r: np.ndarray) -> np.ndarray:
+    """w = floor(r * 2**40) as uint64 (r float32 in [0, 1]; exact)."""
+    r64 = np.asarray(r, dtype=np.float32).astype(np.float64)
+    return np.floor(r64 * TWO40).astype(np.uint64)
+
+
+def fixed_point_draw(r: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """Inverse-CDF draw from unnormalised float32 rows r [N, V] with uniforms u [N]."""
+    w = fixed_point_weights(r)
+    S = w.sum(axis=-1, dtype=np.uint64)
+    k = (np.asarray(u, dtype=np.float32).astype(np.float64) * TWO24).astype(np.uint64)
+    mask = np.uint64(TWO24 - 1)
+    T = (S >> np.uint64(24)) * k + (((S & mask) * k) >> np.uint64(24))
+    C = np.cumsum(w, axis=-1, dtype=np.uint64)
+    return (C <= T[..., None]).sum(axis=-1).astype(np.int64)
+
+
+def reject_sample(p: np.ndarray, q, draft: np.ndarray, n_draft, u_acc: np.ndarray, u_res: np.ndarray):
+    """One round's accept/resample given probability rows.
+
+    p [B, g+1, V] float32 target rows; q [B, g, V] float32 draft rows, or None
+    for a one-hot draft (q_i(x_i) = 1); draft [B, g] token ids; n_draft [B] or
+    None (= g); u_acc [B, g], u_res [B] float32 uniforms.
+    Returns (n [B] int64, emitted [B, g+1] int64, -1 padded).
+    """
+    p = np.asarray(p, dtype=np.float32)
+    B, g1, V = p.shape
+    g = g1 - 1
+    draft = np.asarray(draft, dtype=np.int64).reshape(B, g)
+    nd = np.full(B, g, dtype=np.int64) if n_draft is None else np.clip(np.asarray(n_draft, np.int64), 0, g)
+    rows = np.arange(B)
+    if g > 0:
+        p_x = np.take_along_axis(p[:, :g, :], draft[:, :, None], axis=2)[..., 0]
+        if q is None:
+            q_x = np.ones((B, g), dtype=np.float32)
+        else:
+            q = np.asarray(q, dtype=np.float32)
+            q_x = np.take_along_axis(q, draft[:, :, None], axis=2)[..., 0]
+        ok = accept_flags(p_x, q_x, np.asarray(u_acc, np.float32).reshape(B, g))
+    else:
+        ok = np.zeros((B, 0), dtype=bool)
+    n = accepted_length(ok, nd)
+    pj = p[rows, n]  # [B, V]
+    r = pj.copy()
+    rej = n < nd
+    if rej.any():
+        idx = np.nonzero(rej)[0]
+        if q is None:
+            qj = np.zeros((len(idx), V), dtype=np.float32)
+            qj[np.arange(len(idx)), draft[idx, n[idx]]] = 1.0
+        else:
+            qj = q[idx, n[idx]]
+        r[idx] = np.maximum(np.float32(0.0), pj[idx] - qj)
+    empty = fixed_point_weights(r).sum(axis=-1, dtype=np.uint64) == 0
+    r[empty] = pj[empty]
+    t = fixed_point_draw(r, np.asarray(u_res, np.float32).reshape(B))
+    emitted = np.full((B, g + 1), -1, dtype=np.int64)
+    for b in range(B):
+        emitted[b, : n[b]] = draft[b, : n[b]]
+        emitted[b, n[b]] = t[b]
+    return n, emitted
+
+
+def sample(p: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """Plain draw t ~ p (the gamma = 0 round): rows p [N, V], uniforms u [N]."""
+    p = np.asarray(p, dtype=np.float32)
+    N, V = p.shape
+    n, em = reject_sample(p[:, None, :], None, np.zeros((N, 0), np.int64), None,
+                          np.zeros((N, 0), np.float32), u)
+    return em[:, 0]

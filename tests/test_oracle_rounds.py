@@ -1,0 +1,96 @@
+"""Oracle round driver and n-gram proposer pins."""
+import numpy as np
+
+from oracle import model as OM
+from oracle import rounds as R
+from oracle.ngram import ngram_propose
+from synth import Shape, make_prompt, make_weights, round_uniforms
+
+SHAPE = Shape("r", 64, 3, 4, 2, 16, 96, 64, "f32")
+
+
+def _generate(draft_layers, gamma, n_new, seed=21, B=2, P=7):
+    w = make_weights(SHAPE, seed=seed, norm="random", std=0.1)
+    tgt = OM.Decoder(SHAPE, w)
+    dft = OM.Decoder(SHAPE, w, n_layers=draft_layers)
+    prompt = make_prompt(B, P, SHAPE.vocab, seed=seed)
+    ct, cd = tgt.new_cache(B, P + n_new + gamma + 2), dft.new_cache(B, P + n_new + gamma + 2)
+    R.prefill(tgt, ct, prompt)
+    R.prefill(dft, cd, prompt)
+    committed = [list(prompt[b]) for b in range(B)]
+    rounds = []
+    r = 0
+    while min(len(c) for c in committed) < P + n_new:
+        u = round_uniforms(seed, r, B, gamma)
+        last = np.array([c[-1] for c in committed])
+        prev = np.array([c[-2] for c in committed])
+        xs, q = R.draft_round(dft, cd, prev, last, ct.length, gamma, u["u_draft"])
+        out = R.verify_round(tgt, ct, last, xs, q, None, u["u_acc"], u["u_res"])
+        for b in range(B):
+            committed[b] += [int(t) for t in out["emitted"][b, :out["n"][b] + 1]]
+        rounds.append((xs, q, out))
+        r += 1
+    return committed, rounds, ct, P
+
+
+def test_round_loop_invariants():
+    committed, rounds, ct, P = _generate(draft_layers=1, gamma=3, n_new=12)
+    for xs, q, out in rounds:
+        cnt = (out["emitted"] >= 0).sum(1)
+        assert ((cnt >= 1) & (cnt <= 4)).all()
+        for b in range(xs.shape[0]):
+            assert (out["emitted"][b, :out["n"][b]] == xs[b, :out["n"][b]]).all()
+    # the target cache holds every committed token except the last
+    for b, c in enumerate(committed):
+        assert ct.length[b] == len(c) - 1
+
+
+def test_full_depth_draft_accepts_every_guess():
+    """A drafter identical to the target proposes from q = p, so every guess
+    passes and each round emits gamma + 1 tokens [P1 Algorithm 1 with
+    p = q; P3 acceptance equals the shared mass]."""
+    committed, rounds, ct, P = _generate(draft_layers=SHAPE.n_layers, gamma=3, n_new=10)
+    for xs, q, out in rounds:
+        assert np.abs(q - out["p"][:, :3]).max() < 1e-6
+        assert (out["n"] == 3).all()
+
+
+def test_speculative_output_is_plain_decoding_distribution():
+    """Emitted tokens of the speculative loop follow the target's own
+    distribution: over many seeds, the first generated token's histogram matches
+    the target's p at the last prompt position (chi-square)."""
+    from scipy import stats
+    from oracle import sampler as S
+
+    shape = Shape("r2", 32, 1, 2, 1, 16, 48, 8, "f32")
+    w = make_weights(shape, seed=5, norm="random", std=0.3)
+    tgt = OM.Decoder(shape, w)
+    dft = OM.Decoder(shape.with_(n_layers=1), make_weights(shape, seed=6, std=0.3))
+    B, P, g = 4000, 4, 2
+    prompt = np.tile(make_prompt(1, P, shape.vocab, seed=5), (B, 1))
+    ct, cd = tgt.new_cache(B, P + g + 2), dft.new_cache(B, P + g + 2)
+    R.prefill(tgt, ct, prompt)
+    R.prefill(dft, cd, prompt)
+    u = round_uniforms(77, 0, B, g)
+    xs, q = R.draft_round(dft, cd, prompt[:, -2], prompt[:, -1], ct.length, g, u["u_draft"])
+    out = R.verify_round(tgt, ct, prompt[:, -1], xs, q, None, u["u_acc"], u["u_res"])
+    p0 = out["p"][0, 0]
+    obs = np.bincount(out["emitted"][:, 0], minlength=shape.vocab)
+    assert stats.chisquare(obs, p0 / p0.sum() * B).pvalue > 1e-3
+    # and the draft really differs from the target (acceptance below 1)
+    assert out["n"].mean() < g
+
+
+def test_ngram_proposer():
+    ctx = [5, 6, 7, 8, 9, 1, 5, 6, 7]
+    assert ngram_propose(ctx, 3, 4) == [8, 9, 1, 5]
+    assert ngram_propose(ctx, 3, 2) == [8, 9]
+    # the most recent earlier occurrence wins
+    ctx2 = [1, 2, 3, 10, 1, 2, 3, 20, 21, 1, 2, 3]
+    assert ngram_propose(ctx2, 3, 3) == [20, 21, 1]
+    # proposals can run into the suffix itself and stop at the context end
+    ctx3 = [4, 4, 4, 4]
+    assert ngram_propose(ctx3, 3, 5) == [4]
+    assert ngram_propose([1, 2, 3, 4], 3, 4) == []
+    assert ngram_propose([1, 2, 3], 3, 4) == []
+    assert ngram_propose(ctx, 3, 0) == []

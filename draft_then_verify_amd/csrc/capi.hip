@@ -1,0 +1,284 @@
+// libspecverify C ABI: argument checks, workspace carving, and the launch
+// sequence of a verify pass / decode step on one HIP stream.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "../../include/spec_verify.h"
+#include "kernels.hpp"
+
+#define SPEC_API extern "C" __attribute__((visibility("default")))
+
+struct spec_model {
+  spec_model_cfg cfg;
+  const void* embed;
+  const void* lm_head;
+  const float* final_norm;
+  std::vector<const float*> attn_norm, mlp_norm;
+  std::vector<const void*> wqkv, wo, wgu, wd;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+spec_status fail(spec_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+#define HIP_TRY(expr)                                                                     \
+  do {                                                                                    \
+    hipError_t e_ = (expr);                                                               \
+    if (e_ != hipSuccess) return fail(SPEC_EHIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+constexpr size_t kAlign = 256;
+size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Layout {
+  size_t h, xa, xb, qkv, cs, po, pml, logits, part, csum, total;
+  int n_split;
+};
+
+Layout make_layout(const spec_model_cfg& c, int B, int m, int max_ctx) {
+  Layout L{};
+  const size_t rows = static_cast<size_t>(B) * m;
+  const size_t elt = c.dtype == SPEC_BF16 ? 2 : 4;
+  const int G = c.n_heads / c.n_kv_heads;
+  const int hq = c.n_heads * c.head_dim;
+  const int nch = sv::sampler_chunks(c.vocab);
+  L.n_split = sv::attn_num_splits(B, c.n_kv_heads, G, m, max_ctx);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += up(bytes);
+    return o;
+  };
+  L.h = take(rows * c.d_model * 4);
+  L.xa = take(rows * std::max(c.d_model, hq) * elt);
+  L.xb = take(rows * c.d_ff * elt);
+  L.qkv = take(rows * (c.n_heads + 2 * c.n_kv_heads) * c.head_dim * 4);
+  L.cs = take(rows * (c.head_dim / 2) * 8);
+  L.po = take(static_cast<size_t>(B) * c.n_heads * m * L.n_split * c.head_dim * 4);
+  L.pml = take(static_cast<size_t>(B) * c.n_heads * m * L.n_split * 8);
+  L.logits = take(rows * c.vocab * 4);
+  L.part = take(rows * nch * 8);
+  L.csum = take(static_cast<size_t>(B) * nch * 16);
+  L.total = off;
+  return L;
+}
+
+spec_status check_kv(const spec_model* M, const spec_kv* kv, int B, int m) {
+  if (!M) return fail(SPEC_EINVAL, "model is NULL");
+  if (!kv || !kv->k || !kv->v || !kv->len) return fail(SPEC_EINVAL, "kv cache pointers are NULL");
+  if (B <= 0 || m <= 0) return fail(SPEC_EINVAL, "B=%d and m=%d must be positive", B, m);
+  if (kv->B < B) return fail(SPEC_EINVAL, "kv cache holds %d sequences, pass needs %d", kv->B, B);
+  if (kv->max_ctx <= 0) return fail(SPEC_EINVAL, "kv max_ctx=%d", kv->max_ctx);
+  if (static_cast<int64_t>(B) * m > 65535 * 32) return fail(SPEC_EUNSUPPORTED, "B*m=%lld rows too many", (long long)B * m);
+  return SPEC_OK;
+}
+
+// Launch sequence of one forward pass over B x m rows.
+spec_status run_forward(const spec_model* M, const spec_kv* kv, int B, int m, const int32_t* tokens,
+                        const int32_t* last, const int32_t* draft, float* logits, const Layout& L, char* ws,
+                        hipStream_t s) {
+  const spec_model_cfg& c = M->cfg;
+  const bool bf16 = c.dtype == SPEC_BF16;
+  const int rows = B * m;
+  const int d = c.d_model, H = c.n_heads, Hkv = c.n_kv_heads, hd = c.head_dim, F = c.d_ff, V = c.vocab;
+  const int qkv_rows = (H + 2 * Hkv) * hd;
+  float* h = reinterpret_cast<float*>(ws + L.h);
+  void* xa = ws + L.xa;
+  void* xb = ws + L.xb;
+  float* qkv = reinterpret_cast<float*>(ws + L.qkv);
+  float2* cs = reinterpret_cast<float2*>(ws + L.cs);
+  float* po = reinterpret_cast<float*>(ws + L.po);
+  float2* pml = reinterpret_cast<float2*>(ws + L.pml);
+
+  HIP_TRY(sv::launch_embed(bf16, M->embed, V, d, tokens, last, draft, kv->len, B, m, hd, c.rope_theta, h, cs, s));
+  for (int l = 0; l < c.n_layers; ++l) {
+    HIP_TRY(sv::launch_rmsnorm(bf16, h, M->attn_norm[l], rows, d, c.rms_eps, xa, s));
+    HIP_TRY(sv::launch_gemv(bf16, sv::EPI_STORE, M->wqkv[l], xa, rows, qkv_rows, d, qkv, qkv_rows, nullptr, 0, s));
+    HIP_TRY(sv::launch_rope_append(bf16, qkv, cs, kv->len, B, m, H, Hkv, hd, kv->k, kv->v, l, kv->B, kv->max_ctx, s));
+    HIP_TRY(sv::launch_attention(bf16, qkv, kv->k, kv->v, kv->len, B, m, H, Hkv, hd, l, kv->B, kv->max_ctx, L.n_split,
+                                 po, pml, xa, s));
+    HIP_TRY(sv::launch_gemv(bf16, sv::EPI_RESID, M->wo[l], xa, rows, d, H * hd, h, d, nullptr, 0, s));
+    HIP_TRY(sv::launch_rmsnorm(bf16, h, M->mlp_norm[l], rows, d, c.rms_eps, xa, s));
+    HIP_TRY(sv::launch_gemv(bf16, sv::EPI_SWIGLU, M->wgu[l], xa, rows, F, d, nullptr, 0, xb, F, s));
+    HIP_TRY(sv::launch_gemv(bf16, sv::EPI_RESID, M->wd[l], xb, rows, d, F, h, d, nullptr, 0, s));
+  }
+  if (logits) {
+    HIP_TRY(sv::launch_rmsnorm(bf16, h, M->final_norm, rows, d, c.rms_eps, xa, s));
+    HIP_TRY(sv::launch_gemv(bf16, sv::EPI_STORE, M->lm_head, xa, rows, V, d, logits, V, nullptr, 0, s));
+  }
+  return SPEC_OK;
+}
+
+}  // namespace
+
+SPEC_API const char* spec_last_error(void) { return g_err.c_str(); }
+
+SPEC_API spec_status spec_model_create(const spec_model_cfg* cfg, const spec_weights* w, spec_model** out) {
+  if (!cfg || !w || !out) return fail(SPEC_EINVAL, "NULL argument");
+  *out = nullptr;
+  const spec_model_cfg& c = *cfg;
+  if (c.d_model <= 0 || c.n_layers <= 0 || c.n_heads <= 0 || c.n_kv_heads <= 0 || c.d_ff <= 0 || c.vocab <= 0)
+    return fail(SPEC_EINVAL, "non-positive dimension in model config");
+  if (c.dtype != SPEC_F32 && c.dtype != SPEC_BF16) return fail(SPEC_EINVAL, "dtype %d", c.dtype);
+  if (c.head_dim != 64 && c.head_dim != 128) return fail(SPEC_EUNSUPPORTED, "head_dim %d (64 or 128)", c.head_dim);
+  if (c.n_heads % c.n_kv_heads) return fail(SPEC_EINVAL, "n_heads %% n_kv_heads != 0");
+  const int vec = c.dtype == SPEC_BF16 ? 8 : 4;
+  if (c.d_model % vec || c.d_ff % vec || (c.n_heads * c.head_dim) % vec)
+    return fail(SPEC_EINVAL, "d_model, d_ff and n_heads*head_dim must be multiples of %d", vec);
+  if (!(c.rope_theta > 0.f) || !(c.rms_eps >= 0.f)) return fail(SPEC_EINVAL, "rope_theta / rms_eps");
+  if (!w->embed || !w->lm_head || !w->final_norm || !w->attn_norm || !w->wqkv || !w->wo || !w->mlp_norm || !w->wgu ||
+      !w->wd)
+    return fail(SPEC_EINVAL, "NULL weight pointer");
+  if (!aligned16(w->embed) || !aligned16(w->lm_head)) return fail(SPEC_EINVAL, "embed/lm_head not 16-byte aligned");
+  for (int l = 0; l < c.n_layers; ++l) {
+    if (!w->attn_norm[l] || !w->wqkv[l] || !w->wo[l] || !w->mlp_norm[l] || !w->wgu[l] || !w->wd[l])
+      return fail(SPEC_EINVAL, "NULL weight pointer in layer %d", l);
+    if (!aligned16(w->wqkv[l]) || !aligned16(w->wo[l]) || !aligned16(w->wgu[l]) || !aligned16(w->wd[l]))
+      return fail(SPEC_EINVAL, "layer %d weights not 16-byte aligned", l);
+  }
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SPEC_EDEVICE, "no HIP device: %s", hipGetErrorString(e));
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return fail(SPEC_EDEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+  if (std::string(prop.gcnArchName).rfind("gfx950", 0) != 0)
+    return fail(SPEC_EDEVICE, "device %d is %s, this library is built for gfx950", dev, prop.gcnArchName);
+  spec_model* M = new spec_model;
+  M->cfg = c;
+  M->embed = w->embed;
+  M->lm_head = w->lm_head;
+  M->final_norm = w->final_norm;
+  M->attn_norm.assign(w->attn_norm, w->attn_norm + c.n_layers);
+  M->mlp_norm.assign(w->mlp_norm, w->mlp_norm + c.n_layers);
+  M->wqkv.assign(w->wqkv, w->wqkv + c.n_layers);
+  M->wo.assign(w->wo, w->wo + c.n_layers);
+  M->wgu.assign(w->wgu, w->wgu + c.n_layers);
+  M->wd.assign(w->wd, w->wd + c.n_layers);
+  *out = M;
+  return SPEC_OK;
+}
+
+SPEC_API void spec_model_destroy(spec_model* model) { delete model; }
+
+SPEC_API size_t spec_workspace_bytes(const spec_model* model, int32_t B, int32_t m, int32_t max_ctx) {
+  if (!model || B <= 0 || m <= 0 || max_ctx <= 0) return 0;
+  return make_layout(model->cfg, B, m, max_ctx).total;
+}
+
+SPEC_API size_t spec_sampler_workspace_bytes(int64_t rows, int32_t B, int32_t vocab) {
+  if (rows < 0 || B < 0 || vocab <= 0) return 0;
+  const int nch = sv::sampler_chunks(vocab);
+  return up(static_cast<size_t>(rows) * nch * 8) + up(static_cast<size_t>(B) * nch * 16);
+}
+
+SPEC_API spec_status spec_verify_forward(const spec_model* model, const spec_kv* kv, int32_t B, int32_t m,
+                                         const int32_t* tokens, float* logits, void* ws, size_t ws_bytes,
+                                         hipStream_t stream) {
+  spec_status st = check_kv(model, kv, B, m);
+  if (st != SPEC_OK) return st;
+  if (!tokens) return fail(SPEC_EINVAL, "tokens is NULL");
+  const Layout L = make_layout(model->cfg, B, m, kv->max_ctx);
+  if (!ws || ws_bytes < L.total) return fail(SPEC_ENOMEM, "workspace %zu bytes < %zu needed", ws_bytes, L.total);
+  return run_forward(model, kv, B, m, tokens, nullptr, nullptr, logits, L, static_cast<char*>(ws), stream);
+}
+
+namespace {
+spec_status softmax_rows(const float* logits, int64_t rows, int V, float T, float* probs, float2* part,
+                         hipStream_t s) {
+  const int nch = sv::sampler_chunks(V);
+  for (int64_t r0 = 0; r0 < rows; r0 += 65535) {
+    const int64_t nr = std::min<int64_t>(65535, rows - r0);
+    HIP_TRY(sv::launch_row_partials(logits + r0 * V, nr, V, T, part + r0 * nch, s));
+    if (probs) HIP_TRY(sv::launch_softmax_write(logits + r0 * V, nr, V, T, part + r0 * nch, probs + r0 * V, s));
+  }
+  return SPEC_OK;
+}
+}  // namespace
+
+SPEC_API spec_status spec_softmax_pq(const float* logits, int64_t rows, int32_t vocab, float temperature, float* probs,
+                                     void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!logits || !probs) return fail(SPEC_EINVAL, "NULL logits/probs");
+  if (rows < 0 || vocab <= 0) return fail(SPEC_EINVAL, "rows=%lld vocab=%d", (long long)rows, vocab);
+  if (!(temperature > 0.f)) return fail(SPEC_EINVAL, "temperature must be > 0");
+  if (rows == 0) return SPEC_OK;
+  const size_t need = spec_sampler_workspace_bytes(rows, 0, vocab);
+  if (!ws || ws_bytes < need) return fail(SPEC_ENOMEM, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  return softmax_rows(logits, rows, vocab, temperature, probs, static_cast<float2*>(ws), stream);
+}
+
+namespace {
+spec_status check_sampler_args(int B, int gamma, int V, const int32_t* draft, const float* u_acc, const float* u_res,
+                               const int32_t* n_accepted, const int32_t* emitted) {
+  if (B <= 0 || B > 65535) return fail(SPEC_EINVAL, "B=%d (1..65535)", B);
+  if (gamma < 0 || gamma > 64) return fail(SPEC_EINVAL, "gamma=%d (0..64)", gamma);
+  if (V <= 0 || V >= (1 << 23)) return fail(SPEC_EINVAL, "vocab=%d (1..2^23-1)", V);
+  if (gamma > 0 && (!draft || !u_acc)) return fail(SPEC_EINVAL, "draft/u_acc NULL with gamma > 0");
+  if (!u_res || !n_accepted || !emitted) return fail(SPEC_EINVAL, "u_res/n_accepted/emitted NULL");
+  return SPEC_OK;
+}
+}  // namespace
+
+SPEC_API spec_status spec_reject_sample(int32_t B, int32_t gamma, int32_t vocab, const float* p, const float* q,
+                                        const int32_t* draft, const int32_t* n_draft, const float* u_acc,
+                                        const float* u_res, int32_t* n_accepted, int32_t* emitted, void* ws,
+                                        size_t ws_bytes, hipStream_t stream) {
+  spec_status st = check_sampler_args(B, gamma, vocab, draft, u_acc, u_res, n_accepted, emitted);
+  if (st != SPEC_OK) return st;
+  if (!p) return fail(SPEC_EINVAL, "p is NULL");
+  const size_t need = spec_sampler_workspace_bytes(0, B, vocab);
+  if (!ws || ws_bytes < need) return fail(SPEC_ENOMEM, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  HIP_TRY(sv::launch_reject(B, gamma, vocab, p, nullptr, nullptr, 1.f, q, draft, n_draft, u_acc, u_res, n_accepted,
+                            emitted, nullptr, static_cast<unsigned long long*>(ws), stream));
+  return SPEC_OK;
+}
+
+SPEC_API spec_status spec_decode_step(const spec_model* target, const spec_kv* kv, int32_t B, int32_t gamma,
+                                      float temperature, const int32_t* last_tok, const int32_t* draft,
+                                      const int32_t* n_draft, const float* q, const float* u_acc, const float* u_res,
+                                      int32_t* n_accepted, int32_t* emitted, float* logits_out, void* ws,
+                                      size_t ws_bytes, hipStream_t stream) {
+  const int m = gamma + 1;
+  spec_status st = check_kv(target, kv, B, m);
+  if (st != SPEC_OK) return st;
+  st = check_sampler_args(B, gamma, target->cfg.vocab, draft, u_acc, u_res, n_accepted, emitted);
+  if (st != SPEC_OK) return st;
+  if (!last_tok) return fail(SPEC_EINVAL, "last_tok is NULL");
+  if (!(temperature > 0.f)) return fail(SPEC_EINVAL, "temperature must be > 0");
+  const Layout L = make_layout(target->cfg, B, m, kv->max_ctx);
+  if (!ws || ws_bytes < L.total) return fail(SPEC_ENOMEM, "workspace %zu bytes < %zu needed", ws_bytes, L.total);
+  char* w = static_cast<char*>(ws);
+  float* logits = logits_out ? logits_out : reinterpret_cast<float*>(w + L.logits);
+  st = run_forward(target, kv, B, m, nullptr, last_tok, draft, logits, L, w, stream);
+  if (st != SPEC_OK) return st;
+  const int V = target->cfg.vocab;
+  float2* part = reinterpret_cast<float2*>(w + L.part);
+  st = softmax_rows(logits, static_cast<int64_t>(B) * m, V, temperature, nullptr, part, stream);
+  if (st != SPEC_OK) return st;
+  HIP_TRY(sv::launch_reject(B, gamma, V, nullptr, logits, part, temperature, q, draft, n_draft, u_acc, u_res,
+                            n_accepted, emitted, kv->len, reinterpret_cast<unsigned long long*>(w + L.csum), stream));
+  return SPEC_OK;
+}
+
+SPEC_API spec_status spec_kv_set_len(const spec_kv* kv, int32_t B, const int32_t* src, int32_t add,
+                                     hipStream_t stream) {
+  if (!kv || !kv->len) return fail(SPEC_EINVAL, "kv/len is NULL");
+  if (B <= 0 || B > kv->B) return fail(SPEC_EINVAL, "B=%d outside 1..%d", B, kv->B);
+  HIP_TRY(sv::launch_kv_len(kv->len, src, add, B, stream));
+  return SPEC_OK;
+}

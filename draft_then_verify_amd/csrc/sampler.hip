@@ -1,0 +1,308 @@
+// Vocab-wide softmax and the rejection sampler of a verify round.
+//
+// The rule (first page, "What one iteration actually does", Algorithm 1; and
+// "How Speculative Decoding Works", "Why the output doesn't change"):
+//   accept x_i while u_i * q_i(x_i) <= p_i(x_i)  (reject iff u > p/q, written
+//   without the division, float32); n = the first failure or n_draft;
+//   row j = n: r = max(0, p_j - q_j) after a rejection, r = p_j (bonus) when
+//   every draft passed; t ~ r / sum(r).
+//
+// Rows of 151936 float32 entries (608 KB) do not fit in LDS, so a row is cut
+// in 4096-entry chunks:
+//   1. row_partials: per (row, chunk) the max and sum of exp(l/T - max).
+//      Every consumer merges the chunk pairs in chunk order, so the row
+//      statistics -- and hence every p(v) = exp(l_v/T - M) / Z -- are bitwise
+//      the same wherever they are used (materialised or fused).
+//   2. reject_chunks: per (sequence, chunk) the accept scan (one thread), then
+//      the chunk sums of w = floor(r * 2^40) for the residual row and for p
+//      (the all-zero-residual fallback).  Integer sums are exact, so any
+//      reduction order gives the same S.
+//   3. reject_final: per sequence, T = floor(k * S / 2^24) from k = u * 2^24;
+//      the chunk whose running sum first exceeds T; an in-chunk scan finds the
+//      smallest v with inclusive prefix > T.  Then the outputs and the KV
+//      commit len += n + 1.
+#include <math.h>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace sv {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kChunk = 4096;
+constexpr int kPer = kChunk / kThreads;
+constexpr float kTwo40 = 1099511627776.0f;  // 2^40
+constexpr float kTwo24 = 16777216.0f;       // 2^24
+
+// Row statistics (M, Z) from the chunk partials, merged in chunk order.
+__device__ __forceinline__ float2 merge_stats(const float2* pr, int nch) {
+  float M = -INFINITY;
+  for (int c = 0; c < nch; ++c) M = fmaxf(M, pr[c].x);
+  float Z = 0.f;
+  for (int c = 0; c < nch; ++c) Z = fmaf(pr[c].y, expf(__fsub_rn(pr[c].x, M)), Z);
+  return make_float2(M, Z);
+}
+
+// Where a probability row comes from.
+struct RowSrc {
+  const float* p;        // materialised rows, or nullptr
+  const float* logits;   // fused: logits + partials
+  const float2* part;
+  float T;
+  int nch;
+  int V;
+  __device__ __forceinline__ float2 stats(int64_t row) const {
+    return p ? make_float2(0.f, 1.f) : merge_stats(part + row * nch, nch);
+  }
+  __device__ __forceinline__ float prob(int64_t row, int v, float2 st) const {
+    if (p) return p[row * V + v];
+    return __fdiv_rn(expf(__fsub_rn(__fdiv_rn(logits[row * V + v], T), st.x)), st.y);
+  }
+};
+
+__device__ __forceinline__ unsigned long long fixed_weight(float r) {
+  return static_cast<unsigned long long>(__fmul_rn(r, kTwo40));
+}
+
+// Accept scan for sequence b: number of leading drafts that pass.
+__device__ int accepted_length(const RowSrc& src, int b, int gamma, int nd, const float* q, const int32_t* draft,
+                               const float* u_acc) {
+  for (int i = 0; i < nd; ++i) {
+    const int x = draft[b * gamma + i];
+    if (x < 0 || x >= src.V) return i;
+    const int64_t row = static_cast<int64_t>(b) * (gamma + 1) + i;
+    const float px = src.prob(row, x, src.stats(row));
+    const float qx = q ? q[(static_cast<int64_t>(b) * gamma + i) * src.V + x] : 1.f;
+    if (!(__fmul_rn(u_acc[b * gamma + i], qx) <= px)) return i;
+  }
+  return nd;
+}
+
+__device__ __forceinline__ int n_valid(const int32_t* n_draft, int b, int gamma) {
+  return n_draft ? min(max(n_draft[b], 0), gamma) : gamma;
+}
+
+// The sampled row at entry v: residual max(0, p - q) or p itself.
+__device__ __forceinline__ float sample_mass(float pv, bool use_p, const float* qrow, int x_rej, int v) {
+  if (use_p) return pv;
+  const float qv = qrow ? qrow[v] : (v == x_rej ? 1.f : 0.f);
+  return fmaxf(0.f, __fsub_rn(pv, qv));
+}
+
+__global__ __launch_bounds__(kThreads) void row_partials_kernel(const float* __restrict__ logits, int V, float T,
+                                                                int nch, float2* __restrict__ part) {
+  __shared__ float red[kThreads / kWave];
+  const int64_t row = blockIdx.y;
+  const int c = blockIdx.x;
+  const float* l = logits + row * V;
+  float x[kPer];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const int v = c * kChunk + e * kThreads + threadIdx.x;
+    x[e] = (v < V) ? __fdiv_rn(l[v], T) : -INFINITY;
+    mx = fmaxf(mx, x[e]);
+  }
+  mx = block_max<kThreads>(mx, red);
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) s += (x[e] == -INFINITY) ? 0.f : expf(__fsub_rn(x[e], mx));
+  s = block_sum<kThreads>(s, red);
+  if (threadIdx.x == 0) part[row * nch + c] = make_float2(mx, s);
+}
+
+__global__ __launch_bounds__(kThreads) void softmax_write_kernel(const float* __restrict__ logits, int V, float T,
+                                                                 int nch, const float2* __restrict__ part,
+                                                                 float* __restrict__ probs) {
+  __shared__ float2 st_sh;
+  const int64_t row = blockIdx.y;
+  const int c = blockIdx.x;
+  if (threadIdx.x == 0) st_sh = merge_stats(part + row * nch, nch);
+  __syncthreads();
+  const float2 st = st_sh;
+  RowSrc src{nullptr, logits, part, T, nch, V};
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const int v = c * kChunk + e * kThreads + threadIdx.x;
+    if (v < V) probs[row * V + v] = src.prob(row, v, st);
+  }
+}
+
+struct RejectArgs {
+  RowSrc src;
+  int gamma;
+  const float* q;
+  const int32_t* draft;
+  const int32_t* n_draft;
+  const float* u_acc;
+  const float* u_res;
+  int32_t* n_accepted;
+  int32_t* emitted;
+  int32_t* len_commit;
+  unsigned long long* csum;  // [B][nch][2]: residual sum, p sum
+};
+
+__global__ __launch_bounds__(kThreads) void reject_chunks_kernel(RejectArgs a) {
+  __shared__ int n_sh;
+  __shared__ float2 st_sh;
+  __shared__ unsigned long long red[kThreads / kWave];
+  const int c = blockIdx.x, b = blockIdx.y;
+  const RowSrc& src = a.src;
+  const int nd = n_valid(a.n_draft, b, a.gamma);
+  if (threadIdx.x == 0) {
+    const int n = accepted_length(src, b, a.gamma, nd, a.q, a.draft, a.u_acc);
+    n_sh = n;
+    st_sh = src.stats(static_cast<int64_t>(b) * (a.gamma + 1) + n);
+  }
+  __syncthreads();
+  const int n = n_sh;
+  const float2 st = st_sh;
+  const bool bonus = n == nd;
+  const int64_t row = static_cast<int64_t>(b) * (a.gamma + 1) + n;
+  const int x_rej = bonus ? -1 : a.draft[b * a.gamma + n];
+  const float* qrow = (!bonus && a.q) ? a.q + (static_cast<int64_t>(b) * a.gamma + n) * src.V : nullptr;
+  unsigned long long wr = 0, wp = 0;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const int v = c * kChunk + e * kThreads + threadIdx.x;
+    if (v < src.V) {
+      const float pv = src.prob(row, v, st);
+      wr += fixed_weight(sample_mass(pv, bonus, qrow, x_rej, v));
+      wp += fixed_weight(pv);
+    }
+  }
+  wr = block_sum_u64<kThreads>(wr, red);
+  wp = block_sum_u64<kThreads>(wp, red);
+  if (threadIdx.x == 0) {
+    a.csum[(static_cast<size_t>(b) * src.nch + c) * 2 + 0] = wr;
+    a.csum[(static_cast<size_t>(b) * src.nch + c) * 2 + 1] = wp;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void reject_final_kernel(RejectArgs a) {
+  __shared__ int n_sh, cstar_sh, use_p_sh, tok_sh;
+  __shared__ float2 st_sh;
+  __shared__ unsigned long long base_sh, T_sh;
+  __shared__ unsigned long long scan[kThreads];
+  const int b = blockIdx.x;
+  const RowSrc& src = a.src;
+  const int nch = src.nch;
+  const int nd = n_valid(a.n_draft, b, a.gamma);
+  if (threadIdx.x == 0) {
+    const int n = accepted_length(src, b, a.gamma, nd, a.q, a.draft, a.u_acc);
+    const unsigned long long* cs = a.csum + static_cast<size_t>(b) * nch * 2;
+    unsigned long long Sr = 0, Sp = 0;
+    for (int c = 0; c < nch; ++c) {
+      Sr += cs[2 * c];
+      Sp += cs[2 * c + 1];
+    }
+    const int use_p = (n == nd) || Sr == 0;
+    const unsigned long long S = use_p ? Sp : Sr;
+    float uk = __fmul_rn(a.u_res[b], kTwo24);
+    uk = fminf(fmaxf(uk, 0.f), kTwo24 - 1.f);
+    const unsigned long long k = static_cast<unsigned long long>(uk);
+    const unsigned long long T = (S >> 24) * k + (((S & 0xFFFFFFull) * k) >> 24);
+    unsigned long long acc = 0;
+    int cstar = nch - 1;
+    for (int c = 0; c < nch; ++c) {
+      const unsigned long long w = cs[2 * c + (use_p ? 1 : 0)];
+      if (acc + w > T) {
+        cstar = c;
+        break;
+      }
+      acc += w;
+    }
+    n_sh = n;
+    use_p_sh = use_p;
+    cstar_sh = cstar;
+    base_sh = acc;
+    T_sh = T;
+    tok_sh = -1;
+    st_sh = src.stats(static_cast<int64_t>(b) * (a.gamma + 1) + n);
+  }
+  __syncthreads();
+  const int n = n_sh;
+  const bool use_p = use_p_sh;
+  const int64_t row = static_cast<int64_t>(b) * (a.gamma + 1) + n;
+  const int x_rej = (n == nd) ? -1 : a.draft[b * a.gamma + n];
+  const float* qrow = (n != nd && a.q) ? a.q + (static_cast<int64_t>(b) * a.gamma + n) * src.V : nullptr;
+  const float2 st = st_sh;
+  const int v0 = cstar_sh * kChunk + threadIdx.x * kPer;
+  unsigned long long w[kPer];
+  unsigned long long tsum = 0;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const int v = v0 + e;
+    w[e] = (v < src.V) ? fixed_weight(sample_mass(src.prob(row, v, st), use_p, qrow, x_rej, v)) : 0ull;
+    tsum += w[e];
+  }
+  scan[threadIdx.x] = tsum;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long run = 0;
+    for (int i = 0; i < kThreads; ++i) {
+      const unsigned long long x = scan[i];
+      scan[i] = run;
+      run += x;
+    }
+  }
+  __syncthreads();
+  const unsigned long long T = T_sh;
+  unsigned long long run = base_sh + scan[threadIdx.x];
+  if (run <= T && T < run + tsum) {
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      run += w[e];
+      if (run > T) {
+        tok_sh = v0 + e;
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int tok = tok_sh;
+    if (tok < 0) tok = 0;  // unreachable when S > 0 and k < 2^24
+    a.n_accepted[b] = n;
+    for (int j = 0; j <= a.gamma; ++j)
+      a.emitted[b * (a.gamma + 1) + j] = j < n ? a.draft[b * a.gamma + j] : (j == n ? tok : -1);
+    if (a.len_commit) a.len_commit[b] += n + 1;
+  }
+}
+
+}  // namespace
+
+int sampler_chunks(int vocab) { return (vocab + kChunk - 1) / kChunk; }
+
+hipError_t launch_row_partials(const float* logits, int64_t rows, int vocab, float temperature, float2* part,
+                               hipStream_t s) {
+  const int nch = sampler_chunks(vocab);
+  hipLaunchKernelGGL(row_partials_kernel, dim3(nch, static_cast<unsigned>(rows)), dim3(kThreads), 0, s, logits, vocab,
+                     temperature, nch, part);
+  return hipGetLastError();
+}
+
+hipError_t launch_softmax_write(const float* logits, int64_t rows, int vocab, float temperature, const float2* part,
+                                float* probs, hipStream_t s) {
+  const int nch = sampler_chunks(vocab);
+  hipLaunchKernelGGL(softmax_write_kernel, dim3(nch, static_cast<unsigned>(rows)), dim3(kThreads), 0, s, logits,
+                     vocab, temperature, nch, part, probs);
+  return hipGetLastError();
+}
+
+hipError_t launch_reject(int B, int gamma, int vocab, const float* p, const float* logits, const float2* part,
+                         float temperature, const float* q, const int32_t* draft, const int32_t* n_draft,
+                         const float* u_acc, const float* u_res, int32_t* n_accepted, int32_t* emitted,
+                         int32_t* len_commit, unsigned long long* csum, hipStream_t s) {
+  const int nch = sampler_chunks(vocab);
+  RejectArgs a{RowSrc{p, logits, part, temperature, nch, vocab}, gamma, q, draft, n_draft, u_acc, u_res, n_accepted,
+               emitted, len_commit, csum};
+  hipLaunchKernelGGL(reject_chunks_kernel, dim3(nch, B), dim3(kThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(reject_final_kernel, dim3(B), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace sv

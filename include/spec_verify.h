@@ -1,0 +1,188 @@
+/*
+ * spec_verify.h -- C ABI of the MI355X verify hot path of speculative
+ * (draft-then-verify) decoding.
+ *
+ * What the library computes, by the pages that define it:
+ *   - One round of Algorithm 1 as quoted on "Speculative Decoding Spends
+ *     Arithmetic You May Not Have" (section "What one iteration actually
+ *     does"): the target scores [last committed token, x_1 .. x_gamma] in ONE
+ *     forward pass, giving p_1 .. p_{gamma+1}; drafts are accepted in order
+ *     while u_i * q_i(x_i) <= p_i(x_i); the first rejection is replaced by a
+ *     draw from norm(max(0, p - q)); when all gamma drafts pass, a bonus token
+ *     is drawn from p_{gamma+1}.  One round emits 1 .. gamma+1 tokens.
+ *   - The rule's exactness argument ("How Speculative Decoding Works (and When
+ *     It Doesn't)", section "Why the output doesn't change") is what the
+ *     residual and the bonus preserve.
+ *   - The draw "t ~ p'" is a fixed-point inverse CDF: w_v = floor(r_v * 2^40),
+ *     S = sum w, T = floor(k * S / 2^24) with k = u * 2^24, t = the smallest v
+ *     whose inclusive prefix sum exceeds T.  Integer sums make the draw
+ *     independent of reduction order.
+ *
+ * Conventions for every call below:
+ *   - Array arguments are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees or keeps them beyond the call; a model only
+ *     borrows its weight pointers for its lifetime.
+ *   - Calls are asynchronous on `stream`; results are valid after the stream
+ *     is synchronised.  Host-side argument checks run before any launch.
+ *   - Return value: SPEC_OK (0) or a negative spec_status; spec_last_error()
+ *     returns a thread-local message describing the last failure.
+ *   - Identical inputs give bitwise identical outputs (no floating-point
+ *     atomics; every reduction has a fixed order).
+ *   - Token ids outside [0, vocab) are never used to address memory: they are
+ *     clamped for the embedding gather and count as rejected drafts in the
+ *     sampler.  A pass whose positions would reach max_ctx writes and reads no
+ *     KV row at or beyond max_ctx; its results are then undefined.
+ *   - Uniforms are float32 values in [0, 1); the exact draw above assumes they
+ *     are multiples of 2^-24 (any other value is truncated to that grid).
+ *
+ * Data layout:
+ *   - Weights are row-major [out][in] in the model dtype (float32 or bf16);
+ *     norm gains are float32.
+ *   - KV cache: k and v are [n_layers][B][n_kv_heads][max_ctx][head_dim] in the
+ *     model dtype; len[B] (int32, device) is the number of committed positions
+ *     of each sequence.  A forward pass over m rows writes positions
+ *     len[b] .. len[b]+m-1 and does not change len.
+ *   - Logits and probabilities are float32, row-major [rows][vocab]; the rows
+ *     of a verify pass are ordered [b][i] (sequence-major).
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum spec_status {
+  SPEC_OK = 0,
+  SPEC_EINVAL = -1,        /* invalid argument (checked on the host before any launch) */
+  SPEC_ENOMEM = -2,        /* workspace smaller than the matching *_bytes() query */
+  SPEC_EHIP = -3,          /* a HIP runtime call or a kernel launch failed */
+  SPEC_EUNSUPPORTED = -4,  /* shape the kernels do not handle (see each call) */
+  SPEC_EDEVICE = -5        /* no usable gfx950 device */
+} spec_status;
+
+typedef enum spec_dtype { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
+
+/* Decoder shape.  Llama-style: pre-norm RMSNorm, rotate-half RoPE, grouped-
+ * query attention (query head h reads KV head h / (n_heads / n_kv_heads)),
+ * SwiGLU MLP, no biases.  Requirements: head_dim in {64, 128}; n_heads a
+ * multiple of n_kv_heads; d_model, d_ff and n_heads*head_dim multiples of 8. */
+typedef struct spec_model_cfg {
+  int32_t d_model, n_layers, n_heads, n_kv_heads, head_dim, d_ff, vocab;
+  int32_t dtype; /* spec_dtype of weights, embedding, LM head and KV cache */
+  float rope_theta, rms_eps;
+} spec_model_cfg;
+
+/* Device pointers of one model's weights.  The per-layer arrays are HOST
+ * arrays of n_layers device pointers; they are copied at spec_model_create. */
+typedef struct spec_weights {
+  const void* embed;              /* [vocab][d_model] */
+  const void* lm_head;            /* [vocab][d_model]; may equal embed (tied) */
+  const float* final_norm;        /* [d_model] */
+  const float* const* attn_norm;  /* [n_layers] x [d_model] */
+  const void* const* wqkv;        /* [n_layers] x [(H + 2 Hkv) hd][d_model]: q rows, k rows, v rows */
+  const void* const* wo;          /* [n_layers] x [d_model][H hd] */
+  const float* const* mlp_norm;   /* [n_layers] x [d_model] */
+  const void* const* wgu;         /* [n_layers] x [2 d_ff][d_model]: gate rows, then up rows */
+  const void* const* wd;          /* [n_layers] x [d_model][d_ff] */
+} spec_weights;
+
+/* A per-sequence contiguous KV cache (layout above). */
+typedef struct spec_kv {
+  void* k;
+  void* v;
+  int32_t* len; /* [B] device */
+  int32_t B;
+  int32_t max_ctx;
+} spec_kv;
+
+typedef struct spec_model spec_model;
+
+/* Create a model handle over borrowed weights.  A self-speculative drafter
+ * (the target's first layers, final norm and head) is a second handle with a
+ * smaller n_layers over the same pointers.  Errors: SPEC_EINVAL (shape),
+ * SPEC_EUNSUPPORTED (head_dim), SPEC_EDEVICE (no gfx950 device current). */
+spec_status spec_model_create(const spec_model_cfg* cfg, const spec_weights* w, spec_model** out);
+void spec_model_destroy(spec_model* model);
+
+/* Workspace bytes a verify pass / decode step of B sequences x m rows needs,
+ * for a KV cache of max_ctx positions (the context split of attention depends
+ * on it).  0 on invalid arguments. */
+size_t spec_workspace_bytes(const spec_model* model, int32_t B, int32_t m, int32_t max_ctx);
+
+/* Workspace bytes spec_softmax_pq / spec_reject_sample need for `rows`
+ * probability rows of `vocab` entries and B sequences. */
+size_t spec_sampler_workspace_bytes(int64_t rows, int32_t B, int32_t vocab);
+
+/* The verify pass ("Run Mp in parallel" of Algorithm 1; the target "evaluates
+ * all gamma+1 positions in a single forward pass", first page, mechanism
+ * paragraph): one forward over B sequences x m rows at positions
+ * len[b] .. len[b]+m-1, streaming every weight once per block of 8 rows.
+ *   tokens  [B][m] int32 input ids.
+ *   logits  [B][m][vocab] float32 output, or NULL to skip the LM head
+ *           (prefill).
+ * Writes the m new K/V rows of every layer; len is unchanged (advance it with
+ * spec_kv_set_len).  Errors: SPEC_EINVAL (null/size mismatch, kv->B < B),
+ * SPEC_ENOMEM (ws_bytes < spec_workspace_bytes), SPEC_EHIP. */
+spec_status spec_verify_forward(const spec_model* model, const spec_kv* kv, int32_t B, int32_t m,
+                                const int32_t* tokens, float* logits, void* ws, size_t ws_bytes,
+                                hipStream_t stream);
+
+/* Target/draft probabilities p = softmax(logits / temperature) over `vocab`
+ * entries for `rows` rows ("How Speculative Decoding Works", section "Why the
+ * output doesn't change": p and q are the two models' next-token
+ * distributions).  float32, max-subtracted; the same row statistics the fused
+ * decode step uses, so p is bitwise what spec_decode_step samples from.
+ * temperature > 0.  Errors: SPEC_EINVAL, SPEC_ENOMEM, SPEC_EHIP. */
+spec_status spec_softmax_pq(const float* logits, int64_t rows, int32_t vocab, float temperature,
+                            float* probs, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* The accept / resample / bonus rule on materialised rows (Algorithm 1 lines
+ * "Determine the number of accepted guesses" and "Adjust the distribution").
+ *   p        [B][gamma+1][vocab] target probabilities.
+ *   q        [B][gamma][vocab] draft probabilities, or NULL for a one-hot
+ *            draft (q_i(x_i) = 1, e.g. n-gram lookup).
+ *   draft    [B][gamma] drafted ids x_1 .. x_gamma.
+ *   n_draft  [B] number of valid drafts per sequence (clamped to [0, gamma]),
+ *            or NULL for gamma.
+ *   u_acc    [B][gamma], u_res [B] uniforms.
+ *   n_accepted [B] out: n.   emitted [B][gamma+1] out: x_1 .. x_n, t, then -1.
+ * gamma = 0 is a plain draw t ~ p (draft sampling, plain decoding).
+ * Errors: SPEC_EINVAL, SPEC_ENOMEM, SPEC_EHIP. */
+spec_status spec_reject_sample(int32_t B, int32_t gamma, int32_t vocab, const float* p, const float* q,
+                               const int32_t* draft, const int32_t* n_draft, const float* u_acc,
+                               const float* u_res, int32_t* n_accepted, int32_t* emitted, void* ws,
+                               size_t ws_bytes, hipStream_t stream);
+
+/* One whole verify step: assemble [last_tok, draft] (B x (gamma+1) rows),
+ * run the verify pass, the fused softmax + accept/resample/bonus without
+ * materialising p, and commit the KV cache: len[b] += n[b] + 1 (the last
+ * committed token and the n accepted drafts stay cached; "rejection is
+ * prefix-truncating", first page).  Arguments as in spec_reject_sample;
+ * logits_out [B][gamma+1][vocab] receives the logits when non-NULL.
+ * Errors: as spec_verify_forward. */
+spec_status spec_decode_step(const spec_model* target, const spec_kv* kv, int32_t B, int32_t gamma,
+                             float temperature, const int32_t* last_tok, const int32_t* draft,
+                             const int32_t* n_draft, const float* q, const float* u_acc,
+                             const float* u_res, int32_t* n_accepted, int32_t* emitted,
+                             float* logits_out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* KV length bookkeeping: len[b] = (src ? src[b] : len[b]) + add for b < B.
+ * Used to advance after prefill / draft passes and to rewind a drafter to the
+ * target's length.  Errors: SPEC_EINVAL, SPEC_EHIP. */
+spec_status spec_kv_set_len(const spec_kv* kv, int32_t B, const int32_t* src, int32_t add,
+                            hipStream_t stream);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* spec_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

@@ -1,0 +1,68 @@
+"""The C ABI library: it loads, exports every symbol the header declares, and
+its host-side argument checks reject bad calls before any launch (no GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from draft_then_verify_amd import binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bd.LIB_PATH):
+        from draft_then_verify_amd import build
+        build.build()
+    return bd.load_library()
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "spec_verify.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(spec_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = header_functions()
+    assert len(names) == 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(bd.EXPORTS) == names
+
+
+def test_sampler_workspace_size(lib):
+    # 151936 entries -> 38 chunks of 4096; 8 bytes per (row, chunk), 16 per (sequence, chunk)
+    assert bd.spec_sampler_workspace_bytes(5, 0, 151936) == 5 * 38 * 8 + (256 - 5 * 38 * 8 % 256) % 256
+    assert bd.spec_sampler_workspace_bytes(0, 3, 8) == 256
+    assert bd.spec_sampler_workspace_bytes(-1, 0, 8) == 0
+
+
+def test_host_checks_reject_before_launch(lib):
+    cfg = bd.spec_model_cfg(256, 4, 4, 4, 96, 704, 4096, bd.SPEC_F32, 10000.0, 1e-6)
+    w = bd.spec_weights()
+    h = ctypes.c_void_p()
+    assert lib.spec_model_create(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(h)) == -4  # head_dim 96
+    assert "head_dim" in bd.spec_last_error()
+    cfg.head_dim = 64
+    assert lib.spec_model_create(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(h)) == -1  # NULL weights
+    assert lib.spec_model_create(None, None, None) == -1
+    # sampler argument checks
+    st = lib.spec_reject_sample(0, 4, 100, 1, None, 1, None, 1, 1, 1, 1, 1, 1 << 20, None)
+    assert st == -1 and "B=0" in bd.spec_last_error()
+    st = lib.spec_reject_sample(1, -1, 100, 1, None, 1, None, 1, 1, 1, 1, 1, 1 << 20, None)
+    assert st == -1
+    st = lib.spec_reject_sample(1, 2, 1 << 23, 1, None, 1, None, 1, 1, 1, 1, 1, 1 << 20, None)
+    assert st == -1
+    st = lib.spec_reject_sample(1, 2, 100, 1, None, None, None, 1, 1, 1, 1, 1, 1 << 20, None)
+    assert st == -1  # draft NULL with gamma > 0
+    st = lib.spec_reject_sample(1, 2, 100, 1, None, 1, None, 1, 1, 1, 1, 1, 8, None)
+    assert st == -2  # workspace too small
+    assert lib.spec_softmax_pq(1, 4, 100, 0.0, 1, 1, 1 << 20, None) == -1  # temperature
+    assert lib.spec_kv_set_len(None, 1, None, 1, None) == -1
+    kv = bd.spec_kv(1, 1, 1, 2, 16)
+    assert lib.spec_kv_set_len(ctypes.byref(kv), 3, None, 1, None) == -1
+    assert lib.spec_verify_forward(None, ctypes.byref(kv), 1, 1, 1, None, 1, 1 << 30, None) == -1
+    assert lib.spec_workspace_bytes(None, 1, 1, 16) == 0

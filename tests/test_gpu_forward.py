@@ -1,0 +1,93 @@
+"""GPU parity of the verify forward pass against the oracle: logits within
+1e-4 (float32 models) or 2e-2 (bf16 models), K/V rows written at the right
+positions, deterministic run to run."""
+import numpy as np
+import pytest
+import torch
+
+from draft_then_verify_amd import binding as bd
+from oracle import model as OM
+from oracle import rounds as R
+from synth import SHAPES, Shape, make_prompt, make_weights
+from tests._gpu import gpu_prefill, i32, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(shape, B, P, m, seed, lens_back=None, max_ctx=None, n_layers=None, norm="random"):
+    w = make_weights(shape, seed=seed, norm=norm, layers=n_layers)
+    sh = shape if n_layers is None else shape.with_(n_layers=n_layers)
+    L = sh.n_layers
+    max_ctx = max_ctx or (P + m + 3)
+    model = bd.SpecModel(sh, to_dev(w))
+    kv = bd.KVCache(sh, L, B, max_ctx)
+    prompt = make_prompt(B, P, sh.vocab, seed=seed)
+    gpu_prefill(model, kv, prompt)
+    dec = OM.Decoder(sh, w)
+    cache = dec.new_cache(B, max_ctx)
+    R.prefill(dec, cache, prompt)
+    if lens_back is not None:  # ragged contexts: rewind some sequences
+        cache.length = cache.length - np.asarray(lens_back)
+        kv.len.copy_(torch.as_tensor(cache.length.astype(np.int32)))
+    block = make_prompt(B, m, sh.vocab, seed=seed + 1)
+    logits = torch.empty((B, m, sh.vocab), dtype=torch.float32, device="cuda")
+    ws = bd.workspace(model.workspace_bytes(B, m, max_ctx))
+    bd.spec_verify_forward(model, kv, B, m, i32(block), logits, ws)
+    torch.cuda.synchronize()
+    ref = dec.forward(cache, block)
+    got = logits.cpu().numpy()
+    # repeat: bitwise identical logits
+    logits2 = torch.empty_like(logits)
+    bd.spec_verify_forward(model, kv, B, m, i32(block), logits2, ws)
+    assert torch.equal(logits, logits2)
+    # len is unchanged by a verify pass
+    assert np.array_equal(kv.len.cpu().numpy(), cache.length.astype(np.int32))
+    return got, ref, kv, cache, sh
+
+
+def _tol(shape):
+    return 1e-4 if shape.dtype == "f32" else 2e-2
+
+
+def test_tiny_f32_verify_pass():
+    """The first workload's target (all float32), gamma = 4 verify block."""
+    shape = SHAPES["tiny"]
+    got, ref, kv, cache, sh = _run(shape, B=1, P=64, m=5, seed=101)
+    assert np.abs(got - ref).max() < _tol(shape)
+    # cached K rows equal the oracle's (float32 cache vs fp64 oracle)
+    n = 64 - 1 + 5
+    k = kv.k[:, :, :, :n].float().cpu().numpy()
+    assert np.abs(k - cache.k[:, :, :, :n]).max() < 1e-4
+
+
+def test_small_bf16_verify_pass_ragged_batch():
+    """Second workload's shape (bf16, GQA 16/4, hd 64, vocab 32000) over two
+    layers, three sequences at different context lengths."""
+    shape = SHAPES["small"]
+    got, ref, kv, cache, sh = _run(shape, B=3, P=40, m=5, seed=102, lens_back=[0, 3, 17], n_layers=2)
+    assert np.abs(got - ref).max() < _tol(shape)
+    n = int(cache.length.min()) + 5
+    k = kv.k[:, :, :, :n].float().cpu().numpy()
+    assert np.abs(k - cache.k[:, :, :, :n]).max() < 2e-2
+
+
+def test_hd128_gqa_more_rows_than_a_block():
+    """head_dim 128, 4:1 GQA, 13 rows per sequence (two GEMV row blocks),
+    ragged vocab tail."""
+    shape = Shape("h128", 512, 2, 8, 2, 128, 1024, 5000, "bf16")
+    got, ref, *_ = _run(shape, B=2, P=33, m=13, seed=103)
+    assert np.abs(got - ref).max() < _tol(shape)
+
+
+def test_full_small_target_verify_pass():
+    """The full eight-layer bf16 target of the second workload."""
+    shape = SHAPES["small"]
+    got, ref, *_ = _run(shape, B=1, P=96, m=5, seed=104, norm="ones")
+    assert np.abs(got - ref).max() < _tol(shape)
+
+
+def test_long_context_splits():
+    """Context long enough for many attention splits and several key tiles each."""
+    shape = Shape("ctx", 256, 1, 4, 1, 64, 512, 300, "f32")
+    got, ref, *_ = _run(shape, B=1, P=700, m=5, seed=105, max_ctx=720)
+    assert np.abs(got - ref).max() < 1e-4

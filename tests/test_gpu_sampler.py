@@ -1,0 +1,122 @@
+"""GPU parity of the softmax and rejection-sampler kernels against the oracle.
+
+Integers (n, emitted) must be bit-exact when both sides sample from the same
+float32 probability rows; probabilities match the oracle's fp64 softmax within
+1e-5 absolute."""
+import numpy as np
+import pytest
+import torch
+from scipy import stats
+
+from draft_then_verify_amd import binding as bd
+from oracle import sampler as S
+from synth import make_uniforms
+from tests._gpu import f32, gpu_softmax, i32
+
+pytestmark = pytest.mark.gpu
+SEED = 5150
+
+
+def _rows(rng, n, V, scale):
+    return (rng.normal(size=(n, V)) * scale).astype(np.float32)
+
+
+@pytest.mark.parametrize("V", [8, 4095, 4096, 4097, 32000, 151936])
+def test_softmax_matches_oracle(V):
+    rng = np.random.default_rng(SEED + V)
+    logits = _rows(rng, 7, V, 3.0)
+    logits[0, :] = 0.0           # uniform row
+    logits[1, V // 2] = 40.0     # peaked row
+    p = gpu_softmax(f32(logits), V).cpu().numpy()
+    ref = S.softmax(logits.astype(np.float64))
+    assert np.abs(p - ref).max() < 1e-5
+    # relative accuracy of the small entries too
+    assert np.abs(p - ref).max() / ref.max() < 1e-5
+    # deterministic
+    p2 = gpu_softmax(f32(logits), V).cpu().numpy()
+    assert np.array_equal(p, p2)
+
+
+def _gpu_reject(p, q, drafts, nd, u_acc, u_res):
+    B, g1, V = p.shape
+    g = g1 - 1
+    n = torch.empty(B, dtype=torch.int32, device="cuda")
+    em = torch.empty((B, g1), dtype=torch.int32, device="cuda")
+    ws = bd.workspace(bd.spec_sampler_workspace_bytes(0, B, V))
+    bd.spec_reject_sample(B, g, V, f32(p), None if q is None else f32(q), i32(drafts) if g > 0 else None,
+                          None if nd is None else i32(nd), f32(u_acc) if g > 0 else None, f32(u_res), n, em, ws)
+    return n.cpu().numpy(), em.cpu().numpy()
+
+
+@pytest.mark.parametrize("B,g,V,onehot,ragged", [(1, 4, 151936, False, False), (64, 10, 151936, True, True),
+                                                 (3, 4, 32000, False, True), (257, 2, 4096, False, False),
+                                                 (50, 0, 4097, False, False), (9, 4, 8, True, False)])
+def test_reject_sample_bit_exact(B, g, V, onehot, ragged):
+    rng = np.random.default_rng(SEED + B * 7 + g)
+    lp = _rows(rng, B * (g + 1), V, 2.0)
+    p = gpu_softmax(f32(lp), V).cpu().numpy().reshape(B, g + 1, V)
+    if g == 0:
+        q, drafts = None, np.zeros((B, 0), np.int64)
+    elif onehot:
+        q = None
+        # drafts near the target's mode so that some are accepted
+        drafts = np.argmax(lp.reshape(B, g + 1, V)[:, :g], axis=-1)
+        drafts = np.where(rng.random((B, g)) < 0.5, drafts, rng.integers(0, V, size=(B, g)))
+    else:
+        lq = lp.reshape(B, g + 1, V)[:, :g].reshape(-1, V) + _rows(rng, B * g, V, 0.7)
+        q = gpu_softmax(f32(lq), V).cpu().numpy().reshape(B, g, V)
+        drafts = np.stack([S.fixed_point_draw(q[:, i], make_uniforms((B,), SEED, 3, i)) for i in range(g)], 1)
+    nd = rng.integers(0, g + 1, size=B) if ragged else None
+    u_acc = make_uniforms((B, g), SEED, 1, B)
+    u_res = make_uniforms((B,), SEED, 2, B)
+    n_g, em_g = _gpu_reject(p, q, drafts, nd, u_acc, u_res)
+    n_o, em_o = S.reject_sample(p, q, drafts, nd, u_acc, u_res)
+    assert np.array_equal(n_g, n_o)
+    assert np.array_equal(em_g, em_o)
+    if g:
+        assert 0 < (n_o > 0).mean() or onehot
+
+
+def test_reject_sample_special_rows():
+    """p = q accepts all; the all-zero residual falls back to p; q(x) = 0 accepts;
+    out-of-range draft ids are rejected without reading memory."""
+    V, g = 16, 3
+    rng = np.random.default_rng(SEED)
+    q = rng.dirichlet(np.ones(V), size=(1, g)).astype(np.float32)
+    p = np.concatenate([q, rng.dirichlet(np.ones(V), size=(1, 1)).astype(np.float32)], 1)
+    drafts = np.array([[1, 2, 3]])
+    u = make_uniforms((1, g), SEED, 9)
+    n, em = _gpu_reject(p, q, drafts, None, u, np.array([0.3], np.float32))
+    assert n[0] == g and np.array_equal(em, S.reject_sample(p, q, drafts, None, u, np.array([0.3], np.float32))[1])
+    p2 = np.array([[[0.5, 0.25, 0.25], [1 / 3, 1 / 3, 1 / 3]]], np.float32)
+    q2 = np.array([[[0.5 + 2 ** -20, 0.25, 0.25]]], np.float32)
+    for ur in (0.1, 0.6, 0.9):
+        args = (p2, q2, np.array([[0]]), None, np.array([[1 - 2 ** -24]], np.float32), np.array([ur], np.float32))
+        ng, eg = _gpu_reject(*args)
+        no, eo = S.reject_sample(*args)
+        assert ng[0] == no[0] == 0 and np.array_equal(eg, eo)
+    q3 = np.array([[[0.0, 1.0, 0.0]]], np.float32)
+    ng, eg = _gpu_reject(p2, q3, np.array([[0]]), None, np.array([[0.99]], np.float32), np.array([0.5], np.float32))
+    assert ng[0] == 1 and eg[0, 0] == 0
+    ng, eg = _gpu_reject(p2, None, np.array([[7]]), None, np.array([[0.0]], np.float32), np.array([0.5], np.float32))
+    assert ng[0] == 0 and eg[0, 1] == -1 and 0 <= eg[0, 0] < 3
+
+
+def test_chi_square_on_gpu_v8():
+    """10**6 rounds on V = 8 through the kernel: first token ~ p_1, bonus ~ p_2."""
+    V, g, N, Bc = 8, 1, 10 ** 6, 62500
+    rng = np.random.default_rng(SEED + 1)
+    p_rows = rng.dirichlet(np.ones(V), size=g + 1).astype(np.float32)
+    q_rows = rng.dirichlet(np.ones(V), size=g).astype(np.float32)
+    first, bonus = [], []
+    for c in range(N // Bc):
+        x = S.fixed_point_draw(np.broadcast_to(q_rows[0], (Bc, V)), make_uniforms((Bc,), SEED, 40, c))
+        n, em = _gpu_reject(np.broadcast_to(p_rows, (Bc, g + 1, V)), np.broadcast_to(q_rows, (Bc, g, V)), x[:, None],
+                            None, make_uniforms((Bc, g), SEED, 41, c), make_uniforms((Bc,), SEED, 42, c))
+        first.append(em[:, 0])
+        bonus.append(em[n == 1, 1])
+    first, bonus = np.concatenate(first), np.concatenate(bonus)
+    for obs_t, pr in ((first, p_rows[0]), (bonus, p_rows[1])):
+        obs = np.bincount(obs_t, minlength=V)
+        pr = pr.astype(np.float64) / pr.sum()
+        assert stats.chisquare(obs, pr * obs.sum()).pvalue > 1e-3

@@ -1,0 +1,264 @@
+#!/usr/bin/env python3
+"""Benchmark of the verify hot path on one MI355X.
+
+Workload (default): the Qwen3-8B-shaped target (d 4096, 36 layers, 32/8
+heads, head_dim 128, d_ff 12288, vocab 151936, bf16, random init) with a
+Qwen3-0.6B-shaped draft, B = 1, gamma = 4, a 256-token prompt, 256 new tokens.
+
+* A timed step is one ``spec_decode_step``: assemble the 5 verify rows, the
+  target forward over them (every weight streamed once), softmax, accept /
+  resample / bonus, KV commit.  ``value`` = algorithmic bytes of the pass /
+  time per step (GB/s), inputs resident in HBM.
+* ``roofline`` times the dominant kernel (the SwiGLU gate/up GEMV, 201 MB of
+  weights per launch) with HIP events on its stream, over all 36 layers'
+  weights in turn so no launch reads cached weights.
+* ``emitted_tok_s`` / ``plain_tok_s``: whole generations of 256 tokens with
+  the draft model vs plain decoding (gamma = 0), wall clock incl. the draft.
+* ``cpu_baseline``: the CPU oracle's verify round over a bounded sample (the
+  first layers + head of the same target), host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verify-pass HBM GB/s (% of peak) + emitted tok/s, 8B shape, B=1, γ=4"
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def verify_pass_bytes(shape, B: int, m: int, ctx_sum: int) -> int:
+    """Algorithmic bytes of one verify pass: every linear weight once, the
+    gathered embedding rows, norm gains, the KV rows read (ctx_sum = sum over
+    sequences of the keys attended) and written, logits written and read once."""
+    e = 2 if shape.dtype == "bf16" else 4
+    d, L, F, V = shape.d_model, shape.n_layers, shape.d_ff, shape.vocab
+    hq = shape.n_heads * shape.head_dim
+    weights = L * (shape.qkv_rows * d + d * hq + 2 * F * d + d * F) * e + V * d * e
+    norms = (2 * L + 1) * d * 4
+    kv_tok = shape.kv_bytes_per_token()
+    M = B * m
+    return weights + M * d * e + norms + ctx_sum * kv_tok + M * kv_tok + 2 * M * V * 4
+
+
+def gemv_source_hash() -> str:
+    with open(os.path.join(ROOT, "draft_then_verify_amd", "csrc", "gemv.hip"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic():
+    """HBM bytes per launch of the dominant kernel from committed counter runs,
+    if they were taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "gemv_swiglu_8b_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("gemv_source_sha") != gemv_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(shape, w_gpu, prompt, layers: int) -> dict:
+    """The oracle's verify round over the first `layers` layers + head."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import model as OM
+    from oracle import rounds as R
+    from synth import round_uniforms
+
+    sh = shape.with_(n_layers=layers)
+    w = {}
+    for k, v in w_gpu.items():
+        w[k] = (v[:layers] if k in ("attn_norm", "wqkv", "wo", "mlp_norm", "wgu", "wd") else v).cpu()
+    dec = OM.Decoder(sh, w)
+    P, g = prompt.shape[1], 4
+    cache = dec.new_cache(1, P + g + 2)
+    R.prefill(dec, cache, prompt)
+    rng = np.random.default_rng(7)
+    drafts = rng.integers(0, sh.vocab, size=(1, g))
+    u = round_uniforms(7, 0, 1, g)
+    t0 = time.perf_counter()
+    R.verify_round(dec, cache, prompt[:, -1], drafts, None, None, u["u_acc"], u["u_res"])
+    dt = time.perf_counter() - t0
+    nbytes = verify_pass_bytes(sh, 1, g + 1, P - 1 + g + 1)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count() or 1])
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"one verify round (gamma=4, fp64 NumPy) over the first {layers} of 36 layers + the LM head "
+                      f"of the same 8B-shaped target at context {P - 1}: {nbytes / 1e9:.3f} GB of algorithmic "
+                      f"bytes in {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--new-tokens", type=int, default=256)
+    ap.add_argument("--cpu-layers", type=int, default=3, help="target layers in the CPU-baseline sample")
+    ap.add_argument("--skip-generate", action="store_true", help="skip the emitted tok/s generations")
+    ap.add_argument("--skip-cpu", action="store_true", help="skip the CPU-baseline leg")
+    ap.add_argument("--graph", type=int, default=1, help="time graph replays of the decode step (1) or eager calls (0)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this path has no multi-GPU mode (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from draft_then_verify_amd import binding as bd
+    from draft_then_verify_amd.runner import ModelDrafter, SpecDecoder
+    from synth import SHAPES, make_prompt, make_weights, round_uniforms
+
+    bd.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tshape, dshape = SHAPES["qwen3_8b"], SHAPES["qwen3_0p6b"]
+    B, g, P = 1, 4, 256
+    max_ctx = P + args.new_tokens + g + args.steps + args.warmup + 8
+    t0 = time.perf_counter()
+    wt = make_weights(tshape, seed=3, device="cuda")
+    wd = make_weights(dshape, seed=4, device="cuda")
+    torch.cuda.synchronize()
+    log(f"weights generated in {time.perf_counter() - t0:.1f} s")
+    target = bd.SpecModel(tshape, wt)
+    draft = bd.SpecModel(dshape, wd)
+    prompt = make_prompt(B, P, tshape.vocab, seed=5)
+
+    # ---- timed verify steps --------------------------------------------------------
+    dec = SpecDecoder(target, B, g, max_ctx, drafter=None, seed=6)
+    dec.prefill(prompt)
+    V = tshape.vocab
+    rng = np.random.default_rng(8)
+    last = torch.as_tensor(prompt[:, -1].astype(np.int32)).cuda()
+    drafts = torch.as_tensor(rng.integers(0, V, size=(B, g)).astype(np.int32)).cuda()
+    qlog = torch.randn((B * g, V), device=dev)
+    q = torch.empty_like(qlog)
+    sws = bd.workspace(bd.spec_sampler_workspace_bytes(B * g, B, V))
+    bd.spec_softmax_pq(qlog, B * g, V, 1.0, q, sws)
+    u = round_uniforms(6, 0, B, g)
+    u_acc, u_res = torch.as_tensor(u["u_acc"]).cuda(), torch.as_tensor(u["u_res"]).cuda()
+    n = torch.empty(B, dtype=torch.int32, device=dev)
+    em = torch.empty((B, g + 1), dtype=torch.int32, device=dev)
+
+    def step():
+        bd.spec_decode_step(target, dec.kv, B, g, 1.0, last, drafts, None, q, u_acc, u_res, n, em, None, dec.ws)
+
+    len_before_warm = int(dec.kv.len[0])
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    graph = None
+    if args.graph:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step()  # one eager call on the capture stream before capturing
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+    len0 = int(dec.kv.len[0])
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(args.steps):
+        if graph is not None:
+            graph.replay()
+        else:
+            step()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    len1 = int(dec.kv.len[0])
+    # keys attended per step: len + m at each step; len grows by n + 1 per step
+    ctx_mean = (len0 + len1) / 2.0 + g + 1 - 0.5 * (len1 - len0) / args.steps
+    nbytes = verify_pass_bytes(tshape, B, g + 1, int(round(ctx_mean)))
+    gbs = nbytes / (ms / 1e3) / 1e9
+    log(f"decode step: {ms:.3f} ms, {gbs:.1f} GB/s ({100 * gbs / PEAK_HBM_GBS:.1f}% of peak), "
+        f"context {len0}->{len1} (warmup from {len_before_warm})")
+
+    # ---- dominant kernel: SwiGLU gate/up GEMV over every layer's weights --------------
+    F, d = tshape.d_ff, tshape.d_model
+    x = torch.randn((B * (g + 1), d), device=dev).to(torch.bfloat16)
+    z = torch.empty((B * (g + 1), F), dtype=torch.bfloat16, device=dev)
+    for layer in range(tshape.n_layers):
+        bd.spec_linear(wt["wgu"][layer], x, B * (g + 1), F, d, epilogue=2, z=z)
+    reps = 3
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        for layer in range(tshape.n_layers):
+            bd.spec_linear(wt["wgu"][layer], x, B * (g + 1), F, d, epilogue=2, z=z)
+    e1.record()
+    torch.cuda.synchronize()
+    k_us = e0.elapsed_time(e1) * 1e3 / (reps * tshape.n_layers)
+    k_bytes = 2 * F * d * 2 + B * (g + 1) * (d + F) * 2
+    k_gbs = k_bytes / (k_us / 1e6) / 1e9
+    log(f"gate/up GEMV: {k_us:.1f} us/launch, {k_gbs:.1f} GB/s")
+
+    # ---- emitted tokens/s: speculative vs plain ---------------------------------------
+    gen = {}
+    if not args.skip_generate:
+        drafter = ModelDrafter(draft, B, g, max_ctx)
+        spec = SpecDecoder(target, B, g, max_ctx, drafter=drafter, seed=11)
+        spec.prefill(prompt)
+        rs = spec.generate(args.new_tokens)
+        log(f"speculative: {rs['tok_s']:.1f} tok/s, MAL {rs['mean_acceptance_length']:.2f}, rounds {rs['rounds']}")
+        del spec, drafter
+        plain = SpecDecoder(target, B, 0, max_ctx, seed=12)
+        plain.prefill(prompt)
+        rp = plain.generate(args.new_tokens)
+        log(f"plain: {rp['tok_s']:.1f} tok/s")
+        gen = {"emitted_tok_s": round(rs["tok_s"], 2), "plain_tok_s": round(rp["tok_s"], 2),
+               "spec_over_plain": round(rs["tok_s"] / rp["tok_s"], 3),
+               "mean_acceptance_length": round(rs["mean_acceptance_length"], 3),
+               "acceptance_rate": round(rs["acceptance_rate"], 4),
+               "per_position_acceptance": [round(v, 4) for v in rs["per_position"]],
+               "round_ms_p50": round(rs["round_ms_p50"], 3), "round_ms_p99": round(rs["round_ms_p99"], 3)}
+        del plain
+
+    cpu = None
+    if not args.skip_cpu:
+        t1 = time.perf_counter()
+        cpu = cpu_baseline(tshape, wt, prompt, args.cpu_layers)
+        log(f"cpu baseline: {cpu['value']} GB/s in {time.perf_counter() - t1:.1f} s")
+
+    out = {
+        "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded random-init weights and prompts)",
+        "config": {"workload": "qwen3_8b-shaped target, qwen3_0p6b-shaped draft, B=1, gamma=4, prompt 256, "
+                               "256 new tokens", "B": B, "gamma": g, "prompt_len": P,
+                   "context_mean": round(ctx_mean, 1), "graph_replay": bool(graph is not None)},
+        "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+        "verified_positions_per_s": round(B * (g + 1) / (ms / 1e3), 1),
+        "bytes_per_step": nbytes,
+        **gen,
+        "roofline": {"bound": "hbm", "achieved": round(k_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(k_gbs / PEAK_HBM_GBS, 4), "traffic": stored_traffic(),
+                     "kernel": "gemv_kernel SwiGLU, W_gu [24576, 4096] bf16, M=5",
+                     "us_per_launch": round(k_us, 2), "bytes_per_launch": k_bytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -21,8 +21,8 @@ STATUS = {0: "SPEC_OK", -1: "SPEC_EINVAL", -2: "SPEC_ENOMEM", -3: "SPEC_EHIP", -
 
 # Every symbol the C header declares.
 EXPORTS = ("spec_model_create", "spec_model_destroy", "spec_workspace_bytes", "spec_sampler_workspace_bytes",
-           "spec_verify_forward", "spec_softmax_pq", "spec_reject_sample", "spec_decode_step", "spec_kv_set_len",
-           "spec_last_error")
+           "spec_verify_forward", "spec_softmax_pq", "spec_reject_sample", "spec_decode_step", "spec_linear",
+           "spec_kv_set_len", "spec_last_error")
 
 
 class SpecError(RuntimeError):
@@ -74,6 +74,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "spec_reject_sample": (i32, [i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "spec_decode_step": (i32, [vp, ctypes.POINTER(spec_kv), i32, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                    sz, vp]),
+        "spec_linear": (i32, [i32, i32, vp, vp, i32, i32, i32, vp, vp, vp]),
         "spec_kv_set_len": (i32, [ctypes.POINTER(spec_kv), i32, vp, i32, vp]),
         "spec_last_error": (ctypes.c_char_p, []),
     }
@@ -211,6 +212,11 @@ def spec_decode_step(target: SpecModel, kv: KVCache, B: int, gamma: int, tempera
                                            _ptr(last_tok), _ptr(draft), _ptr(n_draft), _ptr(q), _ptr(u_acc),
                                            _ptr(u_res), _ptr(n_accepted), _ptr(emitted), _ptr(logits_out), _ptr(ws),
                                            _nbytes(ws), _stream(stream)))
+
+
+def spec_linear(W, x, M: int, N: int, K: int, epilogue: int = 0, y=None, z=None, stream=None):
+    dt = SPEC_BF16 if W.dtype == torch.bfloat16 else SPEC_F32
+    _check(load_library().spec_linear(dt, epilogue, _ptr(W), _ptr(x), M, N, K, _ptr(y), _ptr(z), _stream(stream)))
 
 
 def spec_kv_set_len(kv: KVCache, B: int, src, add: int, stream=None):

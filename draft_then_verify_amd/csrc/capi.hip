@@ -275,6 +275,19 @@ SPEC_API spec_status spec_decode_step(const spec_model* target, const spec_kv* k
   return SPEC_OK;
 }
 
+SPEC_API spec_status spec_linear(int32_t dtype, int32_t epilogue, const void* W, const void* x, int32_t M, int32_t N,
+                                 int32_t K, float* y, void* z, hipStream_t stream) {
+  if (dtype != SPEC_F32 && dtype != SPEC_BF16) return fail(SPEC_EINVAL, "dtype %d", dtype);
+  if (epilogue < 0 || epilogue > 2) return fail(SPEC_EINVAL, "epilogue %d", epilogue);
+  if (M <= 0 || N <= 0 || K <= 0) return fail(SPEC_EINVAL, "M=%d N=%d K=%d", M, N, K);
+  const int vec = dtype == SPEC_BF16 ? 8 : 4;
+  if (K % vec) return fail(SPEC_EINVAL, "K=%d not a multiple of %d", K, vec);
+  if (!W || !x || !aligned16(W) || !aligned16(x)) return fail(SPEC_EINVAL, "W/x NULL or not 16-byte aligned");
+  if (epilogue == 2 ? !z : !y) return fail(SPEC_EINVAL, "output pointer NULL");
+  HIP_TRY(sv::launch_gemv(dtype == SPEC_BF16, epilogue, W, x, M, N, K, y, N, z, N, stream));
+  return SPEC_OK;
+}
+
 SPEC_API spec_status spec_kv_set_len(const spec_kv* kv, int32_t B, const int32_t* src, int32_t add,
                                      hipStream_t stream) {
   if (!kv || !kv->len) return fail(SPEC_EINVAL, "kv/len is NULL");

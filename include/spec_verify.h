@@ -172,6 +172,20 @@ spec_status spec_decode_step(const spec_model* target, const spec_kv* kv, int32_
                              const float* u_res, int32_t* n_accepted, int32_t* emitted,
                              float* logits_out, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* The weight-streaming linear of the verify pass on its own: y = x . W^T for
+ * M rows, every weight byte read once per block of 8 rows (a verify pass
+ * "reads the same weights" for all its positions, first page, section "The
+ * speedup is borrowed").
+ *   dtype     SPEC_F32 or SPEC_BF16: type of W, x and z.
+ *   epilogue  0: y[M][N] = acc;  1: y[M][N] += acc (float32 residual);
+ *             2: z[M][N] = silu(g) * u with g from W rows 0..N-1 and u from
+ *                rows N..2N-1 (W is [2N][K]).
+ *   W [N or 2N][K], x [M][K], y float32 [M][N] (epilogues 0, 1), z [M][N]
+ *   (epilogue 2).  K a multiple of 16 bytes of the dtype; W and x 16-byte
+ *   aligned.  Errors: SPEC_EINVAL, SPEC_EHIP. */
+spec_status spec_linear(int32_t dtype, int32_t epilogue, const void* W, const void* x, int32_t M, int32_t N,
+                        int32_t K, float* y, void* z, hipStream_t stream);
+
 /* KV length bookkeeping: len[b] = (src ? src[b] : len[b]) + add for b < B.
  * Used to advance after prefill / draft passes and to rewind a drafter to the
  * target's length.  Errors: SPEC_EINVAL, SPEC_EHIP. */

@@ -110,8 +110,9 @@ class Decoder:
     def _store(self, x: np.ndarray) -> np.ndarray:
         return round_bf16(x) if self.bf16 else x
 
-    def forward(self, cache: KVCache, tokens: np.ndarray) -> np.ndarray:
-        """tokens [B, m] int -> logits [B, m, V] fp64; writes K/V at the m new positions."""
+    def forward(self, cache: KVCache, tokens: np.ndarray, logits: bool = True):
+        """tokens [B, m] int -> logits [B, m, V] fp64 (None when ``logits`` is
+        False, as in prefill); writes K/V at the m new positions."""
         s, w = self.shape, self.w
         tokens = np.asarray(tokens)
         B, m = tokens.shape
@@ -128,10 +129,9 @@ class Decoder:
             v = qkv[..., (H + Hkv) * hd:].reshape(B, m, Hkv, hd)
             q = rope(q, pos, s.rope_theta)
             k = rope(k, pos, s.rope_theta)
-            for b in range(B):
-                for i in range(m):
-                    cache.k[layer, b, :, pos[b, i]] = self._store(k[b, i])
-                    cache.v[layer, b, :, pos[b, i]] = self._store(v[b, i])
+            bidx = np.repeat(np.arange(B), m)
+            cache.k[layer, bidx, :, pos.reshape(-1)] = self._store(k.reshape(B * m, Hkv, hd))
+            cache.v[layer, bidx, :, pos.reshape(-1)] = self._store(v.reshape(B * m, Hkv, hd))
             o = np.zeros((B, m, H, hd))
             for b in range(B):
                 for i in range(m):
@@ -142,5 +142,7 @@ class Decoder:
             gu = self._lin(a2, w["wgu"][layer])
             z = silu(gu[..., :F]) * gu[..., F:]
             h = h + self._lin(z, w["wd"][layer])
+        if not logits:
+            return None
         a = rms_norm(h, w["final_norm"].astype(np.float64), s.rms_eps)
         return self._lin(a, w["lm_head"])

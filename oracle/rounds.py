@@ -61,5 +61,5 @@ def prefill(model, cache, prompt):
     """Write K/V for prompt[:, :-1]; the last prompt token is the first round's input."""
     prompt = np.asarray(prompt, np.int64)
     if prompt.shape[1] > 1:
-        model.forward(cache, prompt[:, :-1])
+        model.forward(cache, prompt[:, :-1], logits=False)
         cache.length = cache.length + prompt.shape[1] - 1

@@ -1,15 +1,28 @@
 // Attention of the verify pass: m query rows per sequence (the last committed
 // token and the gamma drafts) against the sequence's KV cache.
 //
-// The pages: "the cache read serves every query position" (first page,
-// section "The speedup is borrowed"), and decode-time attention stays
-// memory-bound, its KV traffic growing with context and batch ("How
-// Speculative Decoding Works", section "Prefill and Decode").  So one
-// workgroup reads each K/V tile once for all G*m query rows of a KV head
-// (G = H / Hkv query heads share it), with the tile staged in LDS.  At B = 1
-// there are only Hkv (b, kv-head) pairs, so the context is split across
-// workgroups and the partial (max, sum, output) rows are merged afterwards
-// in a fixed order (log-sum-exp combine) -- deterministic, no atomics.
+// The pages: one read of the cache serves every query position of the block
+// (first page, section "The speedup is borrowed"), and decode-time attention
+// stays memory-bound, its KV traffic growing with context and batch ("How
+// Speculative Decoding Works", section "Prefill and Decode").  So a K/V row is
+// fetched from memory once per workgroup and used by every query row that
+// shares its KV head (grouped-query attention: G = H / Hkv query heads).
+//
+// Workgroup = 4 waves = (sequence b, KV head, block of query heads, block of
+// query rows, context split).  The four waves cover up to four query heads
+// of the group (or, when G < 4, more query rows of fewer heads); each wave
+// owns up to MQ query rows of one head.  Per 64-key tile:
+//  * the workgroup copies the K and V tile into LDS with 16-byte loads, all
+//    of a tile's loads in flight at once, the next tile's issued before the
+//    current one is used;
+//  * scores: lane j holds key j of the tile (float32, from LDS) and dots it
+//    with each of its wave's query rows (LDS broadcasts);
+//  * online softmax per row (wave max / sum);
+//  * P.V: lanes take head dimensions; V rows come from LDS.
+// At B = 1 the (sequence, head) pairs are few, so the context is cut into
+// splits, one workgroup each; the partial (max, sum, output) rows are merged
+// by the last workgroup of each (sequence, head block, row block) to finish
+// (an atomic ticket), in split order: deterministic, with no combine launch.
 //
 // Causality inside the new block: query row i sits at position len + i and
 // sees keys 0 .. len + i.
@@ -21,235 +34,364 @@
 namespace sv {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int QT = 32;  // query rows per workgroup tile
-constexpr int KT = 32;  // keys per LDS tile
+constexpr int kThreadsA = 256;
+constexpr int kWaves = kThreadsA / kWave;
+constexpr int KT = 64;  // keys per tile (one per lane)
 
-// Rotate-half RoPE of q (in place) and k; k and v rows go to the cache at
-// position len[b] + i.  Row r = b*m + i.
-template <typename ET>
-__global__ __launch_bounds__(kThreads) void rope_append_kernel(float* __restrict__ qkv, const float2* __restrict__ cs,
-                                                               const int32_t* __restrict__ len, int m, int H, int Hkv,
-                                                               int hd, ET* __restrict__ kc, ET* __restrict__ vc,
-                                                               int layer, int kvB, int max_ctx) {
-  const int r = blockIdx.x;
-  const int b = r / m, i = r - b * m;
-  const int pos = len[b] + i;
-  const bool store = pos >= 0 && pos < max_ctx;
-  const int half = hd / 2;
-  const int ld = (H + 2 * Hkv) * hd;
-  float* row = qkv + static_cast<size_t>(r) * ld;
-  const float2* csr = cs + static_cast<size_t>(r) * half;
-  const size_t cache_row = ((static_cast<size_t>(layer) * kvB + b) * Hkv) * max_ctx + (store ? pos : 0);
-  for (int idx = threadIdx.x; idx < (H + Hkv) * half; idx += kThreads) {
-    const int hh = idx / half, j = idx - hh * half;
-    const float x1 = row[hh * hd + j], x2 = row[hh * hd + j + half];
-    const float2 c = csr[j];
-    const float y1 = x1 * c.x - x2 * c.y;
-    const float y2 = x2 * c.x + x1 * c.y;
-    if (hh < H) {
-      row[hh * hd + j] = y1;
-      row[hh * hd + j + half] = y2;
-    } else if (store) {
-      ET* dst = kc + (cache_row + static_cast<size_t>(hh - H) * max_ctx) * hd;
-      dst[j] = Elt<ET>::from_f(y1);
-      dst[j + half] = Elt<ET>::from_f(y2);
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));  // 16 bytes, kept in registers
+
+template <typename ET> struct Cvt;  // 16 bytes of a K/V row -> floats
+template <> struct Cvt<uint16_t> {
+  static constexpr int n = 8;
+  __device__ __forceinline__ static void run(const v4u& v, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(v[i] << 16);
+      f[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
     }
   }
-  if (store) {
-    const float* vrow = row + (H + Hkv) * hd;
-    for (int idx = threadIdx.x; idx < Hkv * hd; idx += kThreads) {
-      const int kvh = idx / hd, dd = idx - kvh * hd;
-      vc[(cache_row + static_cast<size_t>(kvh) * max_ctx) * hd + dd] = Elt<ET>::from_f(vrow[idx]);
-    }
+};
+template <> struct Cvt<float> {
+  static constexpr int n = 4;
+  __device__ __forceinline__ static void run(const v4u& v, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(v[i]);
+  }
+};
+
+// DPL consecutive elements of a V row in LDS as floats.
+template <typename ET, int DPL> struct VRow;
+template <> struct VRow<uint16_t, 2> {
+  __device__ __forceinline__ static void load(const uint16_t* p, float* f) {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
+    f[0] = __uint_as_float(w << 16);
+    f[1] = __uint_as_float(w & 0xffff0000u);
+  }
+};
+template <> struct VRow<uint16_t, 1> {
+  __device__ __forceinline__ static void load(const uint16_t* p, float* f) { f[0] = bf2f(*p); }
+};
+template <> struct VRow<float, 2> {
+  __device__ __forceinline__ static void load(const float* p, float* f) {
+    const float2 v = *reinterpret_cast<const float2*>(p);
+    f[0] = v.x;
+    f[1] = v.y;
+  }
+};
+template <> struct VRow<float, 1> {
+  __device__ __forceinline__ static void load(const float* p, float* f) { f[0] = *p; }
+};
+
+// Shape of the work split, shared by the launcher and the kernel.
+struct Plan {
+  int hpw;  // query heads per workgroup (min(G, 4))
+  int nhb;  // head blocks per KV head (G / hpw)
+  int rb;   // query rows per workgroup ((4 / hpw) * mq)
+  int nqc;  // row blocks (ceil(m / rb))
+};
+__host__ __device__ inline Plan make_plan(int H, int Hkv, int m, int mq) {
+  Plan p;
+  const int G = H / Hkv;
+  p.hpw = G < kWaves ? G : kWaves;
+  p.nhb = G / p.hpw;
+  p.rb = (kWaves / p.hpw) * mq;
+  p.nqc = (m + p.rb - 1) / p.rb;
+  return p;
+}
+
+template <typename ET, int HD> struct Lds {
+  static constexpr int KROW = HD * static_cast<int>(sizeof(ET));  // bytes of a K/V row
+  static constexpr int KSTR = KROW + 16;                          // padded K row stride (bank spread)
+  static constexpr int CPR = KROW / 16;                           // 16-byte chunks per row
+  static constexpr int NL = KT * CPR / kThreadsA;                 // chunks per thread per tile (K or V)
+  static constexpr size_t k_off = 0;
+  static constexpr size_t v_off = k_off + static_cast<size_t>(KT) * KSTR;
+  static constexpr size_t q_off = v_off + static_cast<size_t>(KT) * KROW;
+  template <int MQ> static constexpr size_t p_off() { return q_off + sizeof(float) * kWaves * MQ * HD; }
+  template <int MQ> static constexpr size_t bytes() { return p_off<MQ>() + sizeof(float) * kWaves * MQ * KT; }
+};
+
+template <typename ET, int HD>
+__device__ __forceinline__ void load_tile(const ET* kc, const ET* vc, size_t kvbase, int k0, int klast,
+                                          v4u (&kr)[Lds<ET, HD>::NL], v4u (&vr)[Lds<ET, HD>::NL]) {
+  using L = Lds<ET, HD>;
+#pragma unroll
+  for (int i = 0; i < L::NL; ++i) {
+    const int c = threadIdx.x + i * kThreadsA;
+    const int row = c / L::CPR, col = c - row * L::CPR;
+    const size_t g = (kvbase + min(k0 + row, klast)) * HD + static_cast<size_t>(col) * Cvt<ET>::n;
+    kr[i] = *reinterpret_cast<const v4u*>(kc + g);
+    vr[i] = *reinterpret_cast<const v4u*>(vc + g);
   }
 }
 
-// grid: x = b * Hkv + kvh, y = context split, z = query tile.
-// Thread t: local query row t / 8, sub-lane t % 8 (scores for keys sub*4 ..
-// sub*4+3 of a tile; output dims sub + 8*k).
 template <typename ET, int HD>
-__global__ __launch_bounds__(kThreads) void attn_partial_kernel(const float* __restrict__ qkv, const ET* __restrict__ kc,
-                                                                const ET* __restrict__ vc, const int32_t* __restrict__ len,
-                                                                int m, int H, int Hkv, int layer, int kvB, int max_ctx,
-                                                                int n_split, float* __restrict__ part_o,
-                                                                float2* __restrict__ part_ml) {
-  constexpr int DPT = HD / 8;
-  __shared__ float qs[QT][HD + 1];
-  __shared__ float ks[KT][HD + 1];
-  __shared__ float vs[KT][HD + 1];
-  __shared__ float ps[QT][KT + 1];
-
-  const int G = H / Hkv;
-  const int b = blockIdx.x / Hkv, kvh = blockIdx.x - b * Hkv;
-  const int s = blockIdx.y, qt = blockIdx.z;
-  const int nq = G * m;
-  const int t = threadIdx.x;
-  const int row = t >> 3, sub = t & 7;
-  const int qr = qt * QT + row;
-  const bool row_valid = qr < nq;
-  const int g = row_valid ? qr / m : 0;
-  const int i = row_valid ? qr - g * m : 0;
-  const int h = kvh * G + g;
-  const int Lb = len[b];
-  const int n_keys = max(0, min(Lb + m, max_ctx));
-  const int per = (n_keys + n_split - 1) / n_split;
-  const int kbeg = s * per;
-  const int kend = min(kbeg + per, n_keys);
-  const int lim = Lb + i;
-  const int qkv_ld = (H + 2 * Hkv) * HD;
-  const float scale = 1.0f / sqrtf(static_cast<float>(HD));
-
-  for (int idx = t; idx < QT * HD; idx += kThreads) {
-    const int rr = idx / HD, dd = idx - rr * HD;
-    const int q2 = qt * QT + rr;
-    float v = 0.f;
-    if (q2 < nq) {
-      const int g2 = q2 / m, i2 = q2 - g2 * m;
-      v = qkv[static_cast<size_t>(b * m + i2) * qkv_ld + (kvh * G + g2) * HD + dd] * scale;
-    }
-    qs[rr][dd] = v;
-  }
-
-  float mrow = -INFINITY, lrow = 0.f;
-  float acc[DPT];
+__device__ __forceinline__ void store_tile(char* ks, char* vs, const v4u (&kr)[Lds<ET, HD>::NL],
+                                           const v4u (&vr)[Lds<ET, HD>::NL]) {
+  using L = Lds<ET, HD>;
 #pragma unroll
-  for (int k = 0; k < DPT; ++k) acc[k] = 0.f;
-  const size_t kvbase = ((static_cast<size_t>(layer) * kvB + b) * Hkv + kvh) * max_ctx;
+  for (int i = 0; i < L::NL; ++i) {
+    const int c = threadIdx.x + i * kThreadsA;
+    const int row = c / L::CPR, col = c - row * L::CPR;
+    *reinterpret_cast<v4u*>(ks + row * L::KSTR + col * 16) = kr[i];
+    *reinterpret_cast<v4u*>(vs + row * L::KROW + col * 16) = vr[i];
+  }
+}
+
+template <typename ET, int HD, int MQ>
+__global__ __launch_bounds__(kThreadsA) void attn_kernel(AttnArgs a) {
+  using L = Lds<ET, HD>;
+  constexpr int DPL = HD / kWave;  // output dims per lane
+  constexpr int CE = Cvt<ET>::n;   // elements per 16-byte chunk
+  static_assert(L::NL * kThreadsA == KT * L::CPR, "tile chunks must split evenly over the threads");
+  extern __shared__ uint4 smem_a[];
+  char* sm = reinterpret_cast<char*>(smem_a);
+  char* ks = sm + L::k_off;
+  ET* vs = reinterpret_cast<ET*>(sm + L::v_off);
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  float (*qs)[HD] = reinterpret_cast<float (*)[HD]>(sm + L::q_off) + wave * MQ;
+  float (*ps)[KT] = reinterpret_cast<float (*)[KT]>(sm + L::template p_off<MQ>()) + wave * MQ;
+  __shared__ int last_sh;
+
+  const int H = a.H, Hkv = a.Hkv, m = a.m;
+  const Plan pl = make_plan(H, Hkv, m, MQ);
+  const int G = H / Hkv;
+  const int hb = blockIdx.x % pl.nhb;
+  const int kvh = (blockIdx.x / pl.nhb) % Hkv;
+  const int b = blockIdx.x / (pl.nhb * Hkv);
+  const int s = blockIdx.y, qc = blockIdx.z;
+  const int h = kvh * G + hb * pl.hpw + wave % pl.hpw;
+  const int i0 = qc * pl.rb + (wave / pl.hpw) * MQ;
+  const int nrows = max(0, min(MQ, m - i0));
+  const int Lb = a.len[b];
+  const int n_keys = max(0, min(Lb + m, a.max_ctx));
+  const int per = (n_keys + a.n_split - 1) / a.n_split;
+  const int kbeg = s * per;
+  // keys past the workgroup's last visible one are not read
+  const int wg_last_row = min(m, (qc + 1) * pl.rb) - 1;
+  const int kend = min(min(kbeg + per, n_keys), max(0, Lb + wg_last_row + 1));
+  const float scale = 1.0f / sqrtf(static_cast<float>(HD));
+  const int qld = H * HD;
+  const ET* kc = static_cast<const ET*>(a.kc);
+  const ET* vc = static_cast<const ET*>(a.vc);
+  const size_t kvbase = ((static_cast<size_t>(a.layer) * a.kvB + b) * Hkv + kvh) * a.max_ctx;
+
+  // tile loads: chunk c = tid + i * 256 -> (row c / CPR, column chunk c % CPR);
+  // rows are clamped into [k0, kend) (row 0 for an empty split), so every
+  // load is unconditional; a prefetch past the last tile re-reads it
+  const int klast = max(kend - 1, 0);
+  v4u kr[L::NL], vr[L::NL];
+  load_tile<ET, HD>(kc, vc, kvbase, kbeg, klast, kr, vr);
+  // this wave's query rows, pre-scaled (rows past nrows are zero)
+#pragma unroll
+  for (int r = 0; r < MQ; ++r) {
+    const float* qr = a.q + static_cast<size_t>(b * m + min(i0 + r, m - 1)) * qld + h * HD + lane * DPL;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) {
+      const float v = qr[k];
+      qs[r][lane * DPL + k] = (r < nrows) ? v * scale : 0.f;
+    }
+  }
+  float mrow[MQ], lrow[MQ], o[MQ][DPL];
+#pragma unroll
+  for (int r = 0; r < MQ; ++r) {
+    mrow[r] = -INFINITY;
+    lrow[r] = 0.f;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) o[r][k] = 0.f;
+  }
 
   for (int k0 = kbeg; k0 < kend; k0 += KT) {
+    const int nt = min(KT, kend - k0);
+    __syncthreads();  // previous tile fully consumed
+    store_tile<ET, HD>(ks, reinterpret_cast<char*>(vs), kr, vr);
     __syncthreads();
-    for (int idx = t; idx < KT * HD; idx += kThreads) {
-      const int jj = idx / HD, dd = idx - jj * HD;
-      const int j = k0 + jj;
-      float kv = 0.f, vv = 0.f;
-      if (j < kend) {
-        kv = Elt<ET>::load(kc + (kvbase + j) * HD + dd);
-        vv = Elt<ET>::load(vc + (kvbase + j) * HD + dd);
+    load_tile<ET, HD>(kc, vc, kvbase, k0 + KT, klast, kr, vr);
+    // scores: lane = key; the key row in float32 registers
+    float kf[HD];
+#pragma unroll
+    for (int c = 0; c < L::CPR; ++c)
+      Cvt<ET>::run(*reinterpret_cast<const v4u*>(ks + lane * L::KSTR + c * 16), kf + c * CE);
+#pragma unroll 1
+    for (int r = 0; r < MQ; ++r) {  // rows past nrows have zero queries
+      float t0 = 0.f, t1 = 0.f;
+#pragma unroll
+      for (int e = 0; e < HD; e += 8) {
+        const float4 qa = *reinterpret_cast<const float4*>(&qs[r][e]);
+        const float4 qb = *reinterpret_cast<const float4*>(&qs[r][e + 4]);
+        t0 = fmaf(qa.x, kf[e], t0);
+        t1 = fmaf(qa.y, kf[e + 1], t1);
+        t0 = fmaf(qa.z, kf[e + 2], t0);
+        t1 = fmaf(qa.w, kf[e + 3], t1);
+        t0 = fmaf(qb.x, kf[e + 4], t0);
+        t1 = fmaf(qb.y, kf[e + 5], t1);
+        t0 = fmaf(qb.z, kf[e + 6], t0);
+        t1 = fmaf(qb.w, kf[e + 7], t1);
       }
-      ks[jj][dd] = kv;
-      vs[jj][dd] = vv;
+      ps[r][lane] = t0 + t1;
+    }
+    // online softmax; p overwrites the score (same lane).  All MQ rows run
+    // branch-free so their reductions interleave; rows past nrows see
+    // zero queries and are never written out.
+#pragma unroll
+    for (int r = 0; r < MQ; ++r) {
+      const bool valid = lane < nt && k0 + lane <= Lb + i0 + r;
+      const float sv = valid ? ps[r][lane] : -INFINITY;
+      const float mnew = fmaxf(mrow[r], wave_max(sv));
+      const bool live = mnew != -INFINITY;
+      const float alpha = live ? expf(mrow[r] - mnew) : 1.f;
+      const float p = (valid && live) ? expf(sv - mnew) : 0.f;
+      lrow[r] = lrow[r] * alpha + wave_sum(p);
+      mrow[r] = mnew;
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) o[r][k] *= alpha;
+      ps[r][lane] = p;
     }
     __syncthreads();
-    float sc[4];
+    // P.V over the tile, four keys at a time (keys past nt have p = 0 and
+    // finite V rows: the clamped copies of the last one)
+    const int nt4 = (nt + 3) & ~3;
+#pragma unroll 2
+    for (int j = 0; j < nt4; j += 4) {
+      float vf[4][DPL];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int jj = sub * 4 + c;
-      float a = 0.f;
-#pragma unroll 8
-      for (int dd = 0; dd < HD; ++dd) a = fmaf(qs[row][dd], ks[jj][dd], a);
-      const int j = k0 + jj;
-      sc[c] = (row_valid && j < kend && j <= lim) ? a : -INFINITY;
-    }
-    float tmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 1, kWave));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 2, kWave));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 4, kWave));
-    const float mnew = fmaxf(mrow, tmax);
-    const float alpha = (mnew == -INFINITY) ? 1.f : expf(mrow - mnew);
-    float psum = 0.f;
+      for (int t = 0; t < 4; ++t) VRow<ET, DPL>::load(vs + (j + t) * HD + lane * DPL, vf[t]);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const float p = (sc[c] == -INFINITY) ? 0.f : expf(sc[c] - mnew);
-      ps[row][sub * 4 + c] = p;
-      psum += p;
-    }
-    psum += __shfl_xor(psum, 1, kWave);
-    psum += __shfl_xor(psum, 2, kWave);
-    psum += __shfl_xor(psum, 4, kWave);
-    lrow = lrow * alpha + psum;
-    mrow = mnew;
+      for (int r = 0; r < MQ; ++r) {
+        const float4 p4 = *reinterpret_cast<const float4*>(&ps[r][j]);
 #pragma unroll
-    for (int k = 0; k < DPT; ++k) acc[k] *= alpha;
-    __syncthreads();
-    for (int jj = 0; jj < KT; ++jj) {
-      const float p = ps[row][jj];
-#pragma unroll
-      for (int k = 0; k < DPT; ++k) acc[k] = fmaf(p, vs[jj][sub + 8 * k], acc[k]);
+        for (int k = 0; k < DPL; ++k) {
+          float t = o[r][k];
+          t = fmaf(p4.x, vf[0][k], t);
+          t = fmaf(p4.y, vf[1][k], t);
+          t = fmaf(p4.z, vf[2][k], t);
+          t = fmaf(p4.w, vf[3][k], t);
+          o[r][k] = t;
+        }
+      }
     }
   }
-  if (row_valid) {
-    const size_t prow = ((static_cast<size_t>(b) * H + h) * m + i) * n_split + s;
-    if (sub == 0) part_ml[prow] = make_float2(mrow, lrow);
+
+  ET* xo = static_cast<ET*>(a.xo);
+  if (a.n_split == 1) {
 #pragma unroll
-    for (int k = 0; k < DPT; ++k) part_o[prow * HD + sub + 8 * k] = acc[k];
+    for (int r = 0; r < MQ; ++r) {
+      if (r < nrows) {
+#pragma unroll
+        for (int k = 0; k < DPL; ++k)
+          xo[static_cast<size_t>(b * m + i0 + r) * qld + h * HD + lane * DPL + k] =
+              Elt<ET>::from_f(lrow[r] > 0.f ? o[r][k] / lrow[r] : 0.f);
+      }
+    }
+    return;
+  }
+
+  const int ns = a.n_split;  // <= 64: one split per lane in the merge
+  const size_t prow0 = ((static_cast<size_t>(b) * H + h) * m + i0) * ns;
+#pragma unroll
+  for (int r = 0; r < MQ; ++r) {
+    if (r < nrows) {
+      const size_t prow = prow0 + static_cast<size_t>(r) * ns + s;
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) a.part_o[prow * HD + lane * DPL + k] = o[r][k];
+      if (lane == 0) a.part_ml[prow] = make_float2(mrow[r], lrow[r]);
+    }
+  }
+  if (!last_block(a.counters + static_cast<size_t>(blockIdx.x) * gridDim.z + qc, ns, &last_sh)) return;
+
+  // merge the splits of each of this wave's rows, in split order
+  for (int r = 0; r < nrows; ++r) {
+    const size_t pr = prow0 + static_cast<size_t>(r) * ns;
+    const float2 ml = (lane < ns) ? a.part_ml[pr + lane] : make_float2(-INFINITY, 0.f);
+    const float M = wave_max(ml.x);
+    const float w = (ml.x == -INFINITY) ? 0.f : expf(ml.x - M);
+    const float l = wave_sum(ml.y * w);
+    ps[0][lane] = w;
+    float acc[DPL];
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) acc[k] = 0.f;
+    for (int s0 = 0; s0 < ns; s0 += 16) {
+      float v[16][DPL];
+#pragma unroll
+      for (int t = 0; t < 16; ++t)
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) v[t][k] = a.part_o[(pr + min(s0 + t, ns - 1)) * HD + lane * DPL + k];
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const float ws = (s0 + t < ns) ? ps[0][s0 + t] : 0.f;
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) acc[k] = fmaf(v[t][k], ws, acc[k]);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < DPL; ++k)
+      xo[static_cast<size_t>(b * m + i0 + r) * qld + h * HD + lane * DPL + k] =
+          Elt<ET>::from_f(l > 0.f ? acc[k] / l : 0.f);
   }
 }
 
-// One block per (row r = b*m + i, head h); HD threads.  Fixed split order.
-template <typename XT, int HD>
-__global__ __launch_bounds__(HD) void attn_combine_kernel(const float* __restrict__ part_o,
-                                                          const float2* __restrict__ part_ml, int m, int H, int n_split,
-                                                          XT* __restrict__ x) {
-  const int idx = blockIdx.x;
-  const int h = idx % H, r = idx / H;
-  const int b = r / m, i = r - b * m;
-  const int d = threadIdx.x;
-  const size_t prow0 = ((static_cast<size_t>(b) * H + h) * m + i) * n_split;
-  float M = -INFINITY;
-  for (int s = 0; s < n_split; ++s) M = fmaxf(M, part_ml[prow0 + s].x);
-  float l = 0.f, o = 0.f;
-  for (int s = 0; s < n_split; ++s) {
-    const float2 ml = part_ml[prow0 + s];
-    const float w = (ml.x == -INFINITY) ? 0.f : expf(ml.x - M);
-    l = fmaf(ml.y, w, l);
-    o = fmaf(part_o[(prow0 + s) * HD + d], w, o);
+template <typename ET, int HD, int MQ>
+hipError_t launch_mq(const AttnArgs& a, int B, hipStream_t s) {
+  using L = Lds<ET, HD>;
+  auto kern = attn_kernel<ET, HD, MQ>;
+  constexpr size_t lds = L::template bytes<MQ>();
+  static bool opt_in = false;
+  if (!opt_in) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+    opt_in = true;
   }
-  x[static_cast<size_t>(r) * (H * HD) + h * HD + d] = Elt<XT>::from_f(l > 0.f ? o / l : 0.f);
+  const Plan pl = make_plan(a.H, a.Hkv, a.m, MQ);
+  if (pl.nqc != a.n_qc || a.n_split < 1 || a.n_split > kWave) return hipErrorInvalidValue;
+  dim3 grid(B * a.Hkv * pl.nhb, a.n_split, pl.nqc);
+  hipLaunchKernelGGL(kern, grid, dim3(kThreadsA), lds, s, a);
+  return hipGetLastError();
 }
 
 template <typename ET, int HD>
-hipError_t attention_typed(const float* qkv, const ET* kc, const ET* vc, const int32_t* len, int B, int m, int H,
-                           int Hkv, int layer, int kvB, int max_ctx, int n_split, float* part_o, float2* part_ml,
-                           ET* x, hipStream_t s) {
-  const int G = H / Hkv;
-  dim3 grid(B * Hkv, n_split, (G * m + QT - 1) / QT);
-  hipLaunchKernelGGL((attn_partial_kernel<ET, HD>), grid, dim3(kThreads), 0, s, qkv, kc, vc, len, m, H, Hkv, layer,
-                     kvB, max_ctx, n_split, part_o, part_ml);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_combine_kernel<ET, HD>), dim3(B * m * H), dim3(HD), 0, s, part_o, part_ml, m, H, n_split,
-                     x);
-  return hipGetLastError();
+hipError_t launch_hd(const AttnArgs& a, int B, hipStream_t s) {
+  switch (a.m < 8 ? a.m : 8) {
+    case 1: return launch_mq<ET, HD, 1>(a, B, s);
+    case 2: return launch_mq<ET, HD, 2>(a, B, s);
+    case 3: return launch_mq<ET, HD, 3>(a, B, s);
+    case 4: return launch_mq<ET, HD, 4>(a, B, s);
+    case 5: return launch_mq<ET, HD, 5>(a, B, s);
+    case 6: return launch_mq<ET, HD, 6>(a, B, s);
+    case 7: return launch_mq<ET, HD, 7>(a, B, s);
+    default: return launch_mq<ET, HD, 8>(a, B, s);
+  }
 }
 
 }  // namespace
 
-int attn_num_splits(int B, int Hkv, int G, int m, int max_ctx) {
-  const int units = B * Hkv * ((G * m + QT - 1) / QT);
+bool attn_supported(int H, int Hkv, int hd) {
+  if (hd != 64 && hd != 128) return false;
+  if (Hkv <= 0 || H % Hkv != 0) return false;
+  const int G = H / Hkv;
+  return G <= kWaves ? (kWaves % G == 0) : (G % kWaves == 0);
+}
+
+int attn_row_blocks(int H, int Hkv, int m) { return make_plan(H, Hkv, m, m < 8 ? m : 8).nqc; }
+
+int attn_num_splits(int B, int H, int Hkv, int m, int max_ctx) {
+  const Plan pl = make_plan(H, Hkv, m, m < 8 ? m : 8);
+  const int units = B * Hkv * pl.nhb * pl.nqc;  // workgroups per split
   int n = (512 + units - 1) / units;
-  n = min(n, max(1, max_ctx / (2 * KT)));
-  return max(1, min(n, 32));
+  n = min(n, (max_ctx + KT - 1) / KT);
+  return max(1, min(n, kWave));
 }
 
-hipError_t launch_rope_append(bool bf16, float* qkv, const float2* cs, const int32_t* len, int B, int m, int H, int Hkv,
-                              int hd, void* kc, void* vc, int layer, int kvB, int max_ctx, hipStream_t s) {
-  if (bf16)
-    hipLaunchKernelGGL(rope_append_kernel<uint16_t>, dim3(B * m), dim3(kThreads), 0, s, qkv, cs, len, m, H, Hkv, hd,
-                       static_cast<uint16_t*>(kc), static_cast<uint16_t*>(vc), layer, kvB, max_ctx);
-  else
-    hipLaunchKernelGGL(rope_append_kernel<float>, dim3(B * m), dim3(kThreads), 0, s, qkv, cs, len, m, H, Hkv, hd,
-                       static_cast<float*>(kc), static_cast<float*>(vc), layer, kvB, max_ctx);
-  return hipGetLastError();
+size_t attn_counters(int B, int H, int Hkv, int m) {
+  const Plan pl = make_plan(H, Hkv, m, m < 8 ? m : 8);
+  return static_cast<size_t>(B) * Hkv * pl.nhb * pl.nqc;
 }
 
-hipError_t launch_attention(bool bf16, const float* qkv, const void* kc, const void* vc, const int32_t* len, int B,
-                            int m, int H, int Hkv, int hd, int layer, int kvB, int max_ctx, int n_split, float* part_o,
-                            float2* part_ml, void* x, hipStream_t s) {
-  if (bf16) {
-    const uint16_t *k = static_cast<const uint16_t*>(kc), *v = static_cast<const uint16_t*>(vc);
-    uint16_t* xx = static_cast<uint16_t*>(x);
-    return hd == 128 ? attention_typed<uint16_t, 128>(qkv, k, v, len, B, m, H, Hkv, layer, kvB, max_ctx, n_split,
-                                                      part_o, part_ml, xx, s)
-                     : attention_typed<uint16_t, 64>(qkv, k, v, len, B, m, H, Hkv, layer, kvB, max_ctx, n_split,
-                                                     part_o, part_ml, xx, s);
-  }
-  const float *k = static_cast<const float*>(kc), *v = static_cast<const float*>(vc);
-  float* xx = static_cast<float*>(x);
-  return hd == 128 ? attention_typed<float, 128>(qkv, k, v, len, B, m, H, Hkv, layer, kvB, max_ctx, n_split, part_o,
-                                                 part_ml, xx, s)
-                   : attention_typed<float, 64>(qkv, k, v, len, B, m, H, Hkv, layer, kvB, max_ctx, n_split, part_o,
-                                                part_ml, xx, s);
+hipError_t launch_attention(bool bf16, int hd, const AttnArgs& a, int B, hipStream_t s) {
+  if (B <= 0 || a.m <= 0) return hipSuccess;
+  if (!attn_supported(a.H, a.Hkv, hd)) return hipErrorInvalidValue;
+  if (bf16) return hd == 128 ? launch_hd<uint16_t, 128>(a, B, s) : launch_hd<uint16_t, 64>(a, B, s);
+  return hd == 128 ? launch_hd<float, 128>(a, B, s) : launch_hd<float, 64>(a, B, s);
 }
 
 }  // namespace sv

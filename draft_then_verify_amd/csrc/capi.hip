@@ -46,18 +46,19 @@ size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 struct Layout {
-  size_t h, xa, xb, qkv, cs, po, pml, logits, part, csum, total;
-  int n_split;
+  size_t h, xn, xo, z, q, cs, po, pml, ctr, logits, part, csum, total;
+  int n_split, n_qc, n_ctr;
 };
 
 Layout make_layout(const spec_model_cfg& c, int B, int m, int max_ctx) {
   Layout L{};
   const size_t rows = static_cast<size_t>(B) * m;
   const size_t elt = c.dtype == SPEC_BF16 ? 2 : 4;
-  const int G = c.n_heads / c.n_kv_heads;
   const int hq = c.n_heads * c.head_dim;
   const int nch = sv::sampler_chunks(c.vocab);
-  L.n_split = sv::attn_num_splits(B, c.n_kv_heads, G, m, max_ctx);
+  L.n_qc = sv::attn_row_blocks(c.n_heads, c.n_kv_heads, m);
+  L.n_split = sv::attn_num_splits(B, c.n_heads, c.n_kv_heads, m, max_ctx);
+  L.n_ctr = static_cast<int>(sv::attn_counters(B, c.n_heads, c.n_kv_heads, m));
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -65,12 +66,14 @@ Layout make_layout(const spec_model_cfg& c, int B, int m, int max_ctx) {
     return o;
   };
   L.h = take(rows * c.d_model * 4);
-  L.xa = take(rows * std::max(c.d_model, hq) * elt);
-  L.xb = take(rows * c.d_ff * elt);
-  L.qkv = take(rows * (c.n_heads + 2 * c.n_kv_heads) * c.head_dim * 4);
+  L.xn = take(rows * c.d_model * elt);
+  L.xo = take(rows * hq * elt);
+  L.z = take(rows * c.d_ff * elt);
+  L.q = take(rows * hq * 4);
   L.cs = take(rows * (c.head_dim / 2) * 8);
   L.po = take(static_cast<size_t>(B) * c.n_heads * m * L.n_split * c.head_dim * 4);
   L.pml = take(static_cast<size_t>(B) * c.n_heads * m * L.n_split * 8);
+  L.ctr = take((static_cast<size_t>(L.n_ctr) + 1) * 4);  // attention tickets + the linears' ticket
   L.logits = take(rows * c.vocab * 4);
   L.part = take(rows * nch * 8);
   L.csum = take(static_cast<size_t>(B) * nch * 16);
@@ -88,7 +91,12 @@ spec_status check_kv(const spec_model* M, const spec_kv* kv, int B, int m) {
   return SPEC_OK;
 }
 
-// Launch sequence of one forward pass over B x m rows.
+// Launch sequence of one forward pass over B x m rows.  The embedding kernel
+// writes the residual rows h and the first RMSNorm's output; per layer
+//   QKV linear (RoPE + KV append) -> attention (split context, merged
+//   in-kernel) -> O linear (+= h, then the MLP RMSNorm) -> gate/up linear
+//   (SwiGLU) -> down linear (+= h, then the next RMSNorm);
+// then the LM head on the final RMSNorm.
 spec_status run_forward(const spec_model* M, const spec_kv* kv, int B, int m, const int32_t* tokens,
                         const int32_t* last, const int32_t* draft, float* logits, const Layout& L, char* ws,
                         hipStream_t s) {
@@ -96,30 +104,87 @@ spec_status run_forward(const spec_model* M, const spec_kv* kv, int B, int m, co
   const bool bf16 = c.dtype == SPEC_BF16;
   const int rows = B * m;
   const int d = c.d_model, H = c.n_heads, Hkv = c.n_kv_heads, hd = c.head_dim, F = c.d_ff, V = c.vocab;
-  const int qkv_rows = (H + 2 * Hkv) * hd;
   float* h = reinterpret_cast<float*>(ws + L.h);
-  void* xa = ws + L.xa;
-  void* xb = ws + L.xb;
-  float* qkv = reinterpret_cast<float*>(ws + L.qkv);
+  void* xn = ws + L.xn;
   float2* cs = reinterpret_cast<float2*>(ws + L.cs);
-  float* po = reinterpret_cast<float*>(ws + L.po);
-  float2* pml = reinterpret_cast<float2*>(ws + L.pml);
+  int* ctr = reinterpret_cast<int*>(ws + L.ctr);
+  int* ticket = ctr + L.n_ctr;
 
-  HIP_TRY(sv::launch_embed(bf16, M->embed, V, d, tokens, last, draft, kv->len, B, m, hd, c.rope_theta, h, cs, s));
+  HIP_TRY(sv::launch_embed(bf16, M->embed, V, d, tokens, last, draft, kv->len, B, m, hd, c.rope_theta,
+                           M->attn_norm[0], c.rms_eps, h, xn, cs, ctr, L.n_ctr + 1, s));
+  sv::GemvArgs qkv;
+  qkv.N = (H + 2 * Hkv) * hd;
+  qkv.K = d;
+  qkv.x = xn;
+  qkv.q = reinterpret_cast<float*>(ws + L.q);
+  qkv.H = H;
+  qkv.Hkv = Hkv;
+  qkv.hd = hd;
+  qkv.cs = cs;
+  qkv.kc = kv->k;
+  qkv.vc = kv->v;
+  qkv.len = kv->len;
+  qkv.m_per_seq = m;
+  qkv.kvB = kv->B;
+  qkv.max_ctx = kv->max_ctx;
+  sv::AttnArgs at;
+  at.q = qkv.q;
+  at.kc = kv->k;
+  at.vc = kv->v;
+  at.len = kv->len;
+  at.m = m;
+  at.H = H;
+  at.Hkv = Hkv;
+  at.kvB = kv->B;
+  at.max_ctx = kv->max_ctx;
+  at.n_split = L.n_split;
+  at.n_qc = L.n_qc;
+  at.part_o = reinterpret_cast<float*>(ws + L.po);
+  at.part_ml = reinterpret_cast<float2*>(ws + L.pml);
+  at.counters = ctr;
+  at.xo = ws + L.xo;
+  sv::GemvArgs o;
+  o.N = d;
+  o.K = H * hd;
+  o.x = ws + L.xo;
+  o.y = h;
+  o.ldy = d;
+  o.norm_out = xn;
+  o.eps = c.rms_eps;
+  o.ticket = ticket;
+  sv::GemvArgs gu;
+  gu.N = F;
+  gu.K = d;
+  gu.x = xn;
+  gu.z = ws + L.z;
+  gu.ldz = F;
+  sv::GemvArgs dn = o;
+  dn.K = F;
+  dn.x = ws + L.z;
   for (int l = 0; l < c.n_layers; ++l) {
-    HIP_TRY(sv::launch_rmsnorm(bf16, h, M->attn_norm[l], rows, d, c.rms_eps, xa, s));
-    HIP_TRY(sv::launch_gemv(bf16, sv::EPI_STORE, M->wqkv[l], xa, rows, qkv_rows, d, qkv, qkv_rows, nullptr, 0, s));
-    HIP_TRY(sv::launch_rope_append(bf16, qkv, cs, kv->len, B, m, H, Hkv, hd, kv->k, kv->v, l, kv->B, kv->max_ctx, s));
-    HIP_TRY(sv::launch_attention(bf16, qkv, kv->k, kv->v, kv->len, B, m, H, Hkv, hd, l, kv->B, kv->max_ctx, L.n_split,
-                                 po, pml, xa, s));
-    HIP_TRY(sv::launch_gemv(bf16, sv::EPI_RESID, M->wo[l], xa, rows, d, H * hd, h, d, nullptr, 0, s));
-    HIP_TRY(sv::launch_rmsnorm(bf16, h, M->mlp_norm[l], rows, d, c.rms_eps, xa, s));
-    HIP_TRY(sv::launch_gemv(bf16, sv::EPI_SWIGLU, M->wgu[l], xa, rows, F, d, nullptr, 0, xb, F, s));
-    HIP_TRY(sv::launch_gemv(bf16, sv::EPI_RESID, M->wd[l], xb, rows, d, F, h, d, nullptr, 0, s));
+    qkv.W = M->wqkv[l];
+    qkv.layer = l;
+    HIP_TRY(sv::launch_gemv(bf16, sv::EPI_QKV, qkv, rows, s));
+    at.layer = l;
+    HIP_TRY(sv::launch_attention(bf16, hd, at, B, s));
+    o.W = M->wo[l];
+    o.norm_gain = M->mlp_norm[l];
+    HIP_TRY(sv::launch_gemv(bf16, sv::EPI_RESID, o, rows, s));
+    gu.W = M->wgu[l];
+    HIP_TRY(sv::launch_gemv(bf16, sv::EPI_SWIGLU, gu, rows, s));
+    dn.W = M->wd[l];
+    dn.norm_gain = l + 1 < c.n_layers ? M->attn_norm[l + 1] : M->final_norm;
+    HIP_TRY(sv::launch_gemv(bf16, sv::EPI_RESID, dn, rows, s));
   }
   if (logits) {
-    HIP_TRY(sv::launch_rmsnorm(bf16, h, M->final_norm, rows, d, c.rms_eps, xa, s));
-    HIP_TRY(sv::launch_gemv(bf16, sv::EPI_STORE, M->lm_head, xa, rows, V, d, logits, V, nullptr, 0, s));
+    sv::GemvArgs lm;
+    lm.W = M->lm_head;
+    lm.N = V;
+    lm.K = d;
+    lm.x = xn;
+    lm.y = logits;
+    lm.ldy = V;
+    HIP_TRY(sv::launch_gemv(bf16, sv::EPI_STORE, lm, rows, s));
   }
   return SPEC_OK;
 }
@@ -137,6 +202,13 @@ SPEC_API spec_status spec_model_create(const spec_model_cfg* cfg, const spec_wei
   if (c.dtype != SPEC_F32 && c.dtype != SPEC_BF16) return fail(SPEC_EINVAL, "dtype %d", c.dtype);
   if (c.head_dim != 64 && c.head_dim != 128) return fail(SPEC_EUNSUPPORTED, "head_dim %d (64 or 128)", c.head_dim);
   if (c.n_heads % c.n_kv_heads) return fail(SPEC_EINVAL, "n_heads %% n_kv_heads != 0");
+  if (!sv::attn_supported(c.n_heads, c.n_kv_heads, c.head_dim))
+    return fail(SPEC_EUNSUPPORTED, "query heads per KV head %d must divide 4 or be a multiple of 4",
+                c.n_heads / c.n_kv_heads);
+  if (c.d_model > 16 * 256) return fail(SPEC_EUNSUPPORTED, "d_model %d > 4096", c.d_model);
+  if (static_cast<size_t>(std::max(c.d_model, std::max(c.d_ff, c.n_heads * c.head_dim))) *
+          (c.dtype == SPEC_BF16 ? 2 : 4) > 159 * 1024)
+    return fail(SPEC_EUNSUPPORTED, "a linear input row does not fit the 159 KiB of LDS");
   const int vec = c.dtype == SPEC_BF16 ? 8 : 4;
   if (c.d_model % vec || c.d_ff % vec || (c.n_heads * c.head_dim) % vec)
     return fail(SPEC_EINVAL, "d_model, d_ff and n_heads*head_dim must be multiples of %d", vec);
@@ -284,7 +356,18 @@ SPEC_API spec_status spec_linear(int32_t dtype, int32_t epilogue, const void* W,
   if (K % vec) return fail(SPEC_EINVAL, "K=%d not a multiple of %d", K, vec);
   if (!W || !x || !aligned16(W) || !aligned16(x)) return fail(SPEC_EINVAL, "W/x NULL or not 16-byte aligned");
   if (epilogue == 2 ? !z : !y) return fail(SPEC_EINVAL, "output pointer NULL");
-  HIP_TRY(sv::launch_gemv(dtype == SPEC_BF16, epilogue, W, x, M, N, K, y, N, z, N, stream));
+  if (static_cast<size_t>(K) * (dtype == SPEC_BF16 ? 2 : 4) > 159 * 1024)
+    return fail(SPEC_EINVAL, "K=%d: an input row must fit the 159 KiB of LDS", K);
+  sv::GemvArgs a;
+  a.W = W;
+  a.N = N;
+  a.K = K;
+  a.x = x;
+  a.y = y;
+  a.ldy = N;
+  a.z = z;
+  a.ldz = N;
+  HIP_TRY(sv::launch_gemv(dtype == SPEC_BF16, epilogue, a, M, stream));
   return SPEC_OK;
 }
 

@@ -34,17 +34,34 @@ template <> struct Elt<uint16_t> {
   __device__ __forceinline__ static uint16_t from_f(float x) { return f2bf(x); }
 };
 
-// Butterfly reductions over the 64 lanes of a wave.  Every lane ends with the
-// same bits: each step adds the same two operands on both partner lanes.
+// Reductions over the 64 lanes of a wave with DPP lane moves (no LDS
+// round trip): pairs, quads, mirrored halves and rows of 16 lanes, then the
+// four row results read as uniform values and combined as (r0 + r1) + (r2 + r3).
+// Every lane receives the same bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+constexpr int kDppQuadSwap1 = 0xb1;    // quad_perm [1,0,3,2]
+constexpr int kDppQuadSwap2 = 0x4e;    // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <-> 7 - i within 8
+constexpr int kDppMirror = 0x140;      // lane i <-> 15 - i within 16
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+  v += dpp_mov<kDppQuadSwap1>(v);
+  v += dpp_mov<kDppQuadSwap2>(v);
+  v += dpp_mov<kDppHalfMirror>(v);
+  v += dpp_mov<kDppMirror>(v);
+  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
-  return v;
+  v = fmaxf(v, dpp_mov<kDppQuadSwap1>(v));
+  v = fmaxf(v, dpp_mov<kDppQuadSwap2>(v));
+  v = fmaxf(v, dpp_mov<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_mov<kDppMirror>(v));
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
 __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
 #pragma unroll
@@ -90,6 +107,99 @@ __device__ __forceinline__ unsigned long long block_sum_u64(unsigned long long v
 #pragma unroll
   for (int i = 1; i < NT / kWave; ++i) s += red[i];
   return s;
+}
+
+// RMSNorm of G consecutive residual rows (h [G][ld] -> out [G][d] in the
+// model dtype) by one workgroup of NT threads:
+// x = cvt(h * rsqrt(mean(h^2) + eps) * g).  d % 4 == 0, d <= 16 * NT,
+// ld % 4 == 0.  Every load is issued before any is used (16-byte loads,
+// indexes clamped, surplus chunks weigh zero): one memory round trip.  Fixed
+// order: per-thread sums, wave butterflies, waves in index order.
+template <int NT, int G, typename OT>
+__device__ __forceinline__ void norm_group(const float* h, int ld, int d, const float* gain, float eps, OT* out,
+                                           float (*red)[8]) {
+  constexpr int CPT = 4;  // 16-byte chunks per thread and row
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int d4 = d / 4;
+  float4 v[G][CPT];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float4* hr = reinterpret_cast<const float4*>(h + static_cast<size_t>(g) * ld);
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) v[g][c] = hr[min(static_cast<int>(threadIdx.x) + c * NT, d4 - 1)];
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      if (static_cast<int>(threadIdx.x) + c * NT < d4) {
+        ss = fmaf(v[g][c].x, v[g][c].x, ss);
+        ss = fmaf(v[g][c].y, v[g][c].y, ss);
+        ss = fmaf(v[g][c].z, v[g][c].z, ss);
+        ss = fmaf(v[g][c].w, v[g][c].w, ss);
+      }
+    }
+    ss = wave_sum(ss);
+    if (lane == 0) red[wave][g] = ss;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float ss = red[0][g];
+#pragma unroll
+    for (int w = 1; w < NT / kWave; ++w) ss += red[w][g];
+    const float scale = rsqrtf(ss / static_cast<float>(d) + eps);
+    OT* o = out + static_cast<size_t>(g) * d;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int e4 = threadIdx.x + c * NT;
+      if (e4 < d4) {
+        const float4 gv = reinterpret_cast<const float4*>(gain)[e4];
+        o[4 * e4 + 0] = Elt<OT>::from_f(v[g][c].x * scale * gv.x);
+        o[4 * e4 + 1] = Elt<OT>::from_f(v[g][c].y * scale * gv.y);
+        o[4 * e4 + 2] = Elt<OT>::from_f(v[g][c].z * scale * gv.z);
+        o[4 * e4 + 3] = Elt<OT>::from_f(v[g][c].w * scale * gv.w);
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// RMSNorm of M (1..8, a compile-time count) rows: one round trip for M <= 5,
+// two otherwise (rows 0-3, then the rest).
+template <int NT, int M, typename OT>
+__device__ __forceinline__ void norm_rows(const float* h, int ld, int d, const float* gain, float eps, OT* out) {
+  static_assert(M >= 1 && M <= 8, "1..8 rows");
+  __shared__ float red_nr[NT / kWave][8];
+  if constexpr (M <= 5) {
+    norm_group<NT, M>(h, ld, d, gain, eps, out, red_nr);
+  } else {
+    norm_group<NT, 4>(h, ld, d, gain, eps, out, red_nr);
+    norm_group<NT, M - 4>(h + 4 * static_cast<size_t>(ld), ld, d, gain, eps, out + 4 * static_cast<size_t>(d), red_nr);
+  }
+}
+
+// True in exactly one of the n workgroups that arrive at `ticket`: the last
+// (which resets it to zero).  Writes made before the call by all n are
+// visible to that workgroup afterwards.  Every wave first drains its own
+// stores (vmcnt(0): the workgroup barrier alone does not wait for global
+// stores); then one thread per workgroup publishes with an agent-scope
+// release, and only the last workgroup acquires.
+__device__ __forceinline__ bool last_block(int* ticket, int n, int* flag_sh) {
+  __builtin_amdgcn_s_waitcnt(0x0f70);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int prev = __hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = prev == n - 1;
+    if (last) {
+      __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    *flag_sh = last;
+  }
+  __syncthreads();
+  return *flag_sh;
 }
 
 }  // namespace sv

@@ -1,0 +1,288 @@
+// Weight-streaming GEMV kernel for the verify pass:
+//   y[M][N] = x[M][K] . W[N][K]^T, M <= 8 activation rows per launch.
+//
+// The pass is bound by reading the weights: a decode/verify pass "reads the
+// entire ... weight set and then does about two floating-point operations per
+// weight" (first page, section "The speedup is borrowed"), and checking five
+// positions instead of one "reads the same weights" (same section).  So every
+// weight byte is loaded exactly once per launch and used for all M rows.
+//
+// Structure (persistent, one launch streams the whole matrix):
+//  * The grid is a few workgroups per CU.  Each workgroup stages the M
+//    activation rows in LDS once (up to 160 KiB on gfx950); in NORM mode the
+//    staging is the RMSNorm itself (sum of squares of the float32 residual
+//    rows, reduced in a fixed order so every workgroup gets the same bits).
+//  * Each wave walks its own list of row tiles (R rows; 2R for SwiGLU's gate
+//    and up rows) as one continuous stream of 1 KiB steps: 64 lanes x 16 B of
+//    one weight row per load instruction.  A ring of U register slots keeps
+//    U * R loads per lane in flight across tile boundaries, so the stream only
+//    drains at the very end of the matrix.  The first U steps are issued
+//    before the activations are staged.
+//  * bf16: v_dot2_f32_bf16 multiplies two bf16 pairs and accumulates in
+//    float32 without converting the weights; float32 models use fma.
+//  * At the end of a tile: one butterfly reduction per (row, activation row)
+//    and the epilogue -- store, add into the float32 residual stream,
+//    silu(g) * u, or (QKV) RoPE on q/k and the K/V append.  For QKV a wave's 4
+//    rows are {j, j+1, j+hd/2, j+1+hd/2} of one head, so both halves of each
+//    rotated pair meet in the same wave.
+#pragma once
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace sv {
+namespace gemv {
+
+constexpr int kThreads = 256;
+constexpr int kWavesPerBlock = kThreads / kWave;
+constexpr int kMaxLds = 159 * 1024;  // dynamic LDS; 1 KiB is left for static arrays
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const u32x4 global_u32x4;
+
+// Weights are read once: non-temporal loads keep them from displacing the
+// activations and KV rows in the caches.  The explicit global address space
+// keeps these as global (not flat) loads, which count only against vmcnt, so
+// waiting for the LDS activation reads never drains the weight stream.
+__device__ __forceinline__ uint4 load_stream(const void* p) {
+  u32x4 v = __builtin_nontemporal_load((global_u32x4*)(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+template <typename WT> struct Dot;
+template <> struct Dot<uint16_t> {  // 8 bf16 x 8 bf16, float32 accumulate
+  __device__ __forceinline__ static float run(const uint4& w, const uint4& x, float acc) {
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.x), __builtin_bit_cast(bf16x2_t, x.x), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.y), __builtin_bit_cast(bf16x2_t, x.y), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.z), __builtin_bit_cast(bf16x2_t, x.z), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.w), __builtin_bit_cast(bf16x2_t, x.w), acc, false);
+    return acc;
+  }
+};
+template <> struct Dot<float> {  // 4 float32 x 4 float32
+  __device__ __forceinline__ static float run(const uint4& w, const uint4& x, float acc) {
+    acc = fmaf(__uint_as_float(w.x), __uint_as_float(x.x), acc);
+    acc = fmaf(__uint_as_float(w.y), __uint_as_float(x.y), acc);
+    acc = fmaf(__uint_as_float(w.z), __uint_as_float(x.z), acc);
+    acc = fmaf(__uint_as_float(w.w), __uint_as_float(x.w), acc);
+    return acc;
+  }
+};
+
+template <int EPI, int R> struct Tiles {
+  static constexpr int NW = (EPI == EPI_SWIGLU) ? 2 * R : R;  // weight rows per tile
+};
+
+// Number of R-row tiles of a launch.
+template <int EPI, int R>
+__host__ __device__ inline int num_tiles(int N) {
+  return EPI == EPI_QKV ? N / 4 : (N + R - 1) / R;
+}
+
+// Weight rows of tile t (clamped into range; the epilogue checks validity).
+template <int EPI, int R>
+__device__ __forceinline__ void tile_rows(const GemvArgs& a, int t, int (&rows)[Tiles<EPI, R>::NW]) {
+  if constexpr (EPI == EPI_QKV) {
+    const int q4 = a.hd / 4;
+    const int hh = t / q4, j = 2 * (t - hh * q4);
+    const int base = hh * a.hd;
+    rows[0] = base + j;
+    rows[1] = base + j + 1;
+    rows[2] = base + j + a.hd / 2;
+    rows[3] = base + j + 1 + a.hd / 2;
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      rows[r] = min(t * R + r, a.N - 1);
+      if constexpr (EPI == EPI_SWIGLU) rows[R + r] = rows[r] + a.N;
+    }
+  }
+}
+
+// Stage the M activation rows of the launch into LDS (model dtype, row
+// stride KP >= K, zero-padded to KP).
+template <typename WT, int M>
+__device__ __forceinline__ void stage_x(const GemvArgs& a, WT* xs, int KP) {
+  constexpr int VE = 16 / sizeof(WT);
+  const uint4* X = static_cast<const uint4*>(a.x);
+  const int kv = a.K / VE, kpv = KP / VE;
+#pragma unroll 4
+  for (int idx = threadIdx.x; idx < M * kpv; idx += kThreads) {
+    const int m = idx / kpv, v = idx - m * kpv;
+    reinterpret_cast<uint4*>(xs)[idx] = (v < kv) ? X[m * kv + v] : make_uint4(0, 0, 0, 0);
+  }
+}
+
+template <typename WT, int M, int R, int EPI>
+__device__ __forceinline__ void epilogue(const GemvArgs& a, int t, float (&acc)[Tiles<EPI, R>::NW][M], int lane) {
+  if constexpr (EPI == EPI_QKV) {
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      if (lane != m) continue;
+      const int H = a.H, Hkv = a.Hkv, hd = a.hd, half = hd / 2;
+      const int q4 = hd / 4;
+      const int hh = t / q4, j = 2 * (t - hh * q4);
+      const int rg = a.row0 + m;
+      const int b = rg / a.m_per_seq, i = rg - b * a.m_per_seq;
+      const float x0 = acc[0][m], x1 = acc[1][m], y0 = acc[2][m], y1 = acc[3][m];
+      if (hh < H + Hkv) {
+        const float2 c0 = a.cs[static_cast<size_t>(rg) * half + j];
+        const float2 c1 = a.cs[static_cast<size_t>(rg) * half + j + 1];
+        const float r0 = x0 * c0.x - y0 * c0.y, s0 = y0 * c0.x + x0 * c0.y;
+        const float r1 = x1 * c1.x - y1 * c1.y, s1 = y1 * c1.x + x1 * c1.y;
+        if (hh < H) {
+          float* qr = a.q + static_cast<size_t>(rg) * (H * hd) + hh * hd;
+          qr[j] = r0;
+          qr[j + 1] = r1;
+          qr[j + half] = s0;
+          qr[j + 1 + half] = s1;
+        } else {
+          const int pos = a.len[b] + i;
+          if (pos >= 0 && pos < a.max_ctx) {
+            WT* dst = static_cast<WT*>(a.kc) +
+                      (((static_cast<size_t>(a.layer) * a.kvB + b) * Hkv + (hh - H)) * a.max_ctx + pos) * hd;
+            dst[j] = Elt<WT>::from_f(r0);
+            dst[j + 1] = Elt<WT>::from_f(r1);
+            dst[j + half] = Elt<WT>::from_f(s0);
+            dst[j + 1 + half] = Elt<WT>::from_f(s1);
+          }
+        }
+      } else {
+        const int pos = a.len[b] + i;
+        if (pos >= 0 && pos < a.max_ctx) {
+          WT* dst = static_cast<WT*>(a.vc) +
+                    (((static_cast<size_t>(a.layer) * a.kvB + b) * Hkv + (hh - H - Hkv)) * a.max_ctx + pos) * hd;
+          dst[j] = Elt<WT>::from_f(x0);
+          dst[j + 1] = Elt<WT>::from_f(x1);
+          dst[j + half] = Elt<WT>::from_f(y0);
+          dst[j + 1 + half] = Elt<WT>::from_f(y1);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int c = t * R + r;
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        if (lane == r * M + m && c < a.N) {
+          if constexpr (EPI == EPI_STORE) {
+            a.y[static_cast<size_t>(m) * a.ldy + c] = acc[r][m];
+          } else if constexpr (EPI == EPI_RESID) {
+            a.y[static_cast<size_t>(m) * a.ldy + c] += acc[r][m];
+          } else {
+            const float g = acc[r][m], u = acc[R + r][m];
+            static_cast<WT*>(a.z)[static_cast<size_t>(m) * a.ldz + c] = Elt<WT>::from_f(g / (1.f + expf(-g)) * u);
+          }
+        }
+      }
+    }
+  }
+}
+
+// Steps of a row: S = ceil(K / STEP); U must divide S.
+// WPE: minimum waves per SIMD the register allocation must allow.
+template <typename WT, int M, int R, int U, int EPI, int WPE>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE))) void gemv_kernel(GemvArgs a) {
+  extern __shared__ uint4 smem_v[];
+  WT* xs = reinterpret_cast<WT*>(smem_v);
+  __shared__ int last_sh;
+  constexpr int VE = 16 / sizeof(WT);
+  constexpr int STEP = kWave * VE;
+  constexpr int NW = Tiles<EPI, R>::NW;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int K = a.K;
+  const int S = (K + STEP - 1) / STEP;
+  const int KP = S * STEP;
+  const WT* W = static_cast<const WT*>(a.W);
+  const int n_tiles = num_tiles<EPI, R>(a.N);
+  const int gw = blockIdx.x * kWavesPerBlock + wave;
+  const int TW = gridDim.x * kWavesPerBlock;
+  const int my_tiles = gw < n_tiles ? (n_tiles - gw + TW - 1) / TW : 0;
+  // per-lane column of step ks: clamped into the row (the padded x is zero there)
+  const int lk = lane * VE;
+
+  const WT* cur[NW];
+  const WT* nxt[NW];
+  auto set_rows = [&](int t, const WT* (&p)[NW]) {
+    int rows[NW];
+    tile_rows<EPI, R>(a, t, rows);
+#pragma unroll
+    for (int r = 0; r < NW; ++r) p[r] = W + static_cast<size_t>(rows[r]) * K;
+  };
+  auto load_step = [&](const WT* const (&p)[NW], int ks, uint4 (&dst)[NW]) {
+    const int k = min(ks * STEP + lk, K - VE);
+#pragma unroll
+    for (int r = 0; r < NW; ++r) dst[r] = load_stream(p[r] + k);
+  };
+
+  uint4 wv[U][NW];
+  if (my_tiles > 0) {
+    set_rows(gw, cur);
+#pragma unroll
+    for (int u = 0; u < U; ++u) load_step(cur, u, wv[u]);
+  }
+  stage_x<WT, M>(a, xs, KP);
+  __syncthreads();
+
+  float acc[NW][M];
+  auto compute = [&](int ks, const uint4 (&w)[NW]) {
+    const int k = ks * STEP + lk;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const uint4 xv = *reinterpret_cast<const uint4*>(xs + static_cast<size_t>(m) * KP + k);
+#pragma unroll
+      for (int r = 0; r < NW; ++r) acc[r][m] = Dot<WT>::run(w[r], xv, acc[r][m]);
+    }
+  };
+  auto finish = [&](int t) {
+#pragma unroll
+    for (int r = 0; r < NW; ++r)
+#pragma unroll
+      for (int m = 0; m < M; ++m) acc[r][m] = wave_sum(acc[r][m]);
+    epilogue<WT, M, R, EPI>(a, t, acc, lane);
+  };
+
+  for (int ti = 0; ti < my_tiles; ++ti) {
+    const int t = gw + ti * TW;
+    const bool more = ti + 1 < my_tiles;
+    if (more) set_rows(t + TW, nxt);
+#pragma unroll
+    for (int r = 0; r < NW; ++r)
+#pragma unroll
+      for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
+    // groups whose refills stay inside this tile
+    for (int s0 = 0; s0 + U < S; s0 += U) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        compute(s0 + u, wv[u]);
+        load_step(cur, s0 + U + u, wv[u]);
+      }
+    }
+    // last group: refill with the next tile's first steps
+    if (more) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        compute(S - U + u, wv[u]);
+        load_step(nxt, u, wv[u]);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) compute(S - U + u, wv[u]);
+    }
+    finish(t);
+    if (more) {
+#pragma unroll
+      for (int r = 0; r < NW; ++r) cur[r] = nxt[r];
+    }
+  }
+  if constexpr (EPI == EPI_RESID) {
+    // the last workgroup normalises the finished residual rows
+    if (a.norm_gain && last_block(a.ticket, static_cast<int>(gridDim.x), &last_sh))
+      norm_rows<kThreads, M>(a.y, a.ldy, a.N, a.norm_gain, a.eps, static_cast<WT*>(a.norm_out));
+  }
+}
+
+}  // namespace gemv
+}  // namespace sv

@@ -6,44 +6,76 @@
 
 namespace sv {
 
-enum GemvEpi { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
+// ---- weight-streaming linear ---------------------------------------------------
+enum GemvEpi { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_QKV = 3 };
 
-// y[M][N] (op) x[M][K] . W[N][K]^T, M any size (streamed in blocks of 8 rows).
-//   EPI_STORE : y[m][n]  = acc            (y float32, ld ldy)
-//   EPI_RESID : y[m][n] += acc            (y float32 residual stream, ld ldy)
-//   EPI_SWIGLU: z[m][n]  = silu(g) * u    with g from W rows n, u from rows n + N;
-//               z in the model dtype (ld ldz)
-// W, x, z: model dtype (bf16 bits or float32).
-hipError_t launch_gemv(bool bf16, int epi, const void* W, const void* x, int M, int N, int K,
-                       float* y, int ldy, void* z, int ldz, hipStream_t s);
+// y[M][N] (op) x[M][K] . W[N][K]^T for any M (in blocks of rows), x in the
+// model dtype.
+//  EPI_STORE : y[m][n]  = acc            (float32, ld ldy)
+//  EPI_RESID : y[m][n] += acc            (float32 residual, ld ldy); when
+//              norm_gain is set, the last workgroup then writes
+//              norm_out[m][:] = cvt(RMSNorm(y[m][:]) * norm_gain) (ld N),
+//              the input of the next linear (ticket: a zeroed int).
+//  EPI_SWIGLU: z[m][n]  = silu(g) * u    g: W rows n, u: rows n + N (dtype, ld ldz)
+//  EPI_QKV   : W = [(H + 2 Hkv) hd][K]; q heads rotated into q [M][H hd];
+//              k heads rotated and v heads copied into the KV cache of
+//              `layer` at position len[b] + i (row = b * m_per_seq + i).
+struct GemvArgs {
+  const void* W = nullptr;
+  int N = 0, K = 0, M = 0;
+  const void* x = nullptr;
+  float* y = nullptr;
+  int ldy = 0;
+  void* z = nullptr;
+  int ldz = 0;
+  // EPI_RESID: the next RMSNorm
+  const float* norm_gain = nullptr;
+  void* norm_out = nullptr;
+  float eps = 0.f;
+  int* ticket = nullptr;
+  // EPI_QKV
+  float* q = nullptr;
+  int H = 0, Hkv = 0, hd = 0;
+  const float2* cs = nullptr;
+  void* kc = nullptr;
+  void* vc = nullptr;
+  const int32_t* len = nullptr;
+  int m_per_seq = 1, row0 = 0, layer = 0, kvB = 0, max_ctx = 0;
+};
+hipError_t launch_gemv(bool bf16, int epi, const GemvArgs& a, int M, hipStream_t s);
 
 // h[r][:] = embed[tok(r)][:] (float32) and the RoPE table cs[r][j] = (cos, sin)
 // of angle pos(r) * theta^(-2j/hd), pos(r) = len[b] + i for row r = b*m + i.
 // tok(r) = tokens[r] if tokens, else (i == 0 ? last[b] : draft[b*(m-1) + i-1]).
+// x[r][:] = cvt(RMSNorm(h[r][:]) * gain) is the first linear's input.
+// Also zeroes the n_ctr tickets of the pass.
 hipError_t launch_embed(bool bf16, const void* embed, int vocab, int d, const int32_t* tokens,
                         const int32_t* last, const int32_t* draft, const int32_t* len, int B, int m,
-                        int hd, float theta, float* h, float2* cs, hipStream_t s);
+                        int hd, float theta, const float* gain, float eps, float* h, void* x, float2* cs,
+                        int* ctr, int n_ctr, hipStream_t s);
 
-// x[r][:] = cvt(h[r][:] * rsqrt(mean(h^2) + eps) * g), cvt = bf16 rounding or none.
-hipError_t launch_rmsnorm(bool bf16, const float* h, const float* g, int rows, int d, float eps, void* x,
-                          hipStream_t s);
-
-// RoPE on q (in place in qkv) and k; append k, v rows to the cache of `layer`.
-hipError_t launch_rope_append(bool bf16, float* qkv, const float2* cs, const int32_t* len, int B, int m,
-                              int H, int Hkv, int hd, void* kc, void* vc, int layer, int kvB, int max_ctx,
-                              hipStream_t s);
-
-// Split-context GQA attention for m query rows per sequence, causal inside
-// the new block, then the log-sum-exp combine into x[r][h*hd + d] (model dtype).
-int attn_num_splits(int B, int Hkv, int G, int m, int max_ctx);
-hipError_t launch_attention(bool bf16, const float* qkv, const void* kc, const void* vc, const int32_t* len,
-                            int B, int m, int H, int Hkv, int hd, int layer, int kvB, int max_ctx,
-                            int n_split, float* part_o, float2* part_ml, void* x, hipStream_t s);
+// ---- attention -------------------------------------------------------------------
+struct AttnArgs {
+  const float* q = nullptr;  // [B*m][H*hd] rotated queries
+  const void* kc = nullptr;
+  const void* vc = nullptr;
+  const int32_t* len = nullptr;
+  int m = 1, H = 0, Hkv = 0, layer = 0, kvB = 0, max_ctx = 0, n_split = 1, n_qc = 1;
+  float* part_o = nullptr;     // [B][H][m][n_split][hd]
+  float2* part_ml = nullptr;   // [B][H][m][n_split]
+  int* counters = nullptr;     // attn_counters(...) tickets, zero between launches
+  void* xo = nullptr;          // [B*m][H*hd] output in the model dtype
+};
+bool attn_supported(int H, int Hkv, int hd);      // hd 64/128, G = H/Hkv divides 4 or is a multiple of 4
+int attn_row_blocks(int H, int Hkv, int m);        // n_qc
+int attn_num_splits(int B, int H, int Hkv, int m, int max_ctx);
+size_t attn_counters(int B, int H, int Hkv, int m);  // tickets the launch uses
+hipError_t launch_attention(bool bf16, int hd, const AttnArgs& a, int B, hipStream_t s);
 
 // len[b] = (src ? src[b] : len[b]) + add
 hipError_t launch_kv_len(int32_t* len, const int32_t* src, int add, int B, hipStream_t s);
 
-// ---- sampler ----------------------------------------------------------------
+// ---- sampler ----------------------------------------------------------------------
 int sampler_chunks(int vocab);
 // part[row][c] = (max, sum exp(l/T - max)) over chunk c of each row.
 hipError_t launch_row_partials(const float* logits, int64_t rows, int vocab, float temperature, float2* part,

@@ -71,6 +71,14 @@ def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray) -> np.ndarray:
     return np.einsum("kgn,knd->kgd", pr, V).reshape(H, hd)
 
 
+def linear(x: np.ndarray, W: np.ndarray, bf16: bool) -> np.ndarray:
+    """y = x W^T in fp64; under the bf16 contract the input x is first rounded
+    to bf16 (W already holds bf16 values)."""
+    if bf16:
+        x = round_bf16(x)
+    return x @ W.astype(np.float64).T
+
+
 class KVCache:
     """Per-sequence contiguous cache: k, v [L, B, Hkv, max_ctx, hd] and the
     committed length per sequence.  A forward pass writes rows at
@@ -103,9 +111,7 @@ class Decoder:
 
     # one linear: y = x W^T with the bf16 input rounding of the precision contract
     def _lin(self, x: np.ndarray, W: np.ndarray) -> np.ndarray:
-        if self.bf16:
-            x = round_bf16(x)
-        return x @ W.astype(np.float64).T
+        return linear(x, W, self.bf16)
 
     def _store(self, x: np.ndarray) -> np.ndarray:
         return round_bf16(x) if self.bf16 else x

@@ -1,0 +1,67 @@
+"""GPU parity of the weight-streaming linear (spec_linear) at every weight
+shape of the 8B-shaped target and of the small target, M = 1 .. 13 rows
+(several 8-row blocks), against the oracle's linear.  bf16 weights and
+inputs, float32 accumulate: the tolerance is relative to sum |x||w|."""
+import numpy as np
+import pytest
+import torch
+
+from draft_then_verify_amd import binding as bd
+from oracle.model import linear
+
+pytestmark = pytest.mark.gpu
+
+SHAPES_8B = [(6144, 4096), (4096, 4096), (12288, 4096), (4096, 12288), (151936, 4096)]
+
+
+def _check(N, K, M, epi, seed, dtype=torch.bfloat16):
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    rows = 2 * N if epi == 2 else N
+    W = (torch.randn((rows, K), generator=g, device="cuda") * 0.02).to(dtype)
+    x = torch.randn((M, K), generator=g, device="cuda").to(dtype)
+    y0 = torch.randn((M, N), generator=g, device="cuda")
+    y = y0.clone() if epi == 1 else torch.empty((M, N), device="cuda")
+    z = torch.empty((M, N), dtype=dtype, device="cuda") if epi == 2 else None
+    bd.spec_linear(W, x, M, N, K, epilogue=epi, y=None if epi == 2 else y, z=z)
+    torch.cuda.synchronize()
+    # sampled output columns (all of them for the smaller matrices)
+    cols = np.arange(N) if N <= 16384 else np.sort(np.random.default_rng(seed).choice(N, 4096, replace=False))
+    Wc = W.float().cpu().numpy()
+    xs = x.float().cpu().numpy().astype(np.float64)
+    bf = dtype == torch.bfloat16
+    ref = linear(xs, Wc[cols], bf)
+    bound = np.abs(xs) @ np.abs(Wc[cols].astype(np.float64)).T
+    if epi == 0:
+        got = y.cpu().numpy()[:, cols]
+    elif epi == 1:
+        got = y.cpu().numpy()[:, cols] - y0.cpu().numpy()[:, cols]
+    else:
+        gate, up = ref, linear(xs, Wc[N + cols], bf)
+        ref = gate / (1 + np.exp(-gate)) * up
+        got = z.float().cpu().numpy()[:, cols]
+        bound = (np.abs(ref) + 1e-3) * 2 ** -7 + 1e-4 * (bound + np.abs(xs) @ np.abs(Wc[N + cols].astype(np.float64)).T)
+        assert (np.abs(got - ref) <= bound).all()
+        return
+    assert (np.abs(got - ref) <= 1e-4 * bound + 1e-6).all()
+
+
+@pytest.mark.parametrize("N,K", SHAPES_8B)
+def test_linear_8b_shapes_m5(N, K):
+    _check(N, K, 5, 0, seed=N + K)
+
+
+@pytest.mark.parametrize("epi", [1, 2])
+def test_linear_epilogues(epi):
+    _check(4096, 4096, 5, epi, seed=7 + epi)
+    _check(2816, 1024, 3, epi, seed=9 + epi)
+
+
+@pytest.mark.parametrize("M", [1, 2, 7, 8, 9, 13])
+def test_linear_row_counts(M):
+    _check(1000, 1024, M, 0, seed=M)
+    _check(6144, 4096, M, 1, seed=100 + M)
+
+
+def test_linear_float32():
+    _check(704, 256, 5, 0, seed=3, dtype=torch.float32)
+    _check(256, 704, 4, 1, seed=4, dtype=torch.float32)

@@ -46,8 +46,8 @@ size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 struct Layout {
-  size_t h, xn, xo, z, q, cs, po, pml, ctr, logits, part, csum, total;
-  int n_split, n_qc, n_ctr;
+  size_t h, xn, xo, z, q, cs, po, pml, ctr, pt, logits, part, csum, total;
+  int n_split, n_qc, n_ctr, ks_o, ks_d;
 };
 
 Layout make_layout(const spec_model_cfg& c, int B, int m, int max_ctx) {
@@ -73,7 +73,10 @@ Layout make_layout(const spec_model_cfg& c, int B, int m, int max_ctx) {
   L.cs = take(rows * (c.head_dim / 2) * 8);
   L.po = take(static_cast<size_t>(B) * c.n_heads * m * L.n_split * c.head_dim * 4);
   L.pml = take(static_cast<size_t>(B) * c.n_heads * m * L.n_split * 8);
-  L.ctr = take((static_cast<size_t>(L.n_ctr) + 1) * 4);  // attention tickets + the linears' ticket
+  L.ctr = take(static_cast<size_t>(L.n_ctr) * 4);  // attention tickets
+  L.ks_o = sv::gemv_ksplit(c.dtype == SPEC_BF16, static_cast<int>(rows), hq);
+  L.ks_d = sv::gemv_ksplit(c.dtype == SPEC_BF16, static_cast<int>(rows), c.d_ff);
+  L.pt = take(static_cast<size_t>(std::max(L.ks_o, L.ks_d)) * rows * c.d_model * 4);  // K-slice partials
   L.logits = take(rows * c.vocab * 4);
   L.part = take(rows * nch * 8);
   L.csum = take(static_cast<size_t>(B) * nch * 16);
@@ -94,8 +97,9 @@ spec_status check_kv(const spec_model* M, const spec_kv* kv, int B, int m) {
 // Launch sequence of one forward pass over B x m rows.  The embedding kernel
 // writes the residual rows h and the first RMSNorm's output; per layer
 //   QKV linear (RoPE + KV append) -> attention (split context, merged
-//   in-kernel) -> O linear (+= h, then the MLP RMSNorm) -> gate/up linear
-//   (SwiGLU) -> down linear (+= h, then the next RMSNorm);
+//   in-kernel) -> O linear (K-slice partials) -> h += partials, MLP RMSNorm
+//   -> gate/up linear (SwiGLU) -> down linear (K-slice partials) -> h +=
+//   partials, the next RMSNorm;
 // then the LM head on the final RMSNorm.
 spec_status run_forward(const spec_model* M, const spec_kv* kv, int B, int m, const int32_t* tokens,
                         const int32_t* last, const int32_t* draft, float* logits, const Layout& L, char* ws,
@@ -108,10 +112,9 @@ spec_status run_forward(const spec_model* M, const spec_kv* kv, int B, int m, co
   void* xn = ws + L.xn;
   float2* cs = reinterpret_cast<float2*>(ws + L.cs);
   int* ctr = reinterpret_cast<int*>(ws + L.ctr);
-  int* ticket = ctr + L.n_ctr;
 
   HIP_TRY(sv::launch_embed(bf16, M->embed, V, d, tokens, last, draft, kv->len, B, m, hd, c.rope_theta,
-                           M->attn_norm[0], c.rms_eps, h, xn, cs, ctr, L.n_ctr + 1, s));
+                           M->attn_norm[0], c.rms_eps, h, xn, cs, ctr, L.n_ctr, s));
   sv::GemvArgs qkv;
   qkv.N = (H + 2 * Hkv) * hd;
   qkv.K = d;
@@ -143,15 +146,16 @@ spec_status run_forward(const spec_model* M, const spec_kv* kv, int B, int m, co
   at.part_ml = reinterpret_cast<float2*>(ws + L.pml);
   at.counters = ctr;
   at.xo = ws + L.xo;
+  float* pt = reinterpret_cast<float*>(ws + L.pt);
+  const size_t pstride = static_cast<size_t>(rows) * d;
   sv::GemvArgs o;
   o.N = d;
   o.K = H * hd;
+  o.ksplit = L.ks_o;
   o.x = ws + L.xo;
-  o.y = h;
+  o.y = pt;
   o.ldy = d;
-  o.norm_out = xn;
-  o.eps = c.rms_eps;
-  o.ticket = ticket;
+  o.ysplit = pstride;
   sv::GemvArgs gu;
   gu.N = F;
   gu.K = d;
@@ -160,6 +164,7 @@ spec_status run_forward(const spec_model* M, const spec_kv* kv, int B, int m, co
   gu.ldz = F;
   sv::GemvArgs dn = o;
   dn.K = F;
+  dn.ksplit = L.ks_d;
   dn.x = ws + L.z;
   for (int l = 0; l < c.n_layers; ++l) {
     qkv.W = M->wqkv[l];
@@ -168,13 +173,14 @@ spec_status run_forward(const spec_model* M, const spec_kv* kv, int B, int m, co
     at.layer = l;
     HIP_TRY(sv::launch_attention(bf16, hd, at, B, s));
     o.W = M->wo[l];
-    o.norm_gain = M->mlp_norm[l];
-    HIP_TRY(sv::launch_gemv(bf16, sv::EPI_RESID, o, rows, s));
+    HIP_TRY(sv::launch_gemv(bf16, sv::EPI_PARTIAL, o, rows, s));
+    HIP_TRY(sv::launch_resid_norm(bf16, h, pt, L.ks_o, pstride, rows, d, M->mlp_norm[l], c.rms_eps, xn, s));
     gu.W = M->wgu[l];
     HIP_TRY(sv::launch_gemv(bf16, sv::EPI_SWIGLU, gu, rows, s));
     dn.W = M->wd[l];
-    dn.norm_gain = l + 1 < c.n_layers ? M->attn_norm[l + 1] : M->final_norm;
-    HIP_TRY(sv::launch_gemv(bf16, sv::EPI_RESID, dn, rows, s));
+    HIP_TRY(sv::launch_gemv(bf16, sv::EPI_PARTIAL, dn, rows, s));
+    HIP_TRY(sv::launch_resid_norm(bf16, h, pt, L.ks_d, pstride, rows, d,
+                                  l + 1 < c.n_layers ? M->attn_norm[l + 1] : M->final_norm, c.rms_eps, xn, s));
   }
   if (logits) {
     sv::GemvArgs lm;

@@ -1,17 +1,17 @@
 // Weight-streaming GEMV kernel for the verify pass:
 //   y[M][N] = x[M][K] . W[N][K]^T, M <= 8 activation rows per launch.
 //
-// The pass is bound by reading the weights: a decode/verify pass "reads the
-// entire ... weight set and then does about two floating-point operations per
-// weight" (first page, section "The speedup is borrowed"), and checking five
-// positions instead of one "reads the same weights" (same section).  So every
+// The pass is bound by reading the weights: a decode or verify pass streams
+// every weight once and does about two floating-point operations per weight
+// read, and scoring the gamma + 1 positions of a round streams the same bytes
+// as scoring one (first page, section "The speedup is borrowed").  So every
 // weight byte is loaded exactly once per launch and used for all M rows.
 //
 // Structure (persistent, one launch streams the whole matrix):
-//  * The grid is a few workgroups per CU.  Each workgroup stages the M
-//    activation rows in LDS once (up to 160 KiB on gfx950); in NORM mode the
-//    staging is the RMSNorm itself (sum of squares of the float32 residual
-//    rows, reduced in a fixed order so every workgroup gets the same bits).
+//  * The grid is a few workgroups per CU (x) times the K slices (y).  Each
+//    workgroup stages its slice of the M activation rows in LDS once (up to
+//    159 KiB on gfx950); slicing K keeps that staging small enough for
+//    several workgroups per CU, and each slice writes its own partial y.
 //  * Each wave walks its own list of row tiles (R rows; 2R for SwiGLU's gate
 //    and up rows) as one continuous stream of 1 KiB steps: 64 lanes x 16 B of
 //    one weight row per load instruction.  A ring of U register slots keeps
@@ -20,11 +20,10 @@
 //    before the activations are staged.
 //  * bf16: v_dot2_f32_bf16 multiplies two bf16 pairs and accumulates in
 //    float32 without converting the weights; float32 models use fma.
-//  * At the end of a tile: one butterfly reduction per (row, activation row)
-//    and the epilogue -- store, add into the float32 residual stream,
-//    silu(g) * u, or (QKV) RoPE on q/k and the K/V append.  For QKV a wave's 4
-//    rows are {j, j+1, j+hd/2, j+1+hd/2} of one head, so both halves of each
-//    rotated pair meet in the same wave.
+//  * At the end of a tile: one wave reduction per (row, activation row) and
+//    the epilogue -- store, add into the float32 residual stream,
+//    silu(g) * u, or (QKV) RoPE on q/k and the K/V append.  For QKV a wave's
+//    2 rows are {j, j+hd/2} of one head, the two halves of a rotated pair.
 #pragma once
 
 #include "common.hpp"
@@ -33,8 +32,6 @@
 namespace sv {
 namespace gemv {
 
-constexpr int kThreads = 256;
-constexpr int kWavesPerBlock = kThreads / kWave;
 constexpr int kMaxLds = 159 * 1024;  // dynamic LDS; 1 KiB is left for static arrays
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -70,26 +67,24 @@ template <> struct Dot<float> {  // 4 float32 x 4 float32
 };
 
 template <int EPI, int R> struct Tiles {
+  static_assert(EPI != EPI_QKV || R == 2, "QKV tiles are rotated pairs");
   static constexpr int NW = (EPI == EPI_SWIGLU) ? 2 * R : R;  // weight rows per tile
 };
 
 // Number of R-row tiles of a launch.
 template <int EPI, int R>
 __host__ __device__ inline int num_tiles(int N) {
-  return EPI == EPI_QKV ? N / 4 : (N + R - 1) / R;
+  return EPI == EPI_QKV ? N / 2 : (N + R - 1) / R;
 }
 
 // Weight rows of tile t (clamped into range; the epilogue checks validity).
 template <int EPI, int R>
 __device__ __forceinline__ void tile_rows(const GemvArgs& a, int t, int (&rows)[Tiles<EPI, R>::NW]) {
   if constexpr (EPI == EPI_QKV) {
-    const int q4 = a.hd / 4;
-    const int hh = t / q4, j = 2 * (t - hh * q4);
-    const int base = hh * a.hd;
-    rows[0] = base + j;
-    rows[1] = base + j + 1;
-    rows[2] = base + j + a.hd / 2;
-    rows[3] = base + j + 1 + a.hd / 2;
+    const int half = a.hd / 2;
+    const int hh = t / half, j = t - hh * half;
+    rows[0] = hh * a.hd + j;
+    rows[1] = hh * a.hd + j + half;
   } else {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -99,52 +94,46 @@ __device__ __forceinline__ void tile_rows(const GemvArgs& a, int t, int (&rows)[
   }
 }
 
-// Stage the M activation rows of the launch into LDS (model dtype, row
-// stride KP >= K, zero-padded to KP).
-template <typename WT, int M>
-__device__ __forceinline__ void stage_x(const GemvArgs& a, WT* xs, int KP) {
+// Stage this workgroup's slice of the M activation rows into LDS (model
+// dtype, row stride KP >= K, zero-padded to KP).
+template <typename WT, int M, int NT>
+__device__ __forceinline__ void stage_x(const WT* x, int ldx, int K, WT* xs, int KP) {
   constexpr int VE = 16 / sizeof(WT);
-  const uint4* X = static_cast<const uint4*>(a.x);
-  const int kv = a.K / VE, kpv = KP / VE;
+  const int kv = K / VE, kpv = KP / VE;
 #pragma unroll 4
-  for (int idx = threadIdx.x; idx < M * kpv; idx += kThreads) {
+  for (int idx = threadIdx.x; idx < M * kpv; idx += NT) {
     const int m = idx / kpv, v = idx - m * kpv;
-    reinterpret_cast<uint4*>(xs)[idx] = (v < kv) ? X[m * kv + v] : make_uint4(0, 0, 0, 0);
+    reinterpret_cast<uint4*>(xs)[idx] =
+        (v < kv) ? reinterpret_cast<const uint4*>(x + static_cast<size_t>(m) * ldx)[v] : make_uint4(0, 0, 0, 0);
   }
 }
 
 template <typename WT, int M, int R, int EPI>
-__device__ __forceinline__ void epilogue(const GemvArgs& a, int t, float (&acc)[Tiles<EPI, R>::NW][M], int lane) {
+__device__ __forceinline__ void epilogue(const GemvArgs& a, float* y, int t, float (&acc)[Tiles<EPI, R>::NW][M],
+                                         int lane) {
   if constexpr (EPI == EPI_QKV) {
 #pragma unroll
     for (int m = 0; m < M; ++m) {
       if (lane != m) continue;
       const int H = a.H, Hkv = a.Hkv, hd = a.hd, half = hd / 2;
-      const int q4 = hd / 4;
-      const int hh = t / q4, j = 2 * (t - hh * q4);
+      const int hh = t / half, j = t - hh * half;
       const int rg = a.row0 + m;
       const int b = rg / a.m_per_seq, i = rg - b * a.m_per_seq;
-      const float x0 = acc[0][m], x1 = acc[1][m], y0 = acc[2][m], y1 = acc[3][m];
+      const float x0 = acc[0][m], y0 = acc[1][m];
       if (hh < H + Hkv) {
-        const float2 c0 = a.cs[static_cast<size_t>(rg) * half + j];
-        const float2 c1 = a.cs[static_cast<size_t>(rg) * half + j + 1];
-        const float r0 = x0 * c0.x - y0 * c0.y, s0 = y0 * c0.x + x0 * c0.y;
-        const float r1 = x1 * c1.x - y1 * c1.y, s1 = y1 * c1.x + x1 * c1.y;
+        const float2 c = a.cs[static_cast<size_t>(rg) * half + j];
+        const float r0 = x0 * c.x - y0 * c.y, s0 = y0 * c.x + x0 * c.y;
         if (hh < H) {
           float* qr = a.q + static_cast<size_t>(rg) * (H * hd) + hh * hd;
           qr[j] = r0;
-          qr[j + 1] = r1;
           qr[j + half] = s0;
-          qr[j + 1 + half] = s1;
         } else {
           const int pos = a.len[b] + i;
           if (pos >= 0 && pos < a.max_ctx) {
             WT* dst = static_cast<WT*>(a.kc) +
                       (((static_cast<size_t>(a.layer) * a.kvB + b) * Hkv + (hh - H)) * a.max_ctx + pos) * hd;
             dst[j] = Elt<WT>::from_f(r0);
-            dst[j + 1] = Elt<WT>::from_f(r1);
             dst[j + half] = Elt<WT>::from_f(s0);
-            dst[j + 1 + half] = Elt<WT>::from_f(s1);
           }
         }
       } else {
@@ -153,9 +142,7 @@ __device__ __forceinline__ void epilogue(const GemvArgs& a, int t, float (&acc)[
           WT* dst = static_cast<WT*>(a.vc) +
                     (((static_cast<size_t>(a.layer) * a.kvB + b) * Hkv + (hh - H - Hkv)) * a.max_ctx + pos) * hd;
           dst[j] = Elt<WT>::from_f(x0);
-          dst[j + 1] = Elt<WT>::from_f(x1);
           dst[j + half] = Elt<WT>::from_f(y0);
-          dst[j + 1 + half] = Elt<WT>::from_f(y1);
         }
       }
     }
@@ -166,10 +153,10 @@ __device__ __forceinline__ void epilogue(const GemvArgs& a, int t, float (&acc)[
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         if (lane == r * M + m && c < a.N) {
-          if constexpr (EPI == EPI_STORE) {
-            a.y[static_cast<size_t>(m) * a.ldy + c] = acc[r][m];
+          if constexpr (EPI == EPI_STORE || EPI == EPI_PARTIAL) {
+            y[static_cast<size_t>(m) * a.ldy + c] = acc[r][m];
           } else if constexpr (EPI == EPI_RESID) {
-            a.y[static_cast<size_t>(m) * a.ldy + c] += acc[r][m];
+            y[static_cast<size_t>(m) * a.ldy + c] += acc[r][m];
           } else {
             const float g = acc[r][m], u = acc[R + r][m];
             static_cast<WT*>(a.z)[static_cast<size_t>(m) * a.ldz + c] = Elt<WT>::from_f(g / (1.f + expf(-g)) * u);
@@ -181,26 +168,28 @@ __device__ __forceinline__ void epilogue(const GemvArgs& a, int t, float (&acc)[
 }
 
 // Steps of a row: S = ceil(K / STEP); U must divide S.
-// WPE: minimum waves per SIMD the register allocation must allow.
-template <typename WT, int M, int R, int U, int EPI, int WPE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE))) void gemv_kernel(GemvArgs a) {
+// WPE: minimum waves per SIMD the register allocation must allow; NT threads.
+template <typename WT, int M, int R, int U, int EPI, int WPE, int NT>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE))) void gemv_kernel(GemvArgs a) {
   extern __shared__ uint4 smem_v[];
   WT* xs = reinterpret_cast<WT*>(smem_v);
-  __shared__ int last_sh;
   constexpr int VE = 16 / sizeof(WT);
   constexpr int STEP = kWave * VE;
   constexpr int NW = Tiles<EPI, R>::NW;
+  constexpr int WPB = NT / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  const int K = a.K;
+  const int K = a.K;  // columns of this workgroup's slice
   const int S = (K + STEP - 1) / STEP;
   const int KP = S * STEP;
-  const WT* W = static_cast<const WT*>(a.W);
+  const int slice = blockIdx.y;
+  const WT* W = static_cast<const WT*>(a.W) + static_cast<size_t>(slice) * K;
+  float* y = a.y ? a.y + static_cast<size_t>(slice) * a.ysplit : nullptr;
   const int n_tiles = num_tiles<EPI, R>(a.N);
-  const int gw = blockIdx.x * kWavesPerBlock + wave;
-  const int TW = gridDim.x * kWavesPerBlock;
+  const int gw = blockIdx.x * WPB + wave;
+  const int TW = gridDim.x * WPB;
   const int my_tiles = gw < n_tiles ? (n_tiles - gw + TW - 1) / TW : 0;
-  // per-lane column of step ks: clamped into the row (the padded x is zero there)
+  // per-lane column of step s: clamped into the row (the padded x is zero there)
   const int lk = lane * VE;
 
   const WT* cur[NW];
@@ -209,10 +198,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE)))
     int rows[NW];
     tile_rows<EPI, R>(a, t, rows);
 #pragma unroll
-    for (int r = 0; r < NW; ++r) p[r] = W + static_cast<size_t>(rows[r]) * K;
+    for (int r = 0; r < NW; ++r) p[r] = W + static_cast<size_t>(rows[r]) * a.ldw;
   };
-  auto load_step = [&](const WT* const (&p)[NW], int ks, uint4 (&dst)[NW]) {
-    const int k = min(ks * STEP + lk, K - VE);
+  auto load_step = [&](const WT* const (&p)[NW], int st, uint4 (&dst)[NW]) {
+    const int k = min(st * STEP + lk, K - VE);
 #pragma unroll
     for (int r = 0; r < NW; ++r) dst[r] = load_stream(p[r] + k);
   };
@@ -223,12 +212,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE)))
 #pragma unroll
     for (int u = 0; u < U; ++u) load_step(cur, u, wv[u]);
   }
-  stage_x<WT, M>(a, xs, KP);
+  stage_x<WT, M, NT>(static_cast<const WT*>(a.x) + static_cast<size_t>(slice) * K, a.ldx, K, xs, KP);
   __syncthreads();
 
   float acc[NW][M];
-  auto compute = [&](int ks, const uint4 (&w)[NW]) {
-    const int k = ks * STEP + lk;
+  auto compute = [&](int st, const uint4 (&w)[NW]) {
+    const int k = st * STEP + lk;
 #pragma unroll
     for (int m = 0; m < M; ++m) {
       const uint4 xv = *reinterpret_cast<const uint4*>(xs + static_cast<size_t>(m) * KP + k);
@@ -241,7 +230,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE)))
     for (int r = 0; r < NW; ++r)
 #pragma unroll
       for (int m = 0; m < M; ++m) acc[r][m] = wave_sum(acc[r][m]);
-    epilogue<WT, M, R, EPI>(a, t, acc, lane);
+    epilogue<WT, M, R, EPI>(a, y, t, acc, lane);
   };
 
   for (int ti = 0; ti < my_tiles; ++ti) {
@@ -276,11 +265,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(WPE)))
 #pragma unroll
       for (int r = 0; r < NW; ++r) cur[r] = nxt[r];
     }
-  }
-  if constexpr (EPI == EPI_RESID) {
-    // the last workgroup normalises the finished residual rows
-    if (a.norm_gain && last_block(a.ticket, static_cast<int>(gridDim.x), &last_sh))
-      norm_rows<kThreads, M>(a.y, a.ldy, a.N, a.norm_gain, a.eps, static_cast<WT*>(a.norm_out));
   }
 }
 

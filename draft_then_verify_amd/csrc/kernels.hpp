@@ -7,32 +7,30 @@
 namespace sv {
 
 // ---- weight-streaming linear ---------------------------------------------------
-enum GemvEpi { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_QKV = 3 };
+enum GemvEpi { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_QKV = 3, EPI_PARTIAL = 4 };
 
 // y[M][N] (op) x[M][K] . W[N][K]^T for any M (in blocks of rows), x in the
 // model dtype.
 //  EPI_STORE : y[m][n]  = acc            (float32, ld ldy)
-//  EPI_RESID : y[m][n] += acc            (float32 residual, ld ldy); when
-//              norm_gain is set, the last workgroup then writes
-//              norm_out[m][:] = cvt(RMSNorm(y[m][:]) * norm_gain) (ld N),
-//              the input of the next linear (ticket: a zeroed int).
+//  EPI_PARTIAL: as EPI_STORE, launch shape of the residual linears; with
+//              ksplit > 1 slice s of K writes its partial to y + s * ysplit
+//  EPI_RESID : y[m][n] += acc            (float32 residual, ld ldy)
 //  EPI_SWIGLU: z[m][n]  = silu(g) * u    g: W rows n, u: rows n + N (dtype, ld ldz)
 //  EPI_QKV   : W = [(H + 2 Hkv) hd][K]; q heads rotated into q [M][H hd];
 //              k heads rotated and v heads copied into the KV cache of
 //              `layer` at position len[b] + i (row = b * m_per_seq + i).
+// ldw / ldx: row strides of W and x (0: K).
 struct GemvArgs {
   const void* W = nullptr;
   int N = 0, K = 0, M = 0;
+  int ldw = 0, ldx = 0;
+  int ksplit = 1;
   const void* x = nullptr;
   float* y = nullptr;
   int ldy = 0;
+  size_t ysplit = 0;
   void* z = nullptr;
   int ldz = 0;
-  // EPI_RESID: the next RMSNorm
-  const float* norm_gain = nullptr;
-  void* norm_out = nullptr;
-  float eps = 0.f;
-  int* ticket = nullptr;
   // EPI_QKV
   float* q = nullptr;
   int H = 0, Hkv = 0, hd = 0;
@@ -43,6 +41,18 @@ struct GemvArgs {
   int m_per_seq = 1, row0 = 0, layer = 0, kvB = 0, max_ctx = 0;
 };
 hipError_t launch_gemv(bool bf16, int epi, const GemvArgs& a, int M, hipStream_t s);
+
+// K slices the residual linears use for an M-row pass (a divisor of K that
+// keeps a workgroup's staged activations near 40 KiB).
+int gemv_ksplit(bool bf16, int M, int K);
+
+// h[r][:] += part[0][r][:] + ... + part[ks-1][r][:] (slices summed in order
+// first, float32; slice stride pstride floats), then
+// x[r][:] = cvt(h[r][:] * rsqrt(mean(h[r][:]^2) + eps) * gain) in the model
+// dtype; d % 4 == 0, d <= 4096.
+// 1 <= ks <= 8.
+hipError_t launch_resid_norm(bool bf16, float* h, const float* part, int ks, size_t pstride, int rows, int d,
+                             const float* gain, float eps, void* x, hipStream_t s);
 
 // h[r][:] = embed[tok(r)][:] (float32) and the RoPE table cs[r][j] = (cos, sin)
 // of angle pos(r) * theta^(-2j/hd), pos(r) = len[b] + i for row r = b*m + i.

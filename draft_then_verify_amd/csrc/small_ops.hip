@@ -1,5 +1,6 @@
 // Small ops of the verify pass: the embedding gather (+ the RoPE angle table
-// of the pass) and KV length bookkeeping.  They move kilobytes.
+// of the pass), the residual sum + RMSNorm between linears and KV length
+// bookkeeping.  They move kilobytes.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -43,6 +44,88 @@ __global__ __launch_bounds__(kThreads) void embed_kernel(const ET* __restrict__ 
   }
 }
 
+// One row per workgroup: h += (part[0] + ... + part[KS-1]) (slices summed in
+// order first), then x = cvt(RMSNorm(h) * gain).  Every load of the row is
+// issued before any is used: one memory round trip.
+template <typename OT, int KS>
+__global__ __launch_bounds__(kThreads) void resid_norm_kernel(float* __restrict__ h, const float* __restrict__ part,
+                                                              size_t pstride, int d, const float* __restrict__ gain,
+                                                              float eps, OT* __restrict__ x) {
+  constexpr int CPT = 4;  // 16-byte chunks per thread (d <= 16 * 256)
+  __shared__ float red[kThreads / kWave];
+  const size_t r = blockIdx.x;
+  const int d4 = d / 4;
+  float4* hr = reinterpret_cast<float4*>(h + r * d);
+  float4 v[CPT], pv[KS][CPT];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int e4 = min(static_cast<int>(threadIdx.x) + c * kThreads, d4 - 1);
+    v[c] = hr[e4];
+#pragma unroll
+    for (int k = 0; k < KS; ++k) pv[k][c] = reinterpret_cast<const float4*>(part + k * pstride + r * d)[e4];
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    float4 acc = pv[0][c];
+#pragma unroll
+    for (int k = 1; k < KS; ++k) {
+      acc.x += pv[k][c].x;
+      acc.y += pv[k][c].y;
+      acc.z += pv[k][c].z;
+      acc.w += pv[k][c].w;
+    }
+    v[c].x += acc.x;
+    v[c].y += acc.y;
+    v[c].z += acc.z;
+    v[c].w += acc.w;
+    if (static_cast<int>(threadIdx.x) + c * kThreads < d4) {
+      hr[threadIdx.x + c * kThreads] = v[c];
+      ss = fmaf(v[c].x, v[c].x, ss);
+      ss = fmaf(v[c].y, v[c].y, ss);
+      ss = fmaf(v[c].z, v[c].z, ss);
+      ss = fmaf(v[c].w, v[c].w, ss);
+    }
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = ss;
+  __syncthreads();
+  float tot = red[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / kWave; ++w) tot += red[w];
+  const float scale = rsqrtf(tot / static_cast<float>(d) + eps);
+  OT* o = x + r * d;
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    const int e4 = threadIdx.x + c * kThreads;
+    if (e4 < d4) {
+      const float4 g = reinterpret_cast<const float4*>(gain)[e4];
+      o[4 * e4 + 0] = Elt<OT>::from_f(v[c].x * scale * g.x);
+      o[4 * e4 + 1] = Elt<OT>::from_f(v[c].y * scale * g.y);
+      o[4 * e4 + 2] = Elt<OT>::from_f(v[c].z * scale * g.z);
+      o[4 * e4 + 3] = Elt<OT>::from_f(v[c].w * scale * g.w);
+    }
+  }
+}
+
+template <typename OT>
+hipError_t launch_resid_norm_t(float* h, const float* part, int ks, size_t pstride, int rows, int d,
+                               const float* gain, float eps, OT* x, hipStream_t s) {
+  const dim3 g(rows), b(kThreads);
+  switch (ks) {
+    case 1: hipLaunchKernelGGL((resid_norm_kernel<OT, 1>), g, b, 0, s, h, part, pstride, d, gain, eps, x); break;
+    case 2: hipLaunchKernelGGL((resid_norm_kernel<OT, 2>), g, b, 0, s, h, part, pstride, d, gain, eps, x); break;
+    case 3: hipLaunchKernelGGL((resid_norm_kernel<OT, 3>), g, b, 0, s, h, part, pstride, d, gain, eps, x); break;
+    case 4: hipLaunchKernelGGL((resid_norm_kernel<OT, 4>), g, b, 0, s, h, part, pstride, d, gain, eps, x); break;
+    case 5: hipLaunchKernelGGL((resid_norm_kernel<OT, 5>), g, b, 0, s, h, part, pstride, d, gain, eps, x); break;
+    case 6: hipLaunchKernelGGL((resid_norm_kernel<OT, 6>), g, b, 0, s, h, part, pstride, d, gain, eps, x); break;
+    case 7: hipLaunchKernelGGL((resid_norm_kernel<OT, 7>), g, b, 0, s, h, part, pstride, d, gain, eps, x); break;
+    case 8: hipLaunchKernelGGL((resid_norm_kernel<OT, 8>), g, b, 0, s, h, part, pstride, d, gain, eps, x); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 __global__ void kv_len_kernel(int32_t* len, const int32_t* src, int add, int B) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b < B) len[b] = (src ? src[b] : len[b]) + add;
@@ -63,6 +146,14 @@ hipError_t launch_embed(bool bf16, const void* embed, int vocab, int d, const in
                        vocab, d, tokens, last, draft, len, m, hd, theta, gain, eps, h, static_cast<float*>(x), cs,
                        ctr, n_ctr);
   return hipGetLastError();
+}
+
+hipError_t launch_resid_norm(bool bf16, float* h, const float* part, int ks, size_t pstride, int rows, int d,
+                             const float* gain, float eps, void* x, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (d % 4 != 0 || d > 16 * kThreads || pstride % 4 != 0) return hipErrorInvalidValue;
+  if (bf16) return launch_resid_norm_t(h, part, ks, pstride, rows, d, gain, eps, static_cast<uint16_t*>(x), s);
+  return launch_resid_norm_t(h, part, ks, pstride, rows, d, gain, eps, static_cast<float*>(x), s);
 }
 
 hipError_t launch_kv_len(int32_t* len, const int32_t* src, int add, int B, hipStream_t s) {

@@ -13,7 +13,7 @@
  *   - The rule's exactness argument ("How Speculative Decoding Works (and When
  *     It Doesn't)", section "Why the output doesn't change") is what the
  *     residual and the bonus preserve.
- *   - The draw "t ~ p'" is a fixed-point inverse CDF: w_v = floor(r_v * 2^40),
+ *   - The draw t ~ p' is a fixed-point inverse CDF: w_v = floor(r_v * 2^40),
  *     S = sum w, T = floor(k * S / 2^24) with k = u * 2^24, t = the smallest v
  *     whose inclusive prefix sum exceeds T.  Integer sums make the draw
  *     independent of reduction order.
@@ -119,9 +119,9 @@ size_t spec_workspace_bytes(const spec_model* model, int32_t B, int32_t m, int32
  * probability rows of `vocab` entries and B sequences. */
 size_t spec_sampler_workspace_bytes(int64_t rows, int32_t B, int32_t vocab);
 
-/* The verify pass ("Run Mp in parallel" of Algorithm 1; the target "evaluates
- * all gamma+1 positions in a single forward pass", first page, mechanism
- * paragraph): one forward over B sequences x m rows at positions
+/* The verify pass (first page, Algorithm 1 and the mechanism section: the
+ * target scores all gamma + 1 positions of a round in one forward pass):
+ * one forward over B sequences x m rows at positions
  * len[b] .. len[b]+m-1, streaming every weight once per block of 8 rows.
  *   tokens  [B][m] int32 input ids.
  *   logits  [B][m][vocab] float32 output, or NULL to skip the LM head
@@ -134,16 +134,17 @@ spec_status spec_verify_forward(const spec_model* model, const spec_kv* kv, int3
                                 hipStream_t stream);
 
 /* Target/draft probabilities p = softmax(logits / temperature) over `vocab`
- * entries for `rows` rows ("How Speculative Decoding Works", section "Why the
- * output doesn't change": p and q are the two models' next-token
- * distributions).  float32, max-subtracted; the same row statistics the fused
+ * entries for `rows` rows (p and q of the acceptance rule are the two
+ * models' next-token distributions: "How Speculative Decoding Works (and
+ * When It Doesn't)", section "Why the output doesn't change").  float32, max-subtracted; the same row statistics the fused
  * decode step uses, so p is bitwise what spec_decode_step samples from.
  * temperature > 0.  Errors: SPEC_EINVAL, SPEC_ENOMEM, SPEC_EHIP. */
 spec_status spec_softmax_pq(const float* logits, int64_t rows, int32_t vocab, float temperature,
                             float* probs, void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* The accept / resample / bonus rule on materialised rows (Algorithm 1 lines
- * "Determine the number of accepted guesses" and "Adjust the distribution").
+/* The accept / resample / bonus rule on materialised rows (first page,
+ * Algorithm 1: the accepted-prefix count, the residual resample and the
+ * bonus draw).
  *   p        [B][gamma+1][vocab] target probabilities.
  *   q        [B][gamma][vocab] draft probabilities, or NULL for a one-hot
  *            draft (q_i(x_i) = 1, e.g. n-gram lookup).
@@ -162,8 +163,8 @@ spec_status spec_reject_sample(int32_t B, int32_t gamma, int32_t vocab, const fl
 /* One whole verify step: assemble [last_tok, draft] (B x (gamma+1) rows),
  * run the verify pass, the fused softmax + accept/resample/bonus without
  * materialising p, and commit the KV cache: len[b] += n[b] + 1 (the last
- * committed token and the n accepted drafts stay cached; "rejection is
- * prefix-truncating", first page).  Arguments as in spec_reject_sample;
+ * committed token and the n accepted drafts stay cached: a rejection cuts
+ * the round's block at that position, first page).  Arguments as in spec_reject_sample;
  * logits_out [B][gamma+1][vocab] receives the logits when non-NULL.
  * Errors: as spec_verify_forward. */
 spec_status spec_decode_step(const spec_model* target, const spec_kv* kv, int32_t B, int32_t gamma,
@@ -174,8 +175,8 @@ spec_status spec_decode_step(const spec_model* target, const spec_kv* kv, int32_
 
 /* The weight-streaming linear of the verify pass on its own: y = x . W^T for
  * M rows, every weight byte read once per block of 8 rows (a verify pass
- * "reads the same weights" for all its positions, first page, section "The
- * speedup is borrowed").
+ * streams the same weight bytes whatever the number of positions it scores,
+ * first page, section "The speedup is borrowed").
  *   dtype     SPEC_F32 or SPEC_BF16: type of W, x and z.
  *   epilogue  0: y[M][N] = acc;  1: y[M][N] += acc (float32 residual);
  *             2: z[M][N] = silu(g) * u with g from W rows 0..N-1 and u from

@@ -8,15 +8,17 @@
 // fetched from memory once per workgroup and used by every query row that
 // shares its KV head (grouped-query attention: G = H / Hkv query heads).
 //
-// Workgroup = 4 waves = (sequence b, KV head, block of query heads, block of
-// query rows, context split).  The four waves cover up to four query heads
-// of the group (or, when G < 4, more query rows of fewer heads); each wave
-// owns up to MQ query rows of one head.  Per 64-key tile:
+// Workgroup = 8 waves = (sequence b, KV head, block of query heads, block of
+// query rows, context split).  The waves cover the query heads of the group
+// (up to 8) times row sub-blocks: with G = 4, two waves per head, each
+// owning MQ = ceil(m / 2) of the rows, so per-wave work stays short.  Per
+// 64-key tile:
 //  * the workgroup copies the K and V tile into LDS with 16-byte loads, all
 //    of a tile's loads in flight at once, the next tile's issued before the
 //    current one is used;
 //  * scores: lane j holds key j of the tile (float32, from LDS) and dots it
-//    with each of its wave's query rows (LDS broadcasts);
+//    with each of its wave's query rows (LDS broadcasts, 8 dimensions of
+//    every row at a time so the reads overlap the FMAs);
 //  * online softmax per row (wave max / sum);
 //  * P.V: lanes take head dimensions; V rows come from LDS.
 // At B = 1 the (sequence, head) pairs are few, so the context is cut into
@@ -34,7 +36,7 @@
 namespace sv {
 namespace {
 
-constexpr int kThreadsA = 256;
+constexpr int kThreadsA = 512;
 constexpr int kWaves = kThreadsA / kWave;
 constexpr int KT = 64;  // keys per tile (one per lane)
 
@@ -84,9 +86,9 @@ template <> struct VRow<float, 1> {
 
 // Shape of the work split, shared by the launcher and the kernel.
 struct Plan {
-  int hpw;  // query heads per workgroup (min(G, 4))
+  int hpw;  // query heads per workgroup (min(G, 8))
   int nhb;  // head blocks per KV head (G / hpw)
-  int rb;   // query rows per workgroup ((4 / hpw) * mq)
+  int rb;   // query rows per workgroup ((8 / hpw) * mq)
   int nqc;  // row blocks (ceil(m / rb))
 };
 __host__ __device__ inline Plan make_plan(int H, int Hkv, int m, int mq) {
@@ -139,11 +141,12 @@ __device__ __forceinline__ void store_tile(char* ks, char* vs, const v4u (&kr)[L
 }
 
 template <typename ET, int HD, int MQ>
-__global__ __launch_bounds__(kThreadsA) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreadsA) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_kernel(AttnArgs a) {
   using L = Lds<ET, HD>;
   constexpr int DPL = HD / kWave;  // output dims per lane
   constexpr int CE = Cvt<ET>::n;   // elements per 16-byte chunk
   static_assert(L::NL * kThreadsA == KT * L::CPR, "tile chunks must split evenly over the threads");
+
   extern __shared__ uint4 smem_a[];
   char* sm = reinterpret_cast<char*>(smem_a);
   char* ks = sm + L::k_off;
@@ -182,15 +185,13 @@ __global__ __launch_bounds__(kThreadsA) void attn_kernel(AttnArgs a) {
   const int klast = max(kend - 1, 0);
   v4u kr[L::NL], vr[L::NL];
   load_tile<ET, HD>(kc, vc, kvbase, kbeg, klast, kr, vr);
-  // this wave's query rows, pre-scaled (rows past nrows are zero)
+  // this wave's query rows, pre-scaled (rows past nrows repeat the last row;
+  // their results are never written)
 #pragma unroll
   for (int r = 0; r < MQ; ++r) {
     const float* qr = a.q + static_cast<size_t>(b * m + min(i0 + r, m - 1)) * qld + h * HD + lane * DPL;
 #pragma unroll
-    for (int k = 0; k < DPL; ++k) {
-      const float v = qr[k];
-      qs[r][lane * DPL + k] = (r < nrows) ? v * scale : 0.f;
-    }
+    for (int k = 0; k < DPL; ++k) qs[r][lane * DPL + k] = qr[k] * scale;
   }
   float mrow[MQ], lrow[MQ], o[MQ][DPL];
 #pragma unroll
@@ -212,27 +213,31 @@ __global__ __launch_bounds__(kThreadsA) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int c = 0; c < L::CPR; ++c)
       Cvt<ET>::run(*reinterpret_cast<const v4u*>(ks + lane * L::KSTR + c * 16), kf + c * CE);
-#pragma unroll 1
-    for (int r = 0; r < MQ; ++r) {  // rows past nrows have zero queries
-      float t0 = 0.f, t1 = 0.f;
+    // 8 dimensions at a time for every row: MQ x 2 independent FMA chains
+    float t[MQ][2];
 #pragma unroll
-      for (int e = 0; e < HD; e += 8) {
-        const float4 qa = *reinterpret_cast<const float4*>(&qs[r][e]);
-        const float4 qb = *reinterpret_cast<const float4*>(&qs[r][e + 4]);
-        t0 = fmaf(qa.x, kf[e], t0);
-        t1 = fmaf(qa.y, kf[e + 1], t1);
-        t0 = fmaf(qa.z, kf[e + 2], t0);
-        t1 = fmaf(qa.w, kf[e + 3], t1);
-        t0 = fmaf(qb.x, kf[e + 4], t0);
-        t1 = fmaf(qb.y, kf[e + 5], t1);
-        t0 = fmaf(qb.z, kf[e + 6], t0);
-        t1 = fmaf(qb.w, kf[e + 7], t1);
+    for (int r = 0; r < MQ; ++r) t[r][0] = t[r][1] = 0.f;
+#pragma unroll
+    for (int c = 0; c < HD; c += 8) {
+#pragma unroll
+      for (int r = 0; r < MQ; ++r) {
+        const float4 qa = *reinterpret_cast<const float4*>(&qs[r][c]);
+        const float4 qb = *reinterpret_cast<const float4*>(&qs[r][c + 4]);
+        t[r][0] = fmaf(qa.x, kf[c], t[r][0]);
+        t[r][1] = fmaf(qa.y, kf[c + 1], t[r][1]);
+        t[r][0] = fmaf(qa.z, kf[c + 2], t[r][0]);
+        t[r][1] = fmaf(qa.w, kf[c + 3], t[r][1]);
+        t[r][0] = fmaf(qb.x, kf[c + 4], t[r][0]);
+        t[r][1] = fmaf(qb.y, kf[c + 5], t[r][1]);
+        t[r][0] = fmaf(qb.z, kf[c + 6], t[r][0]);
+        t[r][1] = fmaf(qb.w, kf[c + 7], t[r][1]);
       }
-      ps[r][lane] = t0 + t1;
     }
+#pragma unroll
+    for (int r = 0; r < MQ; ++r) ps[r][lane] = t[r][0] + t[r][1];
     // online softmax; p overwrites the score (same lane).  All MQ rows run
-    // branch-free so their reductions interleave; rows past nrows see
-    // zero queries and are never written out.
+    // branch-free so their reductions interleave; rows past nrows are never
+    // written out.
 #pragma unroll
     for (int r = 0; r < MQ; ++r) {
       const bool valid = lane < nt && k0 + lane <= Lb + i0 + r;
@@ -251,7 +256,7 @@ __global__ __launch_bounds__(kThreadsA) void attn_kernel(AttnArgs a) {
     // P.V over the tile, four keys at a time (keys past nt have p = 0 and
     // finite V rows: the clamped copies of the last one)
     const int nt4 = (nt + 3) & ~3;
-#pragma unroll 2
+#pragma unroll 4
     for (int j = 0; j < nt4; j += 4) {
       float vf[4][DPL];
 #pragma unroll
@@ -349,9 +354,17 @@ hipError_t launch_mq(const AttnArgs& a, int B, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Query rows per wave: the rows of a block spread over the waves of a head.
+int rows_per_wave(int H, int Hkv, int m) {
+  const int G = H / Hkv;
+  const int wph = kWaves / (G < kWaves ? G : kWaves);
+  const int mq = (m + wph - 1) / wph;
+  return mq < 8 ? mq : 8;
+}
+
 template <typename ET, int HD>
 hipError_t launch_hd(const AttnArgs& a, int B, hipStream_t s) {
-  switch (a.m < 8 ? a.m : 8) {
+  switch (rows_per_wave(a.H, a.Hkv, a.m)) {
     case 1: return launch_mq<ET, HD, 1>(a, B, s);
     case 2: return launch_mq<ET, HD, 2>(a, B, s);
     case 3: return launch_mq<ET, HD, 3>(a, B, s);
@@ -372,10 +385,10 @@ bool attn_supported(int H, int Hkv, int hd) {
   return G <= kWaves ? (kWaves % G == 0) : (G % kWaves == 0);
 }
 
-int attn_row_blocks(int H, int Hkv, int m) { return make_plan(H, Hkv, m, m < 8 ? m : 8).nqc; }
+int attn_row_blocks(int H, int Hkv, int m) { return make_plan(H, Hkv, m, rows_per_wave(H, Hkv, m)).nqc; }
 
 int attn_num_splits(int B, int H, int Hkv, int m, int max_ctx) {
-  const Plan pl = make_plan(H, Hkv, m, m < 8 ? m : 8);
+  const Plan pl = make_plan(H, Hkv, m, rows_per_wave(H, Hkv, m));
   const int units = B * Hkv * pl.nhb * pl.nqc;  // workgroups per split
   int n = (512 + units - 1) / units;
   n = min(n, (max_ctx + KT - 1) / KT);
@@ -383,7 +396,7 @@ int attn_num_splits(int B, int H, int Hkv, int m, int max_ctx) {
 }
 
 size_t attn_counters(int B, int H, int Hkv, int m) {
-  const Plan pl = make_plan(H, Hkv, m, m < 8 ? m : 8);
+  const Plan pl = make_plan(H, Hkv, m, rows_per_wave(H, Hkv, m));
   return static_cast<size_t>(B) * Hkv * pl.nhb * pl.nqc;
 }
 

@@ -209,7 +209,7 @@ SPEC_API spec_status spec_model_create(const spec_model_cfg* cfg, const spec_wei
   if (c.head_dim != 64 && c.head_dim != 128) return fail(SPEC_EUNSUPPORTED, "head_dim %d (64 or 128)", c.head_dim);
   if (c.n_heads % c.n_kv_heads) return fail(SPEC_EINVAL, "n_heads %% n_kv_heads != 0");
   if (!sv::attn_supported(c.n_heads, c.n_kv_heads, c.head_dim))
-    return fail(SPEC_EUNSUPPORTED, "query heads per KV head %d must divide 4 or be a multiple of 4",
+    return fail(SPEC_EUNSUPPORTED, "query heads per KV head %d must divide 8 or be a multiple of 8",
                 c.n_heads / c.n_kv_heads);
   if (c.d_model > 16 * 256) return fail(SPEC_EUNSUPPORTED, "d_model %d > 4096", c.d_model);
   if (static_cast<size_t>(std::max(c.d_model, std::max(c.d_ff, c.n_heads * c.head_dim))) *

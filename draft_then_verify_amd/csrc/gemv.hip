@@ -4,7 +4,8 @@
 // wave walks a strided list of R-row tiles.  Launch shapes per epilogue
 // (rows per tile R, ring depth U, minimum waves per SIMD, workgroups per CU,
 // threads per workgroup) were chosen by timing the 8B-shaped matrices on
-// MI355X with M = 5.  U is lowered to the largest of 8, 4, 2, 1 that divides
+// MI355X with M = 5, the weights rotated through more memory than the
+// 256 MB last-level cache holds.  U is lowered to the largest of 8, 4, 2, 1 that divides
 // the steps per row.  Activation rows go through in blocks of at most 8 that
 // fit the LDS.
 #include <algorithm>
@@ -19,11 +20,11 @@ using gemv::kMaxLds;
 constexpr int kCUs = 256;
 
 template <int EPI> struct Cfg;
-template <> struct Cfg<EPI_SWIGLU> { static constexpr int R = 1, U = 4, WPE = 4, BPC = 3, NT = 256; };
+template <> struct Cfg<EPI_SWIGLU> { static constexpr int R = 1, U = 4, WPE = 2, BPC = 1, NT = 512; };
 template <> struct Cfg<EPI_STORE> { static constexpr int R = 4, U = 4, WPE = 2, BPC = 1, NT = 256; };
-template <> struct Cfg<EPI_PARTIAL> { static constexpr int R = 2, U = 8, WPE = 2, BPC = 2, NT = 256; };
+template <> struct Cfg<EPI_PARTIAL> { static constexpr int R = 1, U = 8, WPE = 3, BPC = 3, NT = 256; };
 template <> struct Cfg<EPI_RESID> { static constexpr int R = 2, U = 8, WPE = 2, BPC = 2, NT = 256; };
-template <> struct Cfg<EPI_QKV> { static constexpr int R = 2, U = 8, WPE = 3, BPC = 3, NT = 256; };
+template <> struct Cfg<EPI_QKV> { static constexpr int R = 2, U = 4, WPE = 3, BPC = 3, NT = 256; };
 
 template <typename WT> constexpr int step_elems() { return kWave * (16 / static_cast<int>(sizeof(WT))); }
 
@@ -52,8 +53,7 @@ hipError_t launch_mu(const GemvArgs& a, hipStream_t s) {
 template <typename WT, int M, int EPI>
 hipError_t launch_m(const GemvArgs& a, hipStream_t s) {
   constexpr int STEP = step_elems<WT>();
-  // (QKV with 6-8 rows: ring depth 4 keeps the 168-register budget)
-  constexpr int U0 = (EPI == EPI_QKV && M > 5) ? 4 : Cfg<EPI>::U;
+  constexpr int U0 = Cfg<EPI>::U;
   const int S = (a.K + STEP - 1) / STEP;
   if (U0 >= 8 && S % 8 == 0) return launch_mu<WT, M, (U0 >= 8 ? 8 : U0), EPI>(a, s);
   if (U0 >= 4 && S % 4 == 0) return launch_mu<WT, M, (U0 >= 4 ? 4 : U0), EPI>(a, s);

@@ -76,7 +76,7 @@ struct AttnArgs {
   int* counters = nullptr;     // attn_counters(...) tickets, zero between launches
   void* xo = nullptr;          // [B*m][H*hd] output in the model dtype
 };
-bool attn_supported(int H, int Hkv, int hd);      // hd 64/128, G = H/Hkv divides 4 or is a multiple of 4
+bool attn_supported(int H, int Hkv, int hd);      // hd 64/128, G = H/Hkv divides 8 or is a multiple of 8
 int attn_row_blocks(int H, int Hkv, int m);        // n_qc
 int attn_num_splits(int B, int H, int Hkv, int m, int max_ctx);
 size_t attn_counters(int B, int H, int Hkv, int m);  // tickets the launch uses

@@ -14,8 +14,11 @@ Qwen3-0.6B-shaped draft, B = 1, gamma = 4, a 256-token prompt, 256 new tokens.
   weights in turn so no launch reads cached weights.
 * ``emitted_tok_s`` / ``plain_tok_s``: whole generations of 256 tokens with
   the draft model vs plain decoding (gamma = 0), wall clock incl. the draft.
-* ``cpu_baseline``: the CPU oracle's verify round over a bounded sample (the
-  first layers + head of the same target), host cores.
+* ``cpu_baseline``: the CPU oracle's verify round over a bounded sample (all
+  36 layers + head of the same target after a short prompt), host cores.
+* ``roofline.traffic``: HBM bytes per launch from the committed counter
+  passes (FETCH_SIZE, WRITE_SIZE, scaled by a 1 GiB copy's counts), null when
+  the kernel sources changed since.
 """
 
 from __future__ import annotations
@@ -52,40 +55,58 @@ def verify_pass_bytes(shape, B: int, m: int, ctx_sum: int) -> int:
     return weights + M * d * e + norms + ctx_sum * kv_tok + M * kv_tok + 2 * M * V * 4
 
 
+GEMV_SOURCES = ("gemv.hip", "gemv_kernels.hpp", "common.hpp", "kernels.hpp")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_swiglu_8b_traffic.md")
+
+
 def gemv_source_hash() -> str:
-    with open(os.path.join(ROOT, "draft_then_verify_amd", "csrc", "gemv.hip"), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the sources the dominant kernel is built from."""
+    h = hashlib.sha256()
+    for name in GEMV_SOURCES:
+        with open(os.path.join(ROOT, "draft_then_verify_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def stored_traffic():
-    """HBM bytes per launch of the dominant kernel from committed counter runs,
-    if they were taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", "gemv_swiglu_8b_traffic.json")
-    if not os.path.exists(path):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    runs (profiles/gemv_swiglu_8b_traffic.md), if they were taken on the
+    current kernel sources; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
         return None
-    with open(path) as f:
-        t = json.load(f)
-    if t.get("gemv_source_sha") != gemv_source_hash():
+    vals = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and line.lstrip().startswith("- "):
+                k, v = line.strip()[2:].split(":", 1)
+                vals[k.strip()] = v.strip().strip("`")
+    if vals.get("gemv_source_sha") != gemv_source_hash():
         return None
-    return t.get("hbm_bytes_per_launch")
+    try:
+        return int(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
-def cpu_baseline(shape, w_gpu, prompt, layers: int) -> dict:
-    """The oracle's verify round over the first `layers` layers + head."""
+def cpu_baseline(shape, w_gpu, prompt_len: int, layers: int) -> dict:
+    """The oracle's verify round (gamma = 4) over the first `layers` layers +
+    the LM head of the target, after a `prompt_len`-token prefill."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
     from oracle import model as OM
     from oracle import rounds as R
-    from synth import round_uniforms
+    from synth import make_prompt, round_uniforms
 
     sh = shape.with_(n_layers=layers)
     w = {}
     for k, v in w_gpu.items():
         w[k] = (v[:layers] if k in ("attn_norm", "wqkv", "wo", "mlp_norm", "wgu", "wd") else v).cpu()
     dec = OM.Decoder(sh, w)
-    P, g = prompt.shape[1], 4
-    cache = dec.new_cache(1, P + g + 2)
+    del w
+    g = 4
+    prompt = make_prompt(1, prompt_len, sh.vocab, seed=15)
+    cache = dec.new_cache(1, prompt_len + g + 2)
     R.prefill(dec, cache, prompt)
     rng = np.random.default_rng(7)
     drafts = rng.integers(0, sh.vocab, size=(1, g))
@@ -93,12 +114,40 @@ def cpu_baseline(shape, w_gpu, prompt, layers: int) -> dict:
     t0 = time.perf_counter()
     R.verify_round(dec, cache, prompt[:, -1], drafts, None, None, u["u_acc"], u["u_res"])
     dt = time.perf_counter() - t0
-    nbytes = verify_pass_bytes(sh, 1, g + 1, P - 1 + g + 1)
+    nbytes = verify_pass_bytes(sh, 1, g + 1, prompt_len - 1 + g + 1)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count() or 1])
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"one verify round (gamma=4, fp64 NumPy) over the first {layers} of 36 layers + the LM head "
-                      f"of the same 8B-shaped target at context {P - 1}: {nbytes / 1e9:.3f} GB of algorithmic "
-                      f"bytes in {dt:.2f} s"}
+            "sample": f"one verify round (gamma=4, B=1; NumPy fp64 math on the bf16-valued weights) over "
+                      f"{layers} of 36 layers + the LM head of the same 8B-shaped target, context "
+                      f"{prompt_len - 1}: {nbytes / 1e9:.3f} GB of algorithmic bytes in {dt:.2f} s"}
+
+
+def kernel_only(reps: int) -> None:
+    """Launch only the dominant kernel (gate/up GEMV over the 36 layers'
+    weights, `reps` times), then a 1 GiB fill (known write bytes) and a sum
+    over it (known read bytes), for counter passes: the two calibrate
+    WRITE_SIZE and FETCH_SIZE against known sizes."""
+    import torch
+
+    from draft_then_verify_amd import binding as bd
+    from synth import SHAPES, make_weights
+
+    bd.load_library()
+    torch.cuda.set_device(0)
+    sh = SHAPES["qwen3_8b"]
+    F, d, M = sh.d_ff, sh.d_model, 5
+    w = make_weights(sh, seed=3, device="cuda", layers=sh.n_layers)["wgu"]
+    x = torch.randn((M, d), device="cuda").to(torch.bfloat16)
+    z = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        for layer in range(sh.n_layers):
+            bd.spec_linear(w[layer], x, M, F, d, epilogue=2, z=z)
+    cal = torch.ones(1 << 28, dtype=torch.float32, device="cuda")  # fill: 1 GiB written
+    total = cal.sum()                                                # reduction: 1 GiB read
+    torch.cuda.synchronize()
+    log(f"kernel-only: {reps * sh.n_layers} gate/up launches; calibration fill + sum over "
+        f"{cal.numel() * 4} bytes (sum {float(total):.0f})")
 
 
 def main():
@@ -107,7 +156,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--new-tokens", type=int, default=256)
-    ap.add_argument("--cpu-layers", type=int, default=3, help="target layers in the CPU-baseline sample")
+    ap.add_argument("--cpu-layers", type=int, default=36, help="target layers in the CPU-baseline sample")
+    ap.add_argument("--cpu-prompt", type=int, default=32, help="prompt tokens before the CPU-baseline round")
+    ap.add_argument("--kernel-only", action="store_true",
+                    help="launch only the dominant kernel and a calibration copy (for counter passes)")
     ap.add_argument("--skip-generate", action="store_true", help="skip the emitted tok/s generations")
     ap.add_argument("--skip-cpu", action="store_true", help="skip the CPU-baseline leg")
     ap.add_argument("--graph", type=int, default=1, help="time graph replays of the decode step (1) or eager calls (0)")
@@ -115,6 +167,10 @@ def main():
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this path has no multi-GPU mode (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+
+    if args.kernel_only:
+        kernel_only(2)
+        return
 
     import numpy as np
     import torch
@@ -237,7 +293,7 @@ def main():
     cpu = None
     if not args.skip_cpu:
         t1 = time.perf_counter()
-        cpu = cpu_baseline(tshape, wt, prompt, args.cpu_layers)
+        cpu = cpu_baseline(tshape, wt, args.cpu_prompt, args.cpu_layers)
         log(f"cpu baseline: {cpu['value']} GB/s in {time.perf_counter() - t1:.1f} s")
 
     out = {

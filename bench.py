@@ -104,22 +104,28 @@ def cpu_baseline(shape, w_gpu, prompt_len: int, layers: int) -> dict:
         w[k] = (v[:layers] if k in ("attn_norm", "wqkv", "wo", "mlp_norm", "wgu", "wd") else v).cpu()
     dec = OM.Decoder(sh, w)
     del w
-    g = 4
+    g, rounds = 4, 3
     prompt = make_prompt(1, prompt_len, sh.vocab, seed=15)
-    cache = dec.new_cache(1, prompt_len + g + 2)
+    cache = dec.new_cache(1, prompt_len + rounds * (g + 1) + 2)
     R.prefill(dec, cache, prompt)
     rng = np.random.default_rng(7)
-    drafts = rng.integers(0, sh.vocab, size=(1, g))
-    u = round_uniforms(7, 0, 1, g)
+    last = prompt[:, -1]
+    nbytes = 0
     t0 = time.perf_counter()
-    R.verify_round(dec, cache, prompt[:, -1], drafts, None, None, u["u_acc"], u["u_res"])
+    for r in range(rounds):
+        ctx = int(cache.length[0])
+        drafts = rng.integers(0, sh.vocab, size=(1, g))
+        u = round_uniforms(7, r, 1, g)
+        out = R.verify_round(dec, cache, last, drafts, None, None, u["u_acc"], u["u_res"])
+        n = int(out["n"][0])
+        last = out["emitted"][:, n]
+        nbytes += verify_pass_bytes(sh, 1, g + 1, ctx + g + 1)
     dt = time.perf_counter() - t0
-    nbytes = verify_pass_bytes(sh, 1, g + 1, prompt_len - 1 + g + 1)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count() or 1])
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"one verify round (gamma=4, B=1; NumPy fp64 math on the bf16-valued weights) over "
+            "sample": f"{rounds} verify rounds (gamma=4, B=1; NumPy fp64 math on the bf16-valued weights) over "
                       f"{layers} of 36 layers + the LM head of the same 8B-shaped target, context "
-                      f"{prompt_len - 1}: {nbytes / 1e9:.3f} GB of algorithmic bytes in {dt:.2f} s"}
+                      f"{prompt_len - 1}+: {nbytes / 1e9:.3f} GB of algorithmic bytes in {dt:.2f} s"}
 
 
 def kernel_only(reps: int) -> None:

@@ -153,8 +153,9 @@ class SpecDecoder:
         return (torch.as_tensor(u["u_acc"]).cuda(), torch.as_tensor(u["u_res"]).cuda(),
                 torch.as_tensor(np.ascontiguousarray(u["u_draft"].T)).cuda())
 
-    def round(self, r: int, uniforms=None):
-        """One speculative round; returns (n [B], emitted [B, gamma+1]) on the host."""
+    def round(self, r: int, uniforms=None, logits_out=None):
+        """One speculative round; returns (n [B], emitted [B, gamma+1]) on the host.
+        ``logits_out`` [B, gamma+1, V] float32 receives the verify logits when given."""
         B, g = self.B, self.gamma
         u_acc, u_res, u_draft = uniforms if uniforms is not None else self._uniforms(r)
         self.last.copy_(torch.as_tensor(np.array([c[-1] for c in self.committed], np.int32)), non_blocking=False)
@@ -167,8 +168,9 @@ class SpecDecoder:
             else:
                 d_host, nd_host = self.drafter.propose(self.committed)
                 drafts, nd = _dev_i32(d_host), _dev_i32(nd_host)
+        self.last_round = (drafts, q, nd)  # this round's draft inputs, for inspection
         bd.spec_decode_step(self.target, self.kv, B, g, self.T, self.last, drafts, nd, q, u_acc if g else None,
-                            u_res, self.n, self.emitted, None, self.ws)
+                            u_res, self.n, self.emitted, logits_out, self.ws)
         n = self.n.cpu().numpy()
         em = self.emitted.cpu().numpy()
         for b in range(B):

@@ -76,7 +76,7 @@ def linear(x: np.ndarray, W: np.ndarray, bf16: bool) -> np.ndarray:
     to bf16 (W already holds bf16 values)."""
     if bf16:
         x = round_bf16(x)
-    return x @ W.astype(np.float64).T
+    return x @ np.asarray(W, dtype=np.float64).T
 
 
 class KVCache:
@@ -99,11 +99,21 @@ class Decoder:
     code", the simpler variant that drafts with the target's own early layers].
     """
 
-    def __init__(self, shape, weights: dict, n_layers: int | None = None):
+    def __init__(self, shape, weights: dict, n_layers: int | None = None, precast: bool = False):
+        """``precast`` stores the weight matrices as float64 once instead of
+        widening them at every matmul: the same arithmetic, traded for memory
+        (used at the 8B shape, where the per-call widening dominates)."""
         self.shape = shape
         self.L = shape.n_layers if n_layers is None else n_layers
         self.bf16 = shape.dtype == "bf16"
-        self.w = {k: _np(v) for k, v in weights.items()}
+        self.w = {}
+        for k, v in weights.items():
+            a = _np(v)
+            if precast and a.ndim >= 2:
+                if k in ("attn_norm", "wqkv", "wo", "mlp_norm", "wgu", "wd"):
+                    a = a[: self.L]
+                a = a.astype(np.float64)
+            self.w[k] = a
 
     def new_cache(self, B: int, max_ctx: int) -> KVCache:
         s = self.shape

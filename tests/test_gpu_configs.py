@@ -1,0 +1,330 @@
+"""End-to-end parity on the five workload configurations: whole speculative
+generations on the GPU, replayed round by round by the oracle, teacher-forced
+(the oracle starts every round from the GPU's committed tokens and gets the
+GPU's drafts, draft rows and uniforms).
+
+Per round:
+* verify logits within 1e-4 (fp32 models) / 2e-2 (bf16 models) of the
+  oracle's own forward pass, probabilities within 1e-5; at the 36-layer 8B
+  shape, where the bf16 rounding points amplify sub-ulp differences beyond
+  2e-2 for the oracle against itself, logits, p and the draft's q rows are
+  held to twice the oracle's own spread under a 1e-6 relative perturbation
+  of every linear output (plus the plain bars);
+* n and emitted bit-exact against the oracle's rule run on the GPU's own p
+  and q rows;
+* against the oracle's own p: identical, except accept decisions with u
+  within 1e-4 of the threshold or between the oracle's and the GPU's
+  thresholds (counted) and draws whose CDF boundary moved
+  within the 1e-5 probability slack (counted and reported: with near-uniform
+  rows of 32000-151936 entries, bf16 rounding noise moves boundaries often);
+* model drafters: each drafted token equals the oracle's draw on the GPU's q
+  row, and the q rows match the oracle's draft model within 1e-5 up to the
+  first draw that differs.
+
+Sizes: configs 1 and 2 run their full generations; the 8B config runs two
+rounds after a short prompt (the oracle at that size is minutes per long
+prefill); the batch sweep and the n-gram config check a seeded subset of the
+sequences of every batch (all when B <= 8).  The oracle holds its weights as
+float64 once (``precast``) so that a round costs a fraction of a second.
+"""
+import copy
+
+import numpy as np
+import pytest
+import torch
+
+from draft_then_verify_amd import binding as bd
+from draft_then_verify_amd.runner import ModelDrafter, NgramDrafter, SpecDecoder, ngram_lookup
+from oracle import model as OM
+from oracle import ngram as NG
+from oracle import rounds as R
+from oracle import sampler as S
+from synth import SHAPES, make_markov_table, make_prompt, make_weights, markov_prompt, round_uniforms
+from tests._gpu import gpu_softmax, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _sub(w: dict, layers: int) -> dict:
+    """The self-speculative draft's weights: the first layers plus the shared
+    embedding, final norm and head."""
+    out = {}
+    for k, v in w.items():
+        out[k] = v[:layers] if k in ("attn_norm", "wqkv", "wo", "mlp_norm", "wgu", "wd") else v
+    return out
+
+
+class NoisyDecoder(OM.Decoder):
+    """The oracle with every linear output scaled by (1 + 1e-6 * N(0, 1)): it
+    measures how far the oracle moves from itself under perturbations the size
+    of float32 accumulation-order differences."""
+
+    def __init__(self, *a, **k):
+        super().__init__(*a, **k)
+        self._rng = np.random.default_rng(0)
+
+    def _lin(self, x, W):
+        y = super()._lin(x, W)
+        return y * (1.0 + 1e-6 * self._rng.standard_normal(y.shape))
+
+
+class Replay:
+    """The oracle's side of a teacher-forced generation for a subset of the
+    GPU's sequences."""
+
+    def __init__(self, shape, w_host, prompt, rows, max_ctx, draft_shape=None, w_draft=None, precast=True,
+                 envelope=False):
+        self.rows = np.asarray(rows)
+        self.tgt = OM.Decoder(shape, w_host, precast=precast)
+        self.envelope = envelope
+        if envelope:
+            # the perturbed oracle shares the weight arrays
+            self.noisy = NoisyDecoder.__new__(NoisyDecoder)
+            self.noisy.__dict__.update(self.tgt.__dict__)
+            self.noisy._rng = np.random.default_rng(0)
+        self.ct = self.tgt.new_cache(len(rows), max_ctx)
+        R.prefill(self.tgt, self.ct, prompt[self.rows])
+        self.dft = None
+        if draft_shape is not None:
+            self.dft = OM.Decoder(draft_shape, w_draft, precast=precast)
+            self.cd = self.dft.new_cache(len(rows), max_ctx)
+            R.prefill(self.dft, self.cd, prompt[self.rows])
+            if envelope:
+                self.noisy_d = NoisyDecoder.__new__(NoisyDecoder)
+                self.noisy_d.__dict__.update(self.dft.__dict__)
+                self.noisy_d._rng = np.random.default_rng(1)
+        self.tol = 1e-4 if shape.dtype == "f32" else 2e-2
+        self.near_accept = 0
+        self.near_draw = 0
+        self.rounds = 0
+
+    def report(self, what):
+        print(f"[{what}] {self.rounds} rounds checked; accept decisions within 1e-4 of the threshold that "
+              f"flipped: {self.near_accept}; draws whose CDF boundary moved within the probability slack: "
+              f"{self.near_draw}", flush=True)
+
+    def check_draft(self, committed, drafts_g, q_g, u_draft):
+        """q rows of the GPU drafter against the oracle draft model, teacher-forced."""
+        r = self.rows
+        prev = np.array([committed[b][-2] for b in r])
+        last = np.array([committed[b][-1] for b in r])
+        tl = self.ct.length.copy()
+        g = drafts_g.shape[1]
+        bar = np.full((len(r), g), 1e-5)
+        if self.envelope:
+            cd2 = copy.deepcopy(self.cd)
+            _, q_n = R.draft_round(self.noisy_d, cd2, prev, last, tl, g, u_draft[r])
+        d_o, q_o = R.draft_round(self.dft, self.cd, prev, last, tl, g, u_draft[r])
+        if self.envelope:
+            bar = np.maximum(bar, 2 * np.abs(q_n - q_o).max(axis=-1))
+        for j, b in enumerate(r):
+            for i in range(g):
+                # the GPU's draw is the oracle's rule on the GPU's own row
+                assert S.sample(q_g[b, i][None], u_draft[b, i][None])[0] == drafts_g[b, i]
+                err = np.abs(q_g[b, i] - q_o[j, i]).max()
+                assert err < bar[j, i], f"round {self.rounds} seq {b} draft step {i}: q differs by {err:.3g}"
+                if d_o[j, i] != drafts_g[b, i]:
+                    self.near_draw += 1
+                    break
+        # teacher forcing: the oracle draft cache holds the GPU's drafted tokens
+        self.cd.length = tl - 1
+        self.dft.forward(self.cd, np.concatenate([prev[:, None], last[:, None], drafts_g[r][:, :g - 1]], axis=1),
+                         logits=False)
+
+    def check_round(self, last, drafts, q, nd, u, logits_g, n_g, em_g):
+        r = self.rows
+        g = drafts.shape[1]
+        len0 = self.ct.length.copy()
+        qs = None if q is None else q[r]
+        nds = None if nd is None else nd[r]
+        if self.envelope:
+            ct2 = copy.deepcopy(self.ct)
+            tokens = np.concatenate([np.asarray(last[r])[:, None], drafts[r]], axis=1)
+            noisy = self.noisy.forward(ct2, tokens)
+        out = R.verify_round(self.tgt, self.ct, last[r], drafts[r], qs, nds, u["u_acc"][r], u["u_res"][r])
+        dev = np.abs(logits_g[r] - out["logits"])
+        if self.envelope:
+            # deep bf16 stacks amplify sub-ulp differences through the bf16
+            # rounding points; the bar is the oracle's own spread
+            env = np.abs(noisy - out["logits"])
+            print(f"logits |gpu - oracle| max {dev.max():.4f} mean {dev.mean():.5f}; "
+                  f"|oracle(1e-6 perturbed) - oracle| max {env.max():.4f} mean {env.mean():.5f}", flush=True)
+            assert dev.max() <= 2 * env.max() + self.tol and dev.mean() <= 2 * env.mean() + 1e-3
+        else:
+            assert dev.max() < self.tol
+        V = logits_g.shape[-1]
+        p_g = gpu_softmax(torch.as_tensor(logits_g[r]).cuda(), V).cpu().numpy()
+        pbar = 1e-5
+        if self.envelope:
+            pbar = max(pbar, 2 * np.abs(S.softmax(noisy, 1.0) - out["p"]).max())
+        assert np.abs(p_g - out["p"]).max() < pbar
+        n_own, em_own = S.reject_sample(p_g, qs, drafts[r], nds, u["u_acc"][r], u["u_res"][r])
+        assert np.array_equal(n_own, n_g[r]) and np.array_equal(em_own, em_g[r])
+        if g > 0:
+            # a decision may differ only where u lies within 1e-4 of the
+            # oracle's threshold min(1, p/q), or between the oracle's and the
+            # GPU's thresholds (their p rows differ within the tolerances)
+            qx = np.ones((len(r), g)) if qs is None else np.take_along_axis(qs, drafts[r][:, :, None], 2)[..., 0]
+            px = np.take_along_axis(out["p"][:, :g], drafts[r][:, :, None], 2)[..., 0]
+            pg = np.take_along_axis(p_g[:, :g], drafts[r][:, :, None], 2)[..., 0]
+            th_o = np.minimum(1.0, px / np.maximum(qx, 1e-30))
+            th_g = np.minimum(1.0, pg / np.maximum(qx, 1e-30))
+            ua = u["u_acc"][r]
+            near = ((np.abs(ua - th_o) < 1e-4) | ((ua - th_o) * (ua - th_g) <= 0)).any(axis=1)
+        else:
+            near = np.zeros(len(r), bool)
+        same_n = out["n"] == n_g[r]
+        assert (same_n | near).all()
+        self.near_accept += int((~same_n).sum())
+        same_t = np.array([em_g[b, n_g[b]] == out["emitted"][j, n_g[b]] for j, b in enumerate(r)])
+        self.near_draw += int((same_n & ~same_t).sum())
+        # teacher forcing: follow the GPU's commit
+        self.ct.length = len0 + n_g[r] + 1
+        self.rounds += 1
+
+
+def _run(dec, replay, n_rounds, u_seed, check_draft=False, stop_at=None):
+    B, g, V = dec.B, dec.gamma, dec.V
+    logits = torch.empty((B, g + 1, V), dtype=torch.float32, device="cuda")
+    r = 0
+    while r < n_rounds:
+        if stop_at is not None and min(len(c) for c in dec.committed) - dec.prompt_len >= stop_at:
+            break
+        u = round_uniforms(u_seed, r, B, g)
+        uni = (torch.as_tensor(u["u_acc"]).cuda(), torch.as_tensor(u["u_res"]).cuda(),
+               torch.as_tensor(np.ascontiguousarray(u["u_draft"].T)).cuda())
+        committed_before = [list(c) for c in dec.committed]
+        last = np.array([c[-1] for c in committed_before])
+        n_g, em_g = dec.round(r, uni, logits_out=logits)
+        drafts, q, nd = dec.last_round
+        drafts = drafts.cpu().numpy().astype(np.int64)
+        q = None if q is None else q.cpu().numpy()
+        nd = None if nd is None else nd.cpu().numpy()
+        if check_draft:
+            replay.check_draft(committed_before, drafts, q, u["u_draft"])
+        replay.check_round(last, drafts, q, nd, u, logits.cpu().numpy(), n_g, em_g)
+        # round invariants
+        assert ((n_g >= 0) & (n_g <= g)).all()
+        for b in range(B):
+            assert (em_g[b, n_g[b] + 1:] == -1).all() and (em_g[b, :n_g[b]] == drafts[b, :n_g[b]]).all()
+        r += 1
+    return r
+
+
+def test_config1_tiny_full_generation():
+    """Tiny fp32 target, self-speculative 1-layer draft, B=1, gamma=4, 64-token
+    prompt, 32 new tokens: every round of the whole generation."""
+    sh = SHAPES["tiny"]
+    w = make_weights(sh, seed=301)
+    dsh = sh.with_(n_layers=1)
+    P, g, N = 64, 4, 32
+    max_ctx = P + N + g + 4
+    prompt = make_prompt(1, P, sh.vocab, seed=301)
+    target = bd.SpecModel(sh, to_dev(w))
+    draft = bd.SpecModel(dsh, to_dev(_sub(w, 1)))
+    dec = SpecDecoder(target, 1, g, max_ctx, drafter=ModelDrafter(draft, 1, g, max_ctx), seed=301)
+    dec.prefill(prompt)
+    rep = Replay(sh, w, prompt, [0], max_ctx, dsh, _sub(w, 1))
+    rounds = _run(dec, rep, N + 1, 301, check_draft=True, stop_at=N)
+    assert len(dec.committed[0]) - P >= N
+    rep.report('config 1')
+    assert rep.near_accept <= max(1, rounds // 10)
+
+
+def test_config2_small_full_generation():
+    """Small bf16 target (8 layers, 16/4 heads), self-speculative 2-layer draft,
+    B=1, gamma=4, 512-token prompt, 256 new tokens: every round."""
+    sh = SHAPES["small"]
+    w = make_weights(sh, seed=302)
+    dsh = sh.with_(n_layers=2)
+    P, g, N = 512, 4, 256
+    max_ctx = P + N + g + 4
+    prompt = make_prompt(1, P, sh.vocab, seed=302)
+    target = bd.SpecModel(sh, to_dev(w))
+    draft = bd.SpecModel(dsh, to_dev(_sub(w, 2)))
+    dec = SpecDecoder(target, 1, g, max_ctx, drafter=ModelDrafter(draft, 1, g, max_ctx), seed=302)
+    dec.prefill(prompt)
+    rep = Replay(sh, w, prompt, [0], max_ctx, dsh, _sub(w, 2))
+    rounds = _run(dec, rep, N + 1, 302, check_draft=True, stop_at=N)
+    assert len(dec.committed[0]) - P >= N
+    rep.report('config 2')
+    assert rep.near_accept <= max(2, rounds // 10)
+
+
+def test_config3_8b_shape_rounds():
+    """The 8B-shaped target with the 0.6B-shaped draft, B=1, gamma=4, at the
+    full model shapes: two rounds after a 24-token prompt."""
+    tsh, dsh = SHAPES["qwen3_8b"], SHAPES["qwen3_0p6b"]
+    P, g = 24, 4
+    max_ctx = P + 2 * (g + 1) + 4
+    wt = make_weights(tsh, seed=303, device="cuda")
+    wd = make_weights(dsh, seed=304, device="cuda")
+    prompt = make_prompt(1, P, tsh.vocab, seed=303)
+    target = bd.SpecModel(tsh, wt)
+    draft = bd.SpecModel(dsh, wd)
+    dec = SpecDecoder(target, 1, g, max_ctx, drafter=ModelDrafter(draft, 1, g, max_ctx), seed=303)
+    dec.prefill(prompt)
+    host = lambda w: {k: (w["embed"].cpu() if (k == "lm_head" and w["lm_head"] is w["embed"]) else v.cpu())
+                      for k, v in w.items()}
+    rep = Replay(tsh, host(wt), prompt, [0], max_ctx, dsh, host(wd), envelope=True)
+    rounds = _run(dec, rep, 2, 303, check_draft=True)
+    rep.report(f'{__name__}')
+    assert rounds == 2 and rep.near_accept <= 1
+
+
+@pytest.mark.parametrize("B", [1, 8, 64, 256])
+def test_config4_batch_sweep_round(B):
+    """Config-2 shapes at B sequences (verify M = 5B rows), 2-layer
+    self-speculative draft: two rounds; the oracle replays every sequence for
+    B <= 8, 8 seeded sequences otherwise.  Prompts are 256 tokens for B <= 8
+    and 16 tokens for B >= 64 (the prefill of B x 255 rows through the M <= 8
+    linear would dominate the test; the verify rounds are the same)."""
+    sh = SHAPES["small"]
+    w = make_weights(sh, seed=304)
+    dsh = sh.with_(n_layers=2)
+    P, g = (256 if B <= 8 else 16), 4
+    max_ctx = P + 2 * (g + 1) + 4
+    prompt = make_prompt(B, P, sh.vocab, seed=304 + B)
+    target = bd.SpecModel(sh, to_dev(w))
+    draft = bd.SpecModel(dsh, to_dev(_sub(w, 2)))
+    dec = SpecDecoder(target, B, g, max_ctx, drafter=ModelDrafter(draft, B, g, max_ctx), seed=304)
+    dec.prefill(prompt)
+    rows = np.arange(B) if B <= 8 else np.sort(np.random.default_rng(B).choice(B, 8, replace=False))
+    rep = Replay(sh, w, prompt, rows, max_ctx, dsh, _sub(w, 2))
+    rounds = _run(dec, rep, 2, 304 + B, check_draft=True)
+    rep.report(f'{__name__}')
+    assert rounds == 2 and rep.near_accept <= 1
+
+
+@pytest.mark.parametrize("B", [1, 64])
+def test_config5_ngram_long_draft(B):
+    """n-gram drafter (trigram prompt lookup, one-hot q) on the config-2 body
+    with V = 151936, gamma = 10, order-2 Markov prompts: two rounds; the oracle
+    replays every sequence for B = 1, 2 seeded sequences of 64.  Misses are
+    filled with the gamma tokens after a seeded prompt offset so every round
+    verifies B x 11 rows.  Prompts are 2048 tokens at B = 1 and 96 at B = 64
+    (the prefill of 64 x 2047 rows through the M <= 8 linear would dominate)."""
+    sh = SHAPES["small_v151936"]
+    w = make_weights(sh, seed=305)
+    P, g = (2048 if B == 1 else 96), 10
+    max_ctx = P + 2 * (g + 1) + 4
+    table = make_markov_table(seed=305)
+    prompt = markov_prompt(B, P, table, seed=305 + B).astype(np.int64)
+    rng = np.random.default_rng(305)
+    offs = rng.integers(0, P - g - 1, size=B)
+
+    def fill(b, L, k):
+        return [int(t) for t in prompt[b, offs[b]:offs[b] + k]]
+
+    target = bd.SpecModel(sh, to_dev(w))
+    drafter = NgramDrafter(B, g, n=3, fill=fill)
+    dec = SpecDecoder(target, B, g, max_ctx, drafter=drafter, seed=305)
+    dec.prefill(prompt)
+    rows = np.arange(B) if B <= 8 else np.sort(np.random.default_rng(B).choice(B, 2, replace=False))
+    rep = Replay(sh, w, prompt, rows, max_ctx)
+    # the proposer itself: the library's lookup equals the oracle's on every row
+    for b in range(B):
+        assert NG.ngram_propose(dec.committed[b], 3, g) == list(ngram_lookup(dec.committed[b], 3, g))
+    rounds = _run(dec, rep, 2, 305 + B)
+    rep.report(f'{__name__}')
+    assert rounds == 2 and rep.near_accept <= 1

@@ -1,0 +1,214 @@
+// Matrix-core linear for the verify pass with more than 8 activation rows:
+//   Y[M][N] (op) X[M][K] . W[N][K]^T, bf16 inputs, float32 accumulation.
+//
+// With B sequences the verify pass has M = B (gamma + 1) rows, and a prefill
+// has B (P - 1).  The arithmetic per weight byte grows with M (first page,
+// section "The speedup is borrowed, and there is a lender": the batch turns
+// the same weight read into more work), so past a few rows the linear is a
+// real dense contraction and belongs on MFMA.  The GEMV kernel would stream
+// the weights once per 8 rows instead.
+//
+// Tiles: a workgroup computes 64 rows x 128 weight rows of Y with 4 waves in
+// a 2 x 2 arrangement; each wave owns 32 x 64 = 2 x 4 tiles of
+// v_mfma_f32_16x16x32_bf16.  The K dimension advances 64 at a time through
+// two LDS buffers; the next block's 16-byte global loads are issued before
+// the current block is multiplied.  Fragment layouts (gfx950): A lane l holds
+// row l % 16, k = 8 (l / 16) .. +7; B lane l holds column l % 16, the same k;
+// D lane l holds rows 4 (l / 16) .. +3 of column l % 16.
+//
+// The epilogues match the GEMV kernel's.  For SwiGLU, a wave's 4 weight tiles
+// are 2 gate tiles and the 2 matching up tiles.  For QKV (head_dim 128) a
+// workgroup is one head, and a wave's tiles are dims {j, j + 64} pairs, so
+// both halves of a rotated pair sit in the same lane.
+//
+// Tile order: the workgroups of one weight tile run on one XCD, because the
+// hardware deals workgroup ids round-robin over the 8 XCDs; the weight tile
+// is then read into one L2 and reused there by every row block.
+#pragma once
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace sv {
+namespace mfma {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+constexpr int BM = 64;     // rows of X per workgroup
+constexpr int BN = 128;    // weight rows per workgroup
+constexpr int KB = 64;     // K per LDS stage
+constexpr int LDK = KB + 8;  // LDS row stride in bf16 (16-byte pad spreads the banks)
+constexpr int NTH = 256;
+constexpr int kXcds = 8;
+
+template <int EPI>
+__host__ __device__ inline int n_tiles(const GemvArgs& a) {
+  if (EPI == EPI_SWIGLU) return (a.N + 63) / 64;
+  if (EPI == EPI_QKV) return a.H + 2 * a.Hkv;
+  return (a.N + BN - 1) / BN;
+}
+
+// Weight row held in local tile row lr (0 .. 127) of weight tile nt.
+template <int EPI>
+__device__ __forceinline__ int w_row(const GemvArgs& a, int nt, int lr) {
+  const int wn = lr >> 6, c = lr & 63;
+  if constexpr (EPI == EPI_SWIGLU) {
+    const int n = min(nt * 64 + wn * 32 + (c & 31), a.N - 1);
+    return c < 32 ? n : a.N + n;
+  } else if constexpr (EPI == EPI_QKV) {
+    const int dim = (c < 32) ? wn * 32 + c : 64 + wn * 32 + (c - 32);
+    return nt * a.hd + dim;
+  } else {
+    return min(nt * BN + lr, a.N - 1);
+  }
+}
+
+template <int EPI>
+__global__ __launch_bounds__(NTH) void gemm_kernel(GemvArgs a, int mtiles, int ntiles) {
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM][LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t ws[2][BN][LDK];
+  const int per = gridDim.x / kXcds;
+  const int tile = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
+  if (tile >= mtiles * ntiles) return;  // padding workgroups leave before any barrier
+  const int mt = tile % mtiles, nt = tile / mtiles;
+  const int M = a.M, K = a.K, slice = blockIdx.y;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int m0 = mt * BM;
+
+  // this thread's global chunks: X 2 x 16 B, W 4 x 16 B per K block
+  const uint16_t* xp[2];
+  const uint16_t* wp[4];
+  int xr[2], xc[2], wr[4], wc[4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int c = threadIdx.x + i * NTH;
+    xr[i] = c >> 3;
+    xc[i] = (c & 7) * 8;
+    xp[i] = static_cast<const uint16_t*>(a.x) + static_cast<size_t>(min(m0 + xr[i], M - 1)) * a.ldx +
+            static_cast<size_t>(slice) * K + xc[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = threadIdx.x + i * NTH;
+    wr[i] = c >> 3;
+    wc[i] = (c & 7) * 8;
+    wp[i] = static_cast<const uint16_t*>(a.W) + static_cast<size_t>(w_row<EPI>(a, nt, wr[i])) * a.ldw +
+            static_cast<size_t>(slice) * K + wc[i];
+  }
+  v4u gx[2], gw[4];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) gx[i] = *reinterpret_cast<const v4u*>(xp[i] + k0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) gw[i] = *reinterpret_cast<const v4u*>(wp[i] + k0);
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) *reinterpret_cast<v4u*>(&xs[buf][xr[i]][xc[i]]) = gx[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<v4u*>(&ws[buf][wr[i]][wc[i]]) = gw[i];
+  };
+
+  f32x4_t acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = K / KB;
+  load(0);
+  store(0);
+  __syncthreads();
+  const int fr = lane & 15, fk = (lane >> 4) * 8;
+  for (int kb = 0; kb < nk; ++kb) {
+    const int buf = kb & 1;
+    if (kb + 1 < nk) load((kb + 1) * KB);
+#pragma unroll
+    for (int ks = 0; ks < KB; ks += 32) {
+      bf16x8_t af[2], bfr[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) af[i] = *reinterpret_cast<const bf16x8_t*>(&xs[buf][wm * 32 + i * 16 + fr][ks + fk]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bfr[j] = *reinterpret_cast<const bf16x8_t*>(&ws[buf][wn * 64 + j * 16 + fr][ks + fk]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    if (kb + 1 < nk) store(buf ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: lane holds rows 4 (lane / 16) + r of each 16-row tile, column lane % 16
+  const int col = lane & 15, rb = (lane >> 4) * 4;
+  float* y = a.y ? a.y + static_cast<size_t>(slice) * a.ysplit : nullptr;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = m0 + wm * 32 + i * 16 + rb + r;
+      if (m >= M) continue;
+      if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int n = nt * 64 + wn * 32 + j * 16 + col;
+          if (n < a.N) {
+            const float g = acc[i][j][r], u = acc[i][j + 2][r];
+            static_cast<uint16_t*>(a.z)[static_cast<size_t>(m) * a.ldz + n] = f2bf(g / (1.f + expf(-g)) * u);
+          }
+        }
+      } else if constexpr (EPI == EPI_QKV) {
+        const int H = a.H, Hkv = a.Hkv, hd = a.hd, half = hd / 2;
+        const int hh = nt;
+        const int rg = a.row0 + m;
+        const int b = rg / a.m_per_seq, ii = rg - b * a.m_per_seq;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int d = wn * 32 + j * 16 + col;  // 0 .. 63; its pair is d + 64
+          const float x0 = acc[i][j][r], y0 = acc[i][j + 2][r];
+          if (hh < H + Hkv) {
+            const float2 c = a.cs[static_cast<size_t>(rg) * half + d];
+            const float r0 = x0 * c.x - y0 * c.y, s0 = y0 * c.x + x0 * c.y;
+            if (hh < H) {
+              float* qr = a.q + static_cast<size_t>(rg) * (H * hd) + hh * hd;
+              qr[d] = r0;
+              qr[d + half] = s0;
+            } else {
+              const int pos = a.len[b] + ii;
+              if (pos >= 0 && pos < a.max_ctx) {
+                uint16_t* dst = static_cast<uint16_t*>(a.kc) +
+                                (((static_cast<size_t>(a.layer) * a.kvB + b) * Hkv + (hh - H)) * a.max_ctx + pos) * hd;
+                dst[d] = f2bf(r0);
+                dst[d + half] = f2bf(s0);
+              }
+            }
+          } else {
+            const int pos = a.len[b] + ii;
+            if (pos >= 0 && pos < a.max_ctx) {
+              uint16_t* dst = static_cast<uint16_t*>(a.vc) +
+                              (((static_cast<size_t>(a.layer) * a.kvB + b) * Hkv + (hh - H - Hkv)) * a.max_ctx + pos) * hd;
+              dst[d] = f2bf(x0);
+              dst[d + half] = f2bf(y0);
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int n = nt * BN + wn * 64 + j * 16 + col;
+          if (n < a.N) {
+            float* dst = y + static_cast<size_t>(m) * a.ldy + n;
+            if constexpr (EPI == EPI_RESID) *dst += acc[i][j][r];
+            else *dst = acc[i][j][r];
+          }
+        }
+      }
+    }
+  }
+}
+
+}  // namespace mfma
+}  // namespace sv

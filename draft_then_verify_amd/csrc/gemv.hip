@@ -7,9 +7,12 @@
 // MI355X with M = 5, the weights rotated through more memory than the
 // 256 MB last-level cache holds.  U is lowered to the largest of 8, 4, 2, 1 that divides
 // the steps per row.  Activation rows go through in blocks of at most 8 that
-// fit the LDS.
+// fit the LDS.  bf16 passes with more than 8 rows go to the matrix-core
+// kernel (gemm_mfma.hpp), which reads the weights once per 64 rows.
 #include <algorithm>
+#include <type_traits>
 
+#include "gemm_mfma.hpp"
 #include "gemv_kernels.hpp"
 
 namespace sv {
@@ -75,6 +78,17 @@ hipError_t launch_rows(const GemvArgs& a, int mb, hipStream_t s) {
   }
 }
 
+template <int EPI>
+hipError_t launch_gemm(const GemvArgs& b, int M, hipStream_t s) {
+  GemvArgs a = b;
+  a.M = M;
+  const int mt = (M + mfma::BM - 1) / mfma::BM, nt = mfma::n_tiles<EPI>(a);
+  const int total = mt * nt;
+  const int grid = (total + mfma::kXcds - 1) / mfma::kXcds * mfma::kXcds;
+  hipLaunchKernelGGL(mfma::gemm_kernel<EPI>, dim3(grid, a.ksplit), dim3(mfma::NTH), 0, s, a, mt, nt);
+  return hipGetLastError();
+}
+
 template <typename WT, int EPI>
 hipError_t launch_all(const GemvArgs& a0, int M, hipStream_t s) {
   constexpr int STEP = step_elems<WT>();
@@ -87,6 +101,8 @@ hipError_t launch_all(const GemvArgs& a0, int M, hipStream_t s) {
   b.K /= b.ksplit;  // the kernel sees one slice
   if (b.K % VE || b.ldw % VE || b.ldx % VE) return hipErrorInvalidValue;
   if (EPI == EPI_QKV && (b.N % 2 || b.hd % 2)) return hipErrorInvalidValue;
+  if (std::is_same<WT, uint16_t>::value && M > 8 && b.K % mfma::KB == 0 && (EPI != EPI_QKV || b.hd == 128))
+    return launch_gemm<EPI>(b, M, s);
   const size_t kp = static_cast<size_t>((b.K + STEP - 1) / STEP) * STEP;
   const int fit = static_cast<int>(kMaxLds / (kp * sizeof(WT)));
   if (fit < 1) return hipErrorInvalidValue;

@@ -1,7 +1,9 @@
-"""GPU parity of the weight-streaming linear (spec_linear) at every weight
-shape of the 8B-shaped target and of the small target, M = 1 .. 13 rows
-(several 8-row blocks), against the oracle's linear.  bf16 weights and
-inputs, float32 accumulate: the tolerance is relative to sum |x||w|."""
+"""GPU parity of the linear (spec_linear) at every weight shape of the
+8B-shaped target and of the small target against the oracle's linear: the
+weight-streaming kernel for M <= 8 (several 8-row blocks for fp32) and the
+matrix-core kernel for bf16 with M > 8 (ragged 64-row blocks, up to the
+1280 rows of a B = 256 verify pass).  bf16 weights and inputs, float32
+accumulate: the tolerance is relative to sum |x||w|."""
 import numpy as np
 import pytest
 import torch
@@ -60,6 +62,18 @@ def test_linear_epilogues(epi):
 def test_linear_row_counts(M):
     _check(1000, 1024, M, 0, seed=M)
     _check(6144, 4096, M, 1, seed=100 + M)
+
+
+@pytest.mark.parametrize("M", [16, 40, 64, 65, 320])
+@pytest.mark.parametrize("epi", [0, 1, 2])
+def test_linear_matrix_cores(M, epi):
+    _check(4096, 4096, M, epi, seed=200 + M + epi)
+
+
+def test_linear_matrix_cores_large():
+    _check(2816, 1024, 1280, 2, seed=301)   # SwiGLU, small-config MLP, B = 256 verify rows
+    _check(32000, 1024, 1280, 0, seed=302)  # small-config LM head
+    _check(151936, 4096, 40, 0, seed=303)   # 8B LM head, B = 8 verify rows
 
 
 def test_linear_float32():

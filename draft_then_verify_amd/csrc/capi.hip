@@ -74,8 +74,8 @@ Layout make_layout(const spec_model_cfg& c, int B, int m, int max_ctx) {
   L.po = take(static_cast<size_t>(B) * c.n_heads * m * L.n_split * c.head_dim * 4);
   L.pml = take(static_cast<size_t>(B) * c.n_heads * m * L.n_split * 8);
   L.ctr = take(static_cast<size_t>(L.n_ctr) * 4);  // attention tickets
-  L.ks_o = sv::gemv_ksplit(c.dtype == SPEC_BF16, static_cast<int>(rows), hq);
-  L.ks_d = sv::gemv_ksplit(c.dtype == SPEC_BF16, static_cast<int>(rows), c.d_ff);
+  L.ks_o = sv::gemv_ksplit(c.dtype == SPEC_BF16, static_cast<int>(rows), c.d_model, hq);
+  L.ks_d = sv::gemv_ksplit(c.dtype == SPEC_BF16, static_cast<int>(rows), c.d_model, c.d_ff);
   L.pt = take(static_cast<size_t>(std::max(L.ks_o, L.ks_d)) * rows * c.d_model * 4);  // K-slice partials
   L.logits = take(rows * c.vocab * 4);
   L.part = take(rows * nch * 8);

@@ -134,7 +134,19 @@ hipError_t launch_dtype(int epi, const GemvArgs& a, int M, hipStream_t s) {
 
 }  // namespace
 
-int gemv_ksplit(bool bf16, int M, int K) {
+int gemv_ksplit(bool bf16, int M, int N, int K) {
+  if (bf16 && M > 8 && K % mfma::KB == 0) {
+    // matrix-core path: enough workgroups (about 2 per CU) from row blocks x
+    // weight tiles x K slices
+    const int tiles = ((M + mfma::BM - 1) / mfma::BM) * ((N + mfma::BN - 1) / mfma::BN);
+    int best = 1;
+    for (int ks = 1; ks <= 8; ++ks) {
+      if (K % (ks * mfma::KB)) continue;
+      best = ks;
+      if (tiles * ks >= 2 * kCUs) break;
+    }
+    return best;
+  }
   const int elt = bf16 ? 2 : 4;
   const int step = kWave * (16 / elt);
   const int mb = std::min(M, 8);

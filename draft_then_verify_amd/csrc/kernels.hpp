@@ -42,9 +42,11 @@ struct GemvArgs {
 };
 hipError_t launch_gemv(bool bf16, int epi, const GemvArgs& a, int M, hipStream_t s);
 
-// K slices the residual linears use for an M-row pass (a divisor of K that
-// keeps a workgroup's staged activations near 40 KiB).
-int gemv_ksplit(bool bf16, int M, int K);
+// K slices the residual linears use for an M-row pass with N outputs: for
+// M <= 8, a divisor of K that keeps a workgroup's staged activations near
+// 40 KiB; for the matrix-core path, enough slices for about 2 workgroups per
+// CU.
+int gemv_ksplit(bool bf16, int M, int N, int K);
 
 // h[r][:] += part[0][r][:] + ... + part[ks-1][r][:] (slices summed in order
 // first, float32; slice stride pstride floats), then

@@ -22,7 +22,7 @@ STATUS = {0: "SPEC_OK", -1: "SPEC_EINVAL", -2: "SPEC_ENOMEM", -3: "SPEC_EHIP", -
 # Every symbol the C header declares.
 EXPORTS = ("spec_model_create", "spec_model_destroy", "spec_workspace_bytes", "spec_sampler_workspace_bytes",
            "spec_verify_forward", "spec_softmax_pq", "spec_reject_sample", "spec_decode_step", "spec_linear",
-           "spec_kv_set_len", "spec_last_error")
+           "spec_kv_set_len", "spec_last_error", "spec_commit_round")
 
 
 class SpecError(RuntimeError):
@@ -76,6 +76,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                    sz, vp]),
         "spec_linear": (i32, [i32, i32, vp, vp, i32, i32, i32, vp, vp, vp]),
         "spec_kv_set_len": (i32, [ctypes.POINTER(spec_kv), i32, vp, i32, vp]),
+        "spec_commit_round": (i32, [i32, i32, vp, vp, vp, vp, vp, vp, i32, vp]),
         "spec_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -217,6 +218,12 @@ def spec_decode_step(target: SpecModel, kv: KVCache, B: int, gamma: int, tempera
 def spec_linear(W, x, M: int, N: int, K: int, epilogue: int = 0, y=None, z=None, stream=None):
     dt = SPEC_BF16 if W.dtype == torch.bfloat16 else SPEC_F32
     _check(load_library().spec_linear(dt, epilogue, _ptr(W), _ptr(x), M, N, K, _ptr(y), _ptr(z), _stream(stream)))
+
+
+def spec_commit_round(B: int, gamma: int, n_accepted, emitted, tok2, last, out_tokens, out_len, cap: int,
+                      stream=None):
+    _check(load_library().spec_commit_round(B, gamma, _ptr(n_accepted), _ptr(emitted), _ptr(tok2), _ptr(last),
+                                            _ptr(out_tokens), _ptr(out_len), cap, _stream(stream)))
 
 
 def spec_kv_set_len(kv: KVCache, B: int, src, add: int, stream=None):

@@ -377,6 +377,16 @@ SPEC_API spec_status spec_linear(int32_t dtype, int32_t epilogue, const void* W,
   return SPEC_OK;
 }
 
+SPEC_API spec_status spec_commit_round(int32_t B, int32_t gamma, const int32_t* n_accepted, const int32_t* emitted,
+                                       int32_t* tok2, int32_t* last, int32_t* out_tokens, int32_t* out_len,
+                                       int32_t cap, hipStream_t stream) {
+  if (B <= 0 || gamma < 0 || cap < 0) return fail(SPEC_EINVAL, "B=%d gamma=%d cap=%d", B, gamma, cap);
+  if (!n_accepted || !emitted || !tok2 || !out_len || (cap > 0 && !out_tokens))
+    return fail(SPEC_EINVAL, "NULL argument");
+  HIP_TRY(sv::launch_commit_round(B, gamma, n_accepted, emitted, tok2, last, out_tokens, out_len, cap, stream));
+  return SPEC_OK;
+}
+
 SPEC_API spec_status spec_kv_set_len(const spec_kv* kv, int32_t B, const int32_t* src, int32_t add,
                                      hipStream_t stream) {
   if (!kv || !kv->len) return fail(SPEC_EINVAL, "kv/len is NULL");

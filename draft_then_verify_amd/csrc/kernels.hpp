@@ -84,6 +84,10 @@ int attn_num_splits(int B, int H, int Hkv, int m, int max_ctx);
 size_t attn_counters(int B, int H, int Hkv, int m);  // tickets the launch uses
 hipError_t launch_attention(bool bf16, int hd, const AttnArgs& a, int B, hipStream_t s);
 
+// Round bookkeeping (see spec_commit_round).
+hipError_t launch_commit_round(int B, int gamma, const int32_t* n_acc, const int32_t* emitted, int32_t* tok2,
+                               int32_t* last, int32_t* out, int32_t* out_len, int cap, hipStream_t s);
+
 // len[b] = (src ? src[b] : len[b]) + add
 hipError_t launch_kv_len(int32_t* len, const int32_t* src, int add, int B, hipStream_t s);
 

@@ -126,6 +126,27 @@ hipError_t launch_resid_norm_t(float* h, const float* part, int ks, size_t pstri
   return hipGetLastError();
 }
 
+// Round bookkeeping on the device: append x_1 .. x_n, t to each sequence's
+// output and make (x_n or the old last token, t) the next round's inputs.
+__global__ void commit_round_kernel(int B, int gamma, const int32_t* __restrict__ n_acc,
+                                    const int32_t* __restrict__ emitted, int32_t* __restrict__ tok2,
+                                    int32_t* __restrict__ last, int32_t* __restrict__ out, int32_t* __restrict__ out_len,
+                                    int cap) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  const int n = min(max(n_acc[b], 0), gamma);
+  const int32_t* em = emitted + static_cast<size_t>(b) * (gamma + 1);
+  const int len = out_len[b];
+  for (int i = 0; i <= n; ++i)
+    if (len + i < cap) out[static_cast<size_t>(b) * cap + len + i] = em[i];
+  out_len[b] = len + n + 1;
+  const int32_t t = em[n];
+  const int32_t prev = n > 0 ? em[n - 1] : tok2[2 * b + 1];
+  tok2[2 * b] = prev;
+  tok2[2 * b + 1] = t;
+  if (last) last[b] = t;
+}
+
 __global__ void kv_len_kernel(int32_t* len, const int32_t* src, int add, int B) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b < B) len[b] = (src ? src[b] : len[b]) + add;
@@ -154,6 +175,13 @@ hipError_t launch_resid_norm(bool bf16, float* h, const float* part, int ks, siz
   if (d % 4 != 0 || d > 16 * kThreads || pstride % 4 != 0) return hipErrorInvalidValue;
   if (bf16) return launch_resid_norm_t(h, part, ks, pstride, rows, d, gain, eps, static_cast<uint16_t*>(x), s);
   return launch_resid_norm_t(h, part, ks, pstride, rows, d, gain, eps, static_cast<float*>(x), s);
+}
+
+hipError_t launch_commit_round(int B, int gamma, const int32_t* n_acc, const int32_t* emitted, int32_t* tok2,
+                               int32_t* last, int32_t* out, int32_t* out_len, int cap, hipStream_t s) {
+  hipLaunchKernelGGL(commit_round_kernel, dim3((B + 255) / 256), dim3(256), 0, s, B, gamma, n_acc, emitted, tok2,
+                     last, out, out_len, cap);
+  return hipGetLastError();
 }
 
 hipError_t launch_kv_len(int32_t* len, const int32_t* src, int add, int B, hipStream_t s) {

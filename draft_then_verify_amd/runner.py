@@ -205,3 +205,72 @@ class SpecDecoder:
             "per_position": (accepted_per_pos / num_drafts).tolist() if g else [],
             "round_ms_p50": float(np.percentile(round_ms, 50)), "round_ms_p99": float(np.percentile(round_ms, 99)),
         }
+
+    def generate_graph(self, n_new: int) -> dict:
+        """The rounds of generate(), with the same uniforms, run as replays of
+        one captured HIP graph per round: the drafter's passes, the verify
+        step and the round bookkeeping (spec_commit_round) all stay on the
+        device.  Per round the host only copies that round's uniforms into the
+        graph's buffers; it reads the output count once per batch of rounds,
+        each batch no longer than the fewest rounds that could finish."""
+        B, g = self.B, self.gamma
+        if g > 0 and not isinstance(self.drafter, ModelDrafter):
+            raise ValueError("graph rounds need a device drafter (ModelDrafter) or gamma = 0")
+        cap = n_new + g + 1
+        dev = "cuda"
+        tok2 = _dev_i32([[c[-2], c[-1]] for c in self.committed])
+        last = _dev_i32([c[-1] for c in self.committed])
+        out = torch.zeros((B, cap), dtype=torch.int32, device=dev)
+        out_len = torch.zeros(B, dtype=torch.int32, device=dev)
+        max_rounds = n_new + 1
+        pool = [self._uniforms(r) for r in range(max_rounds)]
+        ua_all = torch.stack([p[0] for p in pool]) if g else None
+        ur_all = torch.stack([p[1] for p in pool])
+        ud_all = torch.stack([p[2] for p in pool]) if g else None
+        u_acc = torch.empty_like(ua_all[0]) if g else None
+        u_res = torch.empty_like(ur_all[0])
+        u_draft = torch.empty_like(ud_all[0]) if g else None
+
+        def load_uniforms(r):
+            if g:
+                u_acc.copy_(ua_all[r])
+                u_draft.copy_(ud_all[r])
+            u_res.copy_(ur_all[r])
+
+        def body():
+            drafts = q = None
+            if g:
+                drafts, q, _ = self.drafter.draft(tok2, self.kv.len, u_draft)
+            bd.spec_decode_step(self.target, self.kv, B, g, self.T, last, drafts, None, q, u_acc, u_res, self.n,
+                                self.emitted, None, self.ws)
+            bd.spec_commit_round(B, g, self.n, self.emitted, tok2, last, out, out_len, cap)
+
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        # round 0 eagerly (it also performs every kernel's one-time set-up), then capture
+        load_uniforms(0)
+        body()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            body()
+        rounds = 1
+        while True:
+            remaining = n_new - int(out_len.min().item())
+            if remaining <= 0:
+                break
+            for _ in range(max(1, -(-remaining // (g + 1)))):
+                load_uniforms(rounds)
+                graph.replay()
+                rounds += 1
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        total = out_len.cpu().numpy()
+        toks = out.cpu().numpy()
+        tokens = [list(map(int, toks[b, :n_new])) for b in range(B)]
+        for b in range(B):
+            self.committed[b] += list(map(int, toks[b, :min(int(total[b]), cap)]))
+        accepted = int(total.sum()) - rounds * B
+        return {"tokens": tokens, "rounds": rounds, "wall_s": wall, "tok_s": B * n_new / wall,
+                "mean_acceptance_length": 1.0 + accepted / (rounds * B),
+                "acceptance_rate": accepted / max(rounds * B * g, 1)}
+

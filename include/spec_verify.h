@@ -187,6 +187,20 @@ spec_status spec_decode_step(const spec_model* target, const spec_kv* kv, int32_
 spec_status spec_linear(int32_t dtype, int32_t epilogue, const void* W, const void* x, int32_t M, int32_t N,
                         int32_t K, float* y, void* z, hipStream_t stream);
 
+/* Round bookkeeping on the device, so a whole generation can run as graph
+ * replays with no host round trip per round (first page, Algorithm 1: a
+ * round emits x_1 .. x_n, t; the next round starts from t).  For b < B:
+ * appends emitted[b][0 .. n] (n = n_accepted[b], clamped to [0, gamma]) to
+ * out_tokens[b][out_len[b] ...] (positions >= cap are dropped but counted),
+ * out_len[b] += n + 1, tok2[b] = (x_n, or the old tok2[b][1] when n = 0; t),
+ * and last[b] = t when last is not NULL.
+ *   n_accepted [B], emitted [B][gamma+1] as written by spec_decode_step;
+ *   tok2 [B][2] in/out; last [B] out or NULL; out_tokens [B][cap];
+ *   out_len [B] in/out.  Errors: SPEC_EINVAL, SPEC_EHIP. */
+spec_status spec_commit_round(int32_t B, int32_t gamma, const int32_t* n_accepted, const int32_t* emitted,
+                              int32_t* tok2, int32_t* last, int32_t* out_tokens, int32_t* out_len, int32_t cap,
+                              hipStream_t stream);
+
 /* KV length bookkeeping: len[b] = (src ? src[b] : len[b]) + add for b < B.
  * Used to advance after prefill / draft passes and to rewind a drafter to the
  * target's length.  Errors: SPEC_EINVAL, SPEC_EHIP. */

@@ -27,7 +27,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = header_functions()
-    assert len(names) == 11
+    assert len(names) == 12
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(bd.EXPORTS) == names
@@ -66,3 +66,5 @@ def test_host_checks_reject_before_launch(lib):
     assert lib.spec_kv_set_len(ctypes.byref(kv), 3, None, 1, None) == -1
     assert lib.spec_verify_forward(None, ctypes.byref(kv), 1, 1, 1, None, 1, 1 << 30, None) == -1
     assert lib.spec_workspace_bytes(None, 1, 1, 16) == 0
+    assert lib.spec_commit_round(0, 4, 1, 1, 1, None, 1, 1, 8, None) == -1
+    assert lib.spec_commit_round(1, 4, None, 1, 1, None, 1, 1, 8, None) == -1

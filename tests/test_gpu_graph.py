@@ -1,0 +1,50 @@
+"""The graph-replayed generation (drafter passes + verify step + round
+bookkeeping on the device, one HIP graph replay per round) emits exactly the
+tokens of the host-driven generation, which the config tests hold to the
+oracle: same models, prompts and per-round uniforms.  Each replay re-reads
+the uniforms copied in by the host, so every round of the graph is checked."""
+import numpy as np
+import pytest
+
+from draft_then_verify_amd import binding as bd
+from draft_then_verify_amd.runner import ModelDrafter, SpecDecoder
+from synth import SHAPES, make_prompt, make_weights
+from tests._gpu import to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _sub(w, layers):
+    return {k: (v[:layers] if k in ("attn_norm", "wqkv", "wo", "mlp_norm", "wgu", "wd") else v) for k, v in w.items()}
+
+
+def _pair(shape, B, g, P, N, seed, draft_layers):
+    w = make_weights(shape, seed=seed)
+    max_ctx = P + N + g + 4
+    prompt = make_prompt(B, P, shape.vocab, seed=seed)
+    target = bd.SpecModel(shape, to_dev(w))
+    outs = []
+    for mode in ("eager", "graph"):
+        drafter = None
+        if g:
+            dsh = shape.with_(n_layers=draft_layers)
+            drafter = ModelDrafter(bd.SpecModel(dsh, to_dev(_sub(w, draft_layers))), B, g, max_ctx)
+        dec = SpecDecoder(target, B, g, max_ctx, drafter=drafter, seed=seed)
+        dec.prefill(prompt)
+        res = dec.generate(N) if mode == "eager" else dec.generate_graph(N)
+        outs.append(res)
+    assert outs[0]["tokens"] == outs[1]["tokens"]
+    assert outs[0]["rounds"] <= outs[1]["rounds"] <= outs[0]["rounds"] + 1
+    return outs
+
+
+def test_graph_rounds_tiny_speculative():
+    _pair(SHAPES["tiny"], B=1, g=4, P=64, N=32, seed=401, draft_layers=1)
+
+
+def test_graph_rounds_small_batch():
+    _pair(SHAPES["small"], B=3, g=4, P=40, N=48, seed=402, draft_layers=2)
+
+
+def test_graph_rounds_plain_decoding():
+    _pair(SHAPES["small"], B=2, g=0, P=24, N=20, seed=403, draft_layers=0)

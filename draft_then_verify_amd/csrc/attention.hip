@@ -36,8 +36,9 @@
 namespace sv {
 namespace {
 
-constexpr int kThreadsA = 512;
-constexpr int kWaves = kThreadsA / kWave;
+// Waves per workgroup (8: two per query head of a 4-head group; 16 measured
+// no faster at B = 1, gamma = 4).
+__host__ __device__ constexpr int waves_for(int) { return 8; }
 constexpr int KT = 64;  // keys per tile (one per lane)
 
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));  // 16 bytes, kept in registers
@@ -86,22 +87,24 @@ template <> struct VRow<float, 1> {
 
 // Shape of the work split, shared by the launcher and the kernel.
 struct Plan {
-  int hpw;  // query heads per workgroup (min(G, 8))
+  int hpw;  // query heads per workgroup (min(G, waves))
   int nhb;  // head blocks per KV head (G / hpw)
-  int rb;   // query rows per workgroup ((8 / hpw) * mq)
+  int rb;   // query rows per workgroup ((waves / hpw) * mq)
   int nqc;  // row blocks (ceil(m / rb))
 };
-__host__ __device__ inline Plan make_plan(int H, int Hkv, int m, int mq) {
+__host__ __device__ inline Plan make_plan(int H, int Hkv, int m, int mq, int waves) {
   Plan p;
   const int G = H / Hkv;
-  p.hpw = G < kWaves ? G : kWaves;
+  p.hpw = G < waves ? G : waves;
   p.nhb = G / p.hpw;
-  p.rb = (kWaves / p.hpw) * mq;
+  p.rb = (waves / p.hpw) * mq;
   p.nqc = (m + p.rb - 1) / p.rb;
   return p;
 }
 
 template <typename ET, int HD> struct Lds {
+  static constexpr int kWaves = waves_for(HD);
+  static constexpr int kThreadsA = kWaves * kWave;
   static constexpr int KROW = HD * static_cast<int>(sizeof(ET));  // bytes of a K/V row
   static constexpr int KSTR = KROW + 16;                          // padded K row stride (bank spread)
   static constexpr int CPR = KROW / 16;                           // 16-byte chunks per row
@@ -119,7 +122,7 @@ __device__ __forceinline__ void load_tile(const ET* kc, const ET* vc, size_t kvb
   using L = Lds<ET, HD>;
 #pragma unroll
   for (int i = 0; i < L::NL; ++i) {
-    const int c = threadIdx.x + i * kThreadsA;
+    const int c = threadIdx.x + i * L::kThreadsA;
     const int row = c / L::CPR, col = c - row * L::CPR;
     const size_t g = (kvbase + min(k0 + row, klast)) * HD + static_cast<size_t>(col) * Cvt<ET>::n;
     kr[i] = *reinterpret_cast<const v4u*>(kc + g);
@@ -133,7 +136,7 @@ __device__ __forceinline__ void store_tile(char* ks, char* vs, const v4u (&kr)[L
   using L = Lds<ET, HD>;
 #pragma unroll
   for (int i = 0; i < L::NL; ++i) {
-    const int c = threadIdx.x + i * kThreadsA;
+    const int c = threadIdx.x + i * L::kThreadsA;
     const int row = c / L::CPR, col = c - row * L::CPR;
     *reinterpret_cast<v4u*>(ks + row * L::KSTR + col * 16) = kr[i];
     *reinterpret_cast<v4u*>(vs + row * L::KROW + col * 16) = vr[i];
@@ -141,8 +144,10 @@ __device__ __forceinline__ void store_tile(char* ks, char* vs, const v4u (&kr)[L
 }
 
 template <typename ET, int HD, int MQ>
-__global__ __launch_bounds__(kThreadsA) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(waves_for(HD) * kWave) __attribute__((amdgpu_waves_per_eu(waves_for(HD) / 4))) void attn_kernel(
+    AttnArgs a) {
   using L = Lds<ET, HD>;
+  constexpr int kThreadsA = L::kThreadsA;
   constexpr int DPL = HD / kWave;  // output dims per lane
   constexpr int CE = Cvt<ET>::n;   // elements per 16-byte chunk
   static_assert(L::NL * kThreadsA == KT * L::CPR, "tile chunks must split evenly over the threads");
@@ -157,7 +162,7 @@ __global__ __launch_bounds__(kThreadsA) __attribute__((amdgpu_waves_per_eu(1, 1)
   __shared__ int last_sh;
 
   const int H = a.H, Hkv = a.Hkv, m = a.m;
-  const Plan pl = make_plan(H, Hkv, m, MQ);
+  const Plan pl = make_plan(H, Hkv, m, MQ, L::kWaves);
   const int G = H / Hkv;
   const int hb = blockIdx.x % pl.nhb;
   const int kvh = (blockIdx.x / pl.nhb) % Hkv;
@@ -347,24 +352,24 @@ hipError_t launch_mq(const AttnArgs& a, int B, hipStream_t s) {
     if (e != hipSuccess) return e;
     opt_in = true;
   }
-  const Plan pl = make_plan(a.H, a.Hkv, a.m, MQ);
+  const Plan pl = make_plan(a.H, a.Hkv, a.m, MQ, L::kWaves);
   if (pl.nqc != a.n_qc || a.n_split < 1 || a.n_split > kWave) return hipErrorInvalidValue;
   dim3 grid(B * a.Hkv * pl.nhb, a.n_split, pl.nqc);
-  hipLaunchKernelGGL(kern, grid, dim3(kThreadsA), lds, s, a);
+  hipLaunchKernelGGL(kern, grid, dim3(L::kThreadsA), lds, s, a);
   return hipGetLastError();
 }
 
 // Query rows per wave: the rows of a block spread over the waves of a head.
-int rows_per_wave(int H, int Hkv, int m) {
-  const int G = H / Hkv;
-  const int wph = kWaves / (G < kWaves ? G : kWaves);
+int rows_per_wave(int H, int Hkv, int hd, int m) {
+  const int G = H / Hkv, waves = waves_for(hd);
+  const int wph = waves / (G < waves ? G : waves);
   const int mq = (m + wph - 1) / wph;
   return mq < 8 ? mq : 8;
 }
 
 template <typename ET, int HD>
 hipError_t launch_hd(const AttnArgs& a, int B, hipStream_t s) {
-  switch (rows_per_wave(a.H, a.Hkv, a.m)) {
+  switch (rows_per_wave(a.H, a.Hkv, HD, a.m)) {
     case 1: return launch_mq<ET, HD, 1>(a, B, s);
     case 2: return launch_mq<ET, HD, 2>(a, B, s);
     case 3: return launch_mq<ET, HD, 3>(a, B, s);
@@ -381,22 +386,24 @@ hipError_t launch_hd(const AttnArgs& a, int B, hipStream_t s) {
 bool attn_supported(int H, int Hkv, int hd) {
   if (hd != 64 && hd != 128) return false;
   if (Hkv <= 0 || H % Hkv != 0) return false;
-  const int G = H / Hkv;
-  return G <= kWaves ? (kWaves % G == 0) : (G % kWaves == 0);
+  const int G = H / Hkv, waves = waves_for(hd);
+  return G <= waves ? (waves % G == 0) : (G % waves == 0);
 }
 
-int attn_row_blocks(int H, int Hkv, int m) { return make_plan(H, Hkv, m, rows_per_wave(H, Hkv, m)).nqc; }
+int attn_row_blocks(int H, int Hkv, int hd, int m) {
+  return make_plan(H, Hkv, m, rows_per_wave(H, Hkv, hd, m), waves_for(hd)).nqc;
+}
 
-int attn_num_splits(int B, int H, int Hkv, int m, int max_ctx) {
-  const Plan pl = make_plan(H, Hkv, m, rows_per_wave(H, Hkv, m));
+int attn_num_splits(int B, int H, int Hkv, int hd, int m, int max_ctx) {
+  const Plan pl = make_plan(H, Hkv, m, rows_per_wave(H, Hkv, hd, m), waves_for(hd));
   const int units = B * Hkv * pl.nhb * pl.nqc;  // workgroups per split
   int n = (512 + units - 1) / units;
   n = min(n, (max_ctx + KT - 1) / KT);
   return max(1, min(n, kWave));
 }
 
-size_t attn_counters(int B, int H, int Hkv, int m) {
-  const Plan pl = make_plan(H, Hkv, m, rows_per_wave(H, Hkv, m));
+size_t attn_counters(int B, int H, int Hkv, int hd, int m) {
+  const Plan pl = make_plan(H, Hkv, m, rows_per_wave(H, Hkv, hd, m), waves_for(hd));
   return static_cast<size_t>(B) * Hkv * pl.nhb * pl.nqc;
 }
 

@@ -56,9 +56,9 @@ Layout make_layout(const spec_model_cfg& c, int B, int m, int max_ctx) {
   const size_t elt = c.dtype == SPEC_BF16 ? 2 : 4;
   const int hq = c.n_heads * c.head_dim;
   const int nch = sv::sampler_chunks(c.vocab);
-  L.n_qc = sv::attn_row_blocks(c.n_heads, c.n_kv_heads, m);
-  L.n_split = sv::attn_num_splits(B, c.n_heads, c.n_kv_heads, m, max_ctx);
-  L.n_ctr = static_cast<int>(sv::attn_counters(B, c.n_heads, c.n_kv_heads, m));
+  L.n_qc = sv::attn_row_blocks(c.n_heads, c.n_kv_heads, c.head_dim, m);
+  L.n_split = sv::attn_num_splits(B, c.n_heads, c.n_kv_heads, c.head_dim, m, max_ctx);
+  L.n_ctr = static_cast<int>(sv::attn_counters(B, c.n_heads, c.n_kv_heads, c.head_dim, m));
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -209,7 +209,7 @@ SPEC_API spec_status spec_model_create(const spec_model_cfg* cfg, const spec_wei
   if (c.head_dim != 64 && c.head_dim != 128) return fail(SPEC_EUNSUPPORTED, "head_dim %d (64 or 128)", c.head_dim);
   if (c.n_heads % c.n_kv_heads) return fail(SPEC_EINVAL, "n_heads %% n_kv_heads != 0");
   if (!sv::attn_supported(c.n_heads, c.n_kv_heads, c.head_dim))
-    return fail(SPEC_EUNSUPPORTED, "query heads per KV head %d must divide 8 or be a multiple of 8",
+    return fail(SPEC_EUNSUPPORTED, "query heads per KV head %d must divide 8 (16 at head_dim 128) or be a multiple",
                 c.n_heads / c.n_kv_heads);
   if (c.d_model > 16 * 256) return fail(SPEC_EUNSUPPORTED, "d_model %d > 4096", c.d_model);
   if (static_cast<size_t>(std::max(c.d_model, std::max(c.d_ff, c.n_heads * c.head_dim))) *
@@ -304,8 +304,8 @@ namespace {
 spec_status check_sampler_args(int B, int gamma, int V, const int32_t* draft, const float* u_acc, const float* u_res,
                                const int32_t* n_accepted, const int32_t* emitted) {
   if (B <= 0 || B > 65535) return fail(SPEC_EINVAL, "B=%d (1..65535)", B);
-  if (gamma < 0 || gamma > 64) return fail(SPEC_EINVAL, "gamma=%d (0..64)", gamma);
-  if (V <= 0 || V >= (1 << 23)) return fail(SPEC_EINVAL, "vocab=%d (1..2^23-1)", V);
+  if (gamma < 0 || gamma > 63) return fail(SPEC_EINVAL, "gamma=%d (0..63)", gamma);
+  if (V <= 0 || V > 64 * 4096) return fail(SPEC_EINVAL, "vocab=%d (1..262144)", V);
   if (gamma > 0 && (!draft || !u_acc)) return fail(SPEC_EINVAL, "draft/u_acc NULL with gamma > 0");
   if (!u_res || !n_accepted || !emitted) return fail(SPEC_EINVAL, "u_res/n_accepted/emitted NULL");
   return SPEC_OK;

@@ -78,10 +78,12 @@ struct AttnArgs {
   int* counters = nullptr;     // attn_counters(...) tickets, zero between launches
   void* xo = nullptr;          // [B*m][H*hd] output in the model dtype
 };
-bool attn_supported(int H, int Hkv, int hd);      // hd 64/128, G = H/Hkv divides 8 or is a multiple of 8
-int attn_row_blocks(int H, int Hkv, int m);        // n_qc
-int attn_num_splits(int B, int H, int Hkv, int m, int max_ctx);
-size_t attn_counters(int B, int H, int Hkv, int m);  // tickets the launch uses
+// hd 64/128; G = H/Hkv divides the workgroup's waves (16 for hd 128, 8 for
+// hd 64) or is a multiple of them
+bool attn_supported(int H, int Hkv, int hd);
+int attn_row_blocks(int H, int Hkv, int hd, int m);  // n_qc
+int attn_num_splits(int B, int H, int Hkv, int hd, int m, int max_ctx);
+size_t attn_counters(int B, int H, int Hkv, int hd, int m);  // tickets the launch uses
 hipError_t launch_attention(bool bf16, int hd, const AttnArgs& a, int B, hipStream_t s);
 
 // Round bookkeeping (see spec_commit_round).

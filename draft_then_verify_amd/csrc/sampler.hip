@@ -34,14 +34,22 @@ constexpr int kChunk = 4096;
 constexpr int kPer = kChunk / kThreads;
 constexpr float kTwo40 = 1099511627776.0f;  // 2^40
 constexpr float kTwo24 = 16777216.0f;       // 2^24
+constexpr int kMaxRows = 64;                // gamma + 1 rows per sequence at most
+constexpr int kMaxChunks = 64;              // vocab <= 64 * 4096
 
-// Row statistics (M, Z) from the chunk partials, merged in chunk order.
-__device__ __forceinline__ float2 merge_stats(const float2* pr, int nch) {
-  float M = -INFINITY;
-  for (int c = 0; c < nch; ++c) M = fmaxf(M, pr[c].x);
-  float Z = 0.f;
-  for (int c = 0; c < nch; ++c) Z = fmaf(pr[c].y, expf(__fsub_rn(pr[c].x, M)), Z);
-  return make_float2(M, Z);
+// Row statistics (M, Z) from the chunk partials, by one whole wave: lane j
+// takes chunks j, j + 64, ... in order, then a wave max and a wave sum of
+// Z_j = sum over its chunks of Z_c exp(M_c - M).  Every caller (the
+// materialised softmax and the fused sampler) uses this same function, so a
+// probability is bitwise the same wherever it is computed.
+__device__ __forceinline__ float2 wave_stats(const float2* pr, int nch) {
+  const int lane = threadIdx.x & (kWave - 1);
+  float m = -INFINITY;
+  for (int c = lane; c < nch; c += kWave) m = fmaxf(m, pr[c].x);
+  const float M = wave_max(m);
+  float z = 0.f;
+  for (int c = lane; c < nch; c += kWave) z = fmaf(pr[c].y, expf(__fsub_rn(pr[c].x, M)), z);
+  return make_float2(M, wave_sum(z));
 }
 
 // Where a probability row comes from.
@@ -52,8 +60,9 @@ struct RowSrc {
   float T;
   int nch;
   int V;
+  // called by a whole wave
   __device__ __forceinline__ float2 stats(int64_t row) const {
-    return p ? make_float2(0.f, 1.f) : merge_stats(part + row * nch, nch);
+    return p ? make_float2(0.f, 1.f) : wave_stats(part + row * nch, nch);
   }
   __device__ __forceinline__ float prob(int64_t row, int v, float2 st) const {
     if (p) return p[row * V + v];
@@ -65,18 +74,52 @@ __device__ __forceinline__ unsigned long long fixed_weight(float r) {
   return static_cast<unsigned long long>(__fmul_rn(r, kTwo40));
 }
 
-// Accept scan for sequence b: number of leading drafts that pass.
-__device__ int accepted_length(const RowSrc& src, int b, int gamma, int nd, const float* q, const int32_t* draft,
-                               const float* u_acc) {
-  for (int i = 0; i < nd; ++i) {
-    const int x = draft[b * gamma + i];
-    if (x < 0 || x >= src.V) return i;
-    const int64_t row = static_cast<int64_t>(b) * (gamma + 1) + i;
-    const float px = src.prob(row, x, src.stats(row));
-    const float qx = q ? q[(static_cast<int64_t>(b) * gamma + i) * src.V + x] : 1.f;
-    if (!(__fmul_rn(u_acc[b * gamma + i], qx) <= px)) return i;
+// Accept scan for sequence b, by the whole workgroup: the statistics of rows
+// 0 .. nd (waves in parallel) go to st_rows, lane i of wave 0 tests draft i,
+// and n = the first failing i (a ballot), or nd.  Returns n to every thread.
+__device__ int accept_scan(const RowSrc& src, int b, int gamma, int nd, const float* q, const int32_t* draft,
+                           const float* u_acc, float2* st_rows, int* n_sh) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  for (int i = wave; i <= nd; i += kThreads / kWave) {
+    const float2 st = src.stats(static_cast<int64_t>(b) * (gamma + 1) + i);
+    if (lane == 0) st_rows[i] = st;
   }
-  return nd;
+  __syncthreads();
+  if (wave == 0) {
+    bool fail = false;
+    if (lane < nd) {
+      const int x = draft[b * gamma + lane];
+      if (x < 0 || x >= src.V) {
+        fail = true;
+      } else {
+        const int64_t row = static_cast<int64_t>(b) * (gamma + 1) + lane;
+        const float px = src.prob(row, x, st_rows[lane]);
+        const float qx = q ? q[(static_cast<int64_t>(b) * gamma + lane) * src.V + x] : 1.f;
+        fail = !(__fmul_rn(u_acc[b * gamma + lane], qx) <= px);
+      }
+    }
+    const unsigned long long m = __ballot(fail);
+    if (lane == 0) *n_sh = m ? (__ffsll(static_cast<long long>(m)) - 1) : nd;
+  }
+  __syncthreads();
+  return *n_sh;
+}
+
+// Exclusive prefix sums of one value per thread over the workgroup (fixed
+// order: wave scans, then the wave totals in index order).
+__device__ unsigned long long block_exclusive_scan_u64(unsigned long long v, unsigned long long* wsum) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  unsigned long long incl = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const unsigned long long t = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += t;
+  }
+  if (lane == kWave - 1) wsum[wave] = incl;
+  __syncthreads();
+  unsigned long long base = 0;
+  for (int w = 0; w < wave; ++w) base += wsum[w];
+  return base + incl - v;
 }
 
 __device__ __forceinline__ int n_valid(const int32_t* n_draft, int b, int gamma) {
@@ -118,7 +161,10 @@ __global__ __launch_bounds__(kThreads) void softmax_write_kernel(const float* __
   __shared__ float2 st_sh;
   const int64_t row = blockIdx.y;
   const int c = blockIdx.x;
-  if (threadIdx.x == 0) st_sh = merge_stats(part + row * nch, nch);
+  if (threadIdx.x < kWave) {
+    const float2 st = wave_stats(part + row * nch, nch);
+    if (threadIdx.x == 0) st_sh = st;
+  }
   __syncthreads();
   const float2 st = st_sh;
   RowSrc src{nullptr, logits, part, T, nch, V};
@@ -145,19 +191,13 @@ struct RejectArgs {
 
 __global__ __launch_bounds__(kThreads) void reject_chunks_kernel(RejectArgs a) {
   __shared__ int n_sh;
-  __shared__ float2 st_sh;
+  __shared__ float2 st_rows[kMaxRows];
   __shared__ unsigned long long red[kThreads / kWave];
   const int c = blockIdx.x, b = blockIdx.y;
   const RowSrc& src = a.src;
   const int nd = n_valid(a.n_draft, b, a.gamma);
-  if (threadIdx.x == 0) {
-    const int n = accepted_length(src, b, a.gamma, nd, a.q, a.draft, a.u_acc);
-    n_sh = n;
-    st_sh = src.stats(static_cast<int64_t>(b) * (a.gamma + 1) + n);
-  }
-  __syncthreads();
-  const int n = n_sh;
-  const float2 st = st_sh;
+  const int n = accept_scan(src, b, a.gamma, nd, a.q, a.draft, a.u_acc, st_rows, &n_sh);
+  const float2 st = st_rows[n];
   const bool bonus = n == nd;
   const int64_t row = static_cast<int64_t>(b) * (a.gamma + 1) + n;
   const int x_rej = bonus ? -1 : a.draft[b * a.gamma + n];
@@ -182,16 +222,18 @@ __global__ __launch_bounds__(kThreads) void reject_chunks_kernel(RejectArgs a) {
 
 __global__ __launch_bounds__(kThreads) void reject_final_kernel(RejectArgs a) {
   __shared__ int n_sh, cstar_sh, use_p_sh, tok_sh;
-  __shared__ float2 st_sh;
+  __shared__ float2 st_rows[kMaxRows];
   __shared__ unsigned long long base_sh, T_sh;
-  __shared__ unsigned long long scan[kThreads];
+  __shared__ unsigned long long cs[2 * kMaxChunks];
+  __shared__ unsigned long long wsum[kThreads / kWave];
   const int b = blockIdx.x;
   const RowSrc& src = a.src;
   const int nch = src.nch;
   const int nd = n_valid(a.n_draft, b, a.gamma);
+  for (int i = threadIdx.x; i < 2 * nch; i += kThreads) cs[i] = a.csum[static_cast<size_t>(b) * nch * 2 + i];
+  const int n_all = accept_scan(src, b, a.gamma, nd, a.q, a.draft, a.u_acc, st_rows, &n_sh);
   if (threadIdx.x == 0) {
-    const int n = accepted_length(src, b, a.gamma, nd, a.q, a.draft, a.u_acc);
-    const unsigned long long* cs = a.csum + static_cast<size_t>(b) * nch * 2;
+    const int n = n_all;
     unsigned long long Sr = 0, Sp = 0;
     for (int c = 0; c < nch; ++c) {
       Sr += cs[2 * c];
@@ -213,21 +255,19 @@ __global__ __launch_bounds__(kThreads) void reject_final_kernel(RejectArgs a) {
       }
       acc += w;
     }
-    n_sh = n;
     use_p_sh = use_p;
     cstar_sh = cstar;
     base_sh = acc;
     T_sh = T;
     tok_sh = -1;
-    st_sh = src.stats(static_cast<int64_t>(b) * (a.gamma + 1) + n);
   }
   __syncthreads();
-  const int n = n_sh;
+  const int n = n_all;
   const bool use_p = use_p_sh;
   const int64_t row = static_cast<int64_t>(b) * (a.gamma + 1) + n;
   const int x_rej = (n == nd) ? -1 : a.draft[b * a.gamma + n];
   const float* qrow = (n != nd && a.q) ? a.q + (static_cast<int64_t>(b) * a.gamma + n) * src.V : nullptr;
-  const float2 st = st_sh;
+  const float2 st = st_rows[n];
   const int v0 = cstar_sh * kChunk + threadIdx.x * kPer;
   unsigned long long w[kPer];
   unsigned long long tsum = 0;
@@ -237,19 +277,9 @@ __global__ __launch_bounds__(kThreads) void reject_final_kernel(RejectArgs a) {
     w[e] = (v < src.V) ? fixed_weight(sample_mass(src.prob(row, v, st), use_p, qrow, x_rej, v)) : 0ull;
     tsum += w[e];
   }
-  scan[threadIdx.x] = tsum;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    unsigned long long run = 0;
-    for (int i = 0; i < kThreads; ++i) {
-      const unsigned long long x = scan[i];
-      scan[i] = run;
-      run += x;
-    }
-  }
-  __syncthreads();
+  const unsigned long long excl = block_exclusive_scan_u64(tsum, wsum);
   const unsigned long long T = T_sh;
-  unsigned long long run = base_sh + scan[threadIdx.x];
+  unsigned long long run = base_sh + excl;
   if (run <= T && T < run + tsum) {
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {

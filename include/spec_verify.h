@@ -154,6 +154,7 @@ spec_status spec_softmax_pq(const float* logits, int64_t rows, int32_t vocab, fl
  *   u_acc    [B][gamma], u_res [B] uniforms.
  *   n_accepted [B] out: n.   emitted [B][gamma+1] out: x_1 .. x_n, t, then -1.
  * gamma = 0 is a plain draw t ~ p (draft sampling, plain decoding).
+ * Limits: gamma <= 63, vocab <= 262144 (64 chunks of 4096).
  * Errors: SPEC_EINVAL, SPEC_ENOMEM, SPEC_EHIP. */
 spec_status spec_reject_sample(int32_t B, int32_t gamma, int32_t vocab, const float* p, const float* q,
                                const int32_t* draft, const int32_t* n_draft, const float* u_acc,

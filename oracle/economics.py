@@ -49,7 +49,7 @@ def best_k(alpha: float, c: float, ks=(1, 2, 3, 4, 6, 8)):
 def arithmetic_increase(alpha: float, gamma: int, c_hat: float) -> float:
     """Expected increase in total arithmetic, Theorem 3.11 as quoted on
     [P1 "The speedup is borrowed"]: (1 - alpha)(gamma c_hat + gamma + 1) /
-    (1 - alpha^(gamma + 1)).  The page's flattened "alpha^gamma+1" is read as
+    (1 - alpha^(gamma + 1)).  The page's flattened exponent is read as
     alpha^(gamma+1), which is what reproduces its 1.64x."""
     return (1.0 - alpha) * (gamma * c_hat + gamma + 1) / (1.0 - alpha ** (gamma + 1))
 

@@ -1,7 +1,7 @@
 """Oracle decoder forward pass (test infrastructure; see package docstring).
 
-What a verify pass computes [P1 "What one iteration actually does", Algorithm 1
-line "Run Mp in parallel"; P3 "How speculative decoding works"]: the target
+What a verify pass computes [P1 "What one iteration actually does", Algorithm 1,
+the parallel scoring step; P3 "How speculative decoding works"]: the target
 scores every drafted position in one forward pass, row i being the next-token
 distribution after the prefix plus the first i inputs.  The pages name no
 architecture beyond "Llama-style"/"Qwen3-8B-shaped", so the plainest Llama

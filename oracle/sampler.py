@@ -5,14 +5,15 @@ actually does"] and the rule on [P3 "Why the output doesn't change"]:
 
 1. p_i = softmax(logits_i / T) for the gamma+1 verify rows.
 2. Accept test for i = 1..gamma in order: reject iff r_i > p_i(x_i)/q_i(x_i)
-   [P1, Algorithm 1 "Determine the number of accepted guesses"].  Written
+   [P1, Algorithm 1, the step that counts the accepted guesses].  Written
    division-free as: accept iff u_i * q_i(x_i) <= p_i(x_i), evaluated in
    float32 (the same precision on both sides, since it decides an integer).
    q(x) = 0 therefore accepts.
-3. n = index of the first rejection (prefix truncation [P1 "Rejection is
-   prefix-truncating"]), or n_draft when all drafts pass.
+3. n = index of the first rejection (a rejection cuts the rest of the
+   block [P1 "What one iteration actually does"]), or n_draft when all
+   drafts pass.
 4. Corrected distribution for row j = n (0-based): if n < n_draft,
-   norm(max(0, p_j - q_j)) [P1 Algorithm 1 "Adjust the distribution";
+   norm(max(0, p_j - q_j)) [P1, Algorithm 1, the corrected distribution;
    P3 residual]; otherwise p_j itself (the bonus token [P2 "The
    draft-then-verify loop", step 3]).  The subtraction is float32.  An
    all-zero residual (p == q up to rounding) falls back to p_j.

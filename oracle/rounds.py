@@ -25,6 +25,8 @@ from . import sampler
 
 def verify_round(target, cache, last_tok, drafts, q, n_draft, u_acc, u_res, temperature=1.0):
     """Score, accept/resample and commit one round on the oracle's own target.
+    temperature 0 verifies greedily (``sampler.greedy_verify``); q and the
+    uniforms are then unused.
 
     Returns dict(logits fp64 [B, g+1, V], p fp64, n [B], emitted [B, g+1]).
     """
@@ -34,7 +36,10 @@ def verify_round(target, cache, last_tok, drafts, q, n_draft, u_acc, u_res, temp
     tokens = np.concatenate([last_tok[:, None], drafts], axis=1)
     logits = target.forward(cache, tokens)
     p = sampler.softmax(logits, temperature)
-    n, emitted = sampler.reject_sample(p.astype(np.float32), q, drafts, n_draft, u_acc, u_res)
+    if float(temperature) == 0.0:
+        n, emitted = sampler.greedy_verify(logits, drafts, n_draft)
+    else:
+        n, emitted = sampler.reject_sample(p.astype(np.float32), q, drafts, n_draft, u_acc, u_res)
     cache.length = cache.length + n + 1
     return {"logits": logits, "p": p, "n": n, "emitted": emitted}
 

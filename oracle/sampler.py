@@ -36,7 +36,17 @@ TWO24 = 1 << 24
 
 
 def softmax(logits: np.ndarray, temperature: float = 1.0) -> np.ndarray:
-    """Row softmax in fp64 over the last axis of logits / T."""
+    """Row softmax in fp64 over the last axis of logits / T.
+
+    T = 0 is the limit T -> 0: the distribution collapses onto the argmax
+    [P3 "Exactness is a choice"], written as a one-hot row at the lowest
+    index among equal maxima (the tie rule of ``argmax_rows``).
+    """
+    if float(temperature) == 0.0:
+        a = argmax_rows(logits)
+        out = np.zeros(np.shape(logits), dtype=np.float64)
+        np.put_along_axis(out, a[..., None], 1.0, axis=-1)
+        return out
     x = np.asarray(logits, dtype=np.float64) / float(temperature)
     x = x - x.max(axis=-1, keepdims=True)
     e = np.exp(x)
@@ -121,6 +131,41 @@ def reject_sample(p: np.ndarray, q, draft: np.ndarray, n_draft, u_acc: np.ndarra
     for b in range(B):
         emitted[b, : n[b]] = draft[b, : n[b]]
         emitted[b, n[b]] = t[b]
+    return n, emitted
+
+
+def argmax_rows(logits: np.ndarray) -> np.ndarray:
+    """Index of the largest entry of each row (last axis); among equal maxima
+    the lowest index.  The comparison is made in the precision the logits
+    arrive in, so a caller checking float32 logits passes float32."""
+    return np.argmax(np.asarray(logits), axis=-1).astype(np.int64)
+
+
+def greedy_verify(logits: np.ndarray, draft: np.ndarray, n_draft=None):
+    """Greedy (T = 0) verification of one round.
+
+    At temperature zero the target's distribution is its argmax [P3
+    "Exactness is a choice"; P4 section 4.2 on acceptance measured under
+    greedy decoding].  With a_i = argmax(logits_i) for the gamma + 1 rows: draft x_i
+    is accepted while x_i == a_i; n = the first mismatch among the first
+    n_draft drafts, else n_draft; the round emits x_1 .. x_n and then a_n
+    (0-based row n): at a mismatch the target's own choice replaces the
+    draft, and after a full pass a_gamma is the bonus token.
+
+    logits [B, g+1, V]; draft [B, g]; n_draft [B] or None (= g).
+    Returns (n [B] int64, emitted [B, g+1] int64, -1 padded).
+    """
+    logits = np.asarray(logits)
+    B, g1, V = logits.shape
+    g = g1 - 1
+    draft = np.asarray(draft, dtype=np.int64).reshape(B, g)
+    nd = np.full(B, g, dtype=np.int64) if n_draft is None else np.clip(np.asarray(n_draft, np.int64), 0, g)
+    a = argmax_rows(logits)  # [B, g+1]
+    n = accepted_length(draft == a[:, :g], nd)
+    emitted = np.full((B, g + 1), -1, dtype=np.int64)
+    for b in range(B):
+        emitted[b, : n[b]] = draft[b, : n[b]]
+        emitted[b, n[b]] = a[b, n[b]]
     return n, emitted
 
 

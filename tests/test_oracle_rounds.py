@@ -94,3 +94,49 @@ def test_ngram_proposer():
     assert ngram_propose([1, 2, 3, 4], 3, 4) == []
     assert ngram_propose([1, 2, 3], 3, 4) == []
     assert ngram_propose(ctx, 3, 0) == []
+
+
+def test_greedy_speculation_reproduces_greedy_decoding():
+    """At T = 0 speculative decoding is lossless token for token: the emitted
+    sequence equals plain greedy decoding of the target [P3 "Exactness is a
+    choice"], whatever the drafter proposes.  Plain greedy decoding here is
+    one target forward per token and an argmax of its last row."""
+    w = make_weights(SHAPE, seed=31, norm="random", std=0.1)
+    B, P, n_new, gamma = 2, 6, 14, 3
+    prompt = make_prompt(B, P, SHAPE.vocab, seed=31)
+    tgt = OM.Decoder(SHAPE, w)
+    cap = P + n_new + gamma + 2
+    # plain greedy decoding
+    cp = tgt.new_cache(B, cap)
+    logits = tgt.forward(cp, prompt)
+    cp.length = cp.length + P
+    plain = [list(prompt[b]) for b in range(B)]
+    for _ in range(n_new):
+        nxt = logits[:, -1].argmax(-1)
+        for b in range(B):
+            plain[b].append(int(nxt[b]))
+        logits = tgt.forward(cp, nxt[:, None])
+        cp.length = cp.length + 1
+    # speculative, greedy draft from a shallower model of the same weights
+    for draft_layers in (1, 2):
+        dft = OM.Decoder(SHAPE, w, n_layers=draft_layers)
+        ct, cd = tgt.new_cache(B, cap), dft.new_cache(B, cap)
+        R.prefill(tgt, ct, prompt)
+        R.prefill(dft, cd, prompt)
+        spec = [list(prompt[b]) for b in range(B)]
+        accepted = 0
+        r = 0
+        while min(len(c) for c in spec) < P + n_new:
+            u = round_uniforms(31, r, B, gamma)
+            last = np.array([c[-1] for c in spec])
+            prev = np.array([c[-2] for c in spec])
+            xs, q = R.draft_round(dft, cd, prev, last, ct.length, gamma, u["u_draft"], temperature=0.0)
+            assert set(np.unique(q)) <= {0.0, 1.0}
+            out = R.verify_round(tgt, ct, last, xs, q, None, None, None, temperature=0.0)
+            for b in range(B):
+                spec[b] += [int(t) for t in out["emitted"][b, :out["n"][b] + 1]]
+            accepted += int(out["n"].sum())
+            r += 1
+        for b in range(B):
+            assert spec[b][:P + n_new] == plain[b]
+        assert accepted > 0 and r < n_new  # the drafter's guesses were used

@@ -291,3 +291,66 @@ def test_softmax_matches_scipy():
     from scipy.special import softmax as sp_softmax
     assert np.allclose(S.softmax(x), sp_softmax(x, axis=-1), rtol=1e-13, atol=1e-15)
     assert np.allclose(S.softmax(x, 0.5), sp_softmax(2 * x, axis=-1), rtol=1e-13, atol=1e-15)
+
+
+# ---- greedy (T = 0) verification -------------------------------------------------
+
+def test_greedy_verify_hand_worked():
+    """Worked by hand from the definition: a_i = argmax row i (lowest index on
+    ties); accept while x_i == a_i; emit the accepted drafts and a_n."""
+    L = np.array([[[0, 5, 1, 2],      # a_0 = 1
+                   [3, 3, 0, 1],      # tie at 0 and 1 -> a_1 = 0
+                   [0, 0, 9, 9],      # tie at 2 and 3 -> a_2 = 2
+                   [7, 0, 0, 8]]],    # a_3 = 3
+                 np.float32)
+    # all three drafts agree: n = 3, bonus a_3
+    n, em = S.greedy_verify(L, np.array([[1, 0, 2]]))
+    assert n.tolist() == [3] and em.tolist() == [[1, 0, 2, 3]]
+    # the tie loser (index 1 on row 1) is rejected and replaced by a_1 = 0
+    n, em = S.greedy_verify(L, np.array([[1, 1, 2]]))
+    assert n.tolist() == [1] and em.tolist() == [[1, 0, -1, -1]]
+    # first draft wrong: n = 0, emit a_0
+    n, em = S.greedy_verify(L, np.array([[3, 0, 2]]))
+    assert n.tolist() == [0] and em.tolist() == [[1, -1, -1, -1]]
+    # ragged: only the first 2 drafts count, so the bonus comes from row 2
+    n, em = S.greedy_verify(L, np.array([[1, 0, 3]]), n_draft=[2])
+    assert n.tolist() == [2] and em.tolist() == [[1, 0, 2, -1]]
+    # gamma = 0: the round is one greedy decoding step
+    n, em = S.greedy_verify(L[:, :1], np.zeros((1, 0), np.int64))
+    assert n.tolist() == [0] and em.tolist() == [[1]]
+
+
+def test_greedy_ties_and_infinities():
+    L = np.full((1, 1, 9000), -np.inf, np.float32)
+    assert S.greedy_verify(L, np.zeros((1, 0)))[1].tolist() == [[0]]   # all -inf: lowest index
+    L[0, 0, [4097, 8191, 8999]] = 2.5
+    assert S.greedy_verify(L, np.zeros((1, 0)))[1].tolist() == [[4097]]
+    L[0, 0, 12] = np.inf
+    assert S.greedy_verify(L, np.zeros((1, 0)))[1].tolist() == [[12]]
+
+
+def test_greedy_is_the_zero_temperature_limit_of_the_exact_rule():
+    """[P3 "Exactness is a choice"]: at T -> 0 the exact rule and greedy pick
+    the same tokens.  The exact rule (reject_sample) on softmax(l / 1e-4) with
+    a one-hot draft must reproduce greedy_verify for any uniforms in (0, 1)."""
+    rng = np.random.default_rng(SEED + 40)
+    B, g, V = 400, 5, 33
+    logits = rng.normal(size=(B, g + 1, V)) * 3
+    a = logits.argmax(-1)
+    xs = np.where(rng.random((B, g)) < 0.7, a[:, :g], rng.integers(0, V, size=(B, g)))
+    nd = rng.integers(0, g + 1, size=B)
+    n_g, em_g = S.greedy_verify(logits, xs, nd)
+    p = S.softmax(logits, temperature=1e-4).astype(np.float32)
+    for s in range(3):
+        n_e, em_e = _round(p, None, xs, make_uniforms((B, g), SEED, 97, s), make_uniforms((B,), SEED, 98, s), nd)
+        assert np.array_equal(n_g, n_e) and np.array_equal(em_g, em_e)
+    assert 0 < n_g.mean() < g  # both outcomes occur
+
+
+def test_softmax_temperature_zero_is_one_hot_at_argmax():
+    L = np.array([[1.0, 3.0, 3.0, -2.0], [0.0, 0.0, 0.0, 0.0]])
+    assert S.softmax(L, 0.0).tolist() == [[0, 1, 0, 0], [1, 0, 0, 0]]
+    rng = np.random.default_rng(SEED + 41)
+    x = rng.normal(size=(50, 17))
+    assert np.array_equal(S.softmax(x, 0.0).argmax(-1), x.argmax(-1))
+    assert np.allclose(S.softmax(x, 0.0), S.softmax(x, 1e-6), atol=1e-12)

@@ -277,23 +277,32 @@ SPEC_API spec_status spec_verify_forward(const spec_model* model, const spec_kv*
 }
 
 namespace {
+// T > 0: chunk (max, sum exp) partials, and the probabilities when probs is
+// not NULL.  T = 0: chunk (max, argmax) partials, and one-hot rows.
 spec_status softmax_rows(const float* logits, int64_t rows, int V, float T, float* probs, float2* part,
                          hipStream_t s) {
   const int nch = sv::sampler_chunks(V);
   for (int64_t r0 = 0; r0 < rows; r0 += 65535) {
     const int64_t nr = std::min<int64_t>(65535, rows - r0);
-    HIP_TRY(sv::launch_row_partials(logits + r0 * V, nr, V, T, part + r0 * nch, s));
-    if (probs) HIP_TRY(sv::launch_softmax_write(logits + r0 * V, nr, V, T, part + r0 * nch, probs + r0 * V, s));
+    if (T == 0.f) {
+      HIP_TRY(sv::launch_row_argmax(logits + r0 * V, nr, V, part + r0 * nch, s));
+      if (probs) HIP_TRY(sv::launch_onehot_write(nr, V, part + r0 * nch, probs + r0 * V, s));
+    } else {
+      HIP_TRY(sv::launch_row_partials(logits + r0 * V, nr, V, T, part + r0 * nch, s));
+      if (probs) HIP_TRY(sv::launch_softmax_write(logits + r0 * V, nr, V, T, part + r0 * nch, probs + r0 * V, s));
+    }
   }
   return SPEC_OK;
 }
+
+bool valid_temperature(float T) { return T >= 0.f && T <= 3.0e38f; }
 }  // namespace
 
 SPEC_API spec_status spec_softmax_pq(const float* logits, int64_t rows, int32_t vocab, float temperature, float* probs,
                                      void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!logits || !probs) return fail(SPEC_EINVAL, "NULL logits/probs");
   if (rows < 0 || vocab <= 0) return fail(SPEC_EINVAL, "rows=%lld vocab=%d", (long long)rows, vocab);
-  if (!(temperature > 0.f)) return fail(SPEC_EINVAL, "temperature must be > 0");
+  if (!valid_temperature(temperature)) return fail(SPEC_EINVAL, "temperature must be finite and >= 0");
   if (rows == 0) return SPEC_OK;
   const size_t need = spec_sampler_workspace_bytes(rows, 0, vocab);
   if (!ws || ws_bytes < need) return fail(SPEC_ENOMEM, "workspace %zu bytes < %zu needed", ws_bytes, need);
@@ -301,13 +310,15 @@ SPEC_API spec_status spec_softmax_pq(const float* logits, int64_t rows, int32_t 
 }
 
 namespace {
+// greedy: the uniforms are not used and may be NULL.
 spec_status check_sampler_args(int B, int gamma, int V, const int32_t* draft, const float* u_acc, const float* u_res,
-                               const int32_t* n_accepted, const int32_t* emitted) {
+                               const int32_t* n_accepted, const int32_t* emitted, bool greedy = false) {
   if (B <= 0 || B > 65535) return fail(SPEC_EINVAL, "B=%d (1..65535)", B);
   if (gamma < 0 || gamma > 63) return fail(SPEC_EINVAL, "gamma=%d (0..63)", gamma);
   if (V <= 0 || V > 64 * 4096) return fail(SPEC_EINVAL, "vocab=%d (1..262144)", V);
-  if (gamma > 0 && (!draft || !u_acc)) return fail(SPEC_EINVAL, "draft/u_acc NULL with gamma > 0");
-  if (!u_res || !n_accepted || !emitted) return fail(SPEC_EINVAL, "u_res/n_accepted/emitted NULL");
+  if (gamma > 0 && !draft) return fail(SPEC_EINVAL, "draft NULL with gamma > 0");
+  if (!greedy && ((gamma > 0 && !u_acc) || !u_res)) return fail(SPEC_EINVAL, "u_acc/u_res NULL");
+  if (!n_accepted || !emitted) return fail(SPEC_EINVAL, "n_accepted/emitted NULL");
   return SPEC_OK;
 }
 }  // namespace
@@ -334,10 +345,11 @@ SPEC_API spec_status spec_decode_step(const spec_model* target, const spec_kv* k
   const int m = gamma + 1;
   spec_status st = check_kv(target, kv, B, m);
   if (st != SPEC_OK) return st;
-  st = check_sampler_args(B, gamma, target->cfg.vocab, draft, u_acc, u_res, n_accepted, emitted);
+  if (!valid_temperature(temperature)) return fail(SPEC_EINVAL, "temperature must be finite and >= 0");
+  const bool greedy = temperature == 0.f;
+  st = check_sampler_args(B, gamma, target->cfg.vocab, draft, u_acc, u_res, n_accepted, emitted, greedy);
   if (st != SPEC_OK) return st;
   if (!last_tok) return fail(SPEC_EINVAL, "last_tok is NULL");
-  if (!(temperature > 0.f)) return fail(SPEC_EINVAL, "temperature must be > 0");
   const Layout L = make_layout(target->cfg, B, m, kv->max_ctx);
   if (!ws || ws_bytes < L.total) return fail(SPEC_ENOMEM, "workspace %zu bytes < %zu needed", ws_bytes, L.total);
   char* w = static_cast<char*>(ws);
@@ -348,6 +360,10 @@ SPEC_API spec_status spec_decode_step(const spec_model* target, const spec_kv* k
   float2* part = reinterpret_cast<float2*>(w + L.part);
   st = softmax_rows(logits, static_cast<int64_t>(B) * m, V, temperature, nullptr, part, stream);
   if (st != SPEC_OK) return st;
+  if (greedy) {
+    HIP_TRY(sv::launch_greedy(B, gamma, V, part, draft, n_draft, n_accepted, emitted, kv->len, stream));
+    return SPEC_OK;
+  }
   HIP_TRY(sv::launch_reject(B, gamma, V, nullptr, logits, part, temperature, q, draft, n_draft, u_acc, u_res,
                             n_accepted, emitted, kv->len, reinterpret_cast<unsigned long long*>(w + L.csum), stream));
   return SPEC_OK;

@@ -101,6 +101,14 @@ hipError_t launch_row_partials(const float* logits, int64_t rows, int vocab, flo
 // probs = exp(l/T - m) / Z with the row statistics combined from part.
 hipError_t launch_softmax_write(const float* logits, int64_t rows, int vocab, float temperature,
                                 const float2* part, float* probs, hipStream_t s);
+// Temperature 0: part[row][c] = (chunk max, its lowest index as int bits);
+// one-hot rows at the row argmax; greedy accept (x_i == argmax_i) with the
+// argmax of row n emitted after the accepted drafts.
+hipError_t launch_row_argmax(const float* logits, int64_t rows, int vocab, float2* part, hipStream_t s);
+hipError_t launch_onehot_write(int64_t rows, int vocab, const float2* part, float* probs, hipStream_t s);
+hipError_t launch_greedy(int B, int gamma, int vocab, const float2* part, const int32_t* draft,
+                         const int32_t* n_draft, int32_t* n_accepted, int32_t* emitted, int32_t* len_commit,
+                         hipStream_t s);
 // Accept / resample / bonus.  Rows come from `p` (materialised) or from
 // logits + part (fused).  csum is [B][chunks] scratch (2 x uint64 each).
 hipError_t launch_reject(int B, int gamma, int vocab, const float* p, const float* logits, const float2* part,

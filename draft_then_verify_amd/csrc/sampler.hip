@@ -301,7 +301,138 @@ __global__ __launch_bounds__(kThreads) void reject_final_kernel(RejectArgs a) {
   }
 }
 
+// ---- temperature 0 ------------------------------------------------------------------
+// At T = 0 the target's distribution is its argmax ("How Speculative Decoding
+// Works", section "Exactness is a choice"): draft x_i is accepted while it
+// equals a_i = argmax of row i, and the round emits a_n after the accepted
+// drafts (the replacement at a mismatch, or the bonus).  Ties go to the
+// lowest index; a NaN entry is never selected (an all-NaN row selects 0).
+// The order (larger value, then lower index) is total on non-NaN values, so
+// any reduction tree gives the same (value, index).
+
+__device__ __forceinline__ void argmax_merge(float& m, int& i, float m2, int i2) {
+  if (m2 > m || (m2 == m && i2 < i)) {
+    m = m2;
+    i = i2;
+  }
+}
+
+__device__ __forceinline__ void wave_argmax(float& m, int& i) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    const float m2 = __shfl_xor(m, off, kWave);
+    const int i2 = __shfl_xor(i, off, kWave);
+    argmax_merge(m, i, m2, i2);
+  }
+}
+
+// Row argmax from the chunk partials (value, index bits), by one whole wave.
+__device__ __forceinline__ int wave_row_argmax(const float2* pr, int nch, int V) {
+  const int lane = threadIdx.x & (kWave - 1);
+  float m = -INFINITY;
+  int i = V;
+  for (int c = lane; c < nch; c += kWave) argmax_merge(m, i, pr[c].x, __float_as_int(pr[c].y));
+  wave_argmax(m, i);
+  return i < V ? i : 0;
+}
+
+// part[row][c] = (max of chunk c, its lowest index as int bits).
+__global__ __launch_bounds__(kThreads) void row_argmax_kernel(const float* __restrict__ logits, int V, int nch,
+                                                              float2* __restrict__ part) {
+  __shared__ float mred[kThreads / kWave];
+  __shared__ int ired[kThreads / kWave];
+  const int64_t row = blockIdx.y;
+  const int c = blockIdx.x;
+  const float* l = logits + row * V;
+  float m = -INFINITY;
+  int i = V;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const int v = c * kChunk + e * kThreads + threadIdx.x;
+    if (v < V) argmax_merge(m, i, l[v], v);
+  }
+  wave_argmax(m, i);
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  if (lane == 0) {
+    mred[wave] = m;
+    ired[wave] = i;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < kThreads / kWave; ++w) argmax_merge(m, i, mred[w], ired[w]);
+    part[row * nch + c] = make_float2(m, __int_as_float(i));
+  }
+}
+
+// probs[row][v] = (v == argmax) ? 1 : 0.
+__global__ __launch_bounds__(kThreads) void onehot_write_kernel(int V, int nch, const float2* __restrict__ part,
+                                                                float* __restrict__ probs) {
+  __shared__ int a_sh;
+  const int64_t row = blockIdx.y;
+  const int c = blockIdx.x;
+  if (threadIdx.x < kWave) {
+    const int a = wave_row_argmax(part + row * nch, nch, V);
+    if (threadIdx.x == 0) a_sh = a;
+  }
+  __syncthreads();
+  const int a = a_sh;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const int v = c * kChunk + e * kThreads + threadIdx.x;
+    if (v < V) probs[row * V + v] = (v == a) ? 1.f : 0.f;
+  }
+}
+
+// One workgroup per sequence: the argmax of rows 0 .. nd (waves in
+// parallel), then n and the emitted tokens; len_commit[b] += n + 1.
+__global__ __launch_bounds__(kThreads) void greedy_kernel(int V, int nch, int gamma, const float2* __restrict__ part,
+                                                          const int32_t* __restrict__ draft,
+                                                          const int32_t* __restrict__ n_draft,
+                                                          int32_t* __restrict__ n_accepted,
+                                                          int32_t* __restrict__ emitted,
+                                                          int32_t* __restrict__ len_commit) {
+  __shared__ int amax[kMaxRows];
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int nd = n_valid(n_draft, b, gamma);
+  for (int i = wave; i <= nd; i += kThreads / kWave) {
+    const int a = wave_row_argmax(part + (static_cast<int64_t>(b) * (gamma + 1) + i) * nch, nch, V);
+    if (lane == 0) amax[i] = a;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int n = 0;
+    while (n < nd && draft[b * gamma + n] == amax[n]) ++n;
+    n_accepted[b] = n;
+    for (int j = 0; j <= gamma; ++j)
+      emitted[b * (gamma + 1) + j] = j < n ? draft[b * gamma + j] : (j == n ? amax[n] : -1);
+    if (len_commit) len_commit[b] += n + 1;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_row_argmax(const float* logits, int64_t rows, int vocab, float2* part, hipStream_t s) {
+  const int nch = sampler_chunks(vocab);
+  hipLaunchKernelGGL(row_argmax_kernel, dim3(nch, static_cast<unsigned>(rows)), dim3(kThreads), 0, s, logits, vocab,
+                     nch, part);
+  return hipGetLastError();
+}
+
+hipError_t launch_onehot_write(int64_t rows, int vocab, const float2* part, float* probs, hipStream_t s) {
+  const int nch = sampler_chunks(vocab);
+  hipLaunchKernelGGL(onehot_write_kernel, dim3(nch, static_cast<unsigned>(rows)), dim3(kThreads), 0, s, vocab, nch,
+                     part, probs);
+  return hipGetLastError();
+}
+
+hipError_t launch_greedy(int B, int gamma, int vocab, const float2* part, const int32_t* draft,
+                         const int32_t* n_draft, int32_t* n_accepted, int32_t* emitted, int32_t* len_commit,
+                         hipStream_t s) {
+  hipLaunchKernelGGL(greedy_kernel, dim3(B), dim3(kThreads), 0, s, vocab, sampler_chunks(vocab), gamma, part, draft,
+                     n_draft, n_accepted, emitted, len_commit);
+  return hipGetLastError();
+}
 
 int sampler_chunks(int vocab) { return (vocab + kChunk - 1) / kChunk; }
 

@@ -138,7 +138,10 @@ spec_status spec_verify_forward(const spec_model* model, const spec_kv* kv, int3
  * models' next-token distributions: "How Speculative Decoding Works (and
  * When It Doesn't)", section "Why the output doesn't change").  float32, max-subtracted; the same row statistics the fused
  * decode step uses, so p is bitwise what spec_decode_step samples from.
- * temperature > 0.  Errors: SPEC_EINVAL, SPEC_ENOMEM, SPEC_EHIP. */
+ * temperature >= 0 and finite.  temperature = 0 is the T -> 0 limit (same
+ * page, section "Exactness is a choice"): a one-hot row at the argmax, the
+ * lowest index among equal maxima (NaN entries are never selected).
+ * Errors: SPEC_EINVAL, SPEC_ENOMEM, SPEC_EHIP. */
 spec_status spec_softmax_pq(const float* logits, int64_t rows, int32_t vocab, float temperature,
                             float* probs, void* ws, size_t ws_bytes, hipStream_t stream);
 
@@ -167,6 +170,12 @@ spec_status spec_reject_sample(int32_t B, int32_t gamma, int32_t vocab, const fl
  * committed token and the n accepted drafts stay cached: a rejection cuts
  * the round's block at that position, first page).  Arguments as in spec_reject_sample;
  * logits_out [B][gamma+1][vocab] receives the logits when non-NULL.
+ * temperature = 0 verifies greedily ("How Speculative Decoding Works",
+ * section "Exactness is a choice": at temperature zero the target takes its
+ * argmax): x_i is accepted while it equals the argmax of row i (lowest index
+ * on ties), n is the first mismatch (or n_draft), and the argmax of row n
+ * follows the accepted drafts; q, u_acc and u_res are not read and may be
+ * NULL.  temperature must be finite and >= 0.
  * Errors: as spec_verify_forward. */
 spec_status spec_decode_step(const spec_model* target, const spec_kv* kv, int32_t B, int32_t gamma,
                              float temperature, const int32_t* last_tok, const int32_t* draft,

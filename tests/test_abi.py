@@ -60,7 +60,10 @@ def test_host_checks_reject_before_launch(lib):
     assert st == -1  # draft NULL with gamma > 0
     st = lib.spec_reject_sample(1, 2, 100, 1, None, 1, None, 1, 1, 1, 1, 1, 8, None)
     assert st == -2  # workspace too small
-    assert lib.spec_softmax_pq(1, 4, 100, 0.0, 1, 1, 1 << 20, None) == -1  # temperature
+    for bad_t in (-1.0, float("nan"), float("inf")):  # temperature must be finite and >= 0
+        assert lib.spec_softmax_pq(1, 4, 100, bad_t, 1, 1, 1 << 20, None) == -1
+    st = lib.spec_reject_sample(1, 2, 100, 1, None, 1, None, None, 1, 1, 1, 1, 1 << 20, None)
+    assert st == -1  # u_acc NULL with gamma > 0
     assert lib.spec_kv_set_len(None, 1, None, 1, None) == -1
     kv = bd.spec_kv(1, 1, 1, 2, 16)
     assert lib.spec_kv_set_len(ctypes.byref(kv), 3, None, 1, None) == -1

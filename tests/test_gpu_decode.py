@@ -15,7 +15,7 @@ from tests._gpu import f32, gpu_prefill, gpu_softmax, i32, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def _decode_round(shape, B, g, seed, onehot=False, ragged=False, n_layers=None, P=48):
+def _decode_round(shape, B, g, seed, onehot=False, ragged=False, n_layers=None, P=48, T=1.0, chain=False):
     w = make_weights(shape, seed=seed, norm="random", layers=n_layers)
     sh = shape if n_layers is None else shape.with_(n_layers=n_layers)
     max_ctx = P + g + 4
@@ -28,31 +28,71 @@ def _decode_round(shape, B, g, seed, onehot=False, ragged=False, n_layers=None, 
     R.prefill(tgt, ct, prompt)
     # drafts from a one-layer drafter of the oracle (teacher-forced inputs)
     u = round_uniforms(seed, 0, B, g)
-    if onehot:
+    if chain:
+        # the target's own greedy continuation (oracle), with one wrong token
+        # planted at a random position per sequence (or none): every n occurs
+        cc = tgt.new_cache(B, max_ctx)
+        R.prefill(tgt, cc, prompt)
+        tok, drafts = prompt[:, -1], np.zeros((B, g), np.int64)
+        for i in range(g):
+            tok = tgt.forward(cc, tok[:, None])[:, -1].argmax(-1)
+            cc.length = cc.length + 1
+            drafts[:, i] = tok
+        rng = np.random.default_rng(seed + 2)
+        cut = rng.integers(0, g + 1, size=B)
+        for b in range(B):
+            if cut[b] < g:
+                drafts[b, cut[b]] = (drafts[b, cut[b]] + 1 + rng.integers(0, sh.vocab - 1)) % sh.vocab
+        q = None
+    elif onehot:
         rng = np.random.default_rng(seed)
         drafts, q = rng.integers(0, sh.vocab, size=(B, g)), None
     else:
         dft = OM.Decoder(sh, w, n_layers=1)
         cd = dft.new_cache(B, max_ctx)
         R.prefill(dft, cd, prompt)
-        drafts, q = R.draft_round(dft, cd, prompt[:, -2], prompt[:, -1], ct.length, g, u["u_draft"])
+        drafts, q = R.draft_round(dft, cd, prompt[:, -2], prompt[:, -1], ct.length, g, u["u_draft"], temperature=T)
     nd = np.random.default_rng(seed + 1).integers(0, g + 1, size=B) if ragged else None
     n_g = torch.empty(B, dtype=torch.int32, device="cuda")
     em_g = torch.empty((B, g + 1), dtype=torch.int32, device="cuda")
     logits = torch.empty((B, g + 1, sh.vocab), dtype=torch.float32, device="cuda")
     ws = bd.workspace(model.workspace_bytes(B, g + 1, max_ctx))
     len0 = kv.len.clone()
-    bd.spec_decode_step(model, kv, B, g, 1.0, i32(prompt[:, -1]), i32(drafts), None if nd is None else i32(nd),
-                        None if q is None else f32(q), f32(u["u_acc"]), f32(u["u_res"]), n_g, em_g, logits, ws)
+    greedy = T == 0.0
+    # at T = 0 the uniforms and q are not read: pass NULL
+    bd.spec_decode_step(model, kv, B, g, T, i32(prompt[:, -1]), i32(drafts), None if nd is None else i32(nd),
+                        None if (q is None or greedy) else f32(q), None if greedy else f32(u["u_acc"]),
+                        None if greedy else f32(u["u_res"]), n_g, em_g, logits, ws)
     torch.cuda.synchronize()
-    out = R.verify_round(tgt, ct, prompt[:, -1], drafts, q, nd, u["u_acc"], u["u_res"])
+    out = R.verify_round(tgt, ct, prompt[:, -1], drafts, q, nd, u["u_acc"], u["u_res"], temperature=T)
     n_g, em_g = n_g.cpu().numpy(), em_g.cpu().numpy()
     # logits parity
     tol = 1e-4 if sh.dtype == "f32" else 2e-2
-    assert np.abs(logits.cpu().numpy() - out["logits"]).max() < tol
+    lg = logits.cpu().numpy()
+    assert np.abs(lg - out["logits"]).max() < tol
+    assert np.array_equal(kv.len.cpu().numpy(), len0.cpu().numpy() + n_g + 1)
+    if greedy:
+        # the GPU's own float32 logits, verified by the oracle's greedy rule: bit-exact
+        n_o, em_o = S.greedy_verify(lg, drafts, nd)
+        assert np.array_equal(n_g, n_o) and np.array_equal(em_g, em_o)
+        # against the oracle's own logits: every row's argmax agrees unless the
+        # oracle's top two are within the logits tolerance of each other
+        a_g, a_o = lg.argmax(-1), out["logits"].argmax(-1)
+        top = out["logits"].max(-1)
+        gap = top - np.take_along_axis(out["logits"], a_g[..., None], -1)[..., 0]
+        assert ((a_g == a_o) | (gap < 2 * tol)).all()
+        for b in range(B):
+            if (a_g[b] == a_o[b]).all():
+                assert n_g[b] == out["n"][b] and (em_g[b] == out["emitted"][b]).all()
+        return n_g, em_g
     # the GPU's own p rows, sampled by the oracle's rule, give exactly the GPU's integers
-    p_gpu = gpu_softmax(logits, sh.vocab).cpu().numpy()
-    assert np.abs(p_gpu - out["p"]).max() < 1e-5
+    p_gpu = gpu_softmax(logits, sh.vocab, T).cpu().numpy()
+    # the probability tolerance holds for the softmax of the same logits; from
+    # the oracle's own logits, the logits error d moves l/T by up to d/T, so
+    # each p(v) by at most p(v) (exp(2 d / T) - 1)
+    assert np.abs(p_gpu - S.softmax(lg, T)).max() < 1e-5
+    d = np.abs(lg - out["logits"]).max()
+    assert (np.abs(p_gpu - out["p"]) <= out["p"] * np.expm1(2 * d / T) + 1e-5).all()
     n_o, em_o = S.reject_sample(p_gpu, q, drafts, nd, u["u_acc"], u["u_res"])
     assert np.array_equal(n_g, n_o) and np.array_equal(em_g, em_o)
     # against the oracle's own p: identical except decisions within 1e-4 of the threshold
@@ -61,8 +101,6 @@ def _decode_round(shape, B, g, seed, onehot=False, ragged=False, n_layers=None, 
     near = np.abs(u["u_acc"] - np.minimum(1.0, px / np.maximum(qx, 1e-30))) < 1e-4
     same = n_g == out["n"]
     assert (same | near.any(axis=1)).all()
-    # KV commit
-    assert np.array_equal(kv.len.cpu().numpy(), len0.cpu().numpy() + n_g + 1)
     return n_g, em_g
 
 
@@ -79,3 +117,23 @@ def test_decode_step_onehot_ragged_v151936():
     151936-entry vocabulary."""
     shape = SHAPES["small_v151936"]
     _decode_round(shape, B=3, g=10, seed=203, onehot=True, ragged=True, n_layers=1, P=24)
+
+
+@pytest.mark.parametrize("T", [0.6, 1.7])
+def test_decode_step_other_temperatures(T):
+    _decode_round(SHAPES["small"], B=3, g=4, seed=204, n_layers=2, T=T)
+
+
+def test_decode_step_greedy_tiny_f32():
+    n, _ = _decode_round(SHAPES["tiny"], B=8, g=4, seed=205, T=0.0, chain=True)
+    assert n.min() < 4 and n.max() == 4
+
+
+def test_decode_step_greedy_drafter_bf16():
+    _decode_round(SHAPES["small"], B=5, g=6, seed=206, n_layers=2, T=0.0)
+
+
+def test_decode_step_greedy_chain_ragged_v151936():
+    n, _ = _decode_round(SHAPES["small_v151936"], B=6, g=5, seed=207, ragged=True, n_layers=1, P=24, T=0.0,
+                         chain=True)
+    assert n.max() > 0

@@ -18,7 +18,7 @@ def _sub(w, layers):
     return {k: (v[:layers] if k in ("attn_norm", "wqkv", "wo", "mlp_norm", "wgu", "wd") else v) for k, v in w.items()}
 
 
-def _pair(shape, B, g, P, N, seed, draft_layers):
+def _pair(shape, B, g, P, N, seed, draft_layers, T=1.0):
     w = make_weights(shape, seed=seed)
     max_ctx = P + N + g + 4
     prompt = make_prompt(B, P, shape.vocab, seed=seed)
@@ -28,8 +28,8 @@ def _pair(shape, B, g, P, N, seed, draft_layers):
         drafter = None
         if g:
             dsh = shape.with_(n_layers=draft_layers)
-            drafter = ModelDrafter(bd.SpecModel(dsh, to_dev(_sub(w, draft_layers))), B, g, max_ctx)
-        dec = SpecDecoder(target, B, g, max_ctx, drafter=drafter, seed=seed)
+            drafter = ModelDrafter(bd.SpecModel(dsh, to_dev(_sub(w, draft_layers))), B, g, max_ctx, temperature=T)
+        dec = SpecDecoder(target, B, g, max_ctx, drafter=drafter, temperature=T, seed=seed)
         dec.prefill(prompt)
         res = dec.generate(N) if mode == "eager" else dec.generate_graph(N)
         outs.append(res)
@@ -48,3 +48,15 @@ def test_graph_rounds_small_batch():
 
 def test_graph_rounds_plain_decoding():
     _pair(SHAPES["small"], B=2, g=0, P=24, N=20, seed=403, draft_layers=0)
+
+
+def test_greedy_speculation_equals_greedy_decoding():
+    """At temperature 0 the speculative output is plain greedy decoding of the
+    target, token for token ("How Speculative Decoding Works", section
+    "Exactness is a choice"): graph-replayed greedy rounds with a one-layer
+    drafter against gamma = 0 greedy decoding of the same float32 target."""
+    shape = SHAPES["tiny"]
+    spec = _pair(shape, B=2, g=4, P=48, N=40, seed=404, draft_layers=1, T=0.0)
+    plain = _pair(shape, B=2, g=0, P=48, N=40, seed=404, draft_layers=0, T=0.0)
+    assert spec[1]["tokens"] == plain[0]["tokens"]
+    assert spec[1]["rounds"] <= plain[0]["rounds"]

@@ -120,3 +120,21 @@ def test_chi_square_on_gpu_v8():
         obs = np.bincount(obs_t, minlength=V)
         pr = pr.astype(np.float64) / pr.sum()
         assert stats.chisquare(obs, pr * obs.sum()).pvalue > 1e-3
+
+
+@pytest.mark.parametrize("V", [8, 4097, 151936])
+def test_softmax_temperature_zero_one_hot(V):
+    """T = 0 rows are one-hot at the argmax, lowest index among equal maxima,
+    also when the tied maxima sit in different 4096-entry chunks."""
+    rng = np.random.default_rng(SEED + 3 * V)
+    logits = _rows(rng, 9, V, 3.0)
+    logits[0, :] = 0.0                       # all equal: index 0
+    logits[1, :] = -np.inf                   # all -inf: index 0
+    logits[2, [V - 1, V // 2]] = 50.0        # tie: the lower index
+    logits[3, V - 1] = np.inf
+    if V > 4096:
+        logits[4, [4095, 4096]] = 60.0       # tie across a chunk boundary
+        logits[5, [V - 1, V - 2]] = 60.0       # tie in the last chunk
+    p = gpu_softmax(f32(logits), V, 0.0).cpu().numpy()
+    ref = S.softmax(logits, 0.0)
+    assert np.array_equal(p, ref.astype(np.float32))

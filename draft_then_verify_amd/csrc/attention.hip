@@ -359,6 +359,230 @@ hipError_t launch_mq(const AttnArgs& a, int B, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---- short passes: m <= 8 query rows, contexts up to kDecodeMaxCtx -------------
+// One workgroup per (sequence, query head, block of RW query rows): with few
+// sequences the rows are split until there are enough workgroups to spread
+// over the chip, and each workgroup still sees the whole context, so no
+// workgroup waits for another.  Its 8 waves split the keys (wave w takes
+// 64-key tiles w, w + 8, ...) and merge their partial (max, sum, output) rows
+// in LDS at the end, in wave order.
+// Lane l of a wave works on 16-byte chunk chi = l % CPR of rows
+// rho = l / CPR, rho + RPI, ... of the tile: the K and V loads are coalesced
+// (RPI whole rows per load instruction).  Scores: a lane dots its K chunk with
+// the same chunk of each query row (held in registers) and the CPR lanes of a
+// row add their parts with DPP moves inside the 16-lane row, so every lane of
+// the group holds the row's scores.  The softmax update and P.V then need no
+// data movement: the lane scales its V chunks by its rows' p; the RPI row
+// groups are summed once, after the last tile.
+constexpr int kDecWaves = 8;
+constexpr int kDecodeMaxCtx = 2048;
+
+template <typename ET, int HD> struct Dec {
+  static constexpr int CE = 16 / static_cast<int>(sizeof(ET));        // elements per 16-byte chunk
+  static constexpr int CPR = HD / CE;                                 // chunks per K/V row
+  static constexpr int RPI = kWave / CPR;                             // rows per load instruction
+  static constexpr int NI = KT / RPI;                                 // load instructions per tile
+};
+
+// Sum over the N (8 or 16) consecutive lanes of a DPP row group; every lane
+// of the group gets the same bits (each step adds a commuted pair).
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  v += dpp_mov<kDppQuadSwap1>(v);
+  v += dpp_mov<kDppQuadSwap2>(v);
+  v += dpp_mov<kDppHalfMirror>(v);
+  if constexpr (N == 16) v += dpp_mov<kDppMirror>(v);
+  return v;
+}
+
+// Max / sum over the lanes l, l ^ FROM, l ^ 2 FROM, ... (FROM = 8 or 16):
+// the RPI row groups of a wave; all lanes get the same bits.
+template <int FROM>
+__device__ __forceinline__ float groups_max(float v) {
+#pragma unroll
+  for (int off = FROM; off < kWave; off <<= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+template <int FROM>
+__device__ __forceinline__ float groups_sum(float v) {
+#pragma unroll
+  for (int off = FROM; off < kWave; off <<= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+template <typename ET, int HD, int RW>
+__global__ __launch_bounds__(kDecWaves * kWave) __attribute__((amdgpu_waves_per_eu(2))) void attn_decode_kernel(
+    AttnArgs a, int n_rb) {
+  using D = Dec<ET, HD>;
+  constexpr int CE = D::CE, CPR = D::CPR, RPI = D::RPI, NI = D::NI, NT = kDecWaves * kWave;
+  static_assert(CPR == 8 || CPR == 16, "K/V rows of 8 or 16 chunks");
+  __shared__ float mo[kDecWaves][RW][HD];
+  __shared__ float2 ml[kDecWaves][RW];
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+
+  const int H = a.H, Hkv = a.Hkv, m = a.m;
+  const int rb = blockIdx.x % n_rb;
+  const int h = (blockIdx.x / n_rb) % H;
+  const int b = blockIdx.x / (n_rb * H);
+  const int i0 = rb * RW;                 // first query row of the block
+  const int kvh = h / (H / Hkv);
+  const int Lb = a.len[b];
+  // keys the block's rows may see: positions 0 .. Lb + i0 + RW - 1
+  const int kend = max(0, min(min(Lb + m, Lb + i0 + RW), a.max_ctx));
+  const int ntiles = (kend + KT - 1) / KT;
+  const int trips = (ntiles + kDecWaves - 1) / kDecWaves;
+  const int qld = H * HD;
+  const ET* kc = static_cast<const ET*>(a.kc);
+  const ET* vc = static_cast<const ET*>(a.vc);
+  const size_t kvbase = ((static_cast<size_t>(a.layer) * a.kvB + b) * Hkv + kvh) * a.max_ctx;
+  const float scale = 1.0f / sqrtf(static_cast<float>(HD));
+  const int rho = lane / CPR, chi = lane % CPR;
+
+  // this lane's chunk of each query row of the block, pre-scaled (rows past
+  // m repeat row m - 1; their results are never written)
+  float qr[RW][CE];
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    const float* src = a.q + static_cast<size_t>(b * m + min(i0 + r, m - 1)) * qld + h * HD + chi * CE;
+#pragma unroll
+    for (int e = 0; e < CE; ++e) qr[r][e] = src[e] * scale;
+  }
+  float mrow[RW], lrow[RW], o[RW][CE];
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    mrow[r] = -INFINITY;
+    lrow[r] = 0.f;
+#pragma unroll
+    for (int e = 0; e < CE; ++e) o[r][e] = 0.f;
+  }
+
+  for (int it = 0; it < trips; ++it) {
+    const int k0 = (it * kDecWaves + wave) * KT;  // this wave's tile (may lie past kend: all masked)
+    const int klast = max(kend - 1, 0);
+    v4u kr[NI], vr[NI];
+#pragma unroll
+    for (int c = 0; c < NI; ++c) {
+      const size_t g = (kvbase + min(k0 + c * RPI + rho, klast)) * HD + chi * CE;
+      kr[c] = *reinterpret_cast<const v4u*>(kc + g);
+      vr[c] = *reinterpret_cast<const v4u*>(vc + g);
+    }
+    // scores of keys k0 + c * RPI + rho against each row
+    float sc[RW][NI];
+#pragma unroll
+    for (int c = 0; c < NI; ++c) {
+      float kf[CE];
+      Cvt<ET>::run(kr[c], kf);
+#pragma unroll
+      for (int r = 0; r < RW; ++r) {
+        float t0 = 0.f, t1 = 0.f;
+#pragma unroll
+        for (int e = 0; e < CE; e += 2) {
+          t0 = fmaf(qr[r][e], kf[e], t0);
+          t1 = fmaf(qr[r][e + 1], kf[e + 1], t1);
+        }
+        sc[r][c] = group_sum<CPR>(t0 + t1);
+      }
+    }
+    // online softmax per row (row i0 + r sees keys 0 .. Lb + i0 + r), then
+    // this lane's V chunks weighted by its rows' p
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      float mt = -INFINITY;
+#pragma unroll
+      for (int c = 0; c < NI; ++c) {
+        const int key = k0 + c * RPI + rho;
+        if (!(key < kend && key <= Lb + i0 + r)) sc[r][c] = -INFINITY;
+        mt = fmaxf(mt, sc[r][c]);
+      }
+      const float mnew = fmaxf(mrow[r], groups_max<CPR>(mt));
+      const bool live = mnew != -INFINITY;
+      const float alpha = live ? expf(mrow[r] - mnew) : 1.f;
+      float ls = 0.f;
+#pragma unroll
+      for (int c = 0; c < NI; ++c) {
+        sc[r][c] = (live && sc[r][c] != -INFINITY) ? expf(sc[r][c] - mnew) : 0.f;
+        ls += sc[r][c];
+      }
+      lrow[r] = lrow[r] * alpha + groups_sum<CPR>(ls);
+      mrow[r] = mnew;
+#pragma unroll
+      for (int e = 0; e < CE; ++e) o[r][e] *= alpha;
+    }
+#pragma unroll
+    for (int c = 0; c < NI; ++c) {
+      float vf[CE];
+      Cvt<ET>::run(vr[c], vf);
+#pragma unroll
+      for (int r = 0; r < RW; ++r)
+#pragma unroll
+        for (int e = 0; e < CE; ++e) o[r][e] = fmaf(sc[r][c], vf[e], o[r][e]);
+    }
+  }
+  // the row groups' parts of each chunk, then the waves, in order
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+#pragma unroll
+    for (int e = 0; e < CE; ++e) o[r][e] = groups_sum<CPR>(o[r][e]);
+    if (rho == 0) {
+#pragma unroll
+      for (int e = 0; e < CE; ++e) mo[wave][r][chi * CE + e] = o[r][e];
+    }
+    if (lane == 0) ml[wave][r] = make_float2(mrow[r], lrow[r]);
+  }
+  __syncthreads();
+  ET* xo = static_cast<ET*>(a.xo);
+  const int nr = max(0, min(RW, m - i0));
+  for (int idx = threadIdx.x; idx < nr * HD; idx += NT) {
+    const int r = idx / HD, dd = idx - r * HD;
+    float Mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) Mx = fmaxf(Mx, ml[w][r].x);
+    float l = 0.f, acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) {
+      const float2 v = ml[w][r];
+      const float wt = (v.x == -INFINITY) ? 0.f : expf(v.x - Mx);
+      l = fmaf(v.y, wt, l);
+      acc = fmaf(mo[w][r][dd], wt, acc);
+    }
+    xo[static_cast<size_t>(b * m + i0 + r) * qld + h * HD + dd] = Elt<ET>::from_f(l > 0.f ? acc / l : 0.f);
+  }
+}
+
+// Query rows per workgroup: split the m rows until B * H * blocks reaches
+// about one workgroup per CU, and to at most rw_max rows (the register budget:
+// 3 rows for 16-chunk K/V rows, 5 for 8-chunk rows).
+inline int decode_rows_per_block(int B, int H, int m, int rw_max) {
+  const int units = B * H;
+  int blocks = (256 + units - 1) / units;
+  blocks = max(1, min(blocks, m));
+  return min((m + blocks - 1) / blocks, rw_max);
+}
+
+template <typename ET, int HD, int RW>
+hipError_t launch_decode_rw(const AttnArgs& a, int B, hipStream_t s) {
+  const int n_rb = (a.m + RW - 1) / RW;
+  hipLaunchKernelGGL((attn_decode_kernel<ET, HD, RW>), dim3(B * a.H * n_rb), dim3(kDecWaves * kWave), 0, s, a, n_rb);
+  return hipGetLastError();
+}
+
+template <typename ET, int HD>
+hipError_t launch_decode(const AttnArgs& a, int B, hipStream_t s) {
+  constexpr int rw_max = Dec<ET, HD>::CPR == 16 ? 3 : 5;
+  switch (decode_rows_per_block(B, a.H, a.m, rw_max)) {
+    case 1: return launch_decode_rw<ET, HD, 1>(a, B, s);
+    case 2: return launch_decode_rw<ET, HD, 2>(a, B, s);
+    case 3: return launch_decode_rw<ET, HD, 3>(a, B, s);
+    case 4: return launch_decode_rw<ET, HD, (rw_max >= 4 ? 4 : 3)>(a, B, s);
+    default: return launch_decode_rw<ET, HD, (rw_max >= 5 ? 5 : 3)>(a, B, s);
+  }
+}
+
+template <typename ET, int HD>
+constexpr bool decode_fits() {
+  return Dec<ET, HD>::CPR == 8 || Dec<ET, HD>::CPR == 16;
+}
+
 // Query rows per wave: the rows of a block spread over the waves of a head.
 int rows_per_wave(int H, int Hkv, int hd, int m) {
   const int G = H / Hkv, waves = waves_for(hd);
@@ -407,9 +631,19 @@ size_t attn_counters(int B, int H, int Hkv, int hd, int m) {
   return static_cast<size_t>(B) * Hkv * pl.nhb * pl.nqc;
 }
 
+bool attn_decode_path(bool bf16, int hd, int m, int max_ctx) {
+  if (m > 8 || max_ctx > kDecodeMaxCtx) return false;
+  if (bf16) return hd == 128 ? decode_fits<uint16_t, 128>() : decode_fits<uint16_t, 64>();
+  return hd == 128 ? decode_fits<float, 128>() : decode_fits<float, 64>();
+}
+
 hipError_t launch_attention(bool bf16, int hd, const AttnArgs& a, int B, hipStream_t s) {
   if (B <= 0 || a.m <= 0) return hipSuccess;
   if (!attn_supported(a.H, a.Hkv, hd)) return hipErrorInvalidValue;
+  if (attn_decode_path(bf16, hd, a.m, a.max_ctx)) {
+    if (bf16) return hd == 128 ? launch_decode<uint16_t, 128>(a, B, s) : launch_decode<uint16_t, 64>(a, B, s);
+    if (hd == 64) return launch_decode<float, 64>(a, B, s);
+  }
   if (bf16) return hd == 128 ? launch_hd<uint16_t, 128>(a, B, s) : launch_hd<uint16_t, 64>(a, B, s);
   return hd == 128 ? launch_hd<float, 128>(a, B, s) : launch_hd<float, 64>(a, B, s);
 }

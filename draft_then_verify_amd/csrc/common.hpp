@@ -109,16 +109,16 @@ __device__ __forceinline__ unsigned long long block_sum_u64(unsigned long long v
   return s;
 }
 
-// RMSNorm of G consecutive residual rows (h [G][ld] -> out [G][d] in the
-// model dtype) by one workgroup of NT threads:
-// x = cvt(h * rsqrt(mean(h^2) + eps) * g).  d % 4 == 0, d <= 16 * NT,
+// RMSNorm of G consecutive residual rows (h [G][ld] -> out [G][ldo] in the
+// model dtype; out may be global or LDS) by one workgroup of NT threads:
+// x = cvt(h * rsqrt(mean(h^2) + eps) * g).  d % 4 == 0, d <= 4096,
 // ld % 4 == 0.  Every load is issued before any is used (16-byte loads,
 // indexes clamped, surplus chunks weigh zero): one memory round trip.  Fixed
 // order: per-thread sums, wave butterflies, waves in index order.
 template <int NT, int G, typename OT>
 __device__ __forceinline__ void norm_group(const float* h, int ld, int d, const float* gain, float eps, OT* out,
-                                           float (*red)[8]) {
-  constexpr int CPT = 4;  // 16-byte chunks per thread and row
+                                           int ldo, float (*red)[8]) {
+  constexpr int CPT = (4 * 256 + NT - 1) / NT;  // 16-byte chunks per thread and row (d <= 4096)
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int d4 = d / 4;
   float4 v[G][CPT];
@@ -150,7 +150,7 @@ __device__ __forceinline__ void norm_group(const float* h, int ld, int d, const 
 #pragma unroll
     for (int w = 1; w < NT / kWave; ++w) ss += red[w][g];
     const float scale = rsqrtf(ss / static_cast<float>(d) + eps);
-    OT* o = out + static_cast<size_t>(g) * d;
+    OT* o = out + static_cast<size_t>(g) * ldo;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int e4 = threadIdx.x + c * NT;
@@ -167,16 +167,18 @@ __device__ __forceinline__ void norm_group(const float* h, int ld, int d, const 
 }
 
 // RMSNorm of M (1..8, a compile-time count) rows: one round trip for M <= 5,
-// two otherwise (rows 0-3, then the rest).
+// two otherwise (rows 0-3, then the rest).  Output row stride ldo.
 template <int NT, int M, typename OT>
-__device__ __forceinline__ void norm_rows(const float* h, int ld, int d, const float* gain, float eps, OT* out) {
+__device__ __forceinline__ void norm_rows(const float* h, int ld, int d, const float* gain, float eps, OT* out,
+                                          int ldo) {
   static_assert(M >= 1 && M <= 8, "1..8 rows");
   __shared__ float red_nr[NT / kWave][8];
   if constexpr (M <= 5) {
-    norm_group<NT, M>(h, ld, d, gain, eps, out, red_nr);
+    norm_group<NT, M>(h, ld, d, gain, eps, out, ldo, red_nr);
   } else {
-    norm_group<NT, 4>(h, ld, d, gain, eps, out, red_nr);
-    norm_group<NT, M - 4>(h + 4 * static_cast<size_t>(ld), ld, d, gain, eps, out + 4 * static_cast<size_t>(d), red_nr);
+    norm_group<NT, 4>(h, ld, d, gain, eps, out, ldo, red_nr);
+    norm_group<NT, M - 4>(h + 4 * static_cast<size_t>(ld), ld, d, gain, eps, out + 4 * static_cast<size_t>(ldo), ldo,
+                          red_nr);
   }
 }
 

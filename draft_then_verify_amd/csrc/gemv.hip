@@ -4,10 +4,12 @@
 // wave walks a strided list of R-row tiles.  Launch shapes per epilogue
 // (rows per tile R, ring depth U, minimum waves per SIMD, workgroups per CU,
 // threads per workgroup) were chosen by timing the 8B-shaped matrices on
-// MI355X with M = 5, the weights rotated through more memory than the
-// 256 MB last-level cache holds.  U is lowered to the largest of 8, 4, 2, 1 that divides
-// the steps per row.  Activation rows go through in blocks of at most 8 that
-// fit the LDS.  bf16 passes with more than 8 rows go to the matrix-core
+// MI355X with M = 5, 36 distinct matrices per replayed graph so the weights
+// come from HBM.  Wide workgroups, one per CU, stage the activations once per
+// CU: with 3 narrow workgroups per CU the 40 KB of staged rows per workgroup
+// came to as many bytes as the QKV and O weights themselves.  U is lowered to
+// the largest of 8, 4, 2, 1 that divides the steps per row.  Activation rows
+// go through in blocks of at most 8 that fit the LDS.  bf16 passes with more than 8 rows go to the matrix-core
 // kernel (gemm_mfma.hpp), which reads the weights once per 64 rows.
 #include <algorithm>
 #include <type_traits>
@@ -23,11 +25,11 @@ using gemv::kMaxLds;
 constexpr int kCUs = 256;
 
 template <int EPI> struct Cfg;
-template <> struct Cfg<EPI_SWIGLU> { static constexpr int R = 1, U = 4, WPE = 2, BPC = 1, NT = 512; };
+template <> struct Cfg<EPI_SWIGLU> { static constexpr int R = 1, U = 4, WPE = 4, BPC = 1, NT = 1024; };
 template <> struct Cfg<EPI_STORE> { static constexpr int R = 4, U = 4, WPE = 2, BPC = 1, NT = 256; };
-template <> struct Cfg<EPI_PARTIAL> { static constexpr int R = 1, U = 8, WPE = 3, BPC = 3, NT = 256; };
+template <> struct Cfg<EPI_PARTIAL> { static constexpr int R = 1, U = 4, WPE = 4, BPC = 1, NT = 1024; };
 template <> struct Cfg<EPI_RESID> { static constexpr int R = 2, U = 8, WPE = 2, BPC = 2, NT = 256; };
-template <> struct Cfg<EPI_QKV> { static constexpr int R = 2, U = 4, WPE = 3, BPC = 3, NT = 256; };
+template <> struct Cfg<EPI_QKV> { static constexpr int R = 2, U = 4, WPE = 4, BPC = 1, NT = 768; };
 
 template <typename WT> constexpr int step_elems() { return kWave * (16 / static_cast<int>(sizeof(WT))); }
 
@@ -147,12 +149,14 @@ int gemv_ksplit(bool bf16, int M, int N, int K) {
     }
     return best;
   }
+  // weight-streaming path: one workgroup per CU stages its rows' slice of x
+  // in LDS; split K only when a block of rows does not fit
   const int elt = bf16 ? 2 : 4;
   const int step = kWave * (16 / elt);
   const int mb = std::min(M, 8);
   for (int ks = 1; ks <= 8; ++ks) {
     if (K % (ks * step)) continue;
-    if (static_cast<size_t>(mb) * (K / ks) * elt <= 48 * 1024) return ks;
+    if (static_cast<size_t>(mb) * (K / ks) * elt <= static_cast<size_t>(kMaxLds)) return ks;
   }
   return 1;
 }

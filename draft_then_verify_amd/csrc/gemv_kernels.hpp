@@ -212,7 +212,17 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE))) void 
 #pragma unroll
     for (int u = 0; u < U; ++u) load_step(cur, u, wv[u]);
   }
-  stage_x<WT, M, NT>(static_cast<const WT*>(a.x) + static_cast<size_t>(slice) * K, a.ldx, K, xs, KP);
+  if (a.hn) {
+    // x = cvt(RMSNorm(h) * gain), made in LDS (one K slice: K = d); the
+    // padding columns K .. KP-1 are zero
+    norm_rows<NT, M>(a.hn, K, K, a.gain, a.eps, xs, KP);
+    for (int idx = threadIdx.x; idx < M * (KP - K); idx += NT) {
+      const int m = idx / (KP - K);
+      xs[static_cast<size_t>(m) * KP + K + (idx - m * (KP - K))] = Elt<WT>::from_f(0.f);
+    }
+  } else {
+    stage_x<WT, M, NT>(static_cast<const WT*>(a.x) + static_cast<size_t>(slice) * K, a.ldx, K, xs, KP);
+  }
   __syncthreads();
 
   float acc[NW][M];

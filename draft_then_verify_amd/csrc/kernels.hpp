@@ -20,12 +20,18 @@ enum GemvEpi { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_QKV = 3, EPI_PA
 //              k heads rotated and v heads copied into the KV cache of
 //              `layer` at position len[b] + i (row = b * m_per_seq + i).
 // ldw / ldx: row strides of W and x (0: K).
+// hn: when not NULL the activations are not read from x but made from the
+// float32 residual rows hn [M][K] as cvt(RMSNorm(hn) * gain) while being
+// staged (K = d_model, one K slice, M <= 8).
 struct GemvArgs {
   const void* W = nullptr;
   int N = 0, K = 0, M = 0;
   int ldw = 0, ldx = 0;
   int ksplit = 1;
   const void* x = nullptr;
+  const float* hn = nullptr;
+  const float* gain = nullptr;
+  float eps = 0.f;
   float* y = nullptr;
   int ldy = 0;
   size_t ysplit = 0;
@@ -43,8 +49,8 @@ struct GemvArgs {
 hipError_t launch_gemv(bool bf16, int epi, const GemvArgs& a, int M, hipStream_t s);
 
 // K slices the residual linears use for an M-row pass with N outputs: for
-// M <= 8, a divisor of K that keeps a workgroup's staged activations near
-// 40 KiB; for the matrix-core path, enough slices for about 2 workgroups per
+// M <= 8, the fewest that let a workgroup stage its block of activation rows
+// in LDS; for the matrix-core path, enough slices for about 2 workgroups per
 // CU.
 int gemv_ksplit(bool bf16, int M, int N, int K);
 
@@ -85,6 +91,11 @@ int attn_row_blocks(int H, int Hkv, int hd, int m);  // n_qc
 int attn_num_splits(int B, int H, int Hkv, int hd, int m, int max_ctx);
 size_t attn_counters(int B, int H, int Hkv, int hd, int m);  // tickets the launch uses
 hipError_t launch_attention(bool bf16, int hd, const AttnArgs& a, int B, hipStream_t s);
+// True when launch_attention takes the short-pass kernel (m <= 8 rows,
+// max_ctx <= 2048, a K/V row of at most 256 bytes): one workgroup per
+// (sequence, query head), no context splits, so n_split, part_* and counters
+// are not used.
+bool attn_decode_path(bool bf16, int hd, int m, int max_ctx);
 
 // Round bookkeeping (see spec_commit_round).
 hipError_t launch_commit_round(int B, int gamma, const int32_t* n_acc, const int32_t* emitted, int32_t* tok2,

@@ -31,7 +31,7 @@ __global__ __launch_bounds__(kThreads) void embed_kernel(const ET* __restrict__ 
 #pragma unroll 4
   for (int j = threadIdx.x; j < d; j += kThreads) dst[j] = Elt<ET>::load(src + j);
   __syncthreads();
-  norm_rows<kThreads, 1>(dst, d, d, gain, eps, x + static_cast<size_t>(r) * d);
+  if (x) norm_rows<kThreads, 1>(dst, d, d, gain, eps, x + static_cast<size_t>(r) * d, d);
   // RoPE angles in double precision, rounded once to float.
   const int half = hd / 2;
   if (threadIdx.x < half) {

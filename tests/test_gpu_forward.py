@@ -91,3 +91,28 @@ def test_long_context_splits():
     shape = Shape("ctx", 256, 1, 4, 1, 64, 512, 300, "f32")
     got, ref, *_ = _run(shape, B=1, P=700, m=5, seed=105, max_ctx=720)
     assert np.abs(got - ref).max() < 1e-4
+
+
+@pytest.mark.parametrize("B,m,P", [(2, 8, 100), (1, 1, 130), (40, 5, 20), (3, 2, 70)])
+def test_short_pass_attention_row_blocks(B, m, P):
+    """Short passes (m <= 8, context <= 2048) take the attention kernel with
+    one workgroup per (sequence, head, row block): one row per block at small
+    B, blocks of 3 rows (the last one partial) at B = 40."""
+    shape = Shape("h128s", 512, 2, 8, 2, 128, 1024, 3000, "bf16")
+    got, ref, *_ = _run(shape, B=B, P=P, m=m, seed=106 + B + m)
+    assert np.abs(got - ref).max() < _tol(shape)
+
+
+def test_short_pass_hd64_row_blocks_ragged():
+    """head_dim 64 (8 16-byte chunks per bf16 row): blocks of up to 5 rows."""
+    shape = Shape("h64s", 256, 1, 4, 2, 64, 512, 500, "bf16")
+    got, ref, *_ = _run(shape, B=70, P=12, m=5, seed=111, lens_back=[i % 9 for i in range(70)])
+    assert np.abs(got - ref).max() < _tol(shape)
+
+
+def test_long_context_split_kernel():
+    """Past 2048 cached positions the split-context kernel with its
+    last-workgroup merge runs instead."""
+    shape = Shape("ctx2", 256, 1, 4, 1, 64, 512, 300, "f32")
+    got, ref, *_ = _run(shape, B=1, P=2100, m=5, seed=112, max_ctx=2120)
+    assert np.abs(got - ref).max() < 1e-4

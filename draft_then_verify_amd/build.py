@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libspecverify.so")
-SOURCES = ["gemv.hip", "small_ops.hip", "attention.hip", "sampler.hip", "capi.hip"]
+SOURCES = ["gemv.hip", "small_ops.hip", "attention.hip", "sampler.hip", "fused_pass.hip", "capi.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

@@ -384,31 +384,6 @@ template <typename ET, int HD> struct Dec {
   static constexpr int NI = KT / RPI;                                 // load instructions per tile
 };
 
-// Sum over the N (8 or 16) consecutive lanes of a DPP row group; every lane
-// of the group gets the same bits (each step adds a commuted pair).
-template <int N>
-__device__ __forceinline__ float group_sum(float v) {
-  v += dpp_mov<kDppQuadSwap1>(v);
-  v += dpp_mov<kDppQuadSwap2>(v);
-  v += dpp_mov<kDppHalfMirror>(v);
-  if constexpr (N == 16) v += dpp_mov<kDppMirror>(v);
-  return v;
-}
-
-// Max / sum over the lanes l, l ^ FROM, l ^ 2 FROM, ... (FROM = 8 or 16):
-// the RPI row groups of a wave; all lanes get the same bits.
-template <int FROM>
-__device__ __forceinline__ float groups_max(float v) {
-#pragma unroll
-  for (int off = FROM; off < kWave; off <<= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
-  return v;
-}
-template <int FROM>
-__device__ __forceinline__ float groups_sum(float v) {
-#pragma unroll
-  for (int off = FROM; off < kWave; off <<= 1) v += __shfl_xor(v, off, kWave);
-  return v;
-}
 
 template <typename ET, int HD, int RW>
 __global__ __launch_bounds__(kDecWaves * kWave) __attribute__((amdgpu_waves_per_eu(2))) void attn_decode_kernel(

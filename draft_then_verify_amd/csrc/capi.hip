@@ -2,6 +2,7 @@
 // sequence of a verify pass / decode step on one HIP stream.
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 
 #include <algorithm>
 #include <string>
@@ -19,6 +20,7 @@ struct spec_model {
   const float* final_norm;
   std::vector<const float*> attn_norm, mlp_norm;
   std::vector<const void*> wqkv, wo, wgu, wd;
+  sv::FusedLayer* d_layers = nullptr;  // device copy of the per-layer pointers (bf16 models)
 };
 
 namespace {
@@ -58,7 +60,9 @@ Layout make_layout(const spec_model_cfg& c, int B, int m, int max_ctx) {
   const int nch = sv::sampler_chunks(c.vocab);
   L.n_qc = sv::attn_row_blocks(c.n_heads, c.n_kv_heads, c.head_dim, m);
   L.n_split = sv::attn_num_splits(B, c.n_heads, c.n_kv_heads, c.head_dim, m, max_ctx);
-  L.n_ctr = static_cast<int>(sv::attn_counters(B, c.n_heads, c.n_kv_heads, c.head_dim, m));
+  // attention tickets, or the persistent pass's barrier counters + error word
+  L.n_ctr = std::max(static_cast<int>(sv::attn_counters(B, c.n_heads, c.n_kv_heads, c.head_dim, m)),
+                     sv::kFusedBarrierWords + 64);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -94,13 +98,26 @@ spec_status check_kv(const spec_model* M, const spec_kv* kv, int B, int m) {
   return SPEC_OK;
 }
 
+// The persistent pass (one launch for every layer and the LM head) serves
+// passes of at most 8 rows of bf16 models when SPEC_FUSED=1 is set in the
+// environment.  It is not the default: measured on MI355X it is slower than
+// the launch-per-step sequence below (8B shape, 5 rows: 4.30 against
+// 3.63 ms; 0.6B shape, 1 row: 1.06 against 0.91 ms), because each dependent
+// step inside it still waits about as long as a kernel boundary costs.
+bool fused_enabled() {
+  const char* e = getenv("SPEC_FUSED");
+  return e && e[0] == '1';
+}
+
 // Launch sequence of one forward pass over B x m rows.  The embedding kernel
 // writes the residual rows h and the first RMSNorm's output; per layer
-//   QKV linear (RoPE + KV append) -> attention (split context, merged
-//   in-kernel) -> O linear (K-slice partials) -> h += partials, MLP RMSNorm
-//   -> gate/up linear (SwiGLU) -> down linear (K-slice partials) -> h +=
-//   partials, the next RMSNorm;
-// then the LM head on the final RMSNorm.
+//   QKV linear (RoPE + KV append) -> attention -> O linear -> h += O,
+//   MLP RMSNorm -> gate/up linear (SwiGLU) -> down linear -> h += down,
+//   the next RMSNorm;
+// then the LM head on the final RMSNorm.  With at most 8 rows the residual
+// adds happen in the linears' epilogues and each RMSNorm in the next
+// linear's staging; otherwise the linears write K-slice partials that one
+// small kernel sums into h before normalising.
 spec_status run_forward(const spec_model* M, const spec_kv* kv, int B, int m, const int32_t* tokens,
                         const int32_t* last, const int32_t* draft, float* logits, const Layout& L, char* ws,
                         hipStream_t s) {
@@ -115,6 +132,37 @@ spec_status run_forward(const spec_model* M, const spec_kv* kv, int B, int m, co
 
   HIP_TRY(sv::launch_embed(bf16, M->embed, V, d, tokens, last, draft, kv->len, B, m, hd, c.rope_theta,
                            M->attn_norm[0], c.rms_eps, h, xn, cs, ctr, L.n_ctr, s));
+  if (M->d_layers && fused_enabled() && sv::fused_pass_supported(bf16, rows, d, H, Hkv, hd, F)) {
+    sv::FusedArgs fa;
+    fa.layers = M->d_layers;
+    fa.lm_head = M->lm_head;
+    fa.final_norm = M->final_norm;
+    fa.d = d;
+    fa.H = H;
+    fa.Hkv = Hkv;
+    fa.F = F;
+    fa.V = V;
+    fa.L = c.n_layers;
+    fa.eps = c.rms_eps;
+    fa.B = B;
+    fa.m = m;
+    fa.kc = kv->k;
+    fa.vc = kv->v;
+    fa.len = kv->len;
+    fa.kvB = kv->B;
+    fa.max_ctx = kv->max_ctx;
+    fa.cs = cs;
+    fa.xn = xn;
+    fa.h = h;
+    fa.q = reinterpret_cast<float*>(ws + L.q);
+    fa.xo = ws + L.xo;
+    fa.z = ws + L.z;
+    fa.logits = logits ? logits : reinterpret_cast<float*>(ws + L.logits);
+    fa.bar = reinterpret_cast<unsigned*>(ctr);
+    fa.err = ctr + sv::kFusedBarrierWords;
+    HIP_TRY(sv::launch_fused_pass(fa, hd, s));
+    return SPEC_OK;
+  }
   sv::GemvArgs qkv;
   qkv.N = (H + 2 * Hkv) * hd;
   qkv.K = d;
@@ -166,21 +214,47 @@ spec_status run_forward(const spec_model* M, const spec_kv* kv, int B, int m, co
   dn.K = F;
   dn.ksplit = L.ks_d;
   dn.x = ws + L.z;
+  // Passes of at most 8 rows add a residual linear's output straight into h
+  // (one K slice: every output element has one owner), and the next linear
+  // makes its RMSNorm input from h while staging it.  Otherwise the K-slice
+  // partials go through the residual-sum + RMSNorm kernel.
+  const bool o_direct = rows <= 8 && L.ks_o == 1;
+  const bool d_direct = rows <= 8 && L.ks_d == 1;
   for (int l = 0; l < c.n_layers; ++l) {
     qkv.W = M->wqkv[l];
     qkv.layer = l;
+    if (l > 0 && d_direct) {
+      qkv.hn = h;
+      qkv.gain = M->attn_norm[l];
+      qkv.eps = c.rms_eps;
+    }
     HIP_TRY(sv::launch_gemv(bf16, sv::EPI_QKV, qkv, rows, s));
     at.layer = l;
     HIP_TRY(sv::launch_attention(bf16, hd, at, B, s));
     o.W = M->wo[l];
-    HIP_TRY(sv::launch_gemv(bf16, sv::EPI_PARTIAL, o, rows, s));
-    HIP_TRY(sv::launch_resid_norm(bf16, h, pt, L.ks_o, pstride, rows, d, M->mlp_norm[l], c.rms_eps, xn, s));
+    if (o_direct) {
+      sv::GemvArgs od = o;
+      od.y = h;
+      HIP_TRY(sv::launch_gemv(bf16, sv::EPI_RESID, od, rows, s));
+      gu.hn = h;
+      gu.gain = M->mlp_norm[l];
+      gu.eps = c.rms_eps;
+    } else {
+      HIP_TRY(sv::launch_gemv(bf16, sv::EPI_PARTIAL, o, rows, s));
+      HIP_TRY(sv::launch_resid_norm(bf16, h, pt, L.ks_o, pstride, rows, d, M->mlp_norm[l], c.rms_eps, xn, s));
+    }
     gu.W = M->wgu[l];
     HIP_TRY(sv::launch_gemv(bf16, sv::EPI_SWIGLU, gu, rows, s));
     dn.W = M->wd[l];
-    HIP_TRY(sv::launch_gemv(bf16, sv::EPI_PARTIAL, dn, rows, s));
-    HIP_TRY(sv::launch_resid_norm(bf16, h, pt, L.ks_d, pstride, rows, d,
-                                  l + 1 < c.n_layers ? M->attn_norm[l + 1] : M->final_norm, c.rms_eps, xn, s));
+    if (d_direct) {
+      sv::GemvArgs dd = dn;
+      dd.y = h;
+      HIP_TRY(sv::launch_gemv(bf16, sv::EPI_RESID, dd, rows, s));
+    } else {
+      HIP_TRY(sv::launch_gemv(bf16, sv::EPI_PARTIAL, dn, rows, s));
+      HIP_TRY(sv::launch_resid_norm(bf16, h, pt, L.ks_d, pstride, rows, d,
+                                    l + 1 < c.n_layers ? M->attn_norm[l + 1] : M->final_norm, c.rms_eps, xn, s));
+    }
   }
   if (logits) {
     sv::GemvArgs lm;
@@ -188,6 +262,11 @@ spec_status run_forward(const spec_model* M, const spec_kv* kv, int B, int m, co
     lm.N = V;
     lm.K = d;
     lm.x = xn;
+    if (d_direct) {
+      lm.hn = h;
+      lm.gain = M->final_norm;
+      lm.eps = c.rms_eps;
+    }
     lm.y = logits;
     lm.ldy = V;
     HIP_TRY(sv::launch_gemv(bf16, sv::EPI_STORE, lm, rows, s));
@@ -248,11 +327,27 @@ SPEC_API spec_status spec_model_create(const spec_model_cfg* cfg, const spec_wei
   M->wo.assign(w->wo, w->wo + c.n_layers);
   M->wgu.assign(w->wgu, w->wgu + c.n_layers);
   M->wd.assign(w->wd, w->wd + c.n_layers);
+  if (c.dtype == SPEC_BF16) {
+    std::vector<sv::FusedLayer> t(c.n_layers);
+    for (int l = 0; l < c.n_layers; ++l)
+      t[l] = sv::FusedLayer{w->wqkv[l], w->wo[l], w->wgu[l], w->wd[l], w->attn_norm[l], w->mlp_norm[l]};
+    const size_t bytes = sizeof(sv::FusedLayer) * c.n_layers;
+    e = hipMalloc(&M->d_layers, bytes);
+    if (e == hipSuccess) e = hipMemcpy(M->d_layers, t.data(), bytes, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      if (M->d_layers) (void)hipFree(M->d_layers);
+      delete M;
+      return fail(SPEC_ENOMEM, "layer table: %s", hipGetErrorString(e));
+    }
+  }
   *out = M;
   return SPEC_OK;
 }
 
-SPEC_API void spec_model_destroy(spec_model* model) { delete model; }
+SPEC_API void spec_model_destroy(spec_model* model) {
+  if (model && model->d_layers) (void)hipFree(model->d_layers);
+  delete model;
+}
 
 SPEC_API size_t spec_workspace_bytes(const spec_model* model, int32_t B, int32_t m, int32_t max_ctx) {
   if (!model || B <= 0 || m <= 0 || max_ctx <= 0) return 0;

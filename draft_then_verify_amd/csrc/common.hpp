@@ -69,6 +69,32 @@ __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v)
   return v;
 }
 
+// Sum over the N (8 or 16) consecutive lanes of a DPP row group; every lane
+// of the group gets the same bits (each step adds a commuted pair).
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  v += dpp_mov<kDppQuadSwap1>(v);
+  v += dpp_mov<kDppQuadSwap2>(v);
+  v += dpp_mov<kDppHalfMirror>(v);
+  if constexpr (N == 16) v += dpp_mov<kDppMirror>(v);
+  return v;
+}
+
+// Max / sum over the lanes l, l ^ FROM, l ^ 2 FROM, ... (FROM = 8 or 16):
+// the RPI row groups of a wave; all lanes get the same bits.
+template <int FROM>
+__device__ __forceinline__ float groups_max(float v) {
+#pragma unroll
+  for (int off = FROM; off < kWave; off <<= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+template <int FROM>
+__device__ __forceinline__ float groups_sum(float v) {
+#pragma unroll
+  for (int off = FROM; off < kWave; off <<= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
 // Block reductions for blockDim.x == NT (a multiple of 64).  `red` is LDS
 // scratch of NT/64 elements.  Fixed order: wave butterflies, then waves in
 // index order.  All threads receive the result.
@@ -112,32 +138,44 @@ __device__ __forceinline__ unsigned long long block_sum_u64(unsigned long long v
 // RMSNorm of G consecutive residual rows (h [G][ld] -> out [G][ldo] in the
 // model dtype; out may be global or LDS) by one workgroup of NT threads:
 // x = cvt(h * rsqrt(mean(h^2) + eps) * g).  d % 4 == 0, d <= 4096,
-// ld % 4 == 0.  Every load is issued before any is used (16-byte loads,
-// indexes clamped, surplus chunks weigh zero): one memory round trip.  Fixed
-// order: per-thread sums, wave butterflies, waves in index order.
-template <int NT, int G, typename OT>
-__device__ __forceinline__ void norm_group(const float* h, int ld, int d, const float* gain, float eps, OT* out,
-                                           int ldo, float (*red)[8]) {
-  constexpr int CPT = (4 * 256 + NT - 1) / NT;  // 16-byte chunks per thread and row (d <= 4096)
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int d4 = d / 4;
+// ld % 4 == 0.  In two halves: norm_issue puts every load of the rows in
+// flight (16-byte loads, indexes clamped, surplus chunks weigh zero: one
+// memory round trip), norm_commit reduces and writes, so a caller can issue
+// other loads in between.  Fixed order: per-thread sums, wave butterflies,
+// waves in index order.
+template <int NT, int G> struct NormRegs {
+  static constexpr int CPT = (4 * 256 + NT - 1) / NT;  // 16-byte chunks per thread and row (d <= 4096)
   float4 v[G][CPT];
+};
+
+template <int NT, int G>
+__device__ __forceinline__ void norm_issue(const float* h, int ld, int d, NormRegs<NT, G>& r) {
+  constexpr int CPT = NormRegs<NT, G>::CPT;
+  const int d4 = d / 4;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     const float4* hr = reinterpret_cast<const float4*>(h + static_cast<size_t>(g) * ld);
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) v[g][c] = hr[min(static_cast<int>(threadIdx.x) + c * NT, d4 - 1)];
+    for (int c = 0; c < CPT; ++c) r.v[g][c] = hr[min(static_cast<int>(threadIdx.x) + c * NT, d4 - 1)];
   }
+}
+
+template <int NT, int G, typename OT>
+__device__ __forceinline__ void norm_commit(const NormRegs<NT, G>& r, int d, const float* gain, float eps, OT* out,
+                                            int ldo, float (*red)[8]) {
+  constexpr int CPT = NormRegs<NT, G>::CPT;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int d4 = d / 4;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     float ss = 0.f;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       if (static_cast<int>(threadIdx.x) + c * NT < d4) {
-        ss = fmaf(v[g][c].x, v[g][c].x, ss);
-        ss = fmaf(v[g][c].y, v[g][c].y, ss);
-        ss = fmaf(v[g][c].z, v[g][c].z, ss);
-        ss = fmaf(v[g][c].w, v[g][c].w, ss);
+        ss = fmaf(r.v[g][c].x, r.v[g][c].x, ss);
+        ss = fmaf(r.v[g][c].y, r.v[g][c].y, ss);
+        ss = fmaf(r.v[g][c].z, r.v[g][c].z, ss);
+        ss = fmaf(r.v[g][c].w, r.v[g][c].w, ss);
       }
     }
     ss = wave_sum(ss);
@@ -156,14 +194,22 @@ __device__ __forceinline__ void norm_group(const float* h, int ld, int d, const 
       const int e4 = threadIdx.x + c * NT;
       if (e4 < d4) {
         const float4 gv = reinterpret_cast<const float4*>(gain)[e4];
-        o[4 * e4 + 0] = Elt<OT>::from_f(v[g][c].x * scale * gv.x);
-        o[4 * e4 + 1] = Elt<OT>::from_f(v[g][c].y * scale * gv.y);
-        o[4 * e4 + 2] = Elt<OT>::from_f(v[g][c].z * scale * gv.z);
-        o[4 * e4 + 3] = Elt<OT>::from_f(v[g][c].w * scale * gv.w);
+        o[4 * e4 + 0] = Elt<OT>::from_f(r.v[g][c].x * scale * gv.x);
+        o[4 * e4 + 1] = Elt<OT>::from_f(r.v[g][c].y * scale * gv.y);
+        o[4 * e4 + 2] = Elt<OT>::from_f(r.v[g][c].z * scale * gv.z);
+        o[4 * e4 + 3] = Elt<OT>::from_f(r.v[g][c].w * scale * gv.w);
       }
     }
   }
   __syncthreads();
+}
+
+template <int NT, int G, typename OT>
+__device__ __forceinline__ void norm_group(const float* h, int ld, int d, const float* gain, float eps, OT* out,
+                                           int ldo, float (*red)[8]) {
+  NormRegs<NT, G> r;
+  norm_issue<NT, G>(h, ld, d, r);
+  norm_commit<NT, G>(r, d, gain, eps, out, ldo, red);
 }
 
 // RMSNorm of M (1..8, a compile-time count) rows: one round trip for M <= 5,

@@ -28,7 +28,7 @@ template <int EPI> struct Cfg;
 template <> struct Cfg<EPI_SWIGLU> { static constexpr int R = 1, U = 4, WPE = 4, BPC = 1, NT = 1024; };
 template <> struct Cfg<EPI_STORE> { static constexpr int R = 4, U = 4, WPE = 2, BPC = 1, NT = 256; };
 template <> struct Cfg<EPI_PARTIAL> { static constexpr int R = 1, U = 4, WPE = 4, BPC = 1, NT = 1024; };
-template <> struct Cfg<EPI_RESID> { static constexpr int R = 2, U = 8, WPE = 2, BPC = 2, NT = 256; };
+template <> struct Cfg<EPI_RESID> { static constexpr int R = 1, U = 4, WPE = 4, BPC = 1, NT = 1024; };
 template <> struct Cfg<EPI_QKV> { static constexpr int R = 2, U = 4, WPE = 4, BPC = 1, NT = 768; };
 
 template <typename WT> constexpr int step_elems() { return kWave * (16 / static_cast<int>(sizeof(WT))); }
@@ -103,6 +103,8 @@ hipError_t launch_all(const GemvArgs& a0, int M, hipStream_t s) {
   b.K /= b.ksplit;  // the kernel sees one slice
   if (b.K % VE || b.ldw % VE || b.ldx % VE) return hipErrorInvalidValue;
   if (EPI == EPI_QKV && (b.N % 2 || b.hd % 2)) return hipErrorInvalidValue;
+  // the normalising prologue reads whole residual rows: one K slice, GEMV path
+  if (b.hn && (b.ksplit != 1 || M > 8 || b.K % 4)) return hipErrorInvalidValue;
   if (std::is_same<WT, uint16_t>::value && M > 8 && b.K % mfma::KB == 0 && (EPI != EPI_QKV || b.hd == 128))
     return launch_gemm<EPI>(b, M, s);
   const size_t kp = static_cast<size_t>((b.K + STEP - 1) / STEP) * STEP;
@@ -114,7 +116,8 @@ hipError_t launch_all(const GemvArgs& a0, int M, hipStream_t s) {
     const int mb = std::min(blk, M - m0);
     a.M = mb;
     a.row0 = b.row0 + m0;
-    a.x = static_cast<const WT*>(b.x) + static_cast<size_t>(m0) * b.ldx;
+    if (b.x) a.x = static_cast<const WT*>(b.x) + static_cast<size_t>(m0) * b.ldx;
+    if (b.hn) a.hn = b.hn + static_cast<size_t>(m0) * b.K;
     if (a.y) a.y = b.y + static_cast<size_t>(m0) * b.ldy;
     if (a.z) a.z = static_cast<WT*>(b.z) + static_cast<size_t>(m0) * b.ldz;
     hipError_t e = launch_rows<WT, EPI>(a, mb, s);

@@ -16,8 +16,9 @@
 //    and up rows) as one continuous stream of 1 KiB steps: 64 lanes x 16 B of
 //    one weight row per load instruction.  A ring of U register slots keeps
 //    U * R loads per lane in flight across tile boundaries, so the stream only
-//    drains at the very end of the matrix.  The first U steps are issued
-//    before the activations are staged.
+//    drains at the very end of the matrix.  The activation rows are loaded
+//    first and the first U weight steps right behind them (vector loads
+//    complete in issue order), so staging overlaps the weight stream.
 //  * bf16: v_dot2_f32_bf16 multiplies two bf16 pairs and accumulates in
 //    float32 without converting the weights; float32 models use fma.
 //  * At the end of a tile: one wave reduction per (row, activation row) and
@@ -206,6 +207,29 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE))) void 
     for (int r = 0; r < NW; ++r) dst[r] = load_stream(p[r] + k);
   };
 
+  // Prologue.  Vector loads complete in issue order, so the activation loads
+  // go first: the rows arrive, are normalised or copied into LDS while the
+  // first U steps of weights are still in flight behind them.
+  // (bf16: x chunks per thread loaded ahead of the weights, 32 registers; the
+  // float32 kernels keep their registers for the 4-fma dot products)
+  constexpr bool kBf16 = sizeof(WT) == 2;
+  constexpr int XR = kBf16 ? 8 : 1;
+  constexpr bool kEarlyNorm = kBf16 && M * NormRegs<NT, M>::CPT <= 10;  // 40 registers at most
+  __shared__ float red[NT / kWave][8];
+  NormRegs<NT, kEarlyNorm ? M : 1> nr;
+  uint4 xr[XR];
+  const int xkv = K / VE, xkpv = KP / VE, xtot = M * xkpv;
+  const WT* xg = a.hn ? nullptr : static_cast<const WT*>(a.x) + static_cast<size_t>(slice) * K;
+  if (a.hn) {
+    if constexpr (kEarlyNorm) norm_issue<NT, M>(a.hn, K, K, nr);
+  } else {
+#pragma unroll
+    for (int c = 0; c < XR; ++c) {
+      const int idx = min(static_cast<int>(threadIdx.x) + c * NT, xtot - 1);
+      const int m = idx / xkpv, v = min(idx - m * xkpv, xkv - 1);
+      xr[c] = reinterpret_cast<const uint4*>(xg + static_cast<size_t>(m) * a.ldx)[v];
+    }
+  }
   uint4 wv[U][NW];
   if (my_tiles > 0) {
     set_rows(gw, cur);
@@ -215,13 +239,26 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE))) void 
   if (a.hn) {
     // x = cvt(RMSNorm(h) * gain), made in LDS (one K slice: K = d); the
     // padding columns K .. KP-1 are zero
-    norm_rows<NT, M>(a.hn, K, K, a.gain, a.eps, xs, KP);
+    if constexpr (kEarlyNorm) {
+      norm_commit<NT, M>(nr, K, a.gain, a.eps, xs, KP, red);
+    } else {
+      norm_rows<NT, M>(a.hn, K, K, a.gain, a.eps, xs, KP);
+    }
     for (int idx = threadIdx.x; idx < M * (KP - K); idx += NT) {
       const int m = idx / (KP - K);
       xs[static_cast<size_t>(m) * KP + K + (idx - m * (KP - K))] = Elt<WT>::from_f(0.f);
     }
   } else {
-    stage_x<WT, M, NT>(static_cast<const WT*>(a.x) + static_cast<size_t>(slice) * K, a.ldx, K, xs, KP);
+#pragma unroll
+    for (int c = 0; c < XR; ++c) {
+      const int idx = threadIdx.x + c * NT;
+      if (idx < xtot) reinterpret_cast<uint4*>(xs)[idx] = (idx % xkpv < xkv) ? xr[c] : make_uint4(0, 0, 0, 0);
+    }
+    for (int idx = threadIdx.x + XR * NT; idx < xtot; idx += NT) {
+      const int m = idx / xkpv, v = idx - m * xkpv;
+      reinterpret_cast<uint4*>(xs)[idx] =
+          (v < xkv) ? reinterpret_cast<const uint4*>(xg + static_cast<size_t>(m) * a.ldx)[v] : make_uint4(0, 0, 0, 0);
+    }
   }
   __syncthreads();
 

@@ -127,4 +127,42 @@ hipError_t launch_reject(int B, int gamma, int vocab, const float* p, const floa
                          const float* u_acc, const float* u_res, int32_t* n_accepted, int32_t* emitted,
                          int32_t* len_commit, unsigned long long* csum, hipStream_t s);
 
+// ---- the persistent pass (fused_pass.hip) -----------------------------------------
+// One cooperative launch runs every layer and the LM head of a pass of at
+// most 8 rows (bf16 models), after launch_embed; the caller sizes `bar` to
+// kFusedBarrierWords words and zeroes them before each launch (launch_embed
+// does, as part of its tickets).
+struct FusedLayer {
+  const void* wqkv;
+  const void* wo;
+  const void* wgu;
+  const void* wd;
+  const float* attn_norm;
+  const float* mlp_norm;
+};
+struct FusedArgs {
+  const FusedLayer* layers;  // device table [L]
+  const void* lm_head;
+  const float* final_norm;
+  int d, H, Hkv, F, V, L;
+  float eps;
+  int B, m;
+  void* kc;
+  void* vc;
+  const int32_t* len;
+  int kvB, max_ctx;
+  const float2* cs;  // RoPE table [M][hd/2] (launch_embed)
+  const void* xn;    // first layer's normalised input [M][d] (launch_embed)
+  float* h;          // residual rows [M][d] (launch_embed)
+  float* q;          // rotated queries [M][H hd]
+  void* xo;          // attention output [M][H hd]
+  void* z;           // SwiGLU output [M][F]
+  float* logits;     // [M][V]
+  unsigned* bar;     // barrier counters, zero at launch
+  int* err;          // set to 1 when a barrier wait times out
+};
+constexpr int kFusedBarrierWords = 8 * 64;
+bool fused_pass_supported(bool bf16, int rows, int d, int H, int Hkv, int hd, int F);
+hipError_t launch_fused_pass(const FusedArgs& a, int hd, hipStream_t s);
+
 }  // namespace sv

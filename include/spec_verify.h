@@ -211,6 +211,31 @@ spec_status spec_commit_round(int32_t B, int32_t gamma, const int32_t* n_accepte
                               int32_t* tok2, int32_t* last, int32_t* out_tokens, int32_t* out_len, int32_t cap,
                               hipStream_t stream);
 
+/* Prompt lookup on the device: the n-gram drafter ("05 · Speculative
+ * Decoding", section "The three proposers"; first page, section "Checking
+ * it on a real system", method "ngram").  For sequence b the context is
+ * prefix[b][0 .. prefix_len[b]) followed by out[b][0 .. min(out_len[b], cap)).
+ * The most recent earlier occurrence of its last n tokens (the match may not
+ * be the suffix itself) proposes the up to gamma tokens that followed it,
+ * stopping at the end of the context; no occurrence (or a context shorter
+ * than n + 1) proposes nothing.  The proposal is one-hot: verify it with
+ * q = NULL.
+ *   prefix     [B][P] ids, row stride P (the prompt, or everything committed
+ *              before `out` started); prefix_len [B] or NULL for P.
+ *   out, out_len, cap  as maintained by spec_commit_round.
+ *   fill_off   [B] or NULL.  When given, a proposal shorter than gamma is
+ *              padded with prefix[b][fill_off[b] ...] (indexes clamped into
+ *              the row) so that every sequence proposes gamma tokens.
+ *   drafts     [B][gamma] out (entries past n_draft[b] are -1);
+ *   n_draft    [B] out: tokens proposed (gamma when fill_off is given);
+ *   n_found    [B] out or NULL: tokens that came from the lookup.
+ * Limits: 1 <= n <= 16, 0 <= gamma <= 63.  Deterministic.
+ * Errors: SPEC_EINVAL, SPEC_EHIP. */
+spec_status spec_ngram_propose(int32_t B, int32_t n, int32_t gamma, const int32_t* prefix, const int32_t* prefix_len,
+                               int32_t P, const int32_t* out, const int32_t* out_len, int32_t cap,
+                               const int32_t* fill_off, int32_t* drafts, int32_t* n_draft, int32_t* n_found,
+                               hipStream_t stream);
+
 /* KV length bookkeeping: len[b] = (src ? src[b] : len[b]) + add for b < B.
  * Used to advance after prefill / draft passes and to rewind a drafter to the
  * target's length.  Errors: SPEC_EINVAL, SPEC_EHIP. */

@@ -7,8 +7,8 @@ import numpy as np
 import pytest
 
 from draft_then_verify_amd import binding as bd
-from draft_then_verify_amd.runner import ModelDrafter, SpecDecoder
-from synth import SHAPES, make_prompt, make_weights
+from draft_then_verify_amd.runner import DeviceNgramDrafter, ModelDrafter, NgramDrafter, SpecDecoder
+from synth import SHAPES, make_markov_table, make_prompt, make_weights, markov_prompt
 from tests._gpu import to_dev
 
 pytestmark = pytest.mark.gpu
@@ -60,3 +60,31 @@ def test_greedy_speculation_equals_greedy_decoding():
     plain = _pair(shape, B=2, g=0, P=48, N=40, seed=404, draft_layers=0, T=0.0)
     assert spec[1]["tokens"] == plain[0]["tokens"]
     assert spec[1]["rounds"] <= plain[0]["rounds"]
+
+
+@pytest.mark.parametrize("B", [1, 4])
+def test_graph_rounds_device_ngram_equal_host_ngram(B):
+    """Prompt lookup on the device inside the replayed rounds proposes what
+    the host lookup does, so the two generations emit the same tokens: the
+    copy-heavy workload's shape (trigram lookup, gamma = 10, order-2 Markov
+    prompts, misses padded from a seeded prompt offset, one-hot q) on the
+    second workload's body with a 151936-entry vocabulary, two layers."""
+    shape = SHAPES["small_v151936"].with_(n_layers=2)
+    w = make_weights(shape, seed=406)
+    P, g, N = 256, 10, 48
+    max_ctx = P + N + g + 4
+    table = make_markov_table(seed=406)
+    prompt = markov_prompt(B, P, table, seed=407).astype(np.int64)
+    offs = np.random.default_rng(408).integers(0, P - g - 1, size=B)
+    target = bd.SpecModel(shape, to_dev(w))
+    outs = []
+    for mode in ("host", "device"):
+        if mode == "host":
+            drafter = NgramDrafter(B, g, n=3, fill=lambda b, L, k: [int(t) for t in prompt[b, offs[b]:offs[b] + k]])
+        else:
+            drafter = DeviceNgramDrafter(B, g, n=3, fill_off=offs)
+        dec = SpecDecoder(target, B, g, max_ctx, drafter=drafter, seed=406)
+        dec.prefill(prompt)
+        outs.append(dec.generate(N) if mode == "host" else dec.generate_graph(N))
+    assert outs[0]["tokens"] == outs[1]["tokens"]
+    assert outs[0]["rounds"] <= outs[1]["rounds"] <= outs[0]["rounds"] + 1

@@ -21,6 +21,12 @@ Qwen3-0.6B-shaped draft, B = 1, gamma = 4, a 256-token prompt, 256 new tokens.
 * ``roofline.traffic``: HBM bytes per launch from the committed counter
   passes (FETCH_SIZE, WRITE_SIZE, scaled by a 1 GiB copy's counts), null when
   the kernel sources changed since.
+* ``batch_sweep``: speculative vs plain emitted tok/s for B in {1, 8, 64,
+  256} on the second workload's target and 2-layer drafter (gamma = 4,
+  256-token prompts).
+* ``division_check_gamma1``: the gamma = 1 division of the M1 Max page,
+  predicted (1 + p) T_decode / (T_verify + T_draft) against the measured
+  speculative/plain ratio, on the same shapes.
 """
 
 from __future__ import annotations
@@ -130,6 +136,177 @@ def cpu_baseline(shape, w_gpu, prompt_len: int, layers: int) -> dict:
                       f"{prompt_len - 1}+: {nbytes / 1e9:.3f} GB of algorithmic bytes in {dt:.2f} s"}
 
 
+def time_verify_step(target, shape, prompt, B: int, g: int, steps: int, warmup: int, max_ctx: int,
+                     graph: bool = True, seed: int = 6):
+    """Mean time of one spec_decode_step (B x (g+1) rows: the verify pass,
+    softmax, accept/resample/bonus, KV commit) on seeded random drafts and
+    draft rows, after a prefill of the prompt; graph-replayed unless graph
+    is False.  Returns (ms, mean keys attended, context note, graphed)."""
+    import numpy as np
+    import torch
+
+    from draft_then_verify_amd import binding as bd
+    from draft_then_verify_amd.runner import SpecDecoder
+    from synth import round_uniforms
+
+    dev = torch.device("cuda:0")
+    dec = SpecDecoder(target, B, g, max_ctx, drafter=None, seed=seed)
+    dec.prefill(prompt)
+    V = shape.vocab
+    rng = np.random.default_rng(8)
+    last = torch.as_tensor(prompt[:, -1].astype(np.int32)).cuda()
+    drafts = torch.as_tensor(rng.integers(0, V, size=(B, max(g, 1))).astype(np.int32)).cuda()
+    q = None
+    if g:
+        qlog = torch.randn((B * g, V), device=dev)
+        q = torch.empty_like(qlog)
+        sws = bd.workspace(bd.spec_sampler_workspace_bytes(B * g, B, V))
+        bd.spec_softmax_pq(qlog, B * g, V, 1.0, q, sws)
+    u = round_uniforms(seed, 0, B, g)
+    u_acc = torch.as_tensor(u["u_acc"]).cuda() if g else None
+    u_res = torch.as_tensor(u["u_res"]).cuda()
+    n = torch.empty(B, dtype=torch.int32, device=dev)
+    em = torch.empty((B, g + 1), dtype=torch.int32, device=dev)
+
+    def step():
+        bd.spec_decode_step(target, dec.kv, B, g, 1.0, last, drafts if g else None, None, q, u_acc, u_res, n, em,
+                            None, dec.ws)
+
+    len_before_warm = int(dec.kv.len[0])
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    cg = None
+    if graph:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step()  # one eager call on the capture stream before capturing
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        cg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(cg):
+            step()
+        torch.cuda.synchronize()
+    len0 = int(dec.kv.len[0])
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(steps):
+        if cg is not None:
+            cg.replay()
+        else:
+            step()
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    len1 = int(dec.kv.len[0])
+    # keys attended per step: len + m at each step; len grows by n + 1 per step
+    ctx_mean = (len0 + len1) / 2.0 + g + 1 - 0.5 * (len1 - len0) / steps
+    del dec
+    return ms, ctx_mean, f"{len0}->{len1} (warmup from {len_before_warm})", cg is not None
+
+
+def batch_sweep(n_new: int, batches=(1, 8, 64, 256), P: int = 256, g: int = 4) -> list:
+    """The batch sweep on the second workload's shapes: the 8-layer bf16 target
+    with its first 2 layers as the drafter, gamma = 4, P-token random prompts,
+    n_new tokens per sequence; speculative vs plain emitted tok/s per B
+    (graph-replayed rounds; aggregate over the B sequences)."""
+    import torch
+
+    from draft_then_verify_amd import binding as bd
+    from draft_then_verify_amd.runner import ModelDrafter, SpecDecoder
+    from synth import SHAPES, make_prompt, make_weights
+
+    sh = SHAPES["small"]
+    w = make_weights(sh, seed=21, device="cuda")
+    dsh = sh.with_(n_layers=2)
+    wd = {k: (v[:2] if k in ("attn_norm", "wqkv", "wo", "mlp_norm", "wgu", "wd") else v) for k, v in w.items()}
+    target, draft = bd.SpecModel(sh, w), bd.SpecModel(dsh, wd)
+    rows = []
+    for B in batches:
+        prompt = make_prompt(B, P, sh.vocab, seed=22 + B)
+        max_ctx = P + n_new + g + 4
+        spec = SpecDecoder(target, B, g, max_ctx, drafter=ModelDrafter(draft, B, g, max_ctx), seed=23)
+        spec.prefill(prompt)
+        rs = spec.generate_graph(n_new)
+        del spec
+        plain = SpecDecoder(target, B, 0, max_ctx, seed=24)
+        plain.prefill(prompt)
+        rp = plain.generate_graph(n_new)
+        del plain
+        torch.cuda.empty_cache()
+        rows.append({"B": B, "spec_tok_s": round(rs["tok_s"], 1), "plain_tok_s": round(rp["tok_s"], 1),
+                     "spec_over_plain": round(rs["tok_s"] / rp["tok_s"], 3),
+                     "mean_acceptance_length": round(rs["mean_acceptance_length"], 3)})
+        log(f"sweep B={B}: speculative {rs['tok_s']:.0f} tok/s, plain {rp['tok_s']:.0f} tok/s, "
+            f"ratio {rs['tok_s'] / rp['tok_s']:.3f}, MAL {rs['mean_acceptance_length']:.2f}")
+    return rows
+
+
+def time_draft(drafter, kv_len, B: int, g: int, steps: int = 20) -> float:
+    """Mean time of the drafter's work for one round (its passes, softmax
+    and draws), graph-replayed; the drafter rewinds to kv_len - 1 each time."""
+    import torch
+
+    u = torch.full((g, B), 0.5, device="cuda")
+    tok2 = torch.zeros((B, 2), dtype=torch.int32, device="cuda")
+    drafter.draft(tok2, kv_len, u)
+    torch.cuda.synchronize()
+    cg = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(cg):
+        drafter.draft(tok2, kv_len, u)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        cg.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def division_check(n_new: int, P: int = 256) -> dict:
+    """The gamma = 1 division of the M1 Max page (section 2): the speedup
+    predicted from separately measured parts, (1 + p) T_decode / (T_verify +
+    T_draft), against the measured ratio of emitted tok/s, on the second
+    workload's target and 2-layer drafter.  T_decode is a plain graph-replayed
+    round, T_verify a graph-replayed decode step with 2 rows, T_draft the
+    drafter's round on its own, p the acceptance rate of the speculative run."""
+    from draft_then_verify_amd import binding as bd
+    from draft_then_verify_amd.runner import ModelDrafter, SpecDecoder
+    from synth import SHAPES, make_prompt, make_weights
+
+    sh = SHAPES["small"]
+    w = make_weights(sh, seed=31, device="cuda")
+    dsh = sh.with_(n_layers=2)
+    wd = {k: (v[:2] if k in ("attn_norm", "wqkv", "wo", "mlp_norm", "wgu", "wd") else v) for k, v in w.items()}
+    target, draft = bd.SpecModel(sh, w), bd.SpecModel(dsh, wd)
+    B, g = 1, 1
+    prompt = make_prompt(B, P, sh.vocab, seed=32)
+    max_ctx = P + n_new + 64
+    drafter = ModelDrafter(draft, B, g, max_ctx)
+    spec = SpecDecoder(target, B, g, max_ctx, drafter=drafter, seed=33)
+    spec.prefill(prompt)
+    t_draft = time_draft(drafter, spec.kv.len, B, g)
+    rs = spec.generate_graph(n_new)
+    plain = SpecDecoder(target, B, 0, max_ctx, seed=34)
+    plain.prefill(prompt)
+    rp = plain.generate_graph(n_new)
+    t_decode = 1e3 * rp["wall_s"] / rp["rounds"]
+    t_verify, _, _, _ = time_verify_step(target, sh, prompt, B, g, 20, 5, max_ctx)
+    p = rs["acceptance_rate"]
+    predicted = (1 + p) * t_decode / (t_verify + t_draft)
+    measured = rs["tok_s"] / rp["tok_s"]
+    out = {"T_decode_ms": round(t_decode, 4), "T_verify_ms": round(t_verify, 4), "T_draft_ms": round(t_draft, 4),
+           "round_ms": round(1e3 * rs["wall_s"] / rs["rounds"], 4), "p": round(p, 4),
+           "predicted_speedup": round(predicted, 4), "measured_speedup": round(measured, 4),
+           "relative_error": round(predicted / measured - 1, 4)}
+    log(f"division check (gamma=1): T_decode {t_decode:.3f} ms, T_verify {t_verify:.3f} ms, T_draft {t_draft:.3f} ms, "
+        f"p {p:.3f}: predicted {predicted:.3f}, measured {measured:.3f}")
+    return out
+
+
 def kernel_only(reps: int) -> None:
     """Launch only the dominant kernel (gate/up GEMV over the 36 layers'
     weights, `reps` times), then a 1 GiB fill (known write bytes) and a sum
@@ -170,6 +347,8 @@ def main():
                     help="launch only the dominant kernel and a calibration copy (for counter passes)")
     ap.add_argument("--skip-generate", action="store_true", help="skip the emitted tok/s generations")
     ap.add_argument("--skip-cpu", action="store_true", help="skip the CPU-baseline leg")
+    ap.add_argument("--skip-sweep", action="store_true",
+                    help="skip the batch sweep and the gamma = 1 division check (second workload's shapes)")
     ap.add_argument("--graph", type=int, default=1, help="time graph replays of the decode step (1) or eager calls (0)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -180,12 +359,11 @@ def main():
         kernel_only(2)
         return
 
-    import numpy as np
     import torch
 
     from draft_then_verify_amd import binding as bd
     from draft_then_verify_amd.runner import ModelDrafter, SpecDecoder
-    from synth import SHAPES, make_prompt, make_weights, round_uniforms
+    from synth import SHAPES, make_prompt, make_weights
 
     bd.load_library()
     dev = torch.device("cuda:0")
@@ -203,59 +381,11 @@ def main():
     prompt = make_prompt(B, P, tshape.vocab, seed=5)
 
     # ---- timed verify steps --------------------------------------------------------
-    dec = SpecDecoder(target, B, g, max_ctx, drafter=None, seed=6)
-    dec.prefill(prompt)
-    V = tshape.vocab
-    rng = np.random.default_rng(8)
-    last = torch.as_tensor(prompt[:, -1].astype(np.int32)).cuda()
-    drafts = torch.as_tensor(rng.integers(0, V, size=(B, g)).astype(np.int32)).cuda()
-    qlog = torch.randn((B * g, V), device=dev)
-    q = torch.empty_like(qlog)
-    sws = bd.workspace(bd.spec_sampler_workspace_bytes(B * g, B, V))
-    bd.spec_softmax_pq(qlog, B * g, V, 1.0, q, sws)
-    u = round_uniforms(6, 0, B, g)
-    u_acc, u_res = torch.as_tensor(u["u_acc"]).cuda(), torch.as_tensor(u["u_res"]).cuda()
-    n = torch.empty(B, dtype=torch.int32, device=dev)
-    em = torch.empty((B, g + 1), dtype=torch.int32, device=dev)
-
-    def step():
-        bd.spec_decode_step(target, dec.kv, B, g, 1.0, last, drafts, None, q, u_acc, u_res, n, em, None, dec.ws)
-
-    len_before_warm = int(dec.kv.len[0])
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    graph = None
-    if args.graph:
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            step()  # one eager call on the capture stream before capturing
-        torch.cuda.current_stream().wait_stream(s)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            step()
-        torch.cuda.synchronize()
-    len0 = int(dec.kv.len[0])
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record()
-    for _ in range(args.steps):
-        if graph is not None:
-            graph.replay()
-        else:
-            step()
-    ev1.record()
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1) / args.steps
-    len1 = int(dec.kv.len[0])
-    # keys attended per step: len + m at each step; len grows by n + 1 per step
-    ctx_mean = (len0 + len1) / 2.0 + g + 1 - 0.5 * (len1 - len0) / args.steps
+    ms, ctx_mean, len_info, graphed = time_verify_step(target, tshape, prompt, B, g, args.steps, args.warmup,
+                                                       max_ctx, bool(args.graph))
     nbytes = verify_pass_bytes(tshape, B, g + 1, int(round(ctx_mean)))
     gbs = nbytes / (ms / 1e3) / 1e9
-    log(f"decode step: {ms:.3f} ms, {gbs:.1f} GB/s ({100 * gbs / PEAK_HBM_GBS:.1f}% of peak), "
-        f"context {len0}->{len1} (warmup from {len_before_warm})")
+    log(f"decode step: {ms:.3f} ms, {gbs:.1f} GB/s ({100 * gbs / PEAK_HBM_GBS:.1f}% of peak), context {len_info}")
 
     # ---- dominant kernel: SwiGLU gate/up GEMV over every layer's weights --------------
     F, d = tshape.d_ff, tshape.d_model
@@ -298,6 +428,11 @@ def main():
                "generation": "graph-replayed rounds (drafter passes, verify step and bookkeeping on the device)"}
         del plain
 
+    sweep = division = None
+    if not args.skip_sweep:
+        sweep = batch_sweep(args.new_tokens)
+        division = division_check(args.new_tokens)
+
     cpu = None
     if not args.skip_cpu:
         t1 = time.perf_counter()
@@ -310,7 +445,7 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded random-init weights and prompts)",
         "config": {"workload": "qwen3_8b-shaped target, qwen3_0p6b-shaped draft, B=1, gamma=4, prompt 256, "
                                "256 new tokens", "B": B, "gamma": g, "prompt_len": P,
-                   "context_mean": round(ctx_mean, 1), "graph_replay": bool(graph is not None)},
+                   "context_mean": round(ctx_mean, 1), "graph_replay": graphed},
         "pct_of_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
         "verified_positions_per_s": round(B * (g + 1) / (ms / 1e3), 1),
         "bytes_per_step": nbytes,
@@ -320,6 +455,8 @@ def main():
                      "kernel": "gemv_kernel SwiGLU, W_gu [24576, 4096] bf16, M=5",
                      "us_per_launch": round(k_us, 2), "bytes_per_launch": k_bytes},
         "cpu_baseline": cpu,
+        "batch_sweep": sweep,
+        "division_check_gamma1": division,
     }
     print(json.dumps(out), flush=True)
 

@@ -109,9 +109,39 @@ __device__ __forceinline__ void stage_x(const WT* x, int ldx, int K, WT* xs, int
   }
 }
 
+// Values the epilogue of tile t reads from memory, loaded when the tile
+// starts so that the loads are back by its end: the RoPE (cos, sin) and the
+// cache position of lane m's row (QKV), or the residual value the lane adds
+// to (EPI_RESID).  A lane that writes nothing loads nothing.
+struct EpiPre {
+  float2 cs = make_float2(0.f, 0.f);
+  int pos = -1;
+  float y = 0.f;
+};
+
+template <typename WT, int M, int R, int EPI>
+__device__ __forceinline__ EpiPre epilogue_pre(const GemvArgs& a, const float* y, int t, int lane) {
+  EpiPre e;
+  if constexpr (EPI == EPI_QKV) {
+    if (lane < M) {
+      const int half = a.hd / 2;
+      const int hh = t / half, j = t - hh * half;
+      const int rg = a.row0 + lane;
+      const int b = rg / a.m_per_seq, i = rg - b * a.m_per_seq;
+      if (hh < a.H + a.Hkv) e.cs = a.cs[static_cast<size_t>(rg) * half + j];
+      if (hh >= a.H) e.pos = a.len[b] + i;
+    }
+  } else if constexpr (EPI == EPI_RESID) {
+    const int r = lane / M, m = lane - r * M;
+    const int c = t * R + r;
+    if (r < R && c < a.N) e.y = y[static_cast<size_t>(m) * a.ldy + c];
+  }
+  return e;
+}
+
 template <typename WT, int M, int R, int EPI>
 __device__ __forceinline__ void epilogue(const GemvArgs& a, float* y, int t, float (&acc)[Tiles<EPI, R>::NW][M],
-                                         int lane) {
+                                         int lane, const EpiPre& pre) {
   if constexpr (EPI == EPI_QKV) {
 #pragma unroll
     for (int m = 0; m < M; ++m) {
@@ -119,17 +149,17 @@ __device__ __forceinline__ void epilogue(const GemvArgs& a, float* y, int t, flo
       const int H = a.H, Hkv = a.Hkv, hd = a.hd, half = hd / 2;
       const int hh = t / half, j = t - hh * half;
       const int rg = a.row0 + m;
-      const int b = rg / a.m_per_seq, i = rg - b * a.m_per_seq;
+      const int b = rg / a.m_per_seq;
       const float x0 = acc[0][m], y0 = acc[1][m];
       if (hh < H + Hkv) {
-        const float2 c = a.cs[static_cast<size_t>(rg) * half + j];
+        const float2 c = pre.cs;
         const float r0 = x0 * c.x - y0 * c.y, s0 = y0 * c.x + x0 * c.y;
         if (hh < H) {
           float* qr = a.q + static_cast<size_t>(rg) * (H * hd) + hh * hd;
           qr[j] = r0;
           qr[j + half] = s0;
         } else {
-          const int pos = a.len[b] + i;
+          const int pos = pre.pos;
           if (pos >= 0 && pos < a.max_ctx) {
             WT* dst = static_cast<WT*>(a.kc) +
                       (((static_cast<size_t>(a.layer) * a.kvB + b) * Hkv + (hh - H)) * a.max_ctx + pos) * hd;
@@ -138,7 +168,7 @@ __device__ __forceinline__ void epilogue(const GemvArgs& a, float* y, int t, flo
           }
         }
       } else {
-        const int pos = a.len[b] + i;
+        const int pos = pre.pos;
         if (pos >= 0 && pos < a.max_ctx) {
           WT* dst = static_cast<WT*>(a.vc) +
                     (((static_cast<size_t>(a.layer) * a.kvB + b) * Hkv + (hh - H - Hkv)) * a.max_ctx + pos) * hd;
@@ -157,7 +187,7 @@ __device__ __forceinline__ void epilogue(const GemvArgs& a, float* y, int t, flo
           if constexpr (EPI == EPI_STORE || EPI == EPI_PARTIAL) {
             y[static_cast<size_t>(m) * a.ldy + c] = acc[r][m];
           } else if constexpr (EPI == EPI_RESID) {
-            y[static_cast<size_t>(m) * a.ldy + c] += acc[r][m];
+            y[static_cast<size_t>(m) * a.ldy + c] = pre.y + acc[r][m];
           } else {
             const float g = acc[r][m], u = acc[R + r][m];
             static_cast<WT*>(a.z)[static_cast<size_t>(m) * a.ldz + c] = Elt<WT>::from_f(g / (1.f + expf(-g)) * u);
@@ -277,17 +307,18 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE))) void 
       for (int r = 0; r < NW; ++r) acc[r][m] = Dot<WT>::run(w[r], xv, acc[r][m]);
     }
   };
-  auto finish = [&](int t) {
+  auto finish = [&](int t, const EpiPre& pre) {
 #pragma unroll
     for (int r = 0; r < NW; ++r)
 #pragma unroll
       for (int m = 0; m < M; ++m) acc[r][m] = wave_sum(acc[r][m]);
-    epilogue<WT, M, R, EPI>(a, y, t, acc, lane);
+    epilogue<WT, M, R, EPI>(a, y, t, acc, lane, pre);
   };
 
   for (int ti = 0; ti < my_tiles; ++ti) {
     const int t = gw + ti * TW;
     const bool more = ti + 1 < my_tiles;
+    const EpiPre pre = epilogue_pre<WT, M, R, EPI>(a, y, t, lane);
     if (more) set_rows(t + TW, nxt);
 #pragma unroll
     for (int r = 0; r < NW; ++r)
@@ -312,7 +343,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE))) void 
 #pragma unroll
       for (int u = 0; u < U; ++u) compute(S - U + u, wv[u]);
     }
-    finish(t);
+    finish(t, pre);
     if (more) {
 #pragma unroll
       for (int r = 0; r < NW; ++r) cur[r] = nxt[r];

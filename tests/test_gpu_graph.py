@@ -88,3 +88,14 @@ def test_graph_rounds_device_ngram_equal_host_ngram(B):
         outs.append(dec.generate(N) if mode == "host" else dec.generate_graph(N))
     assert outs[0]["tokens"] == outs[1]["tokens"]
     assert outs[0]["rounds"] <= outs[1]["rounds"] <= outs[0]["rounds"] + 1
+
+
+def test_graph_rounds_persistent_pass(monkeypatch):
+    """With SPEC_FUSED=1 the bf16 passes of at most 8 rows run as the
+    persistent launch: cooperative when eager, an ordinary launch under graph
+    capture.  The two generations must emit the same tokens (the launch is
+    deterministic).  Its logits differ from the launch-per-step path's in the
+    last bits (other reduction orders), so draws near a CDF boundary may
+    differ from that path; test_gpu_forward holds both to the oracle."""
+    monkeypatch.setenv("SPEC_FUSED", "1")
+    _pair(SHAPES["small"], B=1, g=4, P=40, N=32, seed=409, draft_layers=2)

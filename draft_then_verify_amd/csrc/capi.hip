@@ -157,7 +157,7 @@ spec_status run_forward(const spec_model* M, const spec_kv* kv, int B, int m, co
     fa.q = reinterpret_cast<float*>(ws + L.q);
     fa.xo = ws + L.xo;
     fa.z = ws + L.z;
-    fa.logits = logits ? logits : reinterpret_cast<float*>(ws + L.logits);
+    fa.logits = logits;  // NULL: no LM head
     fa.bar = reinterpret_cast<unsigned*>(ctr);
     fa.err = ctr + sv::kFusedBarrierWords;
     HIP_TRY(sv::launch_fused_pass(fa, hd, s));

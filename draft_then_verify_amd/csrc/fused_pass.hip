@@ -575,9 +575,10 @@ __global__ __launch_bounds__(NT) void pass_kernel(PassArgs a) {
     if (l + 1 < a.L) {
       if (!handoff(K2{}, ph_qkv(l + 1), true)) return;
     } else {
-      if (!handoff(K0{}, ph_lm, true)) return;
+      if (!handoff(K0{}, ph_lm, a.logits != nullptr)) return;
     }
   }
+  if (!a.logits) return;  // a pass without the LM head (prefill)
   // final RMSNorm + LM head
   stage_norm<M>(a.h, d, KPd, a.final_norm, a.eps, xs, red);
   __syncthreads();

@@ -162,7 +162,7 @@ struct FusedArgs {
   float* q;          // rotated queries [M][H hd]
   void* xo;          // attention output [M][H hd]
   void* z;           // SwiGLU output [M][F]
-  float* logits;     // [M][V]
+  float* logits;     // [M][V], or NULL to skip the LM head
   unsigned* bar;     // barrier counters, zero at launch
   int* err;          // set to 1 when a barrier wait times out
 };

@@ -127,8 +127,13 @@ size_t spec_sampler_workspace_bytes(int64_t rows, int32_t B, int32_t vocab);
  *   logits  [B][m][vocab] float32 output, or NULL to skip the LM head
  *           (prefill).
  * Writes the m new K/V rows of every layer; len is unchanged (advance it with
- * spec_kv_set_len).  Errors: SPEC_EINVAL (null/size mismatch, kv->B < B),
- * SPEC_ENOMEM (ws_bytes < spec_workspace_bytes), SPEC_EHIP. */
+ * spec_kv_set_len).  With SPEC_FUSED=1 in the environment, passes of at most
+ * 8 rows of bf16 models run as one persistent launch of one workgroup per CU
+ * (cooperative; an ordinary launch under stream capture, which then needs
+ * the device free of other work).  Its grid barriers wait a bounded time, so
+ * a launch whose workgroups cannot all run ends early, leaving its outputs
+ * incomplete, rather than hang.  Errors: SPEC_EINVAL (null/size mismatch,
+ * kv->B < B), SPEC_ENOMEM (ws_bytes < spec_workspace_bytes), SPEC_EHIP. */
 spec_status spec_verify_forward(const spec_model* model, const spec_kv* kv, int32_t B, int32_t m,
                                 const int32_t* tokens, float* logits, void* ws, size_t ws_bytes,
                                 hipStream_t stream);

@@ -138,6 +138,7 @@ def test_long_context_split_kernel():
     ("small", 1, 5, 96, None),             # full 8-layer second-workload target, head_dim 64
     ("h128s", 2, 4, 60, [0, 7]),           # head_dim 128, 4:1 GQA, two ragged sequences, 8 rows
     ("h128s", 1, 1, 130, None),            # one row
+    ("small", 1, 5, 6, None),              # the 5-row prefill also runs fused, without the LM head
 ])
 def test_fused_pass(monkeypatch, case):
     name, B, m, P, back = case

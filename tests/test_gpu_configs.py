@@ -7,9 +7,11 @@ Per round:
 * verify logits within 1e-4 (fp32 models) / 2e-2 (bf16 models) of the
   oracle's own forward pass, probabilities within 1e-5; at the 36-layer 8B
   shape, where the bf16 rounding points amplify sub-ulp differences beyond
-  2e-2 for the oracle against itself, logits, p and the draft's q rows are
+  2e-2 for the oracle against itself, logits and the draft's q rows are
   held to twice the oracle's own spread under a 1e-6 relative perturbation
-  of every linear output (plus the plain bars);
+  of every linear output (plus the plain bars), and p is held to 1e-5 of
+  the exact softmax of the GPU's own logits and, against the oracle's p, to
+  the bound p (exp(2 D) - 1) + 1e-5 that a logit deviation D allows;
 * n and emitted bit-exact against the oracle's rule run on the GPU's own p
   and q rows;
 * against the oracle's own p: identical, except accept decisions with u
@@ -154,10 +156,21 @@ class Replay:
             assert dev.max() < self.tol
         V = logits_g.shape[-1]
         p_g = gpu_softmax(torch.as_tensor(logits_g[r]).cuda(), V).cpu().numpy()
-        pbar = 1e-5
         if self.envelope:
-            pbar = max(pbar, 2 * np.abs(S.softmax(noisy, 1.0) - out["p"]).max())
-        assert np.abs(p_g - out["p"]).max() < pbar
+            # p is a function of the logits: the 1e-5 bar holds against the
+            # exact softmax of the GPU's own logits, and against the oracle's
+            # p the move is bounded by the logits' own deviation D, since
+            # log p = z - logsumexp(z) moves by at most 2 D
+            p_own = S.softmax(logits_g[r].astype(np.float64), 1.0)
+            D = dev.max()
+            dp = np.abs(p_g - out["p"])
+            print(f"p |gpu - softmax(gpu logits)| max {np.abs(p_g - p_own).max():.3g}; |gpu - oracle| max "
+                  f"{dp.max():.3g}, bound from the logits {(out['p'] * np.expm1(2 * D)).max() + 1e-5:.3g}",
+                  flush=True)
+            assert np.abs(p_g - p_own).max() < 1e-5
+            assert np.all(dp <= out["p"] * np.expm1(2 * D) + 1e-5)
+        else:
+            assert np.abs(p_g - out["p"]).max() < 1e-5
         n_own, em_own = S.reject_sample(p_g, qs, drafts[r], nds, u["u_acc"][r], u["u_res"][r])
         assert np.array_equal(n_own, n_g[r]) and np.array_equal(em_own, em_g[r])
         if g > 0:

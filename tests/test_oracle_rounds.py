@@ -3,7 +3,7 @@ import numpy as np
 
 from oracle import model as OM
 from oracle import rounds as R
-from oracle.ngram import ngram_propose
+from oracle.ngram import ngram_propose, ngram_propose_window
 from synth import Shape, make_prompt, make_weights, round_uniforms
 
 SHAPE = Shape("r", 64, 3, 4, 2, 16, 96, 64, "f32")
@@ -94,6 +94,45 @@ def test_ngram_proposer():
     assert ngram_propose([1, 2, 3, 4], 3, 4) == []
     assert ngram_propose([1, 2, 3], 3, 4) == []
     assert ngram_propose(ctx, 3, 0) == []
+
+
+def _window_brute(ctx, n_min, n_max, gamma):
+    """Every (length, start) pair scored as (length, start): the largest wins."""
+    L = len(ctx)
+    best = None
+    for n in range(n_min, n_max + 1):
+        for s in range(0, L - n):
+            if ctx[s:s + n] == ctx[L - n:]:
+                best = max(best or (0, -1), (n, s))
+    if best is None or gamma <= 0:
+        return []
+    n, s = best
+    return ctx[s + n:s + n + gamma]
+
+
+def test_ngram_window_prefers_the_longest_match():
+    # the last 4 tokens occur once (start 0); the last 2 also later (start 6)
+    ctx = [1, 2, 3, 4, 50, 51, 3, 4, 60, 61, 1, 2, 3, 4]
+    assert ngram_propose_window(ctx, 2, 4, 3) == [50, 51, 3]
+    assert ngram_propose(ctx, 2, 3) == [60, 61, 1]
+    assert ngram_propose_window(ctx, 2, 2, 3) == [60, 61, 1]
+    # no length in the window occurs earlier, but a shorter one does
+    assert ngram_propose_window([9, 8, 7, 1, 2, 5, 2], 2, 3, 4) == []
+    assert ngram_propose_window([9, 8, 7, 1, 2, 5, 2], 1, 3, 4) == [5, 2]
+    # a window wider than the context falls through to the lengths that fit
+    assert ngram_propose_window([7, 7], 1, 8, 3) == [7]
+
+
+def test_ngram_window_brute_force():
+    rng = np.random.default_rng(11)
+    for _ in range(400):
+        L = int(rng.integers(1, 30))
+        ctx = [int(t) for t in rng.integers(0, 3, L)]
+        n_min = int(rng.integers(1, 5))
+        n_max = n_min + int(rng.integers(0, 5))
+        g = int(rng.integers(0, 6))
+        assert ngram_propose_window(ctx, n_min, n_max, g) == _window_brute(ctx, n_min, n_max, g)
+        assert ngram_propose_window(ctx, n_min, n_min, g) == ngram_propose(ctx, n_min, g)
 
 
 def test_greedy_speculation_reproduces_greedy_decoding():

@@ -77,7 +77,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "spec_linear": (i32, [i32, i32, vp, vp, i32, i32, i32, vp, vp, vp]),
         "spec_kv_set_len": (i32, [ctypes.POINTER(spec_kv), i32, vp, i32, vp]),
         "spec_commit_round": (i32, [i32, i32, vp, vp, vp, vp, vp, vp, i32, vp]),
-        "spec_ngram_propose": (i32, [i32, i32, i32, vp, vp, i32, vp, vp, i32, vp, vp, vp, vp, vp]),
+        "spec_ngram_propose": (i32, [i32, i32, i32, i32, vp, vp, i32, vp, vp, i32, vp, vp, vp, vp, vp]),
         "spec_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -227,11 +227,11 @@ def spec_commit_round(B: int, gamma: int, n_accepted, emitted, tok2, last, out_t
                                             _ptr(out_tokens), _ptr(out_len), cap, _stream(stream)))
 
 
-def spec_ngram_propose(B: int, n: int, gamma: int, prefix, prefix_len, P: int, out, out_len, cap: int, fill_off,
-                       drafts, n_draft, n_found=None, stream=None):
-    _check(load_library().spec_ngram_propose(B, n, gamma, _ptr(prefix), _ptr(prefix_len), P, _ptr(out), _ptr(out_len),
-                                             cap, _ptr(fill_off), _ptr(drafts), _ptr(n_draft), _ptr(n_found),
-                                             _stream(stream)))
+def spec_ngram_propose(B: int, n_min: int, n_max: int, gamma: int, prefix, prefix_len, P: int, out, out_len,
+                       cap: int, fill_off, drafts, n_draft, n_found=None, stream=None):
+    _check(load_library().spec_ngram_propose(B, n_min, n_max, gamma, _ptr(prefix), _ptr(prefix_len), P, _ptr(out),
+                                             _ptr(out_len), cap, _ptr(fill_off), _ptr(drafts), _ptr(n_draft),
+                                             _ptr(n_found), _stream(stream)))
 
 
 def spec_kv_set_len(kv: KVCache, B: int, src, add: int, stream=None):

@@ -498,19 +498,21 @@ SPEC_API spec_status spec_commit_round(int32_t B, int32_t gamma, const int32_t* 
   return SPEC_OK;
 }
 
-SPEC_API spec_status spec_ngram_propose(int32_t B, int32_t n, int32_t gamma, const int32_t* prefix,
-                                        const int32_t* prefix_len, int32_t P, const int32_t* out,
-                                        const int32_t* out_len, int32_t cap, const int32_t* fill_off,
-                                        int32_t* drafts, int32_t* n_draft, int32_t* n_found, hipStream_t stream) {
+SPEC_API spec_status spec_ngram_propose(int32_t B, int32_t n_min, int32_t n_max, int32_t gamma,
+                                        const int32_t* prefix, const int32_t* prefix_len, int32_t P,
+                                        const int32_t* out, const int32_t* out_len, int32_t cap,
+                                        const int32_t* fill_off, int32_t* drafts, int32_t* n_draft,
+                                        int32_t* n_found, hipStream_t stream) {
   if (B <= 0 || B > 65535) return fail(SPEC_EINVAL, "B=%d (1..65535)", B);
-  if (n < 1 || n > 16) return fail(SPEC_EINVAL, "n=%d (1..16)", n);
+  if (n_min < 1 || n_max < n_min || n_max > 16)
+    return fail(SPEC_EINVAL, "n_min=%d n_max=%d (1 <= n_min <= n_max <= 16)", n_min, n_max);
   if (gamma < 0 || gamma > 63) return fail(SPEC_EINVAL, "gamma=%d (0..63)", gamma);
   if (P < 0 || cap < 0) return fail(SPEC_EINVAL, "P=%d cap=%d", P, cap);
   if ((P > 0 && !prefix) || (cap > 0 && (!out || !out_len)) || !n_draft || (gamma > 0 && !drafts))
     return fail(SPEC_EINVAL, "NULL argument");
   if (fill_off && P == 0) return fail(SPEC_EINVAL, "fill_off needs a prefix");
-  HIP_TRY(sv::launch_ngram(B, n, gamma, prefix, prefix_len, P, out, out_len, cap, fill_off, drafts, n_draft, n_found,
-                           stream));
+  HIP_TRY(sv::launch_ngram(B, n_min, n_max, gamma, prefix, prefix_len, P, out, out_len, cap, fill_off, drafts,
+                           n_draft, n_found, stream));
   return SPEC_OK;
 }
 

@@ -102,7 +102,7 @@ hipError_t launch_commit_round(int B, int gamma, const int32_t* n_acc, const int
                                int32_t* last, int32_t* out, int32_t* out_len, int cap, hipStream_t s);
 
 // Prompt lookup (see spec_ngram_propose).
-hipError_t launch_ngram(int B, int n, int gamma, const int32_t* prefix, const int32_t* prefix_len, int P,
+hipError_t launch_ngram(int B, int n_min, int n_max, int gamma, const int32_t* prefix, const int32_t* prefix_len, int P,
                         const int32_t* out, const int32_t* out_len, int cap, const int32_t* fill_off,
                         int32_t* drafts, int32_t* n_draft, int32_t* n_found, hipStream_t s);
 

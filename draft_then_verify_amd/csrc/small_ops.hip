@@ -147,14 +147,16 @@ __global__ void commit_round_kernel(int B, int gamma, const int32_t* __restrict_
   if (last) last[b] = t;
 }
 
-// Prompt lookup, one workgroup per sequence: every thread tests its share of
-// the candidate starts (the n tokens at s equal the context's last n, s <=
-// L - n - 1), the block keeps the largest such s, and the tokens after it
-// are the proposal (the n-gram drafter of the second page, section "The
-// three proposers").  The context is the prefix row followed by the tokens
-// committed since.
+// Prompt lookup, one workgroup per sequence: for a match length n every
+// thread tests its share of the candidate starts (the n tokens at s equal the
+// context's last n, s <= L - n - 1), the block keeps the largest such s, and
+// the tokens after it are the proposal (the n-gram drafter of the second
+// page, section "The three proposers").  The lengths are tried from n_max
+// down to n_min and the first that occurs is taken (the match window of the
+// same page, section "Dial It In").  The context is the prefix row followed
+// by the tokens committed since.
 constexpr int kNgramThreads = 256;
-__global__ __launch_bounds__(kNgramThreads) void ngram_kernel(int n, int gamma, const int32_t* __restrict__ prefix,
+__global__ __launch_bounds__(kNgramThreads) void ngram_kernel(int n_min, int n_max, int gamma, const int32_t* __restrict__ prefix,
                                                               const int32_t* __restrict__ prefix_len, int P,
                                                               const int32_t* __restrict__ out,
                                                               const int32_t* __restrict__ out_len, int cap,
@@ -171,24 +173,35 @@ __global__ __launch_bounds__(kNgramThreads) void ngram_kernel(int n, int gamma, 
   const int32_t* pre = prefix + static_cast<size_t>(b) * P;
   const int32_t* post = cap > 0 ? out + static_cast<size_t>(b) * cap : nullptr;
   auto tok = [&](int i) { return i < lp ? pre[i] : post[i - lp]; };
-  int best = -1;
-  if (gamma > 0 && L >= n + 1) {
-    if (static_cast<int>(threadIdx.x) < n) key[threadIdx.x] = tok(L - n + threadIdx.x);
+  int best = -1, n = n_min;
+  // L and the block maximum are the same in every thread, so every thread
+  // takes the same trips and the barriers below match.  The barrier after
+  // the key is written also keeps the next trip's best_w writes behind the
+  // last reads of this trip's.
+  for (int nn = n_max; gamma > 0 && nn >= n_min; --nn) {
+    if (L < nn + 1) continue;
+    if (static_cast<int>(threadIdx.x) < nn) key[threadIdx.x] = tok(L - nn + threadIdx.x);
     __syncthreads();
-    for (int s = threadIdx.x; s <= L - n - 1; s += kNgramThreads) {
+    int cand = -1;
+    for (int s = threadIdx.x; s <= L - nn - 1; s += kNgramThreads) {
       bool eq = true;
-      for (int j = 0; j < n && eq; ++j) eq = tok(s + j) == key[j];
-      if (eq) best = max(best, s);
+      for (int j = 0; j < nn && eq; ++j) eq = tok(s + j) == key[j];
+      if (eq) cand = max(cand, s);
+    }
+    // block max of cand, waves in order
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) cand = max(cand, __shfl_xor(cand, off, kWave));
+    if ((threadIdx.x & (kWave - 1)) == 0) best_w[threadIdx.x / kWave] = cand;
+    __syncthreads();
+    cand = best_w[0];
+#pragma unroll
+    for (int w = 1; w < kNgramThreads / kWave; ++w) cand = max(cand, best_w[w]);
+    if (cand >= 0) {
+      best = cand;
+      n = nn;
+      break;
     }
   }
-  // block max of best, waves in order
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) best = max(best, __shfl_xor(best, off, kWave));
-  if ((threadIdx.x & (kWave - 1)) == 0) best_w[threadIdx.x / kWave] = best;
-  __syncthreads();
-  best = best_w[0];
-#pragma unroll
-  for (int w = 1; w < kNgramThreads / kWave; ++w) best = max(best, best_w[w]);
   const int found = best >= 0 ? min(gamma, L - (best + n)) : 0;
   const int total = fill_off ? gamma : found;
   for (int i = threadIdx.x; i < gamma; i += kNgramThreads) {
@@ -243,10 +256,10 @@ hipError_t launch_commit_round(int B, int gamma, const int32_t* n_acc, const int
   return hipGetLastError();
 }
 
-hipError_t launch_ngram(int B, int n, int gamma, const int32_t* prefix, const int32_t* prefix_len, int P,
+hipError_t launch_ngram(int B, int n_min, int n_max, int gamma, const int32_t* prefix, const int32_t* prefix_len, int P,
                         const int32_t* out, const int32_t* out_len, int cap, const int32_t* fill_off,
                         int32_t* drafts, int32_t* n_draft, int32_t* n_found, hipStream_t s) {
-  hipLaunchKernelGGL(ngram_kernel, dim3(B), dim3(kNgramThreads), 0, s, n, gamma, prefix, prefix_len, P, out, out_len,
+  hipLaunchKernelGGL(ngram_kernel, dim3(B), dim3(kNgramThreads), 0, s, n_min, n_max, gamma, prefix, prefix_len, P, out, out_len,
                      cap, fill_off, drafts, n_draft, n_found);
   return hipGetLastError();
 }

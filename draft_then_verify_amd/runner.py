@@ -21,6 +21,7 @@ Plain decoding (the speed baseline) is ``spec_decode_step`` with gamma = 0.
 from __future__ import annotations
 
 import time
+from typing import Optional
 
 import numpy as np
 import torch
@@ -34,17 +35,19 @@ def _dev_i32(a) -> torch.Tensor:
     return torch.as_tensor(np.ascontiguousarray(a, dtype=np.int32)).cuda()
 
 
-def ngram_lookup(context, n: int, gamma: int) -> list:
-    """Tokens that followed the most recent earlier occurrence of the last n
-    context tokens (up to gamma of them); [] when there is none."""
+def ngram_lookup(context, n: int, gamma: int, n_max: Optional[int] = None) -> list:
+    """Tokens that followed the most recent earlier occurrence of the last k
+    context tokens (up to gamma of them), for the longest k in [n, n_max]
+    (n_max defaults to n) that occurs; [] when none does."""
     ctx = list(context)
     L = len(ctx)
-    if gamma <= 0 or L < n + 1:
-        return []
-    key = ctx[L - n:]
-    for start in range(L - n - 1, -1, -1):
-        if ctx[start:start + n] == key:
-            return ctx[start + n:start + n + gamma]
+    for k in range(n if n_max is None else n_max, n - 1, -1):
+        if gamma <= 0 or L < k + 1:
+            continue
+        key = ctx[L - k:]
+        for start in range(L - k - 1, -1, -1):
+            if ctx[start:start + k] == key:
+                return ctx[start + k:start + k + gamma]
     return []
 
 
@@ -96,14 +99,16 @@ class ModelDrafter:
 
 
 class NgramDrafter:
-    """Prompt lookup with match length n.  ``fill`` supplies gamma tokens when
-    the lookup proposes fewer (so every round verifies B x (gamma+1) rows);
-    the strict hit count is kept either way."""
+    """Prompt lookup with match lengths n_max down to n (n_max defaults to n).
+    ``fill`` supplies gamma tokens when the lookup proposes fewer (so every
+    round verifies B x (gamma+1) rows); the strict hit count is kept either
+    way."""
 
     kind = "ngram"
 
-    def __init__(self, B: int, gamma: int, n: int = 3, fill=None):
+    def __init__(self, B: int, gamma: int, n: int = 3, fill=None, n_max: Optional[int] = None):
         self.B, self.gamma, self.n, self.fill = B, gamma, n, fill
+        self.n_max = n if n_max is None else n_max
         self.hits = 0
         self.lookups = 0
 
@@ -112,7 +117,7 @@ class NgramDrafter:
         drafts = np.zeros((self.B, g), dtype=np.int32)
         nd = np.zeros(self.B, dtype=np.int32)
         for b, ctx in enumerate(contexts):
-            prop = ngram_lookup(ctx, self.n, g)
+            prop = ngram_lookup(ctx, self.n, g, self.n_max)
             self.lookups += 1
             self.hits += bool(prop)
             if len(prop) < g and self.fill is not None:
@@ -125,14 +130,16 @@ class NgramDrafter:
 class DeviceNgramDrafter:
     """Prompt lookup on the device (``spec_ngram_propose``) for graph-replayed
     rounds: the context is everything committed before the generation started
-    plus the tokens the rounds append on the device.  ``fill_off`` [B]
-    (optional) pads short proposals with the committed prefix from that
-    offset, as NgramDrafter's ``fill`` does with a prompt offset."""
+    plus the tokens the rounds append on the device; match lengths n_max down
+    to n, as NgramDrafter.  ``fill_off`` [B] (optional) pads short proposals
+    with the committed prefix from that offset, as NgramDrafter's ``fill``
+    does with a prompt offset."""
 
     kind = "ngram-device"
 
-    def __init__(self, B: int, gamma: int, n: int = 3, fill_off=None):
+    def __init__(self, B: int, gamma: int, n: int = 3, fill_off=None, n_max: Optional[int] = None):
         self.B, self.gamma, self.n = B, gamma, n
+        self.n_max = n if n_max is None else n_max
         self.fill_off = None if fill_off is None else _dev_i32(fill_off)
         self.drafts = torch.empty((B, max(gamma, 1)), dtype=torch.int32, device="cuda")
         self.n_draft = torch.empty(B, dtype=torch.int32, device="cuda")
@@ -150,7 +157,7 @@ class DeviceNgramDrafter:
         self.P, self.out, self.out_len, self.cap = P, out, out_len, cap
 
     def propose(self):
-        bd.spec_ngram_propose(self.B, self.n, self.gamma, self.prefix, self.prefix_len, self.P, self.out,
+        bd.spec_ngram_propose(self.B, self.n, self.n_max, self.gamma, self.prefix, self.prefix_len, self.P, self.out,
                               self.out_len, self.cap, self.fill_off, self.drafts, self.n_draft, self.n_found)
         return self.drafts, self.n_draft
 

@@ -220,11 +220,14 @@ spec_status spec_commit_round(int32_t B, int32_t gamma, const int32_t* n_accepte
  * Decoding", section "The three proposers"; first page, section "Checking
  * it on a real system", method "ngram").  For sequence b the context is
  * prefix[b][0 .. prefix_len[b]) followed by out[b][0 .. min(out_len[b], cap)).
- * The most recent earlier occurrence of its last n tokens (the match may not
- * be the suffix itself) proposes the up to gamma tokens that followed it,
- * stopping at the end of the context; no occurrence (or a context shorter
- * than n + 1) proposes nothing.  The proposal is one-hot: verify it with
- * q = NULL.
+ * For a match length n, the most recent earlier occurrence of the context's
+ * last n tokens (the match may not be the suffix itself) proposes the up to
+ * gamma tokens that followed it, stopping at the end of the context.  The
+ * lengths n_max, n_max - 1, ..., n_min are tried in that order and the first
+ * that occurs is used (the match window prompt_lookup_min/max of "05 ·
+ * Speculative Decoding", section "Dial It In"); n_min = n_max is a fixed
+ * length.  No occurrence at any length (or a context shorter than n_min + 1)
+ * proposes nothing.  The proposal is one-hot: verify it with q = NULL.
  *   prefix     [B][P] ids, row stride P (the prompt, or everything committed
  *              before `out` started); prefix_len [B] or NULL for P.
  *   out, out_len, cap  as maintained by spec_commit_round.
@@ -234,12 +237,12 @@ spec_status spec_commit_round(int32_t B, int32_t gamma, const int32_t* n_accepte
  *   drafts     [B][gamma] out (entries past n_draft[b] are -1);
  *   n_draft    [B] out: tokens proposed (gamma when fill_off is given);
  *   n_found    [B] out or NULL: tokens that came from the lookup.
- * Limits: 1 <= n <= 16, 0 <= gamma <= 63.  Deterministic.
+ * Limits: 1 <= n_min <= n_max <= 16, 0 <= gamma <= 63.  Deterministic.
  * Errors: SPEC_EINVAL, SPEC_EHIP. */
-spec_status spec_ngram_propose(int32_t B, int32_t n, int32_t gamma, const int32_t* prefix, const int32_t* prefix_len,
-                               int32_t P, const int32_t* out, const int32_t* out_len, int32_t cap,
-                               const int32_t* fill_off, int32_t* drafts, int32_t* n_draft, int32_t* n_found,
-                               hipStream_t stream);
+spec_status spec_ngram_propose(int32_t B, int32_t n_min, int32_t n_max, int32_t gamma, const int32_t* prefix,
+                               const int32_t* prefix_len, int32_t P, const int32_t* out, const int32_t* out_len,
+                               int32_t cap, const int32_t* fill_off, int32_t* drafts, int32_t* n_draft,
+                               int32_t* n_found, hipStream_t stream);
 
 /* KV length bookkeeping: len[b] = (src ? src[b] : len[b]) + add for b < B.
  * Used to advance after prefill / draft passes and to rewind a drafter to the

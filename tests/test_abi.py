@@ -71,8 +71,10 @@ def test_host_checks_reject_before_launch(lib):
     assert lib.spec_workspace_bytes(None, 1, 1, 16) == 0
     assert lib.spec_commit_round(0, 4, 1, 1, 1, None, 1, 1, 8, None) == -1
     assert lib.spec_commit_round(1, 4, None, 1, 1, None, 1, 1, 8, None) == -1
-    # n-gram lookup: n in 1..16, gamma in 0..63, buffers present
-    assert lib.spec_ngram_propose(1, 0, 4, 1, None, 8, None, None, 0, None, 1, 1, None, None) == -1
-    assert lib.spec_ngram_propose(1, 3, 64, 1, None, 8, None, None, 0, None, 1, 1, None, None) == -1
-    assert lib.spec_ngram_propose(1, 3, 4, 1, None, 8, 1, None, 4, None, 1, 1, None, None) == -1  # out_len NULL
-    assert lib.spec_ngram_propose(1, 3, 4, None, None, 0, 1, 1, 4, 1, 1, 1, None, None) == -1   # fill, no prefix
+    # n-gram lookup: 1 <= n_min <= n_max <= 16, gamma in 0..63, buffers present
+    assert lib.spec_ngram_propose(1, 0, 3, 4, 1, None, 8, None, None, 0, None, 1, 1, None, None) == -1
+    assert lib.spec_ngram_propose(1, 4, 3, 4, 1, None, 8, None, None, 0, None, 1, 1, None, None) == -1
+    assert lib.spec_ngram_propose(1, 3, 17, 4, 1, None, 8, None, None, 0, None, 1, 1, None, None) == -1
+    assert lib.spec_ngram_propose(1, 3, 3, 64, 1, None, 8, None, None, 0, None, 1, 1, None, None) == -1
+    assert lib.spec_ngram_propose(1, 3, 3, 4, 1, None, 8, 1, None, 4, None, 1, 1, None, None) == -1  # out_len NULL
+    assert lib.spec_ngram_propose(1, 3, 3, 4, None, None, 0, 1, 1, 4, 1, 1, 1, None, None) == -1   # fill, no prefix

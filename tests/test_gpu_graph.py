@@ -62,13 +62,14 @@ def test_greedy_speculation_equals_greedy_decoding():
     assert spec[1]["rounds"] <= plain[0]["rounds"]
 
 
-@pytest.mark.parametrize("B", [1, 4])
-def test_graph_rounds_device_ngram_equal_host_ngram(B):
+@pytest.mark.parametrize("B,n_min,n_max", [(1, 3, 3), (4, 3, 3), (4, 2, 6)])
+def test_graph_rounds_device_ngram_equal_host_ngram(B, n_min, n_max):
     """Prompt lookup on the device inside the replayed rounds proposes what
     the host lookup does, so the two generations emit the same tokens: the
-    copy-heavy workload's shape (trigram lookup, gamma = 10, order-2 Markov
-    prompts, misses padded from a seeded prompt offset, one-hot q) on the
-    second workload's body with a 151936-entry vocabulary, two layers."""
+    copy-heavy workload's shape (trigram lookup or a 2..6 window, gamma = 10,
+    order-2 Markov prompts, misses padded from a seeded prompt offset, one-hot
+    q) on the second workload's body with a 151936-entry vocabulary, two
+    layers."""
     shape = SHAPES["small_v151936"].with_(n_layers=2)
     w = make_weights(shape, seed=406)
     P, g, N = 256, 10, 48
@@ -80,9 +81,10 @@ def test_graph_rounds_device_ngram_equal_host_ngram(B):
     outs = []
     for mode in ("host", "device"):
         if mode == "host":
-            drafter = NgramDrafter(B, g, n=3, fill=lambda b, L, k: [int(t) for t in prompt[b, offs[b]:offs[b] + k]])
+            drafter = NgramDrafter(B, g, n=n_min, n_max=n_max,
+                                   fill=lambda b, L, k: [int(t) for t in prompt[b, offs[b]:offs[b] + k]])
         else:
-            drafter = DeviceNgramDrafter(B, g, n=3, fill_off=offs)
+            drafter = DeviceNgramDrafter(B, g, n=n_min, n_max=n_max, fill_off=offs)
         dec = SpecDecoder(target, B, g, max_ctx, drafter=drafter, seed=406)
         dec.prefill(prompt)
         outs.append(dec.generate(N) if mode == "host" else dec.generate_graph(N))

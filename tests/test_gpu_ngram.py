@@ -1,40 +1,41 @@
 """The device n-gram (prompt-lookup) proposer against the oracle's: every
 proposal and count bit-exact, on contexts split between a prefix row and the
 tokens committed since, with planted repeats, Markov-chain prompts (many
-matches), contexts shorter than n + 1, ragged lengths and the fill option."""
+matches), contexts shorter than n + 1, ragged lengths, the fill option and
+match-length windows (longest length first)."""
 import numpy as np
 import pytest
 import torch
 
 from draft_then_verify_amd import binding as bd
-from oracle.ngram import ngram_propose
+from oracle.ngram import ngram_propose, ngram_propose_window
 from synth import make_markov_table, markov_prompt
 
 pytestmark = pytest.mark.gpu
 
 
-def _device_propose(prefix_rows, prefix_len, out_rows, out_len, n, gamma, fill_off=None):
+def _device_propose(prefix_rows, prefix_len, out_rows, out_len, n, gamma, fill_off=None, n_max=None):
     B, P = prefix_rows.shape
     cap = out_rows.shape[1]
     dr = torch.full((B, max(gamma, 1)), 7, dtype=torch.int32, device="cuda")
     nd = torch.empty(B, dtype=torch.int32, device="cuda")
     nf = torch.empty(B, dtype=torch.int32, device="cuda")
     t = lambda a: None if a is None else torch.as_tensor(np.ascontiguousarray(a, dtype=np.int32)).cuda()
-    bd.spec_ngram_propose(B, n, gamma, t(prefix_rows), t(prefix_len), P, t(out_rows) if cap else None,
+    bd.spec_ngram_propose(B, n, n if n_max is None else n_max, gamma, t(prefix_rows), t(prefix_len), P, t(out_rows) if cap else None,
                           t(out_len) if cap else None, cap, t(fill_off), dr, nd, nf)
     torch.cuda.synchronize()
     return dr.cpu().numpy()[:, :gamma], nd.cpu().numpy(), nf.cpu().numpy()
 
 
-def _check(prefix_rows, prefix_len, out_rows, out_len, n, gamma, fill_off=None):
-    drafts, nd, nf = _device_propose(prefix_rows, prefix_len, out_rows, out_len, n, gamma, fill_off)
+def _check(prefix_rows, prefix_len, out_rows, out_len, n, gamma, fill_off=None, n_max=None):
+    drafts, nd, nf = _device_propose(prefix_rows, prefix_len, out_rows, out_len, n, gamma, fill_off, n_max)
     B, P = prefix_rows.shape
     cap = out_rows.shape[1]
     for b in range(B):
         lp = P if prefix_len is None else int(prefix_len[b])
         lo = min(int(out_len[b]), cap) if cap else 0
         ctx = list(prefix_rows[b, :lp]) + list(out_rows[b, :lo])
-        want = ngram_propose(ctx, n, gamma)
+        want = ngram_propose(ctx, n, gamma) if n_max is None else ngram_propose_window(ctx, n, n_max, gamma)
         assert nf[b] == len(want), (b, nf[b], want)
         if fill_off is not None:
             pad = [int(prefix_rows[b, min(max(fill_off[b] + i, 0), P - 1)]) for i in range(gamma - len(want))]
@@ -104,3 +105,33 @@ def test_ngram_fill_pads_to_gamma(B):
     olen = rng.integers(0, cap + 1, size=B)
     off = rng.integers(0, P - g - 1, size=B)
     _check(prefix, None, out, olen, 3, g, fill_off=off)
+
+
+@pytest.mark.parametrize("n_min,n_max,gamma", [(3, 8, 4), (1, 4, 10), (2, 16, 7), (5, 5, 3)])
+def test_ngram_window_matches_oracle(n_min, n_max, gamma):
+    """Match-length windows: contexts over 3 ids (long repeats, so the longest
+    length usually wins), over 6 ids (the lengths in the window fall through
+    to shorter ones) and Markov prompts, split at ragged points; plus rows
+    whose last n_max tokens repeat once far back while a shorter suffix
+    repeats recently."""
+    B, P, cap = 48, 256, 48
+    rng = np.random.default_rng(1000 + 10 * n_min + n_max)
+    out_len = rng.integers(0, cap + 5, size=B)
+    prefix_len = rng.integers(1, P + 1, size=B)
+    for ids in (3, 6):
+        prefix = rng.integers(0, ids, size=(B, P)).astype(np.int32)
+        out = rng.integers(0, ids, size=(B, cap)).astype(np.int32)
+        _check(prefix, prefix_len, out, out_len, n_min, gamma, n_max=n_max)
+    table = make_markov_table(seed=90 + n_max)
+    prefix = markov_prompt(B, P, table, seed=91).astype(np.int32)
+    out = markov_prompt(B, cap, table, seed=92).astype(np.int32)
+    _check(prefix, prefix_len, out, out_len, n_min, gamma, n_max=n_max)
+    # planted: the last n_max tokens occur at the start, their last n_min
+    # tokens also just before the end
+    prefix = rng.integers(100, 200, size=(B, P)).astype(np.int32)
+    tail = rng.integers(200, 300, size=(B, n_max)).astype(np.int32)
+    prefix[:, :n_max] = tail
+    prefix[:, P - n_max:] = tail
+    prefix[:, P - n_max - 10:P - n_max - 10 + n_min] = tail[:, n_max - n_min:]
+    nf = _check(prefix, None, np.zeros((B, 0), np.int32), np.zeros(B, np.int32), n_min, gamma, n_max=n_max)
+    assert (nf > 0).all()

@@ -17,9 +17,11 @@
 // D lane l holds rows 4 (l / 16) .. +3 of column l % 16.
 //
 // The epilogues match the GEMV kernel's.  For SwiGLU, a wave's 4 weight tiles
-// are 2 gate tiles and the 2 matching up tiles.  For QKV (head_dim 128) a
-// workgroup is one head, and a wave's tiles are dims {j, j + 64} pairs, so
-// both halves of a rotated pair sit in the same lane.
+// are 2 gate tiles and the 2 matching up tiles.  For QKV with head_dim 128 a
+// workgroup is one head, and a wave's tiles are dims {j, j + 64} pairs; with
+// head_dim 64 a workgroup is two heads, one per wave column, and a wave's
+// tiles are dims {j, j + 32} pairs.  Either way both halves of a rotated pair
+// sit in the same lane.
 //
 // Tile order: the workgroups of one weight tile run on one XCD, because the
 // hardware deals workgroup ids round-robin over the 8 XCDs; the weight tile
@@ -46,7 +48,7 @@ constexpr int kXcds = 8;
 template <int EPI>
 __host__ __device__ inline int n_tiles(const GemvArgs& a) {
   if (EPI == EPI_SWIGLU) return (a.N + 63) / 64;
-  if (EPI == EPI_QKV) return a.H + 2 * a.Hkv;
+  if (EPI == EPI_QKV) return a.hd == 128 ? a.H + 2 * a.Hkv : (a.H + 2 * a.Hkv + 1) / 2;
   return (a.N + BN - 1) / BN;
 }
 
@@ -58,6 +60,7 @@ __device__ __forceinline__ int w_row(const GemvArgs& a, int nt, int lr) {
     const int n = min(nt * 64 + wn * 32 + (c & 31), a.N - 1);
     return c < 32 ? n : a.N + n;
   } else if constexpr (EPI == EPI_QKV) {
+    if (a.hd == 64) return min((2 * nt + wn) * 64 + c, a.N - 1);  // head 2 nt + wn, dim c
     const int dim = (c < 32) ? wn * 32 + c : 64 + wn * 32 + (c - 32);
     return nt * a.hd + dim;
   } else {
@@ -162,12 +165,15 @@ __global__ __launch_bounds__(NTH) void gemm_kernel(GemvArgs a, int mtiles, int n
         }
       } else if constexpr (EPI == EPI_QKV) {
         const int H = a.H, Hkv = a.Hkv, hd = a.hd, half = hd / 2;
-        const int hh = nt;
+        const bool two = hd == 64;  // two heads per workgroup
+        const int hh = two ? 2 * nt + wn : nt;
+        if (hh >= H + 2 * Hkv) continue;  // an odd head count's empty half
         const int rg = a.row0 + m;
         const int b = rg / a.m_per_seq, ii = rg - b * a.m_per_seq;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const int d = wn * 32 + j * 16 + col;  // 0 .. 63; its pair is d + 64
+          // 0 .. half-1; its pair is d + half
+          const int d = two ? j * 16 + col : wn * 32 + j * 16 + col;
           const float x0 = acc[i][j][r], y0 = acc[i][j + 2][r];
           if (hh < H + Hkv) {
             const float2 c = a.cs[static_cast<size_t>(rg) * half + d];

@@ -105,7 +105,8 @@ hipError_t launch_all(const GemvArgs& a0, int M, hipStream_t s) {
   if (EPI == EPI_QKV && (b.N % 2 || b.hd % 2)) return hipErrorInvalidValue;
   // the normalising prologue reads whole residual rows: one K slice, GEMV path
   if (b.hn && (b.ksplit != 1 || M > 8 || b.K % 4)) return hipErrorInvalidValue;
-  if (std::is_same<WT, uint16_t>::value && M > 8 && b.K % mfma::KB == 0 && (EPI != EPI_QKV || b.hd == 128))
+  if (std::is_same<WT, uint16_t>::value && M > 8 && b.K % mfma::KB == 0 &&
+      (EPI != EPI_QKV || b.hd == 128 || b.hd == 64))
     return launch_gemm<EPI>(b, M, s);
   const size_t kp = static_cast<size_t>((b.K + STEP - 1) / STEP) * STEP;
   const int fit = static_cast<int>(kMaxLds / (kp * sizeof(WT)));

@@ -124,6 +124,20 @@ def test_short_pass_hd64_row_blocks_ragged():
     assert np.abs(got - ref).max() < _tol(shape)
 
 
+def test_matrix_core_qkv_hd64_odd_head_count():
+    """head_dim 64 on the matrix-core path (more than 8 rows): a workgroup
+    holds two heads; with 3 query + 3 + 3 KV heads the last workgroup's second
+    head is empty.  The prefill (4 x 19 rows) takes the same path."""
+    shape = Shape("h64odd", 192, 2, 3, 3, 64, 512, 700, "bf16")
+    got, ref, kv, cache, sh = _run(shape, B=4, P=20, m=5, seed=112, lens_back=[0, 2, 5, 1])
+    assert np.abs(got - ref).max() < _tol(shape)
+    n = int(cache.length.min()) + 5
+    k = kv.k[:, :, :, :n].float().cpu().numpy()
+    v = kv.v[:, :, :, :n].float().cpu().numpy()
+    assert np.abs(k - cache.k[:, :, :, :n]).max() < 2e-2
+    assert np.abs(v - cache.v[:, :, :, :n]).max() < 2e-2
+
+
 def test_long_context_split_kernel():
     """Past 2048 cached positions the split-context kernel with its
     last-workgroup merge runs instead."""

@@ -376,6 +376,14 @@ hipError_t launch_mq(const AttnArgs& a, int B, hipStream_t s) {
 // groups are summed once, after the last tile.
 constexpr int kDecWaves = 8;
 constexpr int kDecodeMaxCtx = 2048;
+// Past this many (sequence, query head, row) units a pass takes the split
+// kernel instead: its workgroups serve the query heads of one KV head
+// together, where this kernel re-reads the KV head once per query head.
+// Measured on MI355X, head_dim 64, 16:4 heads, ~300 keys: B = 64 and 256
+// verify passes (5 rows) ran 12% and 34% faster that way, B = 256 one-row
+// passes 15% faster; B = 64 one-row passes (1024 units) ran 6% slower, and
+// 8 or fewer sequences slower still.
+constexpr long long kDecodeMaxUnits = 4096;
 
 template <typename ET, int HD> struct Dec {
   static constexpr int CE = 16 / static_cast<int>(sizeof(ET));        // elements per 16-byte chunk
@@ -615,7 +623,7 @@ bool attn_decode_path(bool bf16, int hd, int m, int max_ctx) {
 hipError_t launch_attention(bool bf16, int hd, const AttnArgs& a, int B, hipStream_t s) {
   if (B <= 0 || a.m <= 0) return hipSuccess;
   if (!attn_supported(a.H, a.Hkv, hd)) return hipErrorInvalidValue;
-  if (attn_decode_path(bf16, hd, a.m, a.max_ctx)) {
+  if (attn_decode_path(bf16, hd, a.m, a.max_ctx) && static_cast<long long>(B) * a.H * a.m < kDecodeMaxUnits) {
     if (bf16) return hd == 128 ? launch_decode<uint16_t, 128>(a, B, s) : launch_decode<uint16_t, 64>(a, B, s);
     if (hd == 64) return launch_decode<float, 64>(a, B, s);
   }

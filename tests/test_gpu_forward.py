@@ -124,6 +124,14 @@ def test_short_pass_hd64_row_blocks_ragged():
     assert np.abs(got - ref).max() < _tol(shape)
 
 
+def test_short_pass_many_units_split_kernel():
+    """A short pass with B * H * m >= 4096 (sequence, head, row) units takes
+    the split kernel (query heads of a KV head together); ragged contexts."""
+    shape = Shape("h64wide", 1024, 1, 16, 4, 64, 512, 500, "bf16")
+    got, ref, *_ = _run(shape, B=60, P=24, m=5, seed=113, lens_back=[i % 7 for i in range(60)])
+    assert np.abs(got - ref).max() < _tol(shape)
+
+
 def test_matrix_core_qkv_hd64_odd_head_count():
     """head_dim 64 on the matrix-core path (more than 8 rows): a workgroup
     holds two heads; with 3 query + 3 + 3 KV heads the last workgroup's second

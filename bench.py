@@ -27,6 +27,9 @@ Qwen3-0.6B-shaped draft, B = 1, gamma = 4, a 256-token prompt, 256 new tokens.
 * ``division_check_gamma1``: the gamma = 1 division of the M1 Max page,
   predicted (1 + p) T_decode / (T_verify + T_draft) against the measured
   speculative/plain ratio, on the same shapes.
+* ``ngram_workload``: the copy-heavy workload (the second workload's body
+  with a 151936-entry vocabulary, 2048-token order-2 Markov prompts, device
+  prompt lookup with gamma = 10) against plain decoding, B in {1, 64}.
 """
 
 from __future__ import annotations
@@ -244,6 +247,49 @@ def batch_sweep(n_new: int, batches=(1, 8, 64, 256), P: int = 256, g: int = 4) -
     return rows
 
 
+def ngram_workload(n_new: int, batches=(1, 64), P: int = 2048, g: int = 10) -> list:
+    """The copy-heavy workload: the second workload's 8-layer body with a
+    151936-entry vocabulary, 2048-token prompts walked from an order-2 Markov
+    chain over 512 ids, prompt lookup on the device (trigram, gamma = 10,
+    misses padded from a seeded prompt offset, one-hot q) against plain
+    decoding; graph-replayed rounds, emitted tok/s over the B sequences."""
+    import numpy as np
+    import torch
+
+    from draft_then_verify_amd import binding as bd
+    from draft_then_verify_amd.runner import DeviceNgramDrafter, SpecDecoder
+    from synth import SHAPES, make_markov_table, make_weights, markov_prompt
+
+    sh = SHAPES["small_v151936"]
+    w = make_weights(sh, seed=31, device="cuda")
+    target = bd.SpecModel(sh, w)
+    table = make_markov_table(seed=32)
+    rows = []
+    for B in batches:
+        prompt = markov_prompt(B, P, table, seed=33 + B).astype(np.int64)
+        offs = np.random.default_rng(34 + B).integers(0, P - g - 1, size=B)
+        max_ctx = P + n_new + g + 4
+        spec = SpecDecoder(target, B, g, max_ctx, drafter=DeviceNgramDrafter(B, g, n=3, fill_off=offs), seed=35)
+        spec.prefill(prompt)
+        rs = spec.generate_graph(n_new)
+        hits = float(spec.drafter.n_found.float().mean().item())
+        del spec
+        plain = SpecDecoder(target, B, 0, max_ctx, seed=36)
+        plain.prefill(prompt)
+        rp = plain.generate_graph(n_new)
+        del plain
+        torch.cuda.empty_cache()
+        rows.append({"B": B, "spec_tok_s": round(rs["tok_s"], 1), "plain_tok_s": round(rp["tok_s"], 1),
+                     "spec_over_plain": round(rs["tok_s"] / rp["tok_s"], 3),
+                     "mean_acceptance_length": round(rs["mean_acceptance_length"], 3),
+                     "lookup_tokens_last_round": round(hits, 2),
+                     "note": "random-init target: a one-hot draft is accepted with probability p(x) ~ 1/V, "
+                             "so this measures the cost of verifying gamma + 1 = 11 rows per emitted token"})
+        log(f"n-gram B={B}: speculative {rs['tok_s']:.0f} tok/s, plain {rp['tok_s']:.0f} tok/s, "
+            f"ratio {rs['tok_s'] / rp['tok_s']:.3f}, MAL {rs['mean_acceptance_length']:.2f}")
+    return rows
+
+
 def time_draft(drafter, kv_len, B: int, g: int, steps: int = 20) -> float:
     """Mean time of the drafter's work for one round (its passes, softmax
     and draws), graph-replayed; the drafter rewinds to kv_len - 1 each time."""
@@ -348,7 +394,8 @@ def main():
     ap.add_argument("--skip-generate", action="store_true", help="skip the emitted tok/s generations")
     ap.add_argument("--skip-cpu", action="store_true", help="skip the CPU-baseline leg")
     ap.add_argument("--skip-sweep", action="store_true",
-                    help="skip the batch sweep and the gamma = 1 division check (second workload's shapes)")
+                    help="skip the batch sweep, the gamma = 1 division check and the n-gram workload "
+                         "(second workload's shapes)")
     ap.add_argument("--graph", type=int, default=1, help="time graph replays of the decode step (1) or eager calls (0)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -428,10 +475,11 @@ def main():
                "generation": "graph-replayed rounds (drafter passes, verify step and bookkeeping on the device)"}
         del plain
 
-    sweep = division = None
+    sweep = division = ngram = None
     if not args.skip_sweep:
         sweep = batch_sweep(args.new_tokens)
         division = division_check(args.new_tokens)
+        ngram = ngram_workload(args.new_tokens)
 
     cpu = None
     if not args.skip_cpu:
@@ -457,6 +505,7 @@ def main():
         "cpu_baseline": cpu,
         "batch_sweep": sweep,
         "division_check_gamma1": division,
+        "ngram_workload": ngram,
     }
     print(json.dumps(out), flush=True)
 

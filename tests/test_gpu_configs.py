@@ -315,11 +315,11 @@ def test_config5_ngram_long_draft(B):
     with V = 151936, gamma = 10, order-2 Markov prompts: two rounds; the oracle
     replays every sequence for B = 1, 2 seeded sequences of 64.  Misses are
     filled with the gamma tokens after a seeded prompt offset so every round
-    verifies B x 11 rows.  Prompts are 2048 tokens at B = 1 and 96 at B = 64
-    (the prefill of 64 x 2047 rows through the M <= 8 linear would dominate)."""
+    verifies B x 11 rows.  Prompts are 2048 tokens (the prefill of 64 x 2047
+    rows runs on the matrix cores)."""
     sh = SHAPES["small_v151936"]
     w = make_weights(sh, seed=305)
-    P, g = (2048 if B == 1 else 96), 10
+    P, g = 2048, 10
     max_ctx = P + 2 * (g + 1) + 4
     table = make_markov_table(seed=305)
     prompt = markov_prompt(B, P, table, seed=305 + B).astype(np.int64)

@@ -289,13 +289,12 @@ def test_config3_8b_shape_rounds():
 def test_config4_batch_sweep_round(B):
     """Config-2 shapes at B sequences (verify M = 5B rows), 2-layer
     self-speculative draft: two rounds; the oracle replays every sequence for
-    B <= 8, 8 seeded sequences otherwise.  Prompts are 256 tokens for B <= 8
-    and 16 tokens for B >= 64 (the prefill of B x 255 rows through the M <= 8
-    linear would dominate the test; the verify rounds are the same)."""
+    B <= 8, 8 seeded sequences otherwise.  Prompts are 256 tokens (the
+    prefill of B x 255 rows runs on the matrix cores)."""
     sh = SHAPES["small"]
     w = make_weights(sh, seed=304)
     dsh = sh.with_(n_layers=2)
-    P, g = (256 if B <= 8 else 16), 4
+    P, g = 256, 4
     max_ctx = P + 2 * (g + 1) + 4
     prompt = make_prompt(B, P, sh.vocab, seed=304 + B)
     target = bd.SpecModel(sh, to_dev(w))

@@ -20,7 +20,10 @@
 //    with each of its wave's query rows (LDS broadcasts, 8 dimensions of
 //    every row at a time so the reads overlap the FMAs);
 //  * online softmax per row (wave max / sum);
-//  * P.V: lanes take head dimensions; V rows come from LDS.
+//  * P.V: lane l takes the 16-byte chunk l % CPR of the V rows of keys
+//    l / CPR, l / CPR + 64 / CPR, ... of the tile (one 16-byte LDS read per
+//    key), and after the last tile the 64 / CPR key groups of each chunk are
+//    summed across lanes in a fixed butterfly.
 // At B = 1 the (sequence, head) pairs are few, so the context is cut into
 // splits, one workgroup each; the partial (max, sum, output) rows are merged
 // by the last workgroup of each (sequence, head block, row block) to finish
@@ -60,29 +63,6 @@ template <> struct Cvt<float> {
 #pragma unroll
     for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(v[i]);
   }
-};
-
-// DPL consecutive elements of a V row in LDS as floats.
-template <typename ET, int DPL> struct VRow;
-template <> struct VRow<uint16_t, 2> {
-  __device__ __forceinline__ static void load(const uint16_t* p, float* f) {
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
-    f[0] = __uint_as_float(w << 16);
-    f[1] = __uint_as_float(w & 0xffff0000u);
-  }
-};
-template <> struct VRow<uint16_t, 1> {
-  __device__ __forceinline__ static void load(const uint16_t* p, float* f) { f[0] = bf2f(*p); }
-};
-template <> struct VRow<float, 2> {
-  __device__ __forceinline__ static void load(const float* p, float* f) {
-    const float2 v = *reinterpret_cast<const float2*>(p);
-    f[0] = v.x;
-    f[1] = v.y;
-  }
-};
-template <> struct VRow<float, 1> {
-  __device__ __forceinline__ static void load(const float* p, float* f) { f[0] = *p; }
 };
 
 // Shape of the work split, shared by the launcher and the kernel.
@@ -148,8 +128,11 @@ __global__ __launch_bounds__(waves_for(HD) * kWave) __attribute__((amdgpu_waves_
     AttnArgs a) {
   using L = Lds<ET, HD>;
   constexpr int kThreadsA = L::kThreadsA;
-  constexpr int DPL = HD / kWave;  // output dims per lane
+  constexpr int DPL = HD / kWave;  // query dims per lane (staging q)
   constexpr int CE = Cvt<ET>::n;   // elements per 16-byte chunk
+  constexpr int VCPR = HD / CE;    // 16-byte chunks per V row
+  constexpr int NG = kWave / VCPR; // key groups in P.V
+  static_assert(kWave % VCPR == 0 && KT % NG == 0, "P.V lane split");
   static_assert(L::NL * kThreadsA == KT * L::CPR, "tile chunks must split evenly over the threads");
 
   extern __shared__ uint4 smem_a[];
@@ -198,13 +181,15 @@ __global__ __launch_bounds__(waves_for(HD) * kWave) __attribute__((amdgpu_waves_
 #pragma unroll
     for (int k = 0; k < DPL; ++k) qs[r][lane * DPL + k] = qr[k] * scale;
   }
-  float mrow[MQ], lrow[MQ], o[MQ][DPL];
+  // P.V accumulators: chunk vch of the V rows, keys vg, vg + NG, ... of each tile
+  const int vch = lane % VCPR, vg = lane / VCPR;
+  float mrow[MQ], lrow[MQ], o[MQ][CE];
 #pragma unroll
   for (int r = 0; r < MQ; ++r) {
     mrow[r] = -INFINITY;
     lrow[r] = 0.f;
 #pragma unroll
-    for (int k = 0; k < DPL; ++k) o[r][k] = 0.f;
+    for (int k = 0; k < CE; ++k) o[r][k] = 0.f;
   }
 
   for (int k0 = kbeg; k0 < kend; k0 += KT) {
@@ -254,42 +239,42 @@ __global__ __launch_bounds__(waves_for(HD) * kWave) __attribute__((amdgpu_waves_
       lrow[r] = lrow[r] * alpha + wave_sum(p);
       mrow[r] = mnew;
 #pragma unroll
-      for (int k = 0; k < DPL; ++k) o[r][k] *= alpha;
+      for (int k = 0; k < CE; ++k) o[r][k] *= alpha;
       ps[r][lane] = p;
     }
     __syncthreads();
-    // P.V over the tile, four keys at a time (keys past nt have p = 0 and
-    // finite V rows: the clamped copies of the last one)
-    const int nt4 = (nt + 3) & ~3;
+    // P.V over the tile: this lane's keys vg + NG t (keys past nt have p = 0
+    // and finite V rows: the clamped copies of the last one)
 #pragma unroll 4
-    for (int j = 0; j < nt4; j += 4) {
-      float vf[4][DPL];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) VRow<ET, DPL>::load(vs + (j + t) * HD + lane * DPL, vf[t]);
+    for (int t = 0; t < KT / NG; ++t) {
+      const int j = vg + t * NG;
+      float vf[CE];
+      Cvt<ET>::run(*reinterpret_cast<const v4u*>(vs + j * HD + vch * CE), vf);
 #pragma unroll
       for (int r = 0; r < MQ; ++r) {
-        const float4 p4 = *reinterpret_cast<const float4*>(&ps[r][j]);
+        const float pj = ps[r][j];
 #pragma unroll
-        for (int k = 0; k < DPL; ++k) {
-          float t = o[r][k];
-          t = fmaf(p4.x, vf[0][k], t);
-          t = fmaf(p4.y, vf[1][k], t);
-          t = fmaf(p4.z, vf[2][k], t);
-          t = fmaf(p4.w, vf[3][k], t);
-          o[r][k] = t;
-        }
+        for (int k = 0; k < CE; ++k) o[r][k] = fmaf(pj, vf[k], o[r][k]);
       }
     }
   }
+  // the key groups of each chunk, summed across lanes (every lane of a chunk
+  // ends with the same sum)
+#pragma unroll
+  for (int off = VCPR; off < kWave; off <<= 1)
+#pragma unroll
+    for (int r = 0; r < MQ; ++r)
+#pragma unroll
+      for (int k = 0; k < CE; ++k) o[r][k] += __shfl_xor(o[r][k], off, kWave);
 
   ET* xo = static_cast<ET*>(a.xo);
   if (a.n_split == 1) {
 #pragma unroll
     for (int r = 0; r < MQ; ++r) {
-      if (r < nrows) {
+      if (r < nrows && vg == 0) {
 #pragma unroll
-        for (int k = 0; k < DPL; ++k)
-          xo[static_cast<size_t>(b * m + i0 + r) * qld + h * HD + lane * DPL + k] =
+        for (int k = 0; k < CE; ++k)
+          xo[static_cast<size_t>(b * m + i0 + r) * qld + h * HD + vch * CE + k] =
               Elt<ET>::from_f(lrow[r] > 0.f ? o[r][k] / lrow[r] : 0.f);
       }
     }
@@ -302,8 +287,10 @@ __global__ __launch_bounds__(waves_for(HD) * kWave) __attribute__((amdgpu_waves_
   for (int r = 0; r < MQ; ++r) {
     if (r < nrows) {
       const size_t prow = prow0 + static_cast<size_t>(r) * ns + s;
+      if (vg == 0) {
 #pragma unroll
-      for (int k = 0; k < DPL; ++k) a.part_o[prow * HD + lane * DPL + k] = o[r][k];
+        for (int k = 0; k < CE; ++k) a.part_o[prow * HD + vch * CE + k] = o[r][k];
+      }
       if (lane == 0) a.part_ml[prow] = make_float2(mrow[r], lrow[r]);
     }
   }

@@ -84,6 +84,20 @@ class ModelDrafter:
         bd.spec_kv_set_len(self.kv, B, target_len, -1)
         bd.spec_verify_forward(self.model, self.kv, B, 2, tok2, self.logits2, self.ws2)
         bd.spec_kv_set_len(self.kv, B, None, 2)
+        if B == 1:
+            # one sequence: the q rows, the drawn tokens and the second
+            # logits row are contiguous slices, so the kernels write them in
+            # place (no copies, and the first softmax covers one row)
+            bd.spec_softmax_pq(self.logits2[:, 1], 1, V, self.T, self.q[:, 0], self.sws)
+            for i in range(self.gamma):
+                if i > 0:
+                    bd.spec_verify_forward(self.model, self.kv, 1, 1, self.drafts[:, i - 1:i], self.logits1,
+                                           self.ws1)
+                    bd.spec_kv_set_len(self.kv, 1, None, 1)
+                    bd.spec_softmax_pq(self.logits1, 1, V, self.T, self.q[:, i], self.sws)
+                bd.spec_reject_sample(1, 0, V, self.q[:, i], None, None, None, None, u_draft[i], self.n_tmp,
+                                      self.drafts[:, i:i + 1], self.sws)
+            return self.drafts, self.q, None
         bd.spec_softmax_pq(self.logits2, 2 * B, V, self.T, self.probs2, self.sws)
         self.qtmp.copy_(self.probs2[:, 1:2])
         for i in range(self.gamma):

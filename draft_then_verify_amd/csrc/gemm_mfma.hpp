@@ -8,9 +8,12 @@
 // real dense contraction and belongs on MFMA.  The GEMV kernel would stream
 // the weights once per 8 rows instead.
 //
-// Tiles: a workgroup computes 64 rows x 128 weight rows of Y with 4 waves in
-// a 2 x 2 arrangement; each wave owns 32 x 64 = 2 x 4 tiles of
-// v_mfma_f32_16x16x32_bf16.  The K dimension advances 64 at a time through
+// Tiles: a workgroup computes BMT rows x 128 weight rows of Y with 4 waves in
+// a 2 x 2 arrangement; each wave owns BMT/2 x 64 = (BMT/32) x 4 tiles of
+// v_mfma_f32_16x16x32_bf16.  BMT is 128 when the launch still has a
+// workgroup per CU with it (each A fragment read from LDS then feeds 4 MFMAs
+// and each B fragment 4: 8 reads per 16 MFMAs against 6 per 8 at BMT = 64,
+// and the LDS reads are what bounds this kernel), else 64.  The K dimension advances 64 at a time through
 // two LDS buffers; the next block's 16-byte global loads are issued before
 // the current block is multiplied.  Fragment layouts (gfx950): A lane l holds
 // row l % 16, k = 8 (l / 16) .. +7; B lane l holds column l % 16, the same k;
@@ -38,7 +41,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 64;     // rows of X per workgroup
+constexpr int BM = 64;     // rows of X per workgroup (the smaller of the two tile heights)
 constexpr int BN = 128;    // weight rows per workgroup
 constexpr int KB = 64;     // K per LDS stage
 constexpr int LDK = KB + 8;  // LDS row stride in bf16 (16-byte pad spreads the banks)
@@ -68,9 +71,11 @@ __device__ __forceinline__ int w_row(const GemvArgs& a, int nt, int lr) {
   }
 }
 
-template <int EPI>
+template <int EPI, int BMT>
 __global__ __launch_bounds__(NTH) void gemm_kernel(GemvArgs a, int mtiles, int ntiles) {
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM][LDK];
+  constexpr int MI = BMT / 32;   // 16-row tiles per wave (a wave covers BMT / 2 rows)
+  constexpr int XL = BMT / 32;   // 16-byte X chunks per thread per K block
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][BMT][LDK];
   __shared__ __attribute__((aligned(16))) uint16_t ws[2][BN][LDK];
   const int per = gridDim.x / kXcds;
   const int tile = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
@@ -79,14 +84,14 @@ __global__ __launch_bounds__(NTH) void gemm_kernel(GemvArgs a, int mtiles, int n
   const int M = a.M, K = a.K, slice = blockIdx.y;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int wm = wave & 1, wn = wave >> 1;
-  const int m0 = mt * BM;
+  const int m0 = mt * BMT;
 
-  // this thread's global chunks: X 2 x 16 B, W 4 x 16 B per K block
-  const uint16_t* xp[2];
+  // this thread's global chunks: X XL x 16 B, W 4 x 16 B per K block
+  const uint16_t* xp[XL];
   const uint16_t* wp[4];
-  int xr[2], xc[2], wr[4], wc[4];
+  int xr[XL], xc[XL], wr[4], wc[4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < XL; ++i) {
     const int c = threadIdx.x + i * NTH;
     xr[i] = c >> 3;
     xc[i] = (c & 7) * 8;
@@ -101,23 +106,23 @@ __global__ __launch_bounds__(NTH) void gemm_kernel(GemvArgs a, int mtiles, int n
     wp[i] = static_cast<const uint16_t*>(a.W) + static_cast<size_t>(w_row<EPI>(a, nt, wr[i])) * a.ldw +
             static_cast<size_t>(slice) * K + wc[i];
   }
-  v4u gx[2], gw[4];
+  v4u gx[XL], gw[4];
   auto load = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) gx[i] = *reinterpret_cast<const v4u*>(xp[i] + k0);
+    for (int i = 0; i < XL; ++i) gx[i] = *reinterpret_cast<const v4u*>(xp[i] + k0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) gw[i] = *reinterpret_cast<const v4u*>(wp[i] + k0);
   };
   auto store = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) *reinterpret_cast<v4u*>(&xs[buf][xr[i]][xc[i]]) = gx[i];
+    for (int i = 0; i < XL; ++i) *reinterpret_cast<v4u*>(&xs[buf][xr[i]][xc[i]]) = gx[i];
 #pragma unroll
     for (int i = 0; i < 4; ++i) *reinterpret_cast<v4u*>(&ws[buf][wr[i]][wc[i]]) = gw[i];
   };
 
-  f32x4_t acc[2][4];
+  f32x4_t acc[MI][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
@@ -131,13 +136,14 @@ __global__ __launch_bounds__(NTH) void gemm_kernel(GemvArgs a, int mtiles, int n
     if (kb + 1 < nk) load((kb + 1) * KB);
 #pragma unroll
     for (int ks = 0; ks < KB; ks += 32) {
-      bf16x8_t af[2], bfr[4];
+      bf16x8_t af[MI], bfr[4];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) af[i] = *reinterpret_cast<const bf16x8_t*>(&xs[buf][wm * 32 + i * 16 + fr][ks + fk]);
+      for (int i = 0; i < MI; ++i)
+        af[i] = *reinterpret_cast<const bf16x8_t*>(&xs[buf][wm * (BMT / 2) + i * 16 + fr][ks + fk]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) bfr[j] = *reinterpret_cast<const bf16x8_t*>(&ws[buf][wn * 64 + j * 16 + fr][ks + fk]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
@@ -149,10 +155,10 @@ __global__ __launch_bounds__(NTH) void gemm_kernel(GemvArgs a, int mtiles, int n
   const int col = lane & 15, rb = (lane >> 4) * 4;
   float* y = a.y ? a.y + static_cast<size_t>(slice) * a.ysplit : nullptr;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < MI; ++i) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int m = m0 + wm * 32 + i * 16 + rb + r;
+      const int m = m0 + wm * (BMT / 2) + i * 16 + rb + r;
       if (m >= M) continue;
       if constexpr (EPI == EPI_SWIGLU) {
 #pragma unroll

@@ -80,15 +80,23 @@ hipError_t launch_rows(const GemvArgs& a, int mb, hipStream_t s) {
   }
 }
 
+template <int EPI, int BMT>
+hipError_t launch_gemm_t(const GemvArgs& a, hipStream_t s) {
+  const int mt = (a.M + BMT - 1) / BMT, nt = mfma::n_tiles<EPI>(a);
+  const int total = mt * nt;
+  const int grid = (total + mfma::kXcds - 1) / mfma::kXcds * mfma::kXcds;
+  hipLaunchKernelGGL((mfma::gemm_kernel<EPI, BMT>), dim3(grid, a.ksplit), dim3(mfma::NTH), 0, s, a, mt, nt);
+  return hipGetLastError();
+}
+
 template <int EPI>
 hipError_t launch_gemm(const GemvArgs& b, int M, hipStream_t s) {
   GemvArgs a = b;
   a.M = M;
-  const int mt = (M + mfma::BM - 1) / mfma::BM, nt = mfma::n_tiles<EPI>(a);
-  const int total = mt * nt;
-  const int grid = (total + mfma::kXcds - 1) / mfma::kXcds * mfma::kXcds;
-  hipLaunchKernelGGL(mfma::gemm_kernel<EPI>, dim3(grid, a.ksplit), dim3(mfma::NTH), 0, s, a, mt, nt);
-  return hipGetLastError();
+  // 128-row tiles while they still give every CU a workgroup (K slices count)
+  const long long tiles128 = static_cast<long long>((M + 127) / 128) * mfma::n_tiles<EPI>(a) * a.ksplit;
+  if (tiles128 >= kCUs) return launch_gemm_t<EPI, 128>(a, s);
+  return launch_gemm_t<EPI, 64>(a, s);
 }
 
 template <typename WT, int EPI>

@@ -27,6 +27,9 @@ Qwen3-0.6B-shaped draft, B = 1, gamma = 4, a 256-token prompt, 256 new tokens.
 * ``division_check_gamma1``: the gamma = 1 division of the M1 Max page,
   predicted (1 + p) T_decode / (T_verify + T_draft) against the measured
   speculative/plain ratio, on the same shapes.
+* ``mfma_linears``: the matrix-core linear at the second workload's weight
+  shapes with M = 1280 rows (a B = 256 verify pass), TFLOP/s per launch from
+  HIP events against the 2.5 PFLOP/s dense bf16 peak.
 * ``ngram_workload``: the copy-heavy workload (the second workload's body
   with a 151936-entry vocabulary, 2048-token order-2 Markov prompts, device
   prompt lookup with gamma = 10) against plain decoding, B in {1, 64}.
@@ -290,6 +293,56 @@ def ngram_workload(n_new: int, batches=(1, 64), P: int = 2048, g: int = 10) -> l
     return rows
 
 
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
+
+
+def mfma_linears(M: int = 1280, reps: int = 20) -> list:
+    """The matrix-core linear at the second workload's weight shapes with
+    M = 1280 rows (a B = 256, gamma = 4 verify pass): TFLOP/s per launch from
+    HIP events on the launching stream, against the dense bf16 peak.  Each
+    shape cycles through 8 weight copies so the weights come from HBM."""
+    import torch
+
+    from draft_then_verify_amd import binding as bd
+
+    d, F, V, hq = 1024, 2816, 32000, 1536
+    cases = [("QKV-shaped, store", hq, d, 0), ("O, residual add", d, d, 1), ("gate/up + SwiGLU", F, d, 2),
+             ("down, residual add", d, F, 1),
+             ("LM head", V, d, 0)]
+    out = []
+    for name, N, K, epi in cases:
+        rows = 2 * N if epi == 2 else N
+        Ws = [(torch.randn((rows, K), device="cuda") * 0.02).to(torch.bfloat16) for _ in range(8)]
+        x = torch.randn((M, K), device="cuda").to(torch.bfloat16)
+        y = torch.zeros((M, N), device="cuda")
+        z = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+        def go(W):
+            if epi == 2:
+                bd.spec_linear(W, x, M, N, K, epilogue=2, z=z)
+            else:
+                bd.spec_linear(W, x, M, N, K, epilogue=epi, y=y)
+
+        for W in Ws:
+            go(W)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for r in range(reps):
+            go(Ws[r % len(Ws)])
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        tflops = 2.0 * M * rows * K / (us * 1e-6) / 1e12
+        out.append({"linear": name, "M": M, "N": rows, "K": K, "us_per_launch": round(us, 2),
+                    "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tflops / PEAK_BF16_TFLOPS, 4)})
+        log(f"matrix-core {name} [{rows} x {K}], M={M}: {us:.1f} us, {tflops:.0f} TFLOP/s")
+        del Ws
+        torch.cuda.empty_cache()
+    return out
+
+
 def time_draft(drafter, kv_len, B: int, g: int, steps: int = 20) -> float:
     """Mean time of the drafter's work for one round (its passes, softmax
     and draws), graph-replayed; the drafter rewinds to kv_len - 1 each time."""
@@ -475,8 +528,9 @@ def main():
                "generation": "graph-replayed rounds (drafter passes, verify step and bookkeeping on the device)"}
         del plain
 
-    sweep = division = ngram = None
+    sweep = division = ngram = mfma = None
     if not args.skip_sweep:
+        mfma = mfma_linears()
         sweep = batch_sweep(args.new_tokens)
         division = division_check(args.new_tokens)
         ngram = ngram_workload(args.new_tokens)
@@ -506,6 +560,7 @@ def main():
         "batch_sweep": sweep,
         "division_check_gamma1": division,
         "ngram_workload": ngram,
+        "mfma_linears": mfma,
     }
     print(json.dumps(out), flush=True)
 

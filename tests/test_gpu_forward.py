@@ -124,6 +124,14 @@ def test_short_pass_hd64_row_blocks_ragged():
     assert np.abs(got - ref).max() < _tol(shape)
 
 
+def test_split_kernel_f32_hd128():
+    """The split kernel with float32 K/V rows of head_dim 128 (32 16-byte
+    chunks per row, two key groups in P.V), 12 rows per sequence."""
+    shape = Shape("f128", 256, 1, 2, 1, 128, 512, 300, "f32")
+    got, ref, *_ = _run(shape, B=2, P=90, m=12, seed=114, lens_back=[0, 7])
+    assert np.abs(got - ref).max() < _tol(shape)
+
+
 def test_short_pass_many_units_split_kernel():
     """A short pass with B * H * m >= 4096 (sequence, head, row) units takes
     the split kernel (query heads of a KV head together); ragged contexts."""

@@ -244,9 +244,13 @@ def batch_sweep(n_new: int, batches=(1, 8, 64, 256), P: int = 256, g: int = 4) -
         torch.cuda.empty_cache()
         rows.append({"B": B, "spec_tok_s": round(rs["tok_s"], 1), "plain_tok_s": round(rp["tok_s"], 1),
                      "spec_over_plain": round(rs["tok_s"] / rp["tok_s"], 3),
-                     "mean_acceptance_length": round(rs["mean_acceptance_length"], 3)})
-        log(f"sweep B={B}: speculative {rs['tok_s']:.0f} tok/s, plain {rp['tok_s']:.0f} tok/s, "
-            f"ratio {rs['tok_s'] / rp['tok_s']:.3f}, MAL {rs['mean_acceptance_length']:.2f}")
+                     "mean_acceptance_length": round(rs["mean_acceptance_length"], 3),
+                     "spec_rounds": rs["rounds"], "spec_round_ms": round(1e3 * rs["wall_s"] / rs["rounds"], 4),
+                     "plain_round_ms": round(1e3 * rp["wall_s"] / rp["rounds"], 4)})
+        log(f"sweep B={B}: speculative {rs['tok_s']:.0f} tok/s ({rs['rounds']} rounds of "
+            f"{1e3 * rs['wall_s'] / rs['rounds']:.3f} ms), plain {rp['tok_s']:.0f} tok/s "
+            f"({1e3 * rp['wall_s'] / rp['rounds']:.3f} ms per token), ratio {rs['tok_s'] / rp['tok_s']:.3f}, "
+            f"MAL {rs['mean_acceptance_length']:.2f}")
     return rows
 
 

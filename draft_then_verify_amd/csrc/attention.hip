@@ -350,9 +350,9 @@ hipError_t launch_mq(const AttnArgs& a, int B, hipStream_t s) {
 // One workgroup per (sequence, query head, block of RW query rows): with few
 // sequences the rows are split until there are enough workgroups to spread
 // over the chip, and each workgroup still sees the whole context, so no
-// workgroup waits for another.  Its 8 waves split the keys (wave w takes
-// 64-key tiles w, w + 8, ...) and merge their partial (max, sum, output) rows
-// in LDS at the end, in wave order.
+// workgroup waits for another.  Its NWV waves split the keys (wave w takes
+// KTD-key tiles w, w + NWV, ...) and merge their partial (max, sum, output)
+// rows in LDS at the end, in wave order.
 // Lane l of a wave works on 16-byte chunk chi = l % CPR of rows
 // rho = l / CPR, rho + RPI, ... of the tile: the K and V loads are coalesced
 // (RPI whole rows per load instruction).  Scores: a lane dots its K chunk with
@@ -376,18 +376,23 @@ template <typename ET, int HD> struct Dec {
   static constexpr int CE = 16 / static_cast<int>(sizeof(ET));        // elements per 16-byte chunk
   static constexpr int CPR = HD / CE;                                 // chunks per K/V row
   static constexpr int RPI = kWave / CPR;                             // rows per load instruction
-  static constexpr int NI = KT / RPI;                                 // load instructions per tile
 };
 
 
-template <typename ET, int HD, int RW>
-__global__ __launch_bounds__(kDecWaves * kWave) __attribute__((amdgpu_waves_per_eu(2))) void attn_decode_kernel(
+// NWV waves of KTD-key tiles: 8 x 64 by default, 16 x 32 for blocks of at
+// most 2 rows (their registers fit the 4 waves per SIMD that 16-wave
+// workgroups need; at ~300 keys all 16 waves then hold keys, where 3 of 8
+// waves of 64-key tiles sat idle: 8B-shaped step 3.639 -> 3.619 ms,
+// 0.6B-shaped drafter rounds 7.45 -> 7.39 ms).
+template <typename ET, int HD, int RW, int NWV, int KTD>
+__global__ __launch_bounds__(NWV * kWave) __attribute__((amdgpu_waves_per_eu(NWV / 4))) void attn_decode_kernel(
     AttnArgs a, int n_rb) {
   using D = Dec<ET, HD>;
-  constexpr int CE = D::CE, CPR = D::CPR, RPI = D::RPI, NI = D::NI, NT = kDecWaves * kWave;
+  constexpr int CE = D::CE, CPR = D::CPR, RPI = D::RPI, NI = KTD / RPI, NT = NWV * kWave;
+  static_assert(NI >= 1 && KTD % RPI == 0, "keys per tile");
   static_assert(CPR == 8 || CPR == 16, "K/V rows of 8 or 16 chunks");
-  __shared__ float mo[kDecWaves][RW][HD];
-  __shared__ float2 ml[kDecWaves][RW];
+  __shared__ float mo[NWV][RW][HD];
+  __shared__ float2 ml[NWV][RW];
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
 
   const int H = a.H, Hkv = a.Hkv, m = a.m;
@@ -399,8 +404,8 @@ __global__ __launch_bounds__(kDecWaves * kWave) __attribute__((amdgpu_waves_per_
   const int Lb = a.len[b];
   // keys the block's rows may see: positions 0 .. Lb + i0 + RW - 1
   const int kend = max(0, min(min(Lb + m, Lb + i0 + RW), a.max_ctx));
-  const int ntiles = (kend + KT - 1) / KT;
-  const int trips = (ntiles + kDecWaves - 1) / kDecWaves;
+  const int ntiles = (kend + KTD - 1) / KTD;
+  const int trips = (ntiles + NWV - 1) / NWV;
   const int qld = H * HD;
   const ET* kc = static_cast<const ET*>(a.kc);
   const ET* vc = static_cast<const ET*>(a.vc);
@@ -427,7 +432,7 @@ __global__ __launch_bounds__(kDecWaves * kWave) __attribute__((amdgpu_waves_per_
   }
 
   for (int it = 0; it < trips; ++it) {
-    const int k0 = (it * kDecWaves + wave) * KT;  // this wave's tile (may lie past kend: all masked)
+    const int k0 = (it * NWV + wave) * KTD;  // this wave's tile (may lie past kend: all masked)
     const int klast = max(kend - 1, 0);
     v4u kr[NI], vr[NI];
 #pragma unroll
@@ -506,10 +511,10 @@ __global__ __launch_bounds__(kDecWaves * kWave) __attribute__((amdgpu_waves_per_
     const int r = idx / HD, dd = idx - r * HD;
     float Mx = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) Mx = fmaxf(Mx, ml[w][r].x);
+    for (int w = 0; w < NWV; ++w) Mx = fmaxf(Mx, ml[w][r].x);
     float l = 0.f, acc = 0.f;
 #pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) {
+    for (int w = 0; w < NWV; ++w) {
       const float2 v = ml[w][r];
       const float wt = (v.x == -INFINITY) ? 0.f : expf(v.x - Mx);
       l = fmaf(v.y, wt, l);
@@ -532,7 +537,9 @@ inline int decode_rows_per_block(int B, int H, int m, int rw_max) {
 template <typename ET, int HD, int RW>
 hipError_t launch_decode_rw(const AttnArgs& a, int B, hipStream_t s) {
   const int n_rb = (a.m + RW - 1) / RW;
-  hipLaunchKernelGGL((attn_decode_kernel<ET, HD, RW>), dim3(B * a.H * n_rb), dim3(kDecWaves * kWave), 0, s, a, n_rb);
+  constexpr int NWV = RW <= 2 ? 16 : kDecWaves, KTD = RW <= 2 ? 32 : KT;
+  hipLaunchKernelGGL((attn_decode_kernel<ET, HD, RW, NWV, KTD>), dim3(B * a.H * n_rb), dim3(NWV * kWave), 0, s, a,
+                     n_rb);
   return hipGetLastError();
 }
 

@@ -33,10 +33,10 @@ template <> struct Cfg<EPI_QKV> { static constexpr int R = 2, U = 4, WPE = 4, BP
 
 template <typename WT> constexpr int step_elems() { return kWave * (16 / static_cast<int>(sizeof(WT))); }
 
-template <typename WT, int M, int U, int EPI>
-hipError_t launch_mu(const GemvArgs& a, hipStream_t s) {
+template <typename WT, int M, int U, int EPI, int NT>
+hipError_t launch_mu_nt(const GemvArgs& a, hipStream_t s) {
   using C = Cfg<EPI>;
-  auto kern = gemv::gemv_kernel<WT, M, C::R, U, EPI, C::WPE, C::NT>;
+  auto kern = gemv::gemv_kernel<WT, M, C::R, U, EPI, C::WPE, NT>;
   static bool lds_opt_in = false;
   if (!lds_opt_in) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -49,10 +49,22 @@ hipError_t launch_mu(const GemvArgs& a, hipStream_t s) {
   const size_t lds = static_cast<size_t>(M) * kp * sizeof(WT);
   const int tiles = gemv::num_tiles<EPI, C::R>(a.N);
   const int per_cu = std::max(1, std::min(C::BPC, static_cast<int>(kMaxLds / std::max<size_t>(lds, 1))));
-  const int wpb = C::NT / kWave;
+  const int wpb = NT / kWave;
   const int bx = std::max(1, std::min((tiles + wpb - 1) / wpb, kCUs * per_cu / a.ksplit));
-  hipLaunchKernelGGL(kern, dim3(bx, a.ksplit), dim3(C::NT), lds, s, a);
+  hipLaunchKernelGGL(kern, dim3(bx, a.ksplit), dim3(NT), lds, s, a);
   return hipGetLastError();
+}
+
+// Wide workgroups unless the launch has too few row tiles to give every CU
+// one: then 256-thread workgroups, so that the stream spreads over all CUs.
+template <typename WT, int M, int U, int EPI>
+hipError_t launch_mu(const GemvArgs& a, hipStream_t s) {
+  using C = Cfg<EPI>;
+  if constexpr (C::NT > 256) {
+    const int tiles = gemv::num_tiles<EPI, C::R>(a.N);
+    if (tiles * a.ksplit < kCUs * (C::NT / kWave)) return launch_mu_nt<WT, M, U, EPI, 256>(a, s);
+  }
+  return launch_mu_nt<WT, M, U, EPI, C::NT>(a, s);
 }
 
 template <typename WT, int M, int EPI>

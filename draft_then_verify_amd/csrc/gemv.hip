@@ -7,7 +7,9 @@
 // MI355X with M = 5, 36 distinct matrices per replayed graph so the weights
 // come from HBM.  Wide workgroups, one per CU, stage the activations once per
 // CU: with 3 narrow workgroups per CU the 40 KB of staged rows per workgroup
-// came to as many bytes as the QKV and O weights themselves.  U is lowered to
+// came to as many bytes as the QKV and O weights themselves.  A launch with
+// fewer row tiles than CUs times the wide shape's waves (the drafter-sized
+// matrices) uses 256-thread workgroups instead, so every CU streams.  U is lowered to
 // the largest of 8, 4, 2, 1 that divides the steps per row.  Activation rows
 // go through in blocks of at most 8 that fit the LDS.  bf16 passes with more than 8 rows go to the matrix-core
 // kernel (gemm_mfma.hpp), which reads the weights once per 64 rows.

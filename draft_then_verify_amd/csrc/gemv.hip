@@ -7,9 +7,9 @@
 // MI355X with M = 5, 36 distinct matrices per replayed graph so the weights
 // come from HBM.  Wide workgroups, one per CU, stage the activations once per
 // CU: with 3 narrow workgroups per CU the 40 KB of staged rows per workgroup
-// came to as many bytes as the QKV and O weights themselves.  A launch with
-// fewer row tiles than CUs times the wide shape's waves (the drafter-sized
-// matrices) uses 256-thread workgroups instead, so every CU streams.  U is lowered to
+// came to as many bytes as the QKV and O weights themselves.  A launch whose
+// wide workgroups would occupy fewer than half the CUs (the drafter-sized O
+// and down) uses 256-thread workgroups instead.  U is lowered to
 // the largest of 8, 4, 2, 1 that divides the steps per row.  Activation rows
 // go through in blocks of at most 8 that fit the LDS.  bf16 passes with more than 8 rows go to the matrix-core
 // kernel (gemm_mfma.hpp), which reads the weights once per 64 rows.
@@ -57,14 +57,17 @@ hipError_t launch_mu_nt(const GemvArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Wide workgroups unless the launch has too few row tiles to give every CU
-// one: then 256-thread workgroups, so that the stream spreads over all CUs.
+// Wide workgroups unless they would occupy fewer than half the CUs: then
+// 256-thread workgroups, so that the stream spreads over the chip.  (The
+// 0.6B-shaped drafter, one row: O and down, 64 wide workgroups, 4.46 -> 4.19
+// and 5.80 -> 4.97 us narrow; QKV and gate/up, 171 and 192 wide workgroups,
+// were faster wide: 6.15 and 6.19 against 6.48 and 6.53 us.)
 template <typename WT, int M, int U, int EPI>
 hipError_t launch_mu(const GemvArgs& a, hipStream_t s) {
   using C = Cfg<EPI>;
   if constexpr (C::NT > 256) {
-    const int tiles = gemv::num_tiles<EPI, C::R>(a.N);
-    if (tiles * a.ksplit < kCUs * (C::NT / kWave)) return launch_mu_nt<WT, M, U, EPI, 256>(a, s);
+    const int wide = (gemv::num_tiles<EPI, C::R>(a.N) + C::NT / kWave - 1) / (C::NT / kWave);
+    if (wide * a.ksplit < kCUs / 2) return launch_mu_nt<WT, M, U, EPI, 256>(a, s);
   }
   return launch_mu_nt<WT, M, U, EPI, C::NT>(a, s);
 }

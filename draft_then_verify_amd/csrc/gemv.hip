@@ -35,10 +35,10 @@ template <> struct Cfg<EPI_QKV> { static constexpr int R = 2, U = 4, WPE = 4, BP
 
 template <typename WT> constexpr int step_elems() { return kWave * (16 / static_cast<int>(sizeof(WT))); }
 
-template <typename WT, int M, int U, int EPI, int NT>
+template <typename WT, int M, int U, int EPI, int NT, int WPE>
 hipError_t launch_mu_nt(const GemvArgs& a, hipStream_t s) {
   using C = Cfg<EPI>;
-  auto kern = gemv::gemv_kernel<WT, M, C::R, U, EPI, C::WPE, NT>;
+  auto kern = gemv::gemv_kernel<WT, M, C::R, U, EPI, WPE, NT>;
   static bool lds_opt_in = false;
   if (!lds_opt_in) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -62,14 +62,27 @@ hipError_t launch_mu_nt(const GemvArgs& a, hipStream_t s) {
 // 0.6B-shaped drafter, one row: O and down, 64 wide workgroups, 4.46 -> 4.19
 // and 5.80 -> 4.97 us narrow; QKV and gate/up, 171 and 192 wide workgroups,
 // were faster wide: 6.15 and 6.19 against 6.48 and 6.53 us.)
+//
+// QKV and gate/up also have a middle shape (512 and 768 threads) for a wide
+// grid between half and all the CUs, taken when it gives every CU a
+// workgroup (the drafter's QKV: 171 wide workgroups -> 256 of 512 threads;
+// its gate/up: 192 -> 256 of 768 threads).
 template <typename WT, int M, int U, int EPI>
 hipError_t launch_mu(const GemvArgs& a, hipStream_t s) {
   using C = Cfg<EPI>;
   if constexpr (C::NT > 256) {
-    const int wide = (gemv::num_tiles<EPI, C::R>(a.N) + C::NT / kWave - 1) / (C::NT / kWave);
-    if (wide * a.ksplit < kCUs / 2) return launch_mu_nt<WT, M, U, EPI, 256>(a, s);
+    const int tiles = gemv::num_tiles<EPI, C::R>(a.N);
+    const int wide = (tiles + C::NT / kWave - 1) / (C::NT / kWave);
+    // the narrower shapes run one workgroup per CU: their register budget is
+    // that of NT / 256 waves per SIMD
+    if (wide * a.ksplit < kCUs / 2) return launch_mu_nt<WT, M, U, EPI, 256, 2>(a, s);
+    if constexpr (EPI == EPI_QKV || EPI == EPI_SWIGLU) {
+      constexpr int MID = EPI == EPI_QKV ? 512 : 768;
+      const int mid = (tiles + MID / kWave - 1) / (MID / kWave);
+      if (wide * a.ksplit < kCUs && mid * a.ksplit >= kCUs) return launch_mu_nt<WT, M, U, EPI, MID, MID / 256>(a, s);
+    }
   }
-  return launch_mu_nt<WT, M, U, EPI, C::NT>(a, s);
+  return launch_mu_nt<WT, M, U, EPI, C::NT, C::WPE>(a, s);
 }
 
 template <typename WT, int M, int EPI>

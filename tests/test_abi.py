@@ -78,3 +78,18 @@ def test_host_checks_reject_before_launch(lib):
     assert lib.spec_ngram_propose(1, 3, 3, 64, 1, None, 8, None, None, 0, None, 1, 1, None, None) == -1
     assert lib.spec_ngram_propose(1, 3, 3, 4, 1, None, 8, 1, None, 4, None, 1, 1, None, None) == -1  # out_len NULL
     assert lib.spec_ngram_propose(1, 3, 3, 4, None, None, 0, 1, 1, 4, 1, 1, 1, None, None) == -1   # fill, no prefix
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """Without the built library the binding raises (there is no fallback
+    path); run in a fresh interpreter, since a loaded library is cached."""
+    import subprocess
+    import sys
+
+    missing = str(tmp_path / "libspecverify.so")
+    code = ("from draft_then_verify_amd import binding as bd\n"
+            f"bd.load_library({missing!r})\n")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                       cwd=str(__import__("pathlib").Path(__file__).resolve().parents[1]))
+    assert r.returncode != 0
+    assert "is missing" in r.stderr and "no fallback" in r.stderr

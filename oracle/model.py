@@ -119,12 +119,9 @@ class Decoder:
         s = self.shape
         return KVCache(self.L, B, s.n_kv_heads, max_ctx, s.head_dim)
 
-    # one linear: y = x W^T with the bf16 input rounding of the precision contract
-    def _lin(self, x: np.ndarray, W: np.ndarray) -> np.ndarray:
-        return linear(x, W, self.bf16)
-
-    def _store(self, x: np.ndarray) -> np.ndarray:
-        return round_bf16(x) if self.bf16 else x
+    def layer_weights(self, layer: int) -> dict:
+        """The weights of one layer (attn_norm, wqkv, wo, mlp_norm, wgu, wd)."""
+        return {k: self.w[k][layer] for k in ("attn_norm", "wqkv", "wo", "mlp_norm", "wgu", "wd")}
 
     def forward(self, cache: KVCache, tokens: np.ndarray, logits: bool = True):
         """tokens [B, m] int -> logits [B, m, V] fp64 (None when ``logits`` is
@@ -132,33 +129,50 @@ class Decoder:
         s, w = self.shape, self.w
         tokens = np.asarray(tokens)
         B, m = tokens.shape
-        H, Hkv, hd, F = s.n_heads, s.n_kv_heads, s.head_dim, s.d_ff
         pos = cache.length[:, None] + np.arange(m)[None, :]  # [B, m]
         if int(pos.max()) >= cache.max_ctx:
             raise ValueError("KV cache too short for this pass")
         h = w["embed"][tokens].astype(np.float64)  # [B, m, d]
         for layer in range(self.L):
-            a = rms_norm(h, w["attn_norm"][layer].astype(np.float64), s.rms_eps)
-            qkv = self._lin(a, w["wqkv"][layer])
-            q = qkv[..., : H * hd].reshape(B, m, H, hd)
-            k = qkv[..., H * hd: (H + Hkv) * hd].reshape(B, m, Hkv, hd)
-            v = qkv[..., (H + Hkv) * hd:].reshape(B, m, Hkv, hd)
-            q = rope(q, pos, s.rope_theta)
-            k = rope(k, pos, s.rope_theta)
-            bidx = np.repeat(np.arange(B), m)
-            cache.k[layer, bidx, :, pos.reshape(-1)] = self._store(k.reshape(B * m, Hkv, hd))
-            cache.v[layer, bidx, :, pos.reshape(-1)] = self._store(v.reshape(B * m, Hkv, hd))
-            o = np.zeros((B, m, H, hd))
-            for b in range(B):
-                for i in range(m):
-                    n_keys = pos[b, i] + 1  # causal: keys 0 .. pos
-                    o[b, i] = attend(q[b, i], cache.k[layer, b, :, :n_keys], cache.v[layer, b, :, :n_keys])
-            h = h + self._lin(o.reshape(B, m, H * hd), w["wo"][layer])
-            a2 = rms_norm(h, w["mlp_norm"][layer].astype(np.float64), s.rms_eps)
-            gu = self._lin(a2, w["wgu"][layer])
-            z = silu(gu[..., :F]) * gu[..., F:]
-            h = h + self._lin(z, w["wd"][layer])
+            h = decoder_layer(s, self.layer_weights(layer), h, cache.k[layer], cache.v[layer], pos, self.bf16)
         if not logits:
             return None
-        a = rms_norm(h, w["final_norm"].astype(np.float64), s.rms_eps)
-        return self._lin(a, w["lm_head"])
+        return final_logits(s, w["final_norm"], w["lm_head"], h, self.bf16)
+
+
+def decoder_layer(s, lw: dict, h: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, pos: np.ndarray,
+                  bf16: bool) -> np.ndarray:
+    """One pre-norm decoder layer over residual rows h [B, m, d] at positions
+    pos [B, m]: attention block then MLP block, each added to the residual.
+    k_cache, v_cache [B, Hkv, max_ctx, hd] are this layer's cache; the new
+    rows are written at pos and row (b, i) attends to keys 0 .. pos[b, i].
+    Returns the new residual rows (fp64)."""
+    B, m = pos.shape
+    H, Hkv, hd, F = s.n_heads, s.n_kv_heads, s.head_dim, s.d_ff
+    store = round_bf16 if bf16 else (lambda x: x)
+    a = rms_norm(h, np.asarray(lw["attn_norm"], np.float64), s.rms_eps)
+    qkv = linear(a, lw["wqkv"], bf16)
+    q = qkv[..., : H * hd].reshape(B, m, H, hd)
+    k = qkv[..., H * hd: (H + Hkv) * hd].reshape(B, m, Hkv, hd)
+    v = qkv[..., (H + Hkv) * hd:].reshape(B, m, Hkv, hd)
+    q = rope(q, pos, s.rope_theta)
+    k = rope(k, pos, s.rope_theta)
+    bidx = np.repeat(np.arange(B), m)
+    k_cache[bidx, :, pos.reshape(-1)] = store(k.reshape(B * m, Hkv, hd))
+    v_cache[bidx, :, pos.reshape(-1)] = store(v.reshape(B * m, Hkv, hd))
+    o = np.zeros((B, m, H, hd))
+    for b in range(B):
+        for i in range(m):
+            n_keys = pos[b, i] + 1  # causal: keys 0 .. pos
+            o[b, i] = attend(q[b, i], k_cache[b, :, :n_keys], v_cache[b, :, :n_keys])
+    h = h + linear(o.reshape(B, m, H * hd), lw["wo"], bf16)
+    a2 = rms_norm(h, np.asarray(lw["mlp_norm"], np.float64), s.rms_eps)
+    gu = linear(a2, lw["wgu"], bf16)
+    z = silu(gu[..., :F]) * gu[..., F:]
+    return h + linear(z, lw["wd"], bf16)
+
+
+def final_logits(s, final_norm, lm_head, h: np.ndarray, bf16: bool) -> np.ndarray:
+    """logits = RMSNorm(h) . W_lm^T (the input rounded to bf16 under the bf16 contract)."""
+    a = rms_norm(h, np.asarray(final_norm, np.float64), s.rms_eps)
+    return linear(a, lm_head, bf16)

@@ -101,7 +101,6 @@ def reject_sample(p: np.ndarray, q, draft: np.ndarray, n_draft, u_acc: np.ndarra
     g = g1 - 1
     draft = np.asarray(draft, dtype=np.int64).reshape(B, g)
     nd = np.full(B, g, dtype=np.int64) if n_draft is None else np.clip(np.asarray(n_draft, np.int64), 0, g)
-    rows = np.arange(B)
     if g > 0:
         p_x = np.take_along_axis(p[:, :g, :], draft[:, :, None], axis=2)[..., 0]
         if q is None:
@@ -113,7 +112,29 @@ def reject_sample(p: np.ndarray, q, draft: np.ndarray, n_draft, u_acc: np.ndarra
     else:
         ok = np.zeros((B, 0), dtype=bool)
     n = accepted_length(ok, nd)
-    pj = p[rows, n]  # [B, V]
+    r = corrected_rows(p, q, draft, n, nd)
+    t = fixed_point_draw(r, np.asarray(u_res, np.float32).reshape(B))
+    emitted = np.full((B, g + 1), -1, dtype=np.int64)
+    for b in range(B):
+        emitted[b, : n[b]] = draft[b, : n[b]]
+        emitted[b, n[b]] = t[b]
+    return n, emitted
+
+
+def corrected_rows(p: np.ndarray, q, draft: np.ndarray, n: np.ndarray, nd: np.ndarray) -> np.ndarray:
+    """Step 4: the row the round's last token is drawn from, per sequence.
+
+    Row j = n of p; after a rejection (n < n_draft) the residual
+    max(0, p_j - q_j) in float32 (a one-hot draft zeroes only the rejected
+    token x_j), else p_j itself (the bonus).  A residual with no mass left on
+    the fixed-point grid falls back to p_j.  p [B, g+1, V], q [B, g, V] or
+    None, draft [B, g], n and nd [B].  Returns float32 [B, V]."""
+    p = np.asarray(p, dtype=np.float32)
+    B, _, V = p.shape
+    n = np.asarray(n, np.int64)
+    nd = np.asarray(nd, np.int64)
+    draft = np.asarray(draft, np.int64).reshape(B, -1)
+    pj = p[np.arange(B), n]  # [B, V]
     r = pj.copy()
     rej = n < nd
     if rej.any():
@@ -122,16 +143,11 @@ def reject_sample(p: np.ndarray, q, draft: np.ndarray, n_draft, u_acc: np.ndarra
             qj = np.zeros((len(idx), V), dtype=np.float32)
             qj[np.arange(len(idx)), draft[idx, n[idx]]] = 1.0
         else:
-            qj = q[idx, n[idx]]
+            qj = np.asarray(q, dtype=np.float32)[idx, n[idx]]
         r[idx] = np.maximum(np.float32(0.0), pj[idx] - qj)
     empty = fixed_point_weights(r).sum(axis=-1, dtype=np.uint64) == 0
     r[empty] = pj[empty]
-    t = fixed_point_draw(r, np.asarray(u_res, np.float32).reshape(B))
-    emitted = np.full((B, g + 1), -1, dtype=np.int64)
-    for b in range(B):
-        emitted[b, : n[b]] = draft[b, : n[b]]
-        emitted[b, n[b]] = t[b]
-    return n, emitted
+    return r
 
 
 def argmax_rows(logits: np.ndarray) -> np.ndarray:

@@ -232,7 +232,7 @@ def batch_sweep(n_new: int, batches=(1, 8, 64, 256), P: int = 256, g: int = 4) -
     rows = []
     for B in batches:
         prompt = make_prompt(B, P, sh.vocab, seed=22 + B)
-        max_ctx = P + n_new + g + 4
+        max_ctx = P + n_new + 2 * g + 4
         spec = SpecDecoder(target, B, g, max_ctx, drafter=ModelDrafter(draft, B, g, max_ctx), seed=23)
         spec.prefill(prompt)
         rs = spec.generate_graph(n_new)
@@ -275,11 +275,10 @@ def ngram_workload(n_new: int, batches=(1, 64), P: int = 2048, g: int = 10) -> l
     for B in batches:
         prompt = markov_prompt(B, P, table, seed=33 + B).astype(np.int64)
         offs = np.random.default_rng(34 + B).integers(0, P - g - 1, size=B)
-        max_ctx = P + n_new + g + 4
+        max_ctx = P + n_new + 2 * g + 4
         spec = SpecDecoder(target, B, g, max_ctx, drafter=DeviceNgramDrafter(B, g, n=3, fill_off=offs), seed=35)
         spec.prefill(prompt)
         rs = spec.generate_graph(n_new)
-        hits = float(spec.drafter.n_found.float().mean().item())
         del spec
         plain = SpecDecoder(target, B, 0, max_ctx, seed=36)
         plain.prefill(prompt)
@@ -289,7 +288,8 @@ def ngram_workload(n_new: int, batches=(1, 64), P: int = 2048, g: int = 10) -> l
         rows.append({"B": B, "spec_tok_s": round(rs["tok_s"], 1), "plain_tok_s": round(rp["tok_s"], 1),
                      "spec_over_plain": round(rs["tok_s"] / rp["tok_s"], 3),
                      "mean_acceptance_length": round(rs["mean_acceptance_length"], 3),
-                     "lookup_tokens_last_round": round(hits, 2),
+                     "ngram_hit_rate": round(rs["ngram_hit_rate"], 4),
+                     "ngram_found_tokens_per_round": round(rs["ngram_found_tokens_per_round"], 3),
                      "note": "random-init target: a one-hot draft is accepted with probability p(x) ~ 1/V, "
                              "so this measures the cost of verifying gamma + 1 = 11 rows per emitted token"})
         log(f"n-gram B={B}: speculative {rs['tok_s']:.0f} tok/s, plain {rp['tok_s']:.0f} tok/s, "
@@ -474,7 +474,7 @@ def main():
     torch.cuda.set_device(dev)
     tshape, dshape = SHAPES["qwen3_8b"], SHAPES["qwen3_0p6b"]
     B, g, P = 1, 4, 256
-    max_ctx = P + args.new_tokens + g + args.steps + args.warmup + 8
+    max_ctx = P + args.new_tokens + 2 * g + args.steps + args.warmup + 8
     t0 = time.perf_counter()
     wt = make_weights(tshape, seed=3, device="cuda")
     wd = make_weights(dshape, seed=4, device="cuda")
@@ -524,11 +524,19 @@ def main():
         plain.prefill(prompt)
         rp = plain.generate_graph(args.new_tokens)
         log(f"plain: {rp['tok_s']:.1f} tok/s")
+        r4 = lambda v: [round(float(x), 4) for x in v]
         gen = {"emitted_tok_s": round(rs["tok_s"], 2), "plain_tok_s": round(rp["tok_s"], 2),
                "spec_over_plain": round(rs["tok_s"] / rp["tok_s"], 3),
                "mean_acceptance_length": round(rs["mean_acceptance_length"], 3),
+               "mean_acceptance_length_ci95": r4(rs["mean_acceptance_length_ci95"]),
                "acceptance_rate": round(rs["acceptance_rate"], 4),
+               "acceptance_rate_ci95": r4(rs["acceptance_rate_ci95"]),
+               "per_position_acceptance": r4(rs["per_position"]),
+               "geometric_fit": {"alpha": round(rs["geometric_alpha"], 4), "mal": round(rs["geometric_mal"], 3)},
+               "rounds": rs["rounds"],
                "round_ms_mean": round(1e3 * rs["wall_s"] / rs["rounds"], 3),
+               "round_ms_p50": round(rs["round_ms_p50"], 3), "round_ms_p99": round(rs["round_ms_p99"], 3),
+               "plain_round_ms_p50": round(rp["round_ms_p50"], 3), "plain_round_ms_p99": round(rp["round_ms_p99"], 3),
                "generation": "graph-replayed rounds (drafter passes, verify step and bookkeeping on the device)"}
         del plain
 

@@ -21,7 +21,8 @@ STATUS = {0: "SPEC_OK", -1: "SPEC_EINVAL", -2: "SPEC_ENOMEM", -3: "SPEC_EHIP", -
 
 # Every symbol the C header declares.
 EXPORTS = ("spec_model_create", "spec_model_destroy", "spec_workspace_bytes", "spec_sampler_workspace_bytes",
-           "spec_verify_forward", "spec_softmax_pq", "spec_reject_sample", "spec_decode_step", "spec_linear",
+           "spec_verify_forward", "spec_verify_forward_trace", "spec_softmax_pq", "spec_reject_sample",
+           "spec_decode_step", "spec_linear",
            "spec_kv_set_len", "spec_last_error", "spec_commit_round", "spec_ngram_propose")
 
 
@@ -51,6 +52,11 @@ class spec_kv(ctypes.Structure):
                 ("max_ctx", ctypes.c_int32)]
 
 
+class spec_trace(ctypes.Structure):
+    _fields_ = [("h", ctypes.c_void_p), ("q", ctypes.c_void_p), ("attn", ctypes.c_void_p), ("h_mid", ctypes.c_void_p),
+                ("mlp", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -70,13 +76,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "spec_workspace_bytes": (sz, [vp, i32, i32, i32]),
         "spec_sampler_workspace_bytes": (sz, [i64, i32, i32]),
         "spec_verify_forward": (i32, [vp, ctypes.POINTER(spec_kv), i32, i32, vp, vp, vp, sz, vp]),
+        "spec_verify_forward_trace": (i32, [vp, ctypes.POINTER(spec_kv), i32, i32, vp, vp, ctypes.POINTER(spec_trace),
+                                            vp, sz, vp]),
         "spec_softmax_pq": (i32, [vp, i64, i32, f32, vp, vp, sz, vp]),
         "spec_reject_sample": (i32, [i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "spec_decode_step": (i32, [vp, ctypes.POINTER(spec_kv), i32, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                    sz, vp]),
         "spec_linear": (i32, [i32, i32, vp, vp, i32, i32, i32, vp, vp, vp]),
         "spec_kv_set_len": (i32, [ctypes.POINTER(spec_kv), i32, vp, i32, vp]),
-        "spec_commit_round": (i32, [i32, i32, vp, vp, vp, vp, vp, vp, i32, vp]),
+        "spec_commit_round": (i32, [i32, i32, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, i32, vp]),
         "spec_ngram_propose": (i32, [i32, i32, i32, i32, vp, vp, i32, vp, vp, i32, vp, vp, vp, vp, vp]),
         "spec_last_error": (ctypes.c_char_p, []),
     }
@@ -196,6 +204,16 @@ def spec_verify_forward(model: SpecModel, kv: KVCache, B: int, m: int, tokens, l
                                               _ptr(logits), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
+def spec_verify_forward_trace(model: SpecModel, kv: KVCache, B: int, m: int, tokens, logits, trace: dict, ws,
+                              stream=None):
+    """trace: dict of device tensors by member name (h, q, attn, h_mid, mlp);
+    missing members are not captured."""
+    t = spec_trace(*[_ptr(trace.get(k)) for k in ("h", "q", "attn", "h_mid", "mlp")])
+    _check(load_library().spec_verify_forward_trace(model.handle, ctypes.byref(kv.struct), B, m, _ptr(tokens),
+                                                    _ptr(logits), ctypes.byref(t), _ptr(ws), _nbytes(ws),
+                                                    _stream(stream)))
+
+
 def spec_softmax_pq(logits, rows: int, vocab: int, temperature: float, probs, ws, stream=None):
     _check(load_library().spec_softmax_pq(_ptr(logits), rows, vocab, temperature, _ptr(probs), _ptr(ws),
                                           _nbytes(ws), _stream(stream)))
@@ -222,9 +240,10 @@ def spec_linear(W, x, M: int, N: int, K: int, epilogue: int = 0, y=None, z=None,
 
 
 def spec_commit_round(B: int, gamma: int, n_accepted, emitted, tok2, last, out_tokens, out_len, cap: int,
-                      stream=None):
+                      n_stop: int = 0, kv_len=None, n_rounds=None, n_log=None, log_cap: int = 0, stream=None):
     _check(load_library().spec_commit_round(B, gamma, _ptr(n_accepted), _ptr(emitted), _ptr(tok2), _ptr(last),
-                                            _ptr(out_tokens), _ptr(out_len), cap, _stream(stream)))
+                                            _ptr(out_tokens), _ptr(out_len), cap, n_stop, _ptr(kv_len),
+                                            _ptr(n_rounds), _ptr(n_log), log_cap, _stream(stream)))
 
 
 def spec_ngram_propose(B: int, n_min: int, n_max: int, gamma: int, prefix, prefix_len, P: int, out, out_len,

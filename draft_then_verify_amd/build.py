@@ -16,7 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libspecverify.so")
-SOURCES = ["gemv.hip", "small_ops.hip", "attention.hip", "sampler.hip", "fused_pass.hip", "capi.hip"]
+SOURCES = ["gemv_epi_swiglu.hip", "gemv_epi_qkv.hip", "gemv_epi_resid.hip", "gemv_epi_partial.hip",
+           "gemv_epi_store.hip", "gemv_epi_lmstat.hip", "attention.hip", "gemv.hip", "small_ops.hip", "sampler.hip", "capi.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

@@ -20,7 +20,6 @@ struct spec_model {
   const float* final_norm;
   std::vector<const float*> attn_norm, mlp_norm;
   std::vector<const void*> wqkv, wo, wgu, wd;
-  sv::FusedLayer* d_layers = nullptr;  // device copy of the per-layer pointers (bf16 models)
 };
 
 namespace {
@@ -48,7 +47,7 @@ size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 struct Layout {
-  size_t h, xn, xo, z, q, cs, po, pml, ctr, pt, logits, part, csum, total;
+  size_t h, xn, xo, z, q, cs, po, pml, ctr, pt, logits, part, csum, tpart, lx, xsel, total;
   int n_split, n_qc, n_ctr, ks_o, ks_d;
 };
 
@@ -60,9 +59,7 @@ Layout make_layout(const spec_model_cfg& c, int B, int m, int max_ctx) {
   const int nch = sv::sampler_chunks(c.vocab);
   L.n_qc = sv::attn_row_blocks(c.n_heads, c.n_kv_heads, c.head_dim, m);
   L.n_split = sv::attn_num_splits(B, c.n_heads, c.n_kv_heads, c.head_dim, m, max_ctx);
-  // attention tickets, or the persistent pass's barrier counters + error word
-  L.n_ctr = std::max(static_cast<int>(sv::attn_counters(B, c.n_heads, c.n_kv_heads, c.head_dim, m)),
-                     sv::kFusedBarrierWords + 64);
+  L.n_ctr = static_cast<int>(sv::attn_counters(B, c.n_heads, c.n_kv_heads, c.head_dim, m));
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -81,9 +78,12 @@ Layout make_layout(const spec_model_cfg& c, int B, int m, int max_ctx) {
   L.ks_o = sv::gemv_ksplit(c.dtype == SPEC_BF16, static_cast<int>(rows), c.d_model, hq);
   L.ks_d = sv::gemv_ksplit(c.dtype == SPEC_BF16, static_cast<int>(rows), c.d_model, c.d_ff);
   L.pt = take(static_cast<size_t>(std::max(L.ks_o, L.ks_d)) * rows * c.d_model * 4);  // K-slice partials
-  L.logits = take(rows * c.vocab * 4);
+  L.logits = take(rows * c.vocab * 4);  // also the recomputed rows [B][vocab] of a fused step
   L.part = take(rows * nch * 8);
   L.csum = take(static_cast<size_t>(B) * nch * 16);
+  L.tpart = take(rows * ((c.vocab + 127) / 128) * 8);  // LM-head tile statistics (fused step)
+  L.lx = take(rows * 4);
+  L.xsel = take(static_cast<size_t>(B) * c.d_model * elt);
   L.total = off;
   return L;
 }
@@ -98,15 +98,16 @@ spec_status check_kv(const spec_model* M, const spec_kv* kv, int B, int m) {
   return SPEC_OK;
 }
 
-// The persistent pass (one launch for every layer and the LM head) serves
-// passes of at most 8 rows of bf16 models when SPEC_FUSED=1 is set in the
-// environment.  It is not the default: measured on MI355X it is slower than
-// the launch-per-step sequence below (8B shape, 5 rows: 4.30 against
-// 3.63 ms; 0.6B shape, 1 row: 1.06 against 0.91 ms), because each dependent
-// step inside it still waits about as long as a kernel boundary costs.
-bool fused_enabled() {
-  const char* e = getenv("SPEC_FUSED");
-  return e && e[0] == '1';
+// Whether a decode step runs the LM head without writing its logits (when
+// the caller does not ask for them).  That needs the matrix-core LM head
+// (bf16, more than 8 rows) and pays one more LM-head pass over the B sampled
+// rows; it is taken when the logits' write and read (2 x rows x vocab x 4
+// bytes) would move more than that extra pass reads (vocab x d_model x 2
+// bytes).  A one-sequence verify pass of the 8B shape writes 3 MB of logits
+// against 1.2 GB of LM head, so it keeps them.
+bool fused_head(const spec_model_cfg& c, int rows) {
+  if (c.dtype != SPEC_BF16 || rows <= 8 || c.d_model % 64) return false;
+  return 2.0 * rows * 4 > 2.0 * c.d_model;
 }
 
 // Launch sequence of one forward pass over B x m rows.  The embedding kernel
@@ -118,9 +119,16 @@ bool fused_enabled() {
 // adds happen in the linears' epilogues and each RMSNorm in the next
 // linear's staging; otherwise the linears write K-slice partials that one
 // small kernel sums into h before normalising.
+// trace (optional): the per-layer values of spec_trace (spec_verify.h).
+// stat (optional, instead of logits): the LM head writes its tile statistics
+// and the drafted tokens' logits (EPI_LMSTAT) rather than the logits.
+struct LmStat {
+  float temperature;
+  const int32_t* draft;
+};
 spec_status run_forward(const spec_model* M, const spec_kv* kv, int B, int m, const int32_t* tokens,
                         const int32_t* last, const int32_t* draft, float* logits, const Layout& L, char* ws,
-                        hipStream_t s) {
+                        hipStream_t s, const spec_trace* trace = nullptr, const LmStat* stat = nullptr) {
   const spec_model_cfg& c = M->cfg;
   const bool bf16 = c.dtype == SPEC_BF16;
   const int rows = B * m;
@@ -132,37 +140,16 @@ spec_status run_forward(const spec_model* M, const spec_kv* kv, int B, int m, co
 
   HIP_TRY(sv::launch_embed(bf16, M->embed, V, d, tokens, last, draft, kv->len, B, m, hd, c.rope_theta,
                            M->attn_norm[0], c.rms_eps, h, xn, cs, ctr, L.n_ctr, s));
-  if (M->d_layers && fused_enabled() && sv::fused_pass_supported(bf16, rows, d, H, Hkv, hd, F)) {
-    sv::FusedArgs fa;
-    fa.layers = M->d_layers;
-    fa.lm_head = M->lm_head;
-    fa.final_norm = M->final_norm;
-    fa.d = d;
-    fa.H = H;
-    fa.Hkv = Hkv;
-    fa.F = F;
-    fa.V = V;
-    fa.L = c.n_layers;
-    fa.eps = c.rms_eps;
-    fa.B = B;
-    fa.m = m;
-    fa.kc = kv->k;
-    fa.vc = kv->v;
-    fa.len = kv->len;
-    fa.kvB = kv->B;
-    fa.max_ctx = kv->max_ctx;
-    fa.cs = cs;
-    fa.xn = xn;
-    fa.h = h;
-    fa.q = reinterpret_cast<float*>(ws + L.q);
-    fa.xo = ws + L.xo;
-    fa.z = ws + L.z;
-    fa.logits = logits;  // NULL: no LM head
-    fa.bar = reinterpret_cast<unsigned*>(ctr);
-    fa.err = ctr + sv::kFusedBarrierWords;
-    HIP_TRY(sv::launch_fused_pass(fa, hd, s));
-    return SPEC_OK;
-  }
+  const size_t elt = bf16 ? 2 : 4;
+  // per-layer copies of the trace: member dst (or NULL) gets bytes from src
+  auto snap = [&](void* dst, int l, const void* src, size_t per_row) -> hipError_t {
+    if (!dst) return hipSuccess;
+    const size_t bytes = static_cast<size_t>(rows) * per_row;
+    return hipMemcpyAsync(static_cast<char*>(dst) + static_cast<size_t>(l) * bytes, src, bytes,
+                          hipMemcpyDeviceToDevice, s);
+  };
+  const spec_trace tr = trace ? *trace : spec_trace{};
+  HIP_TRY(snap(tr.h, 0, h, d * sizeof(float)));
   sv::GemvArgs qkv;
   qkv.N = (H + 2 * Hkv) * hd;
   qkv.K = d;
@@ -229,8 +216,10 @@ spec_status run_forward(const spec_model* M, const spec_kv* kv, int B, int m, co
       qkv.eps = c.rms_eps;
     }
     HIP_TRY(sv::launch_gemv(bf16, sv::EPI_QKV, qkv, rows, s));
+    HIP_TRY(snap(tr.q, l, qkv.q, static_cast<size_t>(H) * hd * sizeof(float)));
     at.layer = l;
     HIP_TRY(sv::launch_attention(bf16, hd, at, B, s));
+    HIP_TRY(snap(tr.attn, l, at.xo, static_cast<size_t>(H) * hd * elt));
     o.W = M->wo[l];
     if (o_direct) {
       sv::GemvArgs od = o;
@@ -243,8 +232,10 @@ spec_status run_forward(const spec_model* M, const spec_kv* kv, int B, int m, co
       HIP_TRY(sv::launch_gemv(bf16, sv::EPI_PARTIAL, o, rows, s));
       HIP_TRY(sv::launch_resid_norm(bf16, h, pt, L.ks_o, pstride, rows, d, M->mlp_norm[l], c.rms_eps, xn, s));
     }
+    HIP_TRY(snap(tr.h_mid, l, h, d * sizeof(float)));
     gu.W = M->wgu[l];
     HIP_TRY(sv::launch_gemv(bf16, sv::EPI_SWIGLU, gu, rows, s));
+    HIP_TRY(snap(tr.mlp, l, gu.z, static_cast<size_t>(F) * elt));
     dn.W = M->wd[l];
     if (d_direct) {
       sv::GemvArgs dd = dn;
@@ -255,8 +246,9 @@ spec_status run_forward(const spec_model* M, const spec_kv* kv, int B, int m, co
       HIP_TRY(sv::launch_resid_norm(bf16, h, pt, L.ks_d, pstride, rows, d,
                                     l + 1 < c.n_layers ? M->attn_norm[l + 1] : M->final_norm, c.rms_eps, xn, s));
     }
+    HIP_TRY(snap(tr.h, l + 1, h, d * sizeof(float)));
   }
-  if (logits) {
+  if (logits || stat) {
     sv::GemvArgs lm;
     lm.W = M->lm_head;
     lm.N = V;
@@ -267,9 +259,18 @@ spec_status run_forward(const spec_model* M, const spec_kv* kv, int B, int m, co
       lm.gain = M->final_norm;
       lm.eps = c.rms_eps;
     }
-    lm.y = logits;
-    lm.ldy = V;
-    HIP_TRY(sv::launch_gemv(bf16, sv::EPI_STORE, lm, rows, s));
+    if (stat) {
+      lm.tpart = reinterpret_cast<float2*>(ws + L.tpart);
+      lm.lx = reinterpret_cast<float*>(ws + L.lx);
+      lm.draft = stat->draft;
+      lm.temp = stat->temperature;
+      lm.m_per_seq = m;
+      HIP_TRY(sv::launch_gemv(bf16, sv::EPI_LMSTAT, lm, rows, s));
+    } else {
+      lm.y = logits;
+      lm.ldy = V;
+      HIP_TRY(sv::launch_gemv(bf16, sv::EPI_STORE, lm, rows, s));
+    }
   }
   return SPEC_OK;
 }
@@ -327,27 +328,11 @@ SPEC_API spec_status spec_model_create(const spec_model_cfg* cfg, const spec_wei
   M->wo.assign(w->wo, w->wo + c.n_layers);
   M->wgu.assign(w->wgu, w->wgu + c.n_layers);
   M->wd.assign(w->wd, w->wd + c.n_layers);
-  if (c.dtype == SPEC_BF16) {
-    std::vector<sv::FusedLayer> t(c.n_layers);
-    for (int l = 0; l < c.n_layers; ++l)
-      t[l] = sv::FusedLayer{w->wqkv[l], w->wo[l], w->wgu[l], w->wd[l], w->attn_norm[l], w->mlp_norm[l]};
-    const size_t bytes = sizeof(sv::FusedLayer) * c.n_layers;
-    e = hipMalloc(&M->d_layers, bytes);
-    if (e == hipSuccess) e = hipMemcpy(M->d_layers, t.data(), bytes, hipMemcpyHostToDevice);
-    if (e != hipSuccess) {
-      if (M->d_layers) (void)hipFree(M->d_layers);
-      delete M;
-      return fail(SPEC_ENOMEM, "layer table: %s", hipGetErrorString(e));
-    }
-  }
   *out = M;
   return SPEC_OK;
 }
 
-SPEC_API void spec_model_destroy(spec_model* model) {
-  if (model && model->d_layers) (void)hipFree(model->d_layers);
-  delete model;
-}
+SPEC_API void spec_model_destroy(spec_model* model) { delete model; }
 
 SPEC_API size_t spec_workspace_bytes(const spec_model* model, int32_t B, int32_t m, int32_t max_ctx) {
   if (!model || B <= 0 || m <= 0 || max_ctx <= 0) return 0;
@@ -369,6 +354,17 @@ SPEC_API spec_status spec_verify_forward(const spec_model* model, const spec_kv*
   const Layout L = make_layout(model->cfg, B, m, kv->max_ctx);
   if (!ws || ws_bytes < L.total) return fail(SPEC_ENOMEM, "workspace %zu bytes < %zu needed", ws_bytes, L.total);
   return run_forward(model, kv, B, m, tokens, nullptr, nullptr, logits, L, static_cast<char*>(ws), stream);
+}
+
+SPEC_API spec_status spec_verify_forward_trace(const spec_model* model, const spec_kv* kv, int32_t B, int32_t m,
+                                               const int32_t* tokens, float* logits, const spec_trace* trace,
+                                               void* ws, size_t ws_bytes, hipStream_t stream) {
+  spec_status st = check_kv(model, kv, B, m);
+  if (st != SPEC_OK) return st;
+  if (!tokens || !trace) return fail(SPEC_EINVAL, "tokens/trace is NULL");
+  const Layout L = make_layout(model->cfg, B, m, kv->max_ctx);
+  if (!ws || ws_bytes < L.total) return fail(SPEC_ENOMEM, "workspace %zu bytes < %zu needed", ws_bytes, L.total);
+  return run_forward(model, kv, B, m, tokens, nullptr, nullptr, logits, L, static_cast<char*>(ws), stream, trace);
 }
 
 namespace {
@@ -427,8 +423,10 @@ SPEC_API spec_status spec_reject_sample(int32_t B, int32_t gamma, int32_t vocab,
   if (!p) return fail(SPEC_EINVAL, "p is NULL");
   const size_t need = spec_sampler_workspace_bytes(0, B, vocab);
   if (!ws || ws_bytes < need) return fail(SPEC_ENOMEM, "workspace %zu bytes < %zu needed", ws_bytes, need);
-  HIP_TRY(sv::launch_reject(B, gamma, vocab, p, nullptr, nullptr, 1.f, q, draft, n_draft, u_acc, u_res, n_accepted,
-                            emitted, nullptr, static_cast<unsigned long long*>(ws), stream));
+  sv::RejectRows rr;
+  rr.p = p;
+  HIP_TRY(sv::launch_reject(rr, B, gamma, vocab, q, draft, n_draft, u_acc, u_res, n_accepted, emitted, nullptr,
+                            static_cast<unsigned long long*>(ws), stream));
   return SPEC_OK;
 }
 
@@ -448,19 +446,58 @@ SPEC_API spec_status spec_decode_step(const spec_model* target, const spec_kv* k
   const Layout L = make_layout(target->cfg, B, m, kv->max_ctx);
   if (!ws || ws_bytes < L.total) return fail(SPEC_ENOMEM, "workspace %zu bytes < %zu needed", ws_bytes, L.total);
   char* w = static_cast<char*>(ws);
+  const int V = target->cfg.vocab;
+  const int rows = B * m;
+  float2* part = reinterpret_cast<float2*>(w + L.part);
+  unsigned long long* csum = reinterpret_cast<unsigned long long*>(w + L.csum);
+  if (!logits_out && fused_head(target->cfg, rows)) {
+    // The LM head leaves its softmax statistics and the drafted tokens'
+    // logits instead of the [rows][vocab] logits; the row each sequence
+    // samples from is recomputed afterwards (same kernel, same bits).
+    const LmStat stat{temperature, draft};
+    st = run_forward(target, kv, B, m, nullptr, last_tok, draft, nullptr, L, w, stream, nullptr, &stat);
+    if (st != SPEC_OK) return st;
+    HIP_TRY(sv::launch_tile_merge(rows, V, reinterpret_cast<const float2*>(w + L.tpart), greedy, part, stream));
+    if (greedy) {
+      HIP_TRY(sv::launch_greedy(B, gamma, V, part, draft, n_draft, n_accepted, emitted, kv->len, stream));
+      return SPEC_OK;
+    }
+    sv::RejectRows rr;
+    rr.part = part;
+    rr.temperature = temperature;
+    rr.lx = reinterpret_cast<const float*>(w + L.lx);
+    HIP_TRY(sv::launch_select_rows(rr, B, gamma, V, q, draft, n_draft, u_acc, w + L.xn, target->cfg.d_model,
+                                   w + L.xsel, stream));
+    float* sel = reinterpret_cast<float*>(w + L.logits);
+    sv::GemvArgs lm;
+    lm.W = target->lm_head;
+    lm.N = V;
+    lm.K = target->cfg.d_model;
+    lm.x = w + L.xsel;
+    lm.y = sel;
+    lm.ldy = V;
+    lm.mfma = true;
+    HIP_TRY(sv::launch_gemv(true, sv::EPI_STORE, lm, B, stream));
+    rr.sel = sel;
+    HIP_TRY(sv::launch_reject(rr, B, gamma, V, q, draft, n_draft, u_acc, u_res, n_accepted, emitted, kv->len, csum,
+                              stream));
+    return SPEC_OK;
+  }
   float* logits = logits_out ? logits_out : reinterpret_cast<float*>(w + L.logits);
   st = run_forward(target, kv, B, m, nullptr, last_tok, draft, logits, L, w, stream);
   if (st != SPEC_OK) return st;
-  const int V = target->cfg.vocab;
-  float2* part = reinterpret_cast<float2*>(w + L.part);
-  st = softmax_rows(logits, static_cast<int64_t>(B) * m, V, temperature, nullptr, part, stream);
+  st = softmax_rows(logits, static_cast<int64_t>(rows), V, temperature, nullptr, part, stream);
   if (st != SPEC_OK) return st;
   if (greedy) {
     HIP_TRY(sv::launch_greedy(B, gamma, V, part, draft, n_draft, n_accepted, emitted, kv->len, stream));
     return SPEC_OK;
   }
-  HIP_TRY(sv::launch_reject(B, gamma, V, nullptr, logits, part, temperature, q, draft, n_draft, u_acc, u_res,
-                            n_accepted, emitted, kv->len, reinterpret_cast<unsigned long long*>(w + L.csum), stream));
+  sv::RejectRows rr;
+  rr.logits = logits;
+  rr.part = part;
+  rr.temperature = temperature;
+  HIP_TRY(sv::launch_reject(rr, B, gamma, V, q, draft, n_draft, u_acc, u_res, n_accepted, emitted, kv->len, csum,
+                            stream));
   return SPEC_OK;
 }
 
@@ -490,11 +527,15 @@ SPEC_API spec_status spec_linear(int32_t dtype, int32_t epilogue, const void* W,
 
 SPEC_API spec_status spec_commit_round(int32_t B, int32_t gamma, const int32_t* n_accepted, const int32_t* emitted,
                                        int32_t* tok2, int32_t* last, int32_t* out_tokens, int32_t* out_len,
-                                       int32_t cap, hipStream_t stream) {
-  if (B <= 0 || gamma < 0 || cap < 0) return fail(SPEC_EINVAL, "B=%d gamma=%d cap=%d", B, gamma, cap);
+                                       int32_t cap, int32_t n_stop, int32_t* kv_len, int32_t* n_rounds,
+                                       int32_t* n_log, int32_t log_cap, hipStream_t stream) {
+  if (B <= 0 || gamma < 0 || cap < 0 || n_stop < 0 || log_cap < 0)
+    return fail(SPEC_EINVAL, "B=%d gamma=%d cap=%d n_stop=%d log_cap=%d", B, gamma, cap, n_stop, log_cap);
   if (!n_accepted || !emitted || !tok2 || !out_len || (cap > 0 && !out_tokens))
     return fail(SPEC_EINVAL, "NULL argument");
-  HIP_TRY(sv::launch_commit_round(B, gamma, n_accepted, emitted, tok2, last, out_tokens, out_len, cap, stream));
+  if (n_log && (!n_rounds || log_cap == 0)) return fail(SPEC_EINVAL, "n_log needs n_rounds and log_cap > 0");
+  HIP_TRY(sv::launch_commit_round(B, gamma, n_accepted, emitted, tok2, last, out_tokens, out_len, cap, n_stop, kv_len,
+                                  n_rounds, n_log, log_cap, stream));
   return SPEC_OK;
 }
 

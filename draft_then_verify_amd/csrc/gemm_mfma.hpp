@@ -33,6 +33,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "lmstat.hpp"
 
 namespace sv {
 namespace mfma {
@@ -153,6 +154,95 @@ __global__ __launch_bounds__(NTH) void gemm_kernel(GemvArgs a, int mtiles, int n
 
   // epilogue: lane holds rows 4 (lane / 16) + r of each 16-row tile, column lane % 16
   const int col = lane & 15, rb = (lane >> 4) * 4;
+  if constexpr (EPI == EPI_LMSTAT) {
+    // Row statistics of the 128-column tile in lmstat.hpp's order: this
+    // wave's 64 columns are half wn of the tile, column wn*64 + 16 j + col in
+    // slot j of lane col.  The two halves meet in LDS.
+    __shared__ float hmax[2][BMT];
+    __shared__ float hsum[2][BMT];
+    __shared__ int hidx[2][BMT];
+    const float T = a.temp;
+    const int N = a.N, nts = (a.N + lmstat::kTile - 1) / lmstat::kTile;
+    const int n0 = nt * lmstat::kTile + wn * 64 + col;
+    auto vals = [&](int i, int r, float (&v)[4]) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = (n0 + j * 16 < N) ? __fdiv_rn(acc[i][j][r], T) : -INFINITY;
+    };
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int lr = wm * (BMT / 2) + i * 16 + rb + r;
+        if (T > 0.f) {
+          float v[4];
+          vals(i, r, v);
+          const float mx = lmstat::group16_max(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+          if (col == 0) hmax[wn][lr] = mx;
+        } else {
+          float mx = -INFINITY;
+          int ix = N;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (n0 + j * 16 < N) lmstat::argmax_merge(mx, ix, acc[i][j][r], n0 + j * 16);
+          lmstat::group16_argmax(mx, ix);
+          if (col == 0) {
+            hmax[wn][lr] = mx;
+            hidx[wn][lr] = ix;
+          }
+        }
+      }
+    __syncthreads();
+    if (T > 0.f) {
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int lr = wm * (BMT / 2) + i * 16 + rb + r;
+          float v[4];
+          vals(i, r, v);
+          const float z = group_sum<16>(lmstat::slot_sum(v, fmaxf(hmax[0][lr], hmax[1][lr])));
+          if (col == 0) hsum[wn][lr] = z;
+        }
+      __syncthreads();
+    }
+    if (wn == 0 && col == 0) {
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int lr = wm * (BMT / 2) + i * 16 + rb + r;
+          const int m = m0 + lr;
+          if (m >= M) continue;
+          float2 st;
+          if (T > 0.f) {
+            st = make_float2(fmaxf(hmax[0][lr], hmax[1][lr]), hsum[0][lr] + hsum[1][lr]);
+          } else {
+            float mx = hmax[0][lr];
+            int ix = hidx[0][lr];
+            lmstat::argmax_merge(mx, ix, hmax[1][lr], hidx[1][lr]);
+            st = make_float2(mx, __int_as_float(ix));
+          }
+          a.tpart[static_cast<size_t>(m) * nts + nt] = st;
+        }
+    }
+    // the logit at the drafted token of each row that scores one
+    const int mps = a.m_per_seq;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + wm * (BMT / 2) + i * 16 + rb + r;
+        if (m >= M || !a.lx) continue;
+        const int rg = a.row0 + m;
+        const int b = rg / mps, ii = rg - b * mps;
+        if (ii >= mps - 1) continue;
+        const int x = a.draft[b * (mps - 1) + ii];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (n0 + j * 16 == x && x < N) a.lx[m] = acc[i][j][r];
+      }
+    return;
+  }
   float* y = a.y ? a.y + static_cast<size_t>(slice) * a.ysplit : nullptr;
 #pragma unroll
   for (int i = 0; i < MI; ++i) {

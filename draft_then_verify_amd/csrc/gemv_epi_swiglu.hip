@@ -1,0 +1,8 @@
+// Instances of the weight-streaming / matrix-core linear for EPI_SWIGLU.
+#include "gemv_launch.hpp"
+
+namespace sv {
+hipError_t launch_gemv_swiglu(bool bf16, const GemvArgs& a, int M, hipStream_t s) {
+  return bf16 ? gemvl::launch_all<uint16_t, EPI_SWIGLU>(a, M, s) : gemvl::launch_all<float, EPI_SWIGLU>(a, M, s);
+}
+}  // namespace sv

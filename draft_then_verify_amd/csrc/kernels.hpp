@@ -7,7 +7,7 @@
 namespace sv {
 
 // ---- weight-streaming linear ---------------------------------------------------
-enum GemvEpi { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_QKV = 3, EPI_PARTIAL = 4 };
+enum GemvEpi { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_QKV = 3, EPI_PARTIAL = 4, EPI_LMSTAT = 5 };
 
 // y[M][N] (op) x[M][K] . W[N][K]^T for any M (in blocks of rows), x in the
 // model dtype.
@@ -19,6 +19,15 @@ enum GemvEpi { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_QKV = 3, EPI_PA
 //  EPI_QKV   : W = [(H + 2 Hkv) hd][K]; q heads rotated into q [M][H hd];
 //              k heads rotated and v heads copied into the KV cache of
 //              `layer` at position len[b] + i (row = b * m_per_seq + i).
+//  EPI_LMSTAT: the LM head without writing logits (bf16, matrix cores
+//              only): per (row, 128-column tile) the softmax statistics of
+//              lmstat.hpp at temperature `temp` (or, at temp = 0, the tile's
+//              (max, lowest argmax as int bits)) into tpart [M][ceil(N/128)],
+//              and lx[row] = the logit of the drafted token the row scores
+//              (row = b * m_per_seq + i, i < m_per_seq - 1 scores
+//              draft[b * (m_per_seq - 1) + i]; ids outside [0, N) are skipped).
+// mfma: take the matrix-core kernel even for M <= 8 (its per-element results
+// do not depend on M, so a recomputed row matches a larger pass bitwise).
 // ldw / ldx: row strides of W and x (0: K).
 // hn: when not NULL the activations are not read from x but made from the
 // float32 residual rows hn [M][K] as cvt(RMSNorm(hn) * gain) while being
@@ -45,6 +54,12 @@ struct GemvArgs {
   void* vc = nullptr;
   const int32_t* len = nullptr;
   int m_per_seq = 1, row0 = 0, layer = 0, kvB = 0, max_ctx = 0;
+  // EPI_LMSTAT
+  float2* tpart = nullptr;
+  float* lx = nullptr;
+  const int32_t* draft = nullptr;
+  float temp = 1.f;
+  bool mfma = false;
 };
 hipError_t launch_gemv(bool bf16, int epi, const GemvArgs& a, int M, hipStream_t s);
 
@@ -99,7 +114,8 @@ bool attn_decode_path(bool bf16, int hd, int m, int max_ctx);
 
 // Round bookkeeping (see spec_commit_round).
 hipError_t launch_commit_round(int B, int gamma, const int32_t* n_acc, const int32_t* emitted, int32_t* tok2,
-                               int32_t* last, int32_t* out, int32_t* out_len, int cap, hipStream_t s);
+                               int32_t* last, int32_t* out, int32_t* out_len, int cap, int n_stop, int32_t* kv_len,
+                               int32_t* n_rounds, int32_t* n_log, int log_cap, hipStream_t s);
 
 // Prompt lookup (see spec_ngram_propose).
 hipError_t launch_ngram(int B, int n_min, int n_max, int gamma, const int32_t* prefix, const int32_t* prefix_len, int P,
@@ -125,49 +141,29 @@ hipError_t launch_onehot_write(int64_t rows, int vocab, const float2* part, floa
 hipError_t launch_greedy(int B, int gamma, int vocab, const float2* part, const int32_t* draft,
                          const int32_t* n_draft, int32_t* n_accepted, int32_t* emitted, int32_t* len_commit,
                          hipStream_t s);
-// Accept / resample / bonus.  Rows come from `p` (materialised) or from
-// logits + part (fused).  csum is [B][chunks] scratch (2 x uint64 each).
-hipError_t launch_reject(int B, int gamma, int vocab, const float* p, const float* logits, const float2* part,
-                         float temperature, const float* q, const int32_t* draft, const int32_t* n_draft,
-                         const float* u_acc, const float* u_res, int32_t* n_accepted, int32_t* emitted,
-                         int32_t* len_commit, unsigned long long* csum, hipStream_t s);
-
-// ---- the persistent pass (fused_pass.hip) -----------------------------------------
-// One cooperative launch runs every layer and the LM head of a pass of at
-// most 8 rows (bf16 models), after launch_embed; the caller sizes `bar` to
-// kFusedBarrierWords words and zeroes them before each launch (launch_embed
-// does, as part of its tickets).
-struct FusedLayer {
-  const void* wqkv;
-  const void* wo;
-  const void* wgu;
-  const void* wd;
-  const float* attn_norm;
-  const float* mlp_norm;
+// Where the sampler's rows come from: materialised probabilities p, or
+// logits + chunk statistics part; for passes whose logits were not written,
+// lx (the logit at each row's drafted token) and sel ([B][vocab], the
+// recomputed logits of the row each sequence samples from).
+struct RejectRows {
+  const float* p = nullptr;
+  const float* logits = nullptr;
+  const float2* part = nullptr;
+  float temperature = 1.f;
+  const float* lx = nullptr;
+  const float* sel = nullptr;
 };
-struct FusedArgs {
-  const FusedLayer* layers;  // device table [L]
-  const void* lm_head;
-  const float* final_norm;
-  int d, H, Hkv, F, V, L;
-  float eps;
-  int B, m;
-  void* kc;
-  void* vc;
-  const int32_t* len;
-  int kvB, max_ctx;
-  const float2* cs;  // RoPE table [M][hd/2] (launch_embed)
-  const void* xn;    // first layer's normalised input [M][d] (launch_embed)
-  float* h;          // residual rows [M][d] (launch_embed)
-  float* q;          // rotated queries [M][H hd]
-  void* xo;          // attention output [M][H hd]
-  void* z;           // SwiGLU output [M][F]
-  float* logits;     // [M][V], or NULL to skip the LM head
-  unsigned* bar;     // barrier counters, zero at launch
-  int* err;          // set to 1 when a barrier wait times out
-};
-constexpr int kFusedBarrierWords = 8 * 64;
-bool fused_pass_supported(bool bf16, int rows, int d, int H, int Hkv, int hd, int F);
-hipError_t launch_fused_pass(const FusedArgs& a, int hd, hipStream_t s);
+// Accept / resample / bonus.  csum is [B][chunks] scratch (2 x uint64 each).
+hipError_t launch_reject(const RejectRows& rr, int B, int gamma, int vocab, const float* q, const int32_t* draft,
+                         const int32_t* n_draft, const float* u_acc, const float* u_res, int32_t* n_accepted,
+                         int32_t* emitted, int32_t* len_commit, unsigned long long* csum, hipStream_t s);
+// Chunk statistics part [rows][chunks] from the LM head's tile statistics
+// tpart [rows][ceil(vocab/128)] (EPI_LMSTAT).
+hipError_t launch_tile_merge(int64_t rows, int vocab, const float2* tpart, bool greedy, float2* part, hipStream_t s);
+// xsel[b] = xn[b * (gamma + 1) + n_b] (bf16 rows of d), n_b from the accept
+// scan: the LM head inputs of the rows the sequences sample from.
+hipError_t launch_select_rows(const RejectRows& rr, int B, int gamma, int vocab, const float* q, const int32_t* draft,
+                              const int32_t* n_draft, const float* u_acc, const void* xn, int d, void* xsel,
+                              hipStream_t s);
 
 }  // namespace sv

@@ -9,7 +9,10 @@
 //
 // Rows of 151936 float32 entries (608 KB) do not fit in LDS, so a row is cut
 // in 4096-entry chunks:
-//   1. row_partials: per (row, chunk) the max and sum of exp(l/T - max).
+//   1. row_partials: per (row, chunk) the max and sum of exp(l/T - max),
+//      built from 128-column tiles in the order of lmstat.hpp -- the order
+//      in which the matrix-core LM head produces them without writing the
+//      logits (tile_merge then turns its tiles into the same chunk pairs).
 //      Every consumer merges the chunk pairs in chunk order, so the row
 //      statistics -- and hence every p(v) = exp(l_v/T - M) / Z -- are bitwise
 //      the same wherever they are used (materialised or fused).
@@ -25,6 +28,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "lmstat.hpp"
 
 namespace sv {
 namespace {
@@ -55,18 +59,33 @@ __device__ __forceinline__ float2 wave_stats(const float2* pr, int nch) {
 // Where a probability row comes from.
 struct RowSrc {
   const float* p;        // materialised rows, or nullptr
-  const float* logits;   // fused: logits + partials
+  const float* logits;   // logits + partials
   const float2* part;
   float T;
   int nch;
   int V;
+  // Large passes whose logits were never written: the LM head gathered the
+  // logit of each row's drafted token (lx [rows]) and the row each sequence
+  // samples from was recomputed (sel [B][V]; rows per sequence m).
+  const float* lx;
+  const float* sel;
+  int m;
   // called by a whole wave
   __device__ __forceinline__ float2 stats(int64_t row) const {
     return p ? make_float2(0.f, 1.f) : wave_stats(part + row * nch, nch);
   }
+  __device__ __forceinline__ float from_logit(float l, float2 st) const {
+    return __fdiv_rn(expf(__fsub_rn(__fdiv_rn(l, T), st.x)), st.y);
+  }
+  // p(v) of the row a sequence samples from (the only full row read)
   __device__ __forceinline__ float prob(int64_t row, int v, float2 st) const {
     if (p) return p[row * V + v];
-    return __fdiv_rn(expf(__fsub_rn(__fdiv_rn(logits[row * V + v], T), st.x)), st.y);
+    const float* l = sel ? sel + (row / m) * V : logits + row * V;
+    return from_logit(l[v], st);
+  }
+  // p(x) at the drafted token x the row scores
+  __device__ __forceinline__ float prob_x(int64_t row, int x, float2 st) const {
+    return lx ? from_logit(lx[row], st) : prob(row, x, st);
   }
 };
 
@@ -93,7 +112,7 @@ __device__ int accept_scan(const RowSrc& src, int b, int gamma, int nd, const fl
         fail = true;
       } else {
         const int64_t row = static_cast<int64_t>(b) * (gamma + 1) + lane;
-        const float px = src.prob(row, x, st_rows[lane]);
+        const float px = src.prob_x(row, x, st_rows[lane]);
         const float qx = q ? q[(static_cast<int64_t>(b) * gamma + lane) * src.V + x] : 1.f;
         fail = !(__fmul_rn(u_acc[b * gamma + lane], qx) <= px);
       }
@@ -133,26 +152,61 @@ __device__ __forceinline__ float sample_mass(float pv, bool use_p, const float* 
   return fmaxf(0.f, __fsub_rn(pv, qv));
 }
 
+// (max, sum exp) of chunk c of a row from materialised logits: 16-lane
+// groups take the chunk's 32 tiles (two each) in lmstat.hpp's order, and
+// thread 0 merges the tiles in order.
 __global__ __launch_bounds__(kThreads) void row_partials_kernel(const float* __restrict__ logits, int V, float T,
                                                                 int nch, float2* __restrict__ part) {
-  __shared__ float red[kThreads / kWave];
+  __shared__ float2 tst[lmstat::kTilesPerChunk];
   const int64_t row = blockIdx.y;
   const int c = blockIdx.x;
   const float* l = logits + row * V;
-  float x[kPer];
-  float mx = -INFINITY;
+  const int col = threadIdx.x & 15, grp = threadIdx.x >> 4;
+  constexpr int kGroups = kThreads / 16;
+  for (int t = grp; t < lmstat::kTilesPerChunk; t += kGroups) {
+    const int c0 = c * kChunk + t * lmstat::kTile + col;
+    float v[2][4];
+    float mx = -INFINITY;
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) {
-    const int v = c * kChunk + e * kThreads + threadIdx.x;
-    x[e] = (v < V) ? __fdiv_rn(l[v], T) : -INFINITY;
-    mx = fmaxf(mx, x[e]);
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int idx = c0 + h * 64 + j * 16;
+        v[h][j] = idx < V ? __fdiv_rn(l[idx], T) : -INFINITY;
+        mx = fmaxf(mx, v[h][j]);
+      }
+    mx = lmstat::group16_max(mx);
+    const float z0 = group_sum<16>(lmstat::slot_sum(v[0], mx));
+    const float z1 = group_sum<16>(lmstat::slot_sum(v[1], mx));
+    if (col == 0) tst[t] = make_float2(mx, z0 + z1);
   }
-  mx = block_max<kThreads>(mx, red);
-  float s = 0.f;
-#pragma unroll
-  for (int e = 0; e < kPer; ++e) s += (x[e] == -INFINITY) ? 0.f : expf(__fsub_rn(x[e], mx));
-  s = block_sum<kThreads>(s, red);
-  if (threadIdx.x == 0) part[row * nch + c] = make_float2(mx, s);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int tiles = min(lmstat::kTilesPerChunk, (V - c * kChunk + lmstat::kTile - 1) / lmstat::kTile);
+    part[row * nch + c] = lmstat::merge_tiles(tst, tiles);
+  }
+}
+
+// Chunk pairs from the LM head's tile statistics (EPI_LMSTAT), one thread
+// per (row, chunk): (M, Z) merged in tile order at T > 0, (max, lowest
+// argmax) at T = 0.
+__global__ __launch_bounds__(kThreads) void tile_merge_kernel(int64_t rows, int V, int nch, int nts, bool greedy,
+                                                              const float2* __restrict__ tpart,
+                                                              float2* __restrict__ part) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (i >= rows * nch) return;
+  const int64_t row = i / nch;
+  const int c = static_cast<int>(i - row * nch);
+  const float2* t = tpart + row * nts + c * lmstat::kTilesPerChunk;
+  const int n = min(lmstat::kTilesPerChunk, nts - c * lmstat::kTilesPerChunk);
+  if (greedy) {
+    float m = -INFINITY;
+    int ix = V;
+    for (int k = 0; k < n; ++k) lmstat::argmax_merge(m, ix, t[k].x, __float_as_int(t[k].y));
+    part[i] = make_float2(m, __int_as_float(ix));
+  } else {
+    part[i] = lmstat::merge_tiles(t, n);
+  }
 }
 
 __global__ __launch_bounds__(kThreads) void softmax_write_kernel(const float* __restrict__ logits, int V, float T,
@@ -301,6 +355,20 @@ __global__ __launch_bounds__(kThreads) void reject_final_kernel(RejectArgs a) {
   }
 }
 
+// The row each sequence samples from (row n after the accept scan) is copied
+// from the LM head's input rows xn [rows][d] to xsel [B][d], for the
+// recompute of that row's logits.
+__global__ __launch_bounds__(kThreads) void select_rows_kernel(RejectArgs a, const uint16_t* __restrict__ xn, int d,
+                                                               uint16_t* __restrict__ xsel) {
+  __shared__ int n_sh;
+  __shared__ float2 st_rows[kMaxRows];
+  const int b = blockIdx.x;
+  const int nd = n_valid(a.n_draft, b, a.gamma);
+  const int n = accept_scan(a.src, b, a.gamma, nd, a.q, a.draft, a.u_acc, st_rows, &n_sh);
+  const uint16_t* src = xn + (static_cast<size_t>(b) * (a.gamma + 1) + n) * d;
+  for (int k = threadIdx.x; k < d; k += kThreads) xsel[static_cast<size_t>(b) * d + k] = src[k];
+}
+
 // ---- temperature 0 ------------------------------------------------------------------
 // At T = 0 the target's distribution is its argmax ("How Speculative Decoding
 // Works", section "Exactness is a choice"): draft x_i is accepted while it
@@ -310,12 +378,7 @@ __global__ __launch_bounds__(kThreads) void reject_final_kernel(RejectArgs a) {
 // The order (larger value, then lower index) is total on non-NaN values, so
 // any reduction tree gives the same (value, index).
 
-__device__ __forceinline__ void argmax_merge(float& m, int& i, float m2, int i2) {
-  if (m2 > m || (m2 == m && i2 < i)) {
-    m = m2;
-    i = i2;
-  }
-}
+using lmstat::argmax_merge;
 
 __device__ __forceinline__ void wave_argmax(float& m, int& i) {
 #pragma unroll
@@ -452,13 +515,40 @@ hipError_t launch_softmax_write(const float* logits, int64_t rows, int vocab, fl
   return hipGetLastError();
 }
 
-hipError_t launch_reject(int B, int gamma, int vocab, const float* p, const float* logits, const float2* part,
-                         float temperature, const float* q, const int32_t* draft, const int32_t* n_draft,
-                         const float* u_acc, const float* u_res, int32_t* n_accepted, int32_t* emitted,
-                         int32_t* len_commit, unsigned long long* csum, hipStream_t s) {
+hipError_t launch_tile_merge(int64_t rows, int vocab, const float2* tpart, bool greedy, float2* part, hipStream_t s) {
   const int nch = sampler_chunks(vocab);
-  RejectArgs a{RowSrc{p, logits, part, temperature, nch, vocab}, gamma, q, draft, n_draft, u_acc, u_res, n_accepted,
-               emitted, len_commit, csum};
+  const int nts = (vocab + lmstat::kTile - 1) / lmstat::kTile;
+  const int64_t n = rows * nch;
+  hipLaunchKernelGGL(tile_merge_kernel, dim3(static_cast<unsigned>((n + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                     s, rows, vocab, nch, nts, greedy, tpart, part);
+  return hipGetLastError();
+}
+
+namespace {
+RejectArgs reject_args(const RejectRows& rr, int B, int gamma, int vocab, const float* q, const int32_t* draft,
+                       const int32_t* n_draft, const float* u_acc, const float* u_res, int32_t* n_accepted,
+                       int32_t* emitted, int32_t* len_commit, unsigned long long* csum) {
+  const int nch = sampler_chunks(vocab);
+  return RejectArgs{RowSrc{rr.p, rr.logits, rr.part, rr.temperature, nch, vocab, rr.lx, rr.sel, gamma + 1},
+                    gamma, q, draft, n_draft, u_acc, u_res, n_accepted, emitted, len_commit, csum};
+}
+}  // namespace
+
+hipError_t launch_select_rows(const RejectRows& rr, int B, int gamma, int vocab, const float* q, const int32_t* draft,
+                              const int32_t* n_draft, const float* u_acc, const void* xn, int d, void* xsel,
+                              hipStream_t s) {
+  RejectArgs a = reject_args(rr, B, gamma, vocab, q, draft, n_draft, u_acc, nullptr, nullptr, nullptr, nullptr, nullptr);
+  hipLaunchKernelGGL(select_rows_kernel, dim3(B), dim3(kThreads), 0, s, a, static_cast<const uint16_t*>(xn), d,
+                     static_cast<uint16_t*>(xsel));
+  return hipGetLastError();
+}
+
+hipError_t launch_reject(const RejectRows& rr, int B, int gamma, int vocab, const float* q, const int32_t* draft,
+                         const int32_t* n_draft, const float* u_acc, const float* u_res, int32_t* n_accepted,
+                         int32_t* emitted, int32_t* len_commit, unsigned long long* csum, hipStream_t s) {
+  const int nch = sampler_chunks(vocab);
+  RejectArgs a = reject_args(rr, B, gamma, vocab, q, draft, n_draft, u_acc, u_res, n_accepted, emitted, len_commit,
+                             csum);
   hipLaunchKernelGGL(reject_chunks_kernel, dim3(nch, B), dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

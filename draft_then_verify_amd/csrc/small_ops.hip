@@ -131,12 +131,18 @@ hipError_t launch_resid_norm_t(float* h, const float* part, int ks, size_t pstri
 __global__ void commit_round_kernel(int B, int gamma, const int32_t* __restrict__ n_acc,
                                     const int32_t* __restrict__ emitted, int32_t* __restrict__ tok2,
                                     int32_t* __restrict__ last, int32_t* __restrict__ out, int32_t* __restrict__ out_len,
-                                    int cap) {
+                                    int cap, int n_stop, int32_t* __restrict__ kv_len, int32_t* __restrict__ n_rounds,
+                                    int32_t* __restrict__ n_log, int log_cap) {
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= B) return;
   const int n = min(max(n_acc[b], 0), gamma);
-  const int32_t* em = emitted + static_cast<size_t>(b) * (gamma + 1);
   const int len = out_len[b];
+  if (n_stop > 0 && len >= n_stop) {
+    // finished before this round: discard the round and undo its KV commit
+    if (kv_len) kv_len[b] -= n + 1;
+    return;
+  }
+  const int32_t* em = emitted + static_cast<size_t>(b) * (gamma + 1);
   for (int i = 0; i <= n; ++i)
     if (len + i < cap) out[static_cast<size_t>(b) * cap + len + i] = em[i];
   out_len[b] = len + n + 1;
@@ -145,6 +151,11 @@ __global__ void commit_round_kernel(int B, int gamma, const int32_t* __restrict_
   tok2[2 * b] = prev;
   tok2[2 * b + 1] = t;
   if (last) last[b] = t;
+  if (n_rounds) {
+    const int r = n_rounds[b];
+    if (n_log && r < log_cap) n_log[static_cast<size_t>(b) * log_cap + r] = n;
+    n_rounds[b] = r + 1;
+  }
 }
 
 // Prompt lookup, one workgroup per sequence: for a match length n every
@@ -250,9 +261,10 @@ hipError_t launch_resid_norm(bool bf16, float* h, const float* part, int ks, siz
 }
 
 hipError_t launch_commit_round(int B, int gamma, const int32_t* n_acc, const int32_t* emitted, int32_t* tok2,
-                               int32_t* last, int32_t* out, int32_t* out_len, int cap, hipStream_t s) {
+                               int32_t* last, int32_t* out, int32_t* out_len, int cap, int n_stop, int32_t* kv_len,
+                               int32_t* n_rounds, int32_t* n_log, int log_cap, hipStream_t s) {
   hipLaunchKernelGGL(commit_round_kernel, dim3((B + 255) / 256), dim3(256), 0, s, B, gamma, n_acc, emitted, tok2,
-                     last, out, out_len, cap);
+                     last, out, out_len, cap, n_stop, kv_len, n_rounds, n_log, log_cap);
   return hipGetLastError();
 }
 

@@ -11,10 +11,11 @@ Drafters:
     its own KV cache and re-feeds the last two committed tokens each round
     (its length is first rewound to the target's length - 1), then samples
     x_i ~ q_i with ``spec_reject_sample(gamma=0)``, all on the device.
-  * NgramDrafter -- prompt lookup on the host [second page, "The three
-    proposers"]; its proposals are one-hot, so q is NULL.
-  * DeviceNgramDrafter -- the same lookup on the device, for graph-replayed
-    rounds with no host round trip.
+  * DeviceNgramDrafter -- prompt lookup on the device [second page, "The
+    three proposers"] (``spec_ngram_propose``); its proposals are one-hot,
+    so q is NULL.  Eager rounds hand it the committed context each round;
+    graph-replayed rounds bind it once to the device buffers the rounds
+    append to.
 Plain decoding (the speed baseline) is ``spec_decode_step`` with gamma = 0.
 """
 
@@ -35,20 +36,50 @@ def _dev_i32(a) -> torch.Tensor:
     return torch.as_tensor(np.ascontiguousarray(a, dtype=np.int32)).cuda()
 
 
-def ngram_lookup(context, n: int, gamma: int, n_max: Optional[int] = None) -> list:
-    """Tokens that followed the most recent earlier occurrence of the last k
-    context tokens (up to gamma of them), for the longest k in [n, n_max]
-    (n_max defaults to n) that occurs; [] when none does."""
-    ctx = list(context)
-    L = len(ctx)
-    for k in range(n if n_max is None else n_max, n - 1, -1):
-        if gamma <= 0 or L < k + 1:
-            continue
-        key = ctx[L - k:]
-        for start in range(L - k - 1, -1, -1):
-            if ctx[start:start + k] == key:
-                return ctx[start + k:start + k + gamma]
-    return []
+def wilson_interval(k: int, n: int, z: float = 1.96) -> tuple:
+    """Wilson score interval of a binomial proportion k / n."""
+    if n <= 0:
+        return (0.0, 1.0)
+    ph = k / n
+    den = 1.0 + z * z / n
+    mid = (ph + z * z / (2 * n)) / den
+    half = z * np.sqrt(ph * (1 - ph) / n + z * z / (4 * n * n)) / den
+    return (float(max(0.0, mid - half)), float(min(1.0, mid + half)))
+
+
+def acceptance_stats(n_rounds, gamma: int) -> dict:
+    """Acceptance figures from the accepted lengths of every round of every
+    sequence (a list of arrays), as the first page reads them off a server's
+    log (section "Checking it on a real system": mean acceptance length,
+    acceptance rate, per-position acceptance over the number of drafts):
+      * per_position[i] = P(n >= i + 1), unconditional;
+      * acceptance_rate = accepted / drafted with its 95% Wilson interval;
+      * mean_acceptance_length = 1 + accepted / rounds with a 95% normal
+        interval over rounds;
+      * the truncated geometric fit of the i.i.d. model of the same page
+        (section "Why gamma has a ceiling": P(n >= i) = alpha^i for
+        i <= gamma): the maximum-likelihood alpha = sum n / (sum n +
+        #{n < gamma}), and the mean acceptance length it predicts,
+        (1 - alpha^(gamma + 1)) / (1 - alpha)."""
+    ns = np.concatenate([np.asarray(x, np.int64).reshape(-1) for x in n_rounds]) if len(n_rounds) else np.zeros(0)
+    R = int(ns.size)
+    out = {"rounds_counted": R}
+    if R == 0 or gamma <= 0:
+        return out
+    acc = int(ns.sum())
+    tokens = 1.0 + ns
+    sd = float(tokens.std(ddof=1)) if R > 1 else 0.0
+    mal = float(tokens.mean())
+    out["mean_acceptance_length"] = mal
+    out["mean_acceptance_length_ci95"] = (float(mal - 1.96 * sd / np.sqrt(R)), float(mal + 1.96 * sd / np.sqrt(R)))
+    out["acceptance_rate"] = acc / (R * gamma)
+    out["acceptance_rate_ci95"] = wilson_interval(acc, R * gamma)
+    out["per_position"] = [float((ns > i).mean()) for i in range(gamma)]
+    short = int((ns < gamma).sum())
+    alpha = acc / (acc + short) if acc + short > 0 else 1.0
+    out["geometric_alpha"] = float(alpha)
+    out["geometric_mal"] = float(gamma + 1 if alpha >= 1.0 else (1 - alpha ** (gamma + 1)) / (1 - alpha))
+    return out
 
 
 class ModelDrafter:
@@ -112,35 +143,6 @@ class ModelDrafter:
         return self.drafts, self.q, None
 
 
-class NgramDrafter:
-    """Prompt lookup with match lengths n_max down to n (n_max defaults to n).
-    ``fill`` supplies gamma tokens when the lookup proposes fewer (so every
-    round verifies B x (gamma+1) rows); the strict hit count is kept either
-    way."""
-
-    kind = "ngram"
-
-    def __init__(self, B: int, gamma: int, n: int = 3, fill=None, n_max: Optional[int] = None):
-        self.B, self.gamma, self.n, self.fill = B, gamma, n, fill
-        self.n_max = n if n_max is None else n_max
-        self.hits = 0
-        self.lookups = 0
-
-    def propose(self, contexts):
-        g = self.gamma
-        drafts = np.zeros((self.B, g), dtype=np.int32)
-        nd = np.zeros(self.B, dtype=np.int32)
-        for b, ctx in enumerate(contexts):
-            prop = ngram_lookup(ctx, self.n, g, self.n_max)
-            self.lookups += 1
-            self.hits += bool(prop)
-            if len(prop) < g and self.fill is not None:
-                prop = list(prop) + list(self.fill(b, len(ctx), g - len(prop)))
-            nd[b] = len(prop)
-            drafts[b, :len(prop)] = prop
-        return drafts, nd
-
-
 class DeviceNgramDrafter:
     """Prompt lookup on the device (``spec_ngram_propose``) for graph-replayed
     rounds: the context is everything committed before the generation started
@@ -158,21 +160,33 @@ class DeviceNgramDrafter:
         self.drafts = torch.empty((B, max(gamma, 1)), dtype=torch.int32, device="cuda")
         self.n_draft = torch.empty(B, dtype=torch.int32, device="cuda")
         self.n_found = torch.empty(B, dtype=torch.int32, device="cuda")
+        # strict hit counts over the unfinished sequences' rounds
+        self.hit_rounds = torch.zeros(B, dtype=torch.int32, device="cuda")
+        self.found_tokens = torch.zeros(B, dtype=torch.int32, device="cuda")
 
-    def bind(self, committed, out, out_len, cap: int):
+    def bind(self, committed, out, out_len, cap: int, n_stop: int = 0):
         """Set the context: committed [B] lists (the prefix rows) and the
-        device buffers the rounds append to."""
+        device buffers the rounds append to; rounds of sequences that hold
+        n_stop tokens already are not counted in the hit statistics."""
         P = max(len(c) for c in committed)
         rows = np.zeros((self.B, P), dtype=np.int32)
         for b, c in enumerate(committed):
             rows[b, :len(c)] = c
         self.prefix = _dev_i32(rows)
         self.prefix_len = _dev_i32([len(c) for c in committed])
-        self.P, self.out, self.out_len, self.cap = P, out, out_len, cap
+        self.P, self.out, self.out_len, self.cap, self.n_stop = P, out, out_len, cap, n_stop
+        if out_len is not None:
+            self.hit_rounds.zero_()
+            self.found_tokens.zero_()
 
     def propose(self):
         bd.spec_ngram_propose(self.B, self.n, self.n_max, self.gamma, self.prefix, self.prefix_len, self.P, self.out,
                               self.out_len, self.cap, self.fill_off, self.drafts, self.n_draft, self.n_found)
+        # statistics only (not part of the proposal): rounds whose lookup found
+        # at least one token, and the tokens it found
+        active = (self.out_len < self.n_stop).int() if (self.n_stop > 0 and self.out_len is not None) else 1
+        self.hit_rounds += (self.n_found > 0).int() * active
+        self.found_tokens += self.n_found * active
         return self.drafts, self.n_draft
 
 
@@ -222,8 +236,10 @@ class SpecDecoder:
                 self.tok2.copy_(torch.as_tensor(pairs))
                 drafts, q, nd = self.drafter.draft(self.tok2, self.kv.len, u_draft)
             else:
-                d_host, nd_host = self.drafter.propose(self.committed)
-                drafts, nd = _dev_i32(d_host), _dev_i32(nd_host)
+                # eager: the proposer's prefix rows are the whole committed context
+                self.drafter.bind(self.committed, None, None, 0)
+                drafts, nd = self.drafter.propose()
+                drafts = drafts[:, :g].contiguous()
         self.last_round = (drafts, q, nd)  # this round's draft inputs, for inspection
         bd.spec_decode_step(self.target, self.kv, B, g, self.T, self.last, drafts, nd, q, u_acc if g else None,
                             u_res, self.n, self.emitted, logits_out, self.ws)
@@ -234,44 +250,55 @@ class SpecDecoder:
         return n, em
 
     def generate(self, n_new: int, preload_uniforms: bool = True) -> dict:
-        """Rounds until every sequence has n_new new tokens (then truncated)."""
+        """Rounds until every sequence has n_new new tokens (then truncated).
+        Acceptance figures count each sequence's rounds until it had n_new."""
         B, g = self.B, self.gamma
         max_rounds = n_new + 1
         pool = [self._uniforms(r) for r in range(max_rounds)] if preload_uniforms else None
         torch.cuda.synchronize()
-        accepted_per_pos = np.zeros(max(g, 1), dtype=np.int64)
-        rounds, accepted, t0 = 0, 0, time.perf_counter()
+        per_seq = [[] for _ in range(B)]
+        rounds, t0 = 0, time.perf_counter()
         round_ms = []
         while min(len(c) for c in self.committed) - self.prompt_len < n_new:
+            done = [len(c) - self.prompt_len >= n_new for c in self.committed]
             t1 = time.perf_counter()
             n, _ = self.round(rounds, pool[rounds] if pool else None)
             round_ms.append((time.perf_counter() - t1) * 1e3)
-            accepted += int(n.sum())
-            for i in range(g):
-                accepted_per_pos[i] += int((n > i).sum())
+            for b in range(B):
+                if not done[b]:
+                    per_seq[b].append(int(n[b]))
             rounds += 1
         wall = time.perf_counter() - t0
         tokens = [c[self.prompt_len:self.prompt_len + n_new] for c in self.committed]
-        num_drafts = rounds * B
-        return {
-            "tokens": tokens, "rounds": rounds, "wall_s": wall, "tok_s": B * n_new / wall,
-            "accepted": accepted, "drafted": num_drafts * g, "num_drafts": num_drafts,
-            "mean_acceptance_length": 1.0 + accepted / num_drafts,
-            "acceptance_rate": accepted / max(num_drafts * g, 1),
-            "per_position": (accepted_per_pos / num_drafts).tolist() if g else [],
-            "round_ms_p50": float(np.percentile(round_ms, 50)), "round_ms_p99": float(np.percentile(round_ms, 99)),
-        }
+        stats = acceptance_stats(per_seq, g)
+        res = {"tokens": tokens, "rounds": rounds, "wall_s": wall, "tok_s": B * n_new / wall,
+               "round_ms_p50": float(np.percentile(round_ms, 50)), "round_ms_p99": float(np.percentile(round_ms, 99)),
+               **stats}
+        if "mean_acceptance_length" not in res:
+            res["mean_acceptance_length"] = 1.0
+            res["acceptance_rate"] = 0.0
+        return res
 
-    def generate_graph(self, n_new: int) -> dict:
+    def generate_graph(self, n_new: int, check=None, logits_out=None) -> dict:
         """The rounds of generate(), with the same uniforms, run as replays of
         one captured HIP graph per round: the drafter's passes, the verify
         step and the round bookkeeping (spec_commit_round) all stay on the
         device.  Per round the host only copies that round's uniforms into the
-        graph's buffers; it reads the output count once per batch of rounds,
-        each batch no longer than the fewest rounds that could finish."""
+        graph's buffers; it reads the output counts once per batch of rounds,
+        each batch no longer than the fewest rounds that could finish.  A
+        sequence that has its n_new tokens is frozen by spec_commit_round (its
+        later rounds are discarded and its KV length restored), so the cache
+        never grows past prompt + n_new + 2 gamma positions.
+
+        ``check(r, info)``, when given, runs after every round (one replay per
+        host synchronisation) with that round's inputs and outputs, for
+        checking graph-replayed rounds against a reference; ``logits_out``
+        [B, gamma+1, V] then receives the verify logits."""
         B, g = self.B, self.gamma
         if g > 0 and not isinstance(self.drafter, (ModelDrafter, DeviceNgramDrafter)):
             raise ValueError("graph rounds need a device drafter (ModelDrafter, DeviceNgramDrafter) or gamma = 0")
+        if max(len(c) for c in self.committed) - 1 + n_new + 2 * g + 1 > self.kv.max_ctx:
+            raise ValueError("KV cache too short: needs prompt + n_new + 2 gamma positions")
         cap = n_new + g + 1
         dev = "cuda"
         tok2 = _dev_i32([[c[-2], c[-1]] for c in self.committed])
@@ -279,6 +306,8 @@ class SpecDecoder:
         out = torch.zeros((B, cap), dtype=torch.int32, device=dev)
         out_len = torch.zeros(B, dtype=torch.int32, device=dev)
         max_rounds = n_new + 1
+        n_rounds = torch.zeros(B, dtype=torch.int32, device=dev)
+        n_log = torch.full((B, max_rounds), -1, dtype=torch.int32, device=dev)
         pool = [self._uniforms(r) for r in range(max_rounds)]
         ua_all = torch.stack([p[0] for p in pool]) if g else None
         ur_all = torch.stack([p[1] for p in pool])
@@ -295,17 +324,37 @@ class SpecDecoder:
 
         ngram = isinstance(self.drafter, DeviceNgramDrafter)
         if ngram:
-            self.drafter.bind(self.committed, out, out_len, cap)
+            self.drafter.bind(self.committed, out, out_len, cap, n_new)
+        drafts = q = nd = None
 
         def body():
-            drafts = q = nd = None
+            nonlocal drafts, q, nd
             if g and ngram:
                 drafts, nd = self.drafter.propose()
             elif g:
                 drafts, q, _ = self.drafter.draft(tok2, self.kv.len, u_draft)
             bd.spec_decode_step(self.target, self.kv, B, g, self.T, last, drafts, nd, q, u_acc, u_res, self.n,
-                                self.emitted, None, self.ws)
-            bd.spec_commit_round(B, g, self.n, self.emitted, tok2, last, out, out_len, cap)
+                                self.emitted, logits_out, self.ws)
+            bd.spec_commit_round(B, g, self.n, self.emitted, tok2, last, out, out_len, cap, n_new, self.kv.len,
+                                 n_rounds, n_log, max_rounds)
+
+        host_ctx = [list(c) for c in self.committed] if check else None
+
+        def after_round(r):
+            torch.cuda.synchronize()
+            ol = out_len.cpu().numpy()
+            toks = out.cpu().numpy()
+            ctx_before = [list(c) for c in host_ctx]
+            for b in range(B):
+                host_ctx[b] = self.committed[b] + list(map(int, toks[b, :min(int(ol[b]), cap)]))
+            u = {"u_acc": ua_all[r].cpu().numpy() if g else np.zeros((B, 0), np.float32),
+                 "u_res": ur_all[r].cpu().numpy(),
+                 "u_draft": ud_all[r].cpu().numpy().T if g else np.zeros((B, 0), np.float32)}
+            check(r, {"context": ctx_before, "drafts": None if drafts is None else drafts[:, :g].cpu().numpy(),
+                      "q": None if q is None else q.cpu().numpy(), "n_draft": None if nd is None else nd.cpu().numpy(),
+                      "u": u, "n": self.n.cpu().numpy(), "emitted": self.emitted.cpu().numpy(),
+                      "logits": None if logits_out is None else logits_out.cpu().numpy(),
+                      "kv_len": self.kv.len.cpu().numpy(), "out_len": ol})
 
         # Round 0 runs eagerly (it also performs every kernel's one-time
         # set-up) and is timed; the capture that follows records the round
@@ -316,29 +365,55 @@ class SpecDecoder:
         body()
         torch.cuda.synchronize()
         wall0 = time.perf_counter() - t0
+        if check:
+            after_round(0)
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             body()
         torch.cuda.synchronize()
+        events = [torch.cuda.Event(enable_timing=True)]
+        events[0].record()
         t0 = time.perf_counter()
         rounds = 1
-        while True:
+        while rounds < max_rounds:
             remaining = n_new - int(out_len.min().item())
             if remaining <= 0:
                 break
-            for _ in range(max(1, -(-remaining // (g + 1)))):
+            batch = 1 if check else max(1, -(-remaining // (g + 1)))
+            for _ in range(min(batch, max_rounds - rounds)):
                 load_uniforms(rounds)
                 graph.replay()
+                ev = torch.cuda.Event(enable_timing=True)
+                ev.record()
+                events.append(ev)
+                if check:
+                    after_round(rounds)
                 rounds += 1
         torch.cuda.synchronize()
         wall = wall0 + time.perf_counter() - t0
         total = out_len.cpu().numpy()
+        if int(total.min()) < n_new:
+            raise RuntimeError("generation did not finish within n_new + 1 rounds")
+        if int(self.kv.len.max().item()) + g + 1 > self.kv.max_ctx:
+            raise RuntimeError("KV length passed max_ctx")
         toks = out.cpu().numpy()
         tokens = [list(map(int, toks[b, :n_new])) for b in range(B)]
         for b in range(B):
             self.committed[b] += list(map(int, toks[b, :min(int(total[b]), cap)]))
-        accepted = int(total.sum()) - rounds * B
-        return {"tokens": tokens, "rounds": rounds, "wall_s": wall, "tok_s": B * n_new / wall,
-                "mean_acceptance_length": 1.0 + accepted / (rounds * B),
-                "acceptance_rate": accepted / max(rounds * B * g, 1)}
-
+        nr = n_rounds.cpu().numpy()
+        logs = n_log.cpu().numpy()
+        stats = acceptance_stats([logs[b, :nr[b]] for b in range(B)], g)
+        round_ms = [events[i].elapsed_time(events[i + 1]) for i in range(len(events) - 1)] if check is None else []
+        res = {"tokens": tokens, "rounds": rounds, "wall_s": wall, "tok_s": B * n_new / wall,
+               "sequence_rounds": nr.tolist(), **stats}
+        if "mean_acceptance_length" not in res:
+            res["mean_acceptance_length"] = 1.0
+            res["acceptance_rate"] = 0.0
+        if round_ms:
+            res["round_ms_p50"] = float(np.percentile(round_ms, 50))
+            res["round_ms_p99"] = float(np.percentile(round_ms, 99))
+        if ngram:
+            hits = int(self.drafter.hit_rounds.sum().item())
+            res["ngram_hit_rate"] = hits / max(int(nr.sum()), 1)
+            res["ngram_found_tokens_per_round"] = int(self.drafter.found_tokens.sum().item()) / max(int(nr.sum()), 1)
+        return res

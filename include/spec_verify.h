@@ -127,16 +127,44 @@ size_t spec_sampler_workspace_bytes(int64_t rows, int32_t B, int32_t vocab);
  *   logits  [B][m][vocab] float32 output, or NULL to skip the LM head
  *           (prefill).
  * Writes the m new K/V rows of every layer; len is unchanged (advance it with
- * spec_kv_set_len).  With SPEC_FUSED=1 in the environment, passes of at most
- * 8 rows of bf16 models run as one persistent launch of one workgroup per CU
- * (cooperative; an ordinary launch under stream capture, which then needs
- * the device free of other work).  Its grid barriers wait a bounded time, so
- * a launch whose workgroups cannot all run ends early, leaving its outputs
- * incomplete, rather than hang.  Errors: SPEC_EINVAL (null/size mismatch,
+ * spec_kv_set_len).  Errors: SPEC_EINVAL (null/size mismatch,
  * kv->B < B), SPEC_ENOMEM (ws_bytes < spec_workspace_bytes), SPEC_EHIP. */
 spec_status spec_verify_forward(const spec_model* model, const spec_kv* kv, int32_t B, int32_t m,
                                 const int32_t* tokens, float* logits, void* ws, size_t ws_bytes,
                                 hipStream_t stream);
+
+/* The values inside a forward pass, per layer, for checking a pass one step
+ * at a time.  The verify pass of the first page (section "What one iteration
+ * actually does") runs every position through the same layer stack; each
+ * member below is the input of the next step in that stack, after its
+ * rounding to the model dtype, so a reference can run every step on exactly
+ * the inputs the kernels had.  rows = B * m, ordered [b][i].  Members are
+ * caller-owned device buffers, each may be NULL (not captured):
+ *   h      [n_layers + 1][rows][d_model] float32: the residual rows entering
+ *          each layer (entry 0: the embedding rows), then the final rows.
+ *   q      [n_layers][rows][n_heads * head_dim] float32: rotated queries.
+ *   attn   [n_layers][rows][n_heads * head_dim] model dtype: attention
+ *          output, the O linear's input.
+ *   h_mid  [n_layers][rows][d_model] float32: residual after the attention
+ *          block.
+ *   mlp    [n_layers][rows][d_ff] model dtype: SwiGLU output, the down
+ *          linear's input.
+ * (The new K and V rows are in the cache.) */
+typedef struct spec_trace {
+  float* h;
+  float* q;
+  void* attn;
+  float* h_mid;
+  void* mlp;
+} spec_trace;
+
+/* spec_verify_forward with its per-layer values copied out (spec_trace):
+ * the same launches and results, plus one device-to-device copy per
+ * captured value and layer.  Errors: as spec_verify_forward; trace NULL is
+ * SPEC_EINVAL. */
+spec_status spec_verify_forward_trace(const spec_model* model, const spec_kv* kv, int32_t B, int32_t m,
+                                      const int32_t* tokens, float* logits, const spec_trace* trace, void* ws,
+                                      size_t ws_bytes, hipStream_t stream);
 
 /* Target/draft probabilities p = softmax(logits / temperature) over `vocab`
  * entries for `rows` rows (p and q of the acceptance rule are the two
@@ -211,9 +239,21 @@ spec_status spec_linear(int32_t dtype, int32_t epilogue, const void* W, const vo
  * and last[b] = t when last is not NULL.
  *   n_accepted [B], emitted [B][gamma+1] as written by spec_decode_step;
  *   tok2 [B][2] in/out; last [B] out or NULL; out_tokens [B][cap];
- *   out_len [B] in/out.  Errors: SPEC_EINVAL, SPEC_EHIP. */
+ *   out_len [B] in/out.
+ *   n_stop     0, or a token count: a sequence whose out_len had already
+ *              reached n_stop before this round is finished and frozen: the
+ *              round's outputs are discarded, and when kv_len is given
+ *              (the target cache's len [B]) the decode step's commit is
+ *              undone (kv_len[b] -= n + 1), so its cache stops growing.
+ *   n_rounds   [B] in/out or NULL: rounds counted for each unfrozen sequence.
+ *   n_log      [B][log_cap] out or NULL (needs n_rounds): n of the sequence's
+ *              k-th counted round at [b][k] for k < log_cap (the accepted
+ *              lengths behind the per-position acceptance counts of the first
+ *              page, section "Checking it on a real system").
+ * Errors: SPEC_EINVAL, SPEC_EHIP. */
 spec_status spec_commit_round(int32_t B, int32_t gamma, const int32_t* n_accepted, const int32_t* emitted,
                               int32_t* tok2, int32_t* last, int32_t* out_tokens, int32_t* out_len, int32_t cap,
+                              int32_t n_stop, int32_t* kv_len, int32_t* n_rounds, int32_t* n_log, int32_t log_cap,
                               hipStream_t stream);
 
 /* Prompt lookup on the device: the n-gram drafter ("05 · Speculative

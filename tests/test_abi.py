@@ -27,7 +27,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = header_functions()
-    assert len(names) == 13
+    assert len(names) == 14
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(bd.EXPORTS) == names
@@ -69,8 +69,11 @@ def test_host_checks_reject_before_launch(lib):
     assert lib.spec_kv_set_len(ctypes.byref(kv), 3, None, 1, None) == -1
     assert lib.spec_verify_forward(None, ctypes.byref(kv), 1, 1, 1, None, 1, 1 << 30, None) == -1
     assert lib.spec_workspace_bytes(None, 1, 1, 16) == 0
-    assert lib.spec_commit_round(0, 4, 1, 1, 1, None, 1, 1, 8, None) == -1
-    assert lib.spec_commit_round(1, 4, None, 1, 1, None, 1, 1, 8, None) == -1
+    assert lib.spec_commit_round(0, 4, 1, 1, 1, None, 1, 1, 8, 0, None, None, None, 0, None) == -1
+    assert lib.spec_commit_round(1, 4, None, 1, 1, None, 1, 1, 8, 0, None, None, None, 0, None) == -1
+    assert lib.spec_commit_round(1, 4, 1, 1, 1, None, 1, 1, 8, -1, None, None, None, 0, None) == -1  # n_stop < 0
+    assert lib.spec_commit_round(1, 4, 1, 1, 1, None, 1, 1, 8, 0, None, None, 1, 4, None) == -1  # log, no counts
+    assert lib.spec_commit_round(1, 4, 1, 1, 1, None, 1, 1, 8, 0, None, 1, 1, 0, None) == -1  # log_cap 0
     # n-gram lookup: 1 <= n_min <= n_max <= 16, gamma in 0..63, buffers present
     assert lib.spec_ngram_propose(1, 0, 3, 4, 1, None, 8, None, None, 0, None, 1, 1, None, None) == -1
     assert lib.spec_ngram_propose(1, 4, 3, 4, 1, None, 8, None, None, 0, None, 1, 1, None, None) == -1

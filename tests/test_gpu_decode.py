@@ -137,3 +137,83 @@ def test_decode_step_greedy_chain_ragged_v151936():
     n, _ = _decode_round(SHAPES["small_v151936"], B=6, g=5, seed=207, ragged=True, n_layers=1, P=24, T=0.0,
                          chain=True)
     assert n.max() > 0
+
+
+def _fused_vs_materialised(shape, B, g, seed, T, onehot, ragged, P=16, rounds=2):
+    """Decode steps of B sequences whose pass takes the LM head without
+    writing logits (more rows than a quarter of d_model): each step is run
+    twice from the same cache state, once with logits_out (materialised
+    logits, then the sampler) and once without (tile statistics in the LM
+    head's epilogue, the sampled rows recomputed).  The integer outputs and
+    the committed lengths must be identical, and the materialised step's
+    integers are the oracle's rule on its own p rows."""
+    w = make_weights(shape, seed=seed, norm="random")
+    max_ctx = P + rounds * (g + 1) + 4
+    model = bd.SpecModel(shape, to_dev(w))
+    kv = bd.KVCache(shape, shape.n_layers, B, max_ctx)
+    prompt = make_prompt(B, P, shape.vocab, seed=seed)
+    gpu_prefill(model, kv, prompt)
+    V = shape.vocab
+    rng = np.random.default_rng(seed)
+    ws = bd.workspace(model.workspace_bytes(B, g + 1, max_ctx))
+    logits = torch.empty((B, g + 1, V), dtype=torch.float32, device="cuda")
+    last = prompt[:, -1].astype(np.int64)
+    greedy = T == 0.0
+    for r in range(rounds):
+        drafts = rng.integers(0, V, size=(B, g))
+        if r == 1 and g > 1:
+            drafts[::3, 0] = -1  # out-of-range ids are rejected drafts
+        nd = rng.integers(0, g + 1, size=B) if ragged else None
+        q = None
+        if not onehot:
+            qlog = torch.randn((B * g, V), device="cuda") * 3
+            qd = gpu_softmax(qlog, V)
+            q = qd.reshape(B, g, V).cpu().numpy()
+        u = round_uniforms(seed, r, B, g)
+        len0 = kv.len.clone()
+        outs = []
+        for lo in (logits, None):
+            kv.len.copy_(len0)
+            n_g = torch.empty(B, dtype=torch.int32, device="cuda")
+            em_g = torch.empty((B, g + 1), dtype=torch.int32, device="cuda")
+            bd.spec_decode_step(model, kv, B, g, T, i32(last), i32(drafts), None if nd is None else i32(nd),
+                                None if (q is None or greedy) else f32(q), None if greedy else f32(u["u_acc"]),
+                                None if greedy else f32(u["u_res"]), n_g, em_g, lo, ws)
+            torch.cuda.synchronize()
+            outs.append((n_g.cpu().numpy(), em_g.cpu().numpy(), kv.len.cpu().numpy()))
+        (n_m, em_m, len_m), (n_f, em_f, len_f) = outs
+        assert np.array_equal(n_m, n_f) and np.array_equal(em_m, em_f) and np.array_equal(len_m, len_f)
+        # the oracle's rule on the step's own rows, for the sequences whose
+        # drafts are all valid ids (the oracle is defined for those only)
+        ok = (drafts >= 0).all(axis=1)
+        lg = logits.cpu().numpy()[ok]
+        if greedy:
+            n_o, em_o = S.greedy_verify(lg, drafts[ok], None if nd is None else nd[ok])
+        else:
+            p_gpu = gpu_softmax(logits, V, T).cpu().numpy()[ok]
+            n_o, em_o = S.reject_sample(p_gpu, None if q is None else q[ok], drafts[ok],
+                                        None if nd is None else nd[ok], u["u_acc"][ok], u["u_res"][ok])
+        assert np.array_equal(n_m[ok], n_o) and np.array_equal(em_m[ok], em_o)
+        last = em_f[np.arange(B), n_f]
+    return n_f
+
+
+@pytest.mark.parametrize("T", [1.0, 0.6, 0.0])
+def test_fused_head_batch_sweep_shape(T):
+    """Config-4 shape at B = 64 (320 verify rows), draft rows q, T in {1, 0.6, 0}."""
+    _fused_vs_materialised(SHAPES["small"].with_(n_layers=2), B=64, g=4, seed=210, T=T, onehot=False, ragged=False)
+
+
+def test_fused_head_ngram_shape_v151936():
+    """Config-5 shape at B = 64 (704 verify rows): one-hot ragged drafts over
+    151936 entries."""
+    _fused_vs_materialised(SHAPES["small_v151936"].with_(n_layers=1), B=64, g=10, seed=211, T=1.0, onehot=True,
+                           ragged=True)
+
+
+def test_fused_head_few_sequences_many_rows():
+    """B = 6 sequences of 63 rows each (378 rows): the recomputed rows are
+    fewer than 8, so the recompute is forced onto the matrix cores, matching
+    the larger pass bitwise."""
+    _fused_vs_materialised(SHAPES["small"].with_(n_layers=1), B=6, g=62, seed=212, T=1.0, onehot=False,
+                           ragged=True, rounds=1)

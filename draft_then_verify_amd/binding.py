@@ -22,7 +22,7 @@ STATUS = {0: "SPEC_OK", -1: "SPEC_EINVAL", -2: "SPEC_ENOMEM", -3: "SPEC_EHIP", -
 # Every symbol the C header declares.
 EXPORTS = ("spec_model_create", "spec_model_destroy", "spec_workspace_bytes", "spec_sampler_workspace_bytes",
            "spec_verify_forward", "spec_verify_forward_trace", "spec_softmax_pq", "spec_reject_sample",
-           "spec_decode_step", "spec_linear",
+           "spec_decode_step", "spec_decode_step_static", "spec_linear",
            "spec_kv_set_len", "spec_last_error", "spec_commit_round", "spec_ngram_propose")
 
 
@@ -82,6 +82,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "spec_reject_sample": (i32, [i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "spec_decode_step": (i32, [vp, ctypes.POINTER(spec_kv), i32, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                    sz, vp]),
+        "spec_decode_step_static": (i32, [vp, ctypes.POINTER(spec_kv), i32, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                          vp, vp]),
         "spec_linear": (i32, [i32, i32, vp, vp, i32, i32, i32, vp, vp, vp]),
         "spec_kv_set_len": (i32, [ctypes.POINTER(spec_kv), i32, vp, i32, vp]),
         "spec_commit_round": (i32, [i32, i32, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, i32, vp]),
@@ -232,6 +234,14 @@ def spec_decode_step(target: SpecModel, kv: KVCache, B: int, gamma: int, tempera
                                            _ptr(last_tok), _ptr(draft), _ptr(n_draft), _ptr(q), _ptr(u_acc),
                                            _ptr(u_res), _ptr(n_accepted), _ptr(emitted), _ptr(logits_out), _ptr(ws),
                                            _nbytes(ws), _stream(stream)))
+
+
+def spec_decode_step_static(target: SpecModel, kv: KVCache, B: int, gamma: int, temperature: float, last_tok, draft,
+                            n_draft, q, u_acc, u_res, n_accepted, emitted, logits_out, stream=None):
+    _check(load_library().spec_decode_step_static(target.handle, ctypes.byref(kv.struct), B, gamma, temperature,
+                                                  _ptr(last_tok), _ptr(draft), _ptr(n_draft), _ptr(q), _ptr(u_acc),
+                                                  _ptr(u_res), _ptr(n_accepted), _ptr(emitted), _ptr(logits_out),
+                                                  _stream(stream)))
 
 
 def spec_linear(W, x, M: int, N: int, K: int, epilogue: int = 0, y=None, z=None, stream=None):

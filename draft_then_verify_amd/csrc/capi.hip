@@ -5,6 +5,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -499,6 +500,56 @@ SPEC_API spec_status spec_decode_step(const spec_model* target, const spec_kv* k
   HIP_TRY(sv::launch_reject(rr, B, gamma, V, q, draft, n_draft, u_acc, u_res, n_accepted, emitted, kv->len, csum,
                             stream));
   return SPEC_OK;
+}
+
+// ---- the decode step with a workspace inside the library ----------------------------
+// For callers that cannot allocate: each GPU holds one copy of `scratch` for
+// the life of the process.  Host code never passes the array's name to a
+// kernel (on the host it is only a stand-in for the symbol): the device
+// address of each GPU's copy is looked up once, with that device current, and
+// kept per device.
+namespace {
+constexpr size_t kScratchBytes = static_cast<size_t>(SPEC_STATIC_WORKSPACE_BYTES);
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+spec_status scratch_address(void** out) {
+  int dev = -1;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(SPEC_EDEVICE, "device %d outside 0..%d", dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return fail(SPEC_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SPEC_OK;
+}
+}  // namespace
+
+SPEC_API spec_status spec_decode_step_static(const spec_model* target, const spec_kv* kv, int32_t B, int32_t gamma,
+                                             float temperature, const int32_t* last_tok, const int32_t* draft,
+                                             const int32_t* n_draft, const float* q, const float* u_acc,
+                                             const float* u_res, int32_t* n_accepted, int32_t* emitted,
+                                             float* logits_out, hipStream_t stream) {
+  spec_status st = check_kv(target, kv, B, gamma + 1);
+  if (st != SPEC_OK) return st;
+  const size_t need = make_layout(target->cfg, B, gamma + 1, kv->max_ctx).total;
+  if (need > kScratchBytes)
+    return fail(SPEC_EUNSUPPORTED, "this step needs %zu bytes of workspace; the library's holds %zu", need,
+                kScratchBytes);
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != SPEC_OK) return st;
+  return spec_decode_step(target, kv, B, gamma, temperature, last_tok, draft, n_draft, q, u_acc, u_res, n_accepted,
+                          emitted, logits_out, ws, kScratchBytes, stream);
 }
 
 SPEC_API spec_status spec_linear(int32_t dtype, int32_t epilogue, const void* W, const void* x, int32_t M, int32_t N,

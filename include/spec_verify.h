@@ -216,6 +216,25 @@ spec_status spec_decode_step(const spec_model* target, const spec_kv* kv, int32_
                              const float* u_res, int32_t* n_accepted, int32_t* emitted,
                              float* logits_out, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* spec_decode_step for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops or harnesses that forbid hipMalloc):
+ * the workspace is a device array inside the library,
+ * SPEC_STATIC_WORKSPACE_BYTES per GPU, held by each GPU the library runs on
+ * until the process ends.  The caller still owns the KV cache, the inputs
+ * and the outputs.  Calls no allocating routine.  Every call on a GPU uses
+ * that GPU's one array: calls that overlap on one GPU (other streams, other
+ * threads) race and their results are undefined; calls in stream order are
+ * safe (nothing in the array carries over from one call to the next).
+ * Arguments and results as spec_decode_step.  Errors: as spec_decode_step,
+ * and SPEC_EUNSUPPORTED when the step's workspace (spec_workspace_bytes of
+ * B sequences x gamma + 1 rows) exceeds the array. */
+#define SPEC_STATIC_WORKSPACE_BYTES (64u * 1024u * 1024u)
+spec_status spec_decode_step_static(const spec_model* target, const spec_kv* kv, int32_t B, int32_t gamma,
+                                    float temperature, const int32_t* last_tok, const int32_t* draft,
+                                    const int32_t* n_draft, const float* q, const float* u_acc,
+                                    const float* u_res, int32_t* n_accepted, int32_t* emitted, float* logits_out,
+                                    hipStream_t stream);
+
 /* The weight-streaming linear of the verify pass on its own: y = x . W^T for
  * M rows, every weight byte read once per block of 8 rows (a verify pass
  * streams the same weight bytes whatever the number of positions it scores,

@@ -84,7 +84,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                    sz, vp]),
         "spec_decode_step_static": (i32, [vp, ctypes.POINTER(spec_kv), i32, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp,
                                           vp, vp]),
-        "spec_linear": (i32, [i32, i32, vp, vp, i32, i32, i32, vp, vp, vp]),
+        "spec_linear": (i32, [i32, i32, vp, vp, i32, i32, i32, vp, vp, vp, vp, f32, vp]),
         "spec_kv_set_len": (i32, [ctypes.POINTER(spec_kv), i32, vp, i32, vp]),
         "spec_commit_round": (i32, [i32, i32, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, i32, vp]),
         "spec_ngram_propose": (i32, [i32, i32, i32, i32, vp, vp, i32, vp, vp, i32, vp, vp, vp, vp, vp]),
@@ -244,9 +244,12 @@ def spec_decode_step_static(target: SpecModel, kv: KVCache, B: int, gamma: int, 
                                                   _stream(stream)))
 
 
-def spec_linear(W, x, M: int, N: int, K: int, epilogue: int = 0, y=None, z=None, stream=None):
+def spec_linear(W, x, M: int, N: int, K: int, epilogue: int = 0, y=None, z=None, hn=None, gain=None, eps: float = 1e-6,
+                stream=None):
+    """y / z from x, or (hn given) from RMSNorm(hn) * gain made while staging."""
     dt = SPEC_BF16 if W.dtype == torch.bfloat16 else SPEC_F32
-    _check(load_library().spec_linear(dt, epilogue, _ptr(W), _ptr(x), M, N, K, _ptr(y), _ptr(z), _stream(stream)))
+    _check(load_library().spec_linear(dt, epilogue, _ptr(W), _ptr(x), M, N, K, _ptr(y), _ptr(z), _ptr(hn), _ptr(gain),
+                                      eps, _stream(stream)))
 
 
 def spec_commit_round(B: int, gamma: int, n_accepted, emitted, tok2, last, out_tokens, out_len, cap: int,

@@ -346,6 +346,50 @@ SPEC_API size_t spec_sampler_workspace_bytes(int64_t rows, int32_t B, int32_t vo
   return up(static_cast<size_t>(rows) * nch * 8) + up(static_cast<size_t>(B) * nch * 16);
 }
 
+// ---- validation mode (SPEC_CHECK=1) -------------------------------------------------
+// The checks write one flag word, a device variable of the library looked up
+// per device (its host-side name is only a stand-in for the symbol).
+namespace {
+bool check_mode() {
+  const char* e = getenv("SPEC_CHECK");
+  return e && e[0] == '1';
+}
+std::mutex g_flag_mu;
+int* g_flag_ptr[64] = {};
+}  // namespace
+
+static __device__ int check_flag;
+
+namespace {
+spec_status check_begin(int** flag, hipStream_t s) {
+  int dev = -1;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= 64) return fail(SPEC_EDEVICE, "device %d outside 0..63", dev);
+  {
+    std::lock_guard<std::mutex> lock(g_flag_mu);
+    if (!g_flag_ptr[dev]) {
+      void* p = nullptr;
+      const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(check_flag));
+      if (e != hipSuccess || !p) return fail(SPEC_EHIP, "hipGetSymbolAddress(check_flag): %s", hipGetErrorString(e));
+      g_flag_ptr[dev] = static_cast<int*>(p);
+    }
+    *flag = g_flag_ptr[dev];
+  }
+  HIP_TRY(sv::launch_check_clear(*flag, s));
+  return SPEC_OK;
+}
+
+// Waits for the stream, then reports what the checks found.
+spec_status check_end(int* flag, hipStream_t s, const char* call) {
+  HIP_TRY(hipStreamSynchronize(s));
+  int h = 0;
+  HIP_TRY(hipMemcpy(&h, flag, sizeof(int), hipMemcpyDeviceToHost));
+  if (h & 1) return fail(SPEC_EDEVICE, "%s: a token id outside [0, vocab) (SPEC_CHECK)", call);
+  if (h & 2) return fail(SPEC_EDEVICE, "%s: a non-finite logit or probability (SPEC_CHECK)", call);
+  return SPEC_OK;
+}
+}  // namespace
+
 SPEC_API spec_status spec_verify_forward(const spec_model* model, const spec_kv* kv, int32_t B, int32_t m,
                                          const int32_t* tokens, float* logits, void* ws, size_t ws_bytes,
                                          hipStream_t stream) {
@@ -354,7 +398,14 @@ SPEC_API spec_status spec_verify_forward(const spec_model* model, const spec_kv*
   if (!tokens) return fail(SPEC_EINVAL, "tokens is NULL");
   const Layout L = make_layout(model->cfg, B, m, kv->max_ctx);
   if (!ws || ws_bytes < L.total) return fail(SPEC_ENOMEM, "workspace %zu bytes < %zu needed", ws_bytes, L.total);
-  return run_forward(model, kv, B, m, tokens, nullptr, nullptr, logits, L, static_cast<char*>(ws), stream);
+  st = run_forward(model, kv, B, m, tokens, nullptr, nullptr, logits, L, static_cast<char*>(ws), stream);
+  if (st != SPEC_OK || !check_mode()) return st;
+  int* flag = nullptr;
+  if ((st = check_begin(&flag, stream)) != SPEC_OK) return st;
+  const int V = model->cfg.vocab;
+  HIP_TRY(sv::launch_check_ids(tokens, B, m, nullptr, V, flag, stream));
+  HIP_TRY(sv::launch_check_finite(logits, static_cast<int64_t>(B) * m * V, flag, stream));
+  return check_end(flag, stream, "spec_verify_forward");
 }
 
 SPEC_API spec_status spec_verify_forward_trace(const spec_model* model, const spec_kv* kv, int32_t B, int32_t m,
@@ -398,7 +449,12 @@ SPEC_API spec_status spec_softmax_pq(const float* logits, int64_t rows, int32_t 
   if (rows == 0) return SPEC_OK;
   const size_t need = spec_sampler_workspace_bytes(rows, 0, vocab);
   if (!ws || ws_bytes < need) return fail(SPEC_ENOMEM, "workspace %zu bytes < %zu needed", ws_bytes, need);
-  return softmax_rows(logits, rows, vocab, temperature, probs, static_cast<float2*>(ws), stream);
+  spec_status st = softmax_rows(logits, rows, vocab, temperature, probs, static_cast<float2*>(ws), stream);
+  if (st != SPEC_OK || !check_mode()) return st;
+  int* flag = nullptr;
+  if ((st = check_begin(&flag, stream)) != SPEC_OK) return st;
+  HIP_TRY(sv::launch_check_finite(logits, rows * vocab, flag, stream));
+  return check_end(flag, stream, "spec_softmax_pq");
 }
 
 namespace {
@@ -428,7 +484,13 @@ SPEC_API spec_status spec_reject_sample(int32_t B, int32_t gamma, int32_t vocab,
   rr.p = p;
   HIP_TRY(sv::launch_reject(rr, B, gamma, vocab, q, draft, n_draft, u_acc, u_res, n_accepted, emitted, nullptr,
                             static_cast<unsigned long long*>(ws), stream));
-  return SPEC_OK;
+  if (!check_mode()) return SPEC_OK;
+  int* flag = nullptr;
+  if ((st = check_begin(&flag, stream)) != SPEC_OK) return st;
+  HIP_TRY(sv::launch_check_ids(draft, B, gamma, n_draft, vocab, flag, stream));
+  HIP_TRY(sv::launch_check_finite(p, static_cast<int64_t>(B) * (gamma + 1) * vocab, flag, stream));
+  HIP_TRY(sv::launch_check_finite(q, static_cast<int64_t>(B) * gamma * vocab, flag, stream));
+  return check_end(flag, stream, "spec_reject_sample");
 }
 
 SPEC_API spec_status spec_decode_step(const spec_model* target, const spec_kv* kv, int32_t B, int32_t gamma,
@@ -451,7 +513,8 @@ SPEC_API spec_status spec_decode_step(const spec_model* target, const spec_kv* k
   const int rows = B * m;
   float2* part = reinterpret_cast<float2*>(w + L.part);
   unsigned long long* csum = reinterpret_cast<unsigned long long*>(w + L.csum);
-  if (!logits_out && fused_head(target->cfg, rows)) {
+  const bool check = check_mode();
+  if (!logits_out && !check && fused_head(target->cfg, rows)) {
     // The LM head leaves its softmax statistics and the drafted tokens'
     // logits instead of the [rows][vocab] logits; the row each sequence
     // samples from is recomputed afterwards (same kernel, same bits).
@@ -491,15 +554,22 @@ SPEC_API spec_status spec_decode_step(const spec_model* target, const spec_kv* k
   if (st != SPEC_OK) return st;
   if (greedy) {
     HIP_TRY(sv::launch_greedy(B, gamma, V, part, draft, n_draft, n_accepted, emitted, kv->len, stream));
-    return SPEC_OK;
+  } else {
+    sv::RejectRows rr;
+    rr.logits = logits;
+    rr.part = part;
+    rr.temperature = temperature;
+    HIP_TRY(sv::launch_reject(rr, B, gamma, V, q, draft, n_draft, u_acc, u_res, n_accepted, emitted, kv->len, csum,
+                              stream));
   }
-  sv::RejectRows rr;
-  rr.logits = logits;
-  rr.part = part;
-  rr.temperature = temperature;
-  HIP_TRY(sv::launch_reject(rr, B, gamma, V, q, draft, n_draft, u_acc, u_res, n_accepted, emitted, kv->len, csum,
-                            stream));
-  return SPEC_OK;
+  if (!check) return SPEC_OK;
+  int* flag = nullptr;
+  if ((st = check_begin(&flag, stream)) != SPEC_OK) return st;
+  HIP_TRY(sv::launch_check_ids(last_tok, B, 1, nullptr, V, flag, stream));
+  HIP_TRY(sv::launch_check_ids(draft, B, gamma, n_draft, V, flag, stream));
+  HIP_TRY(sv::launch_check_finite(logits, static_cast<int64_t>(rows) * V, flag, stream));
+  if (!greedy) HIP_TRY(sv::launch_check_finite(q, static_cast<int64_t>(B) * gamma * V, flag, stream));
+  return check_end(flag, stream, "spec_decode_step");
 }
 
 // ---- the decode step with a workspace inside the library ----------------------------
@@ -553,13 +623,21 @@ SPEC_API spec_status spec_decode_step_static(const spec_model* target, const spe
 }
 
 SPEC_API spec_status spec_linear(int32_t dtype, int32_t epilogue, const void* W, const void* x, int32_t M, int32_t N,
-                                 int32_t K, float* y, void* z, hipStream_t stream) {
+                                 int32_t K, float* y, void* z, const float* hn, const float* gain, float eps,
+                                 hipStream_t stream) {
   if (dtype != SPEC_F32 && dtype != SPEC_BF16) return fail(SPEC_EINVAL, "dtype %d", dtype);
   if (epilogue < 0 || epilogue > 2) return fail(SPEC_EINVAL, "epilogue %d", epilogue);
   if (M <= 0 || N <= 0 || K <= 0) return fail(SPEC_EINVAL, "M=%d N=%d K=%d", M, N, K);
   const int vec = dtype == SPEC_BF16 ? 8 : 4;
   if (K % vec) return fail(SPEC_EINVAL, "K=%d not a multiple of %d", K, vec);
-  if (!W || !x || !aligned16(W) || !aligned16(x)) return fail(SPEC_EINVAL, "W/x NULL or not 16-byte aligned");
+  if (!W || !aligned16(W)) return fail(SPEC_EINVAL, "W NULL or not 16-byte aligned");
+  if (hn) {
+    if (!gain || !aligned16(hn) || !aligned16(gain)) return fail(SPEC_EINVAL, "hn/gain NULL or not 16-byte aligned");
+    if (M > 8 || K > 4096 || !(eps >= 0.f))
+      return fail(SPEC_EINVAL, "normalised input: M=%d must be <= 8, K=%d <= 4096, eps >= 0", M, K);
+  } else if (!x || !aligned16(x)) {
+    return fail(SPEC_EINVAL, "x NULL or not 16-byte aligned");
+  }
   if (epilogue == 2 ? !z : !y) return fail(SPEC_EINVAL, "output pointer NULL");
   if (static_cast<size_t>(K) * (dtype == SPEC_BF16 ? 2 : 4) > 159 * 1024)
     return fail(SPEC_EINVAL, "K=%d: an input row must fit the 159 KiB of LDS", K);
@@ -567,7 +645,10 @@ SPEC_API spec_status spec_linear(int32_t dtype, int32_t epilogue, const void* W,
   a.W = W;
   a.N = N;
   a.K = K;
-  a.x = x;
+  a.x = hn ? nullptr : x;
+  a.hn = hn;
+  a.gain = gain;
+  a.eps = eps;
   a.y = y;
   a.ldy = N;
   a.z = z;

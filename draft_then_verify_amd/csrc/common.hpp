@@ -13,13 +13,10 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
 
-// float32 -> bfloat16, round to nearest, ties to even; NaN stays NaN.
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u) return static_cast<uint16_t>((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
-}
+// float32 -> bfloat16, round to nearest, ties to even; NaN stays NaN.  One
+// v_cvt_pk_bf16_f32 on gfx950 (a bit-level rounding with its NaN test costs
+// about 20 instructions and an exec-mask branch per element).
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f)); }
 
 // Model element type: float (f32 models) or uint16_t holding bf16 bits.
 template <typename T> struct Elt;
@@ -141,69 +138,94 @@ __device__ __forceinline__ unsigned long long block_sum_u64(unsigned long long v
 // ld % 4 == 0.  In two halves: norm_issue puts every load of the rows in
 // flight (16-byte loads, indexes clamped, surplus chunks weigh zero: one
 // memory round trip), norm_commit reduces and writes, so a caller can issue
-// other loads in between.  Fixed order: per-thread sums, wave butterflies,
-// waves in index order.
+// other loads in between.  The sum of squares is taken in one fixed order
+// whatever the workgroup size, so every RMSNorm of the library gives the
+// same bits for the same row: the row is cut into blocks of 64 16-byte
+// chunks (256 elements); in a block each lane adds the squares of its 4
+// elements (one fma chain), the wave adds its lanes by butterfly, and the
+// block sums are added in block order.
+constexpr int kNormBlocks = 16;  // blocks of a row of at most 4096 elements
 template <int NT, int G> struct NormRegs {
   static constexpr int CPT = (4 * 256 + NT - 1) / NT;  // 16-byte chunks per thread and row (d <= 4096)
   float4 v[G][CPT];
+  float4 g[CPT];  // the gain's chunks (loaded with the rows: loads return in issue order)
 };
 
 template <int NT, int G>
-__device__ __forceinline__ void norm_issue(const float* h, int ld, int d, NormRegs<NT, G>& r) {
+__device__ __forceinline__ void norm_issue(const float* h, int ld, int d, const float* gain, NormRegs<NT, G>& r) {
   constexpr int CPT = NormRegs<NT, G>::CPT;
   const int d4 = d / 4;
   const int wbase = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) & ~(kWave - 1));
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) {
+    r.g[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (wbase + c * NT < d4)
+      r.g[c] = reinterpret_cast<const float4*>(gain)[min(static_cast<int>(threadIdx.x) + c * NT, d4 - 1)];
+  }
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     const float4* hr = reinterpret_cast<const float4*>(h + static_cast<size_t>(g) * ld);
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       // whole waves past the row issue nothing (their chunks weigh zero)
-      if (wbase + c * NT < d4) r.v[g][c] = hr[min(static_cast<int>(threadIdx.x) + c * NT, d4 - 1)];
-      else r.v[g][c] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (wbase + c * NT < d4) {
+        const int e4 = min(static_cast<int>(threadIdx.x) + c * NT, d4 - 1);
+        r.v[g][c] = hr[e4];
+      } else {
+        r.v[g][c] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
     }
   }
 }
 
+// o[0..3] = cvt(v * scale * g) as one 8-byte (bf16) or 16-byte store; o is
+// aligned to it.
+template <typename OT>
+__device__ __forceinline__ void store4(OT* o, const float4& v, float scale, const float4& g) {
+  if constexpr (sizeof(OT) == 2) {
+    uint2 pk;
+    pk.x = static_cast<uint32_t>(f2bf(v.x * scale * g.x)) | (static_cast<uint32_t>(f2bf(v.y * scale * g.y)) << 16);
+    pk.y = static_cast<uint32_t>(f2bf(v.z * scale * g.z)) | (static_cast<uint32_t>(f2bf(v.w * scale * g.w)) << 16);
+    *reinterpret_cast<uint2*>(o) = pk;
+  } else {
+    *reinterpret_cast<float4*>(o) = make_float4(v.x * scale * g.x, v.y * scale * g.y, v.z * scale * g.z, v.w * scale * g.w);
+  }
+}
+
 template <int NT, int G, typename OT>
-__device__ __forceinline__ void norm_commit(const NormRegs<NT, G>& r, int d, const float* gain, float eps, OT* out,
-                                            int ldo, float (*red)[8]) {
+__device__ __forceinline__ void norm_commit(const NormRegs<NT, G>& r, int d, float eps, OT* out, int ldo,
+                                            float (*red)[8]) {
   constexpr int CPT = NormRegs<NT, G>::CPT;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int d4 = d / 4;
+  const int d4 = d / 4, nblk = (d4 + kWave - 1) / kWave;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    float ss = 0.f;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      if (static_cast<int>(threadIdx.x) + c * NT < d4) {
-        ss = fmaf(r.v[g][c].x, r.v[g][c].x, ss);
-        ss = fmaf(r.v[g][c].y, r.v[g][c].y, ss);
-        ss = fmaf(r.v[g][c].z, r.v[g][c].z, ss);
-        ss = fmaf(r.v[g][c].w, r.v[g][c].w, ss);
+      if (wave * kWave + c * NT < d4) {  // the wave holds block c * NT / 64 + wave
+        float ss = 0.f;
+        if (static_cast<int>(threadIdx.x) + c * NT < d4) {
+          ss = fmaf(r.v[g][c].x, r.v[g][c].x, ss);
+          ss = fmaf(r.v[g][c].y, r.v[g][c].y, ss);
+          ss = fmaf(r.v[g][c].z, r.v[g][c].z, ss);
+          ss = fmaf(r.v[g][c].w, r.v[g][c].w, ss);
+        }
+        ss = wave_sum(ss);
+        if (lane == 0) red[c * (NT / kWave) + wave][g] = ss;
       }
     }
-    ss = wave_sum(ss);
-    if (lane == 0) red[wave][g] = ss;
   }
   __syncthreads();
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     float ss = red[0][g];
-#pragma unroll
-    for (int w = 1; w < NT / kWave; ++w) ss += red[w][g];
+    for (int b = 1; b < nblk; ++b) ss += red[b][g];
     const float scale = rsqrtf(ss / static_cast<float>(d) + eps);
     OT* o = out + static_cast<size_t>(g) * ldo;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int e4 = threadIdx.x + c * NT;
-      if (e4 < d4) {
-        const float4 gv = reinterpret_cast<const float4*>(gain)[e4];
-        o[4 * e4 + 0] = Elt<OT>::from_f(r.v[g][c].x * scale * gv.x);
-        o[4 * e4 + 1] = Elt<OT>::from_f(r.v[g][c].y * scale * gv.y);
-        o[4 * e4 + 2] = Elt<OT>::from_f(r.v[g][c].z * scale * gv.z);
-        o[4 * e4 + 3] = Elt<OT>::from_f(r.v[g][c].w * scale * gv.w);
-      }
+      if (e4 < d4) store4<OT>(o + 4 * e4, r.v[g][c], scale, r.g[c]);
     }
   }
   __syncthreads();
@@ -213,8 +235,8 @@ template <int NT, int G, typename OT>
 __device__ __forceinline__ void norm_group(const float* h, int ld, int d, const float* gain, float eps, OT* out,
                                            int ldo, float (*red)[8]) {
   NormRegs<NT, G> r;
-  norm_issue<NT, G>(h, ld, d, r);
-  norm_commit<NT, G>(r, d, gain, eps, out, ldo, red);
+  norm_issue<NT, G>(h, ld, d, gain, r);
+  norm_commit<NT, G>(r, d, eps, out, ldo, red);
 }
 
 // RMSNorm of M (1..8, a compile-time count) rows: one round trip for M <= 5,
@@ -223,13 +245,13 @@ template <int NT, int M, typename OT>
 __device__ __forceinline__ void norm_rows(const float* h, int ld, int d, const float* gain, float eps, OT* out,
                                           int ldo) {
   static_assert(M >= 1 && M <= 8, "1..8 rows");
-  __shared__ float red_nr[NT / kWave][8];
+  __shared__ float red_nr[kNormBlocks][8];
   if constexpr (M <= 5) {
-    norm_group<NT, M>(h, ld, d, gain, eps, out, ldo, red_nr);
+    norm_group<NT, M, OT>(h, ld, d, gain, eps, out, ldo, red_nr);
   } else {
-    norm_group<NT, 4>(h, ld, d, gain, eps, out, ldo, red_nr);
-    norm_group<NT, M - 4>(h + 4 * static_cast<size_t>(ld), ld, d, gain, eps, out + 4 * static_cast<size_t>(ldo), ldo,
-                          red_nr);
+    norm_group<NT, 4, OT>(h, ld, d, gain, eps, out, ldo, red_nr);
+    norm_group<NT, M - 4, OT>(h + 4 * static_cast<size_t>(ld), ld, d, gain, eps, out + 4 * static_cast<size_t>(ldo),
+                                  ldo, red_nr);
   }
 }
 

@@ -34,6 +34,10 @@ namespace sv {
 namespace gemv {
 
 constexpr int kMaxLds = 159 * 1024;  // dynamic LDS; 1 KiB is left for static arrays
+// Weight steps a wave issues before the activation staging (see the
+// prologue of gemv_kernel); the rest of the ring follows it.  Measured on the
+// 8B-shaped 5-row step: 1, 2, 4 steps -> 3.479, 3.416, 3.433 ms.
+constexpr int kPreSteps = 2;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) const u32x4 global_u32x4;
@@ -134,7 +138,10 @@ __device__ __forceinline__ EpiPre epilogue_pre(const GemvArgs& a, const float* y
   } else if constexpr (EPI == EPI_RESID) {
     const int r = lane / M, m = lane - r * M;
     const int c = t * R + r;
-    if (r < R && c < a.N) e.y = y[static_cast<size_t>(m) * a.ldy + c];
+    if (r < R && c < a.N) {
+      const float* src = y + static_cast<size_t>(m) * a.ldy + c;
+      e.y = *src;
+    }
   }
   return e;
 }
@@ -200,8 +207,10 @@ __device__ __forceinline__ void epilogue(const GemvArgs& a, float* y, int t, flo
 
 // Steps of a row: S = ceil(K / STEP); U must divide S.
 // WPE: minimum waves per SIMD the register allocation must allow; NT threads.
+// Workgroup blockIdx.x of gridDim.x over K slice blockIdx.y.
 template <typename WT, int M, int R, int U, int EPI, int WPE, int NT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE))) void gemv_kernel(GemvArgs a) {
+  const int wg = blockIdx.x, nwg = gridDim.x, slice = blockIdx.y;
   extern __shared__ uint4 smem_v[];
   WT* xs = reinterpret_cast<WT*>(smem_v);
   constexpr int VE = 16 / sizeof(WT);
@@ -213,12 +222,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE))) void 
   const int K = a.K;  // columns of this workgroup's slice
   const int S = (K + STEP - 1) / STEP;
   const int KP = S * STEP;
-  const int slice = blockIdx.y;
   const WT* W = static_cast<const WT*>(a.W) + static_cast<size_t>(slice) * K;
   float* y = a.y ? a.y + static_cast<size_t>(slice) * a.ysplit : nullptr;
   const int n_tiles = num_tiles<EPI, R>(a.N);
-  const int gw = blockIdx.x * WPB + wave;
-  const int TW = gridDim.x * WPB;
+  const int gw = wg * WPB + wave;
+  const int TW = nwg * WPB;
   const int my_tiles = gw < n_tiles ? (n_tiles - gw + TW - 1) / TW : 0;
   // per-lane column of step s: clamped into the row (the padded x is zero there)
   const int lk = lane * VE;
@@ -237,21 +245,35 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE))) void 
     for (int r = 0; r < NW; ++r) dst[r] = load_stream(p[r] + k);
   };
 
-  // Prologue.  Vector loads complete in issue order, so the activation loads
-  // go first: the rows arrive, are normalised or copied into LDS while the
-  // first U steps of weights are still in flight behind them.
+  // Prologue.  Loads complete in issue order (per wave, and through the
+  // CU's vector L1 across waves), so:
+  //  1. every wave issues its activation loads, and a bare s_barrier (no
+  //     fence, no wait) keeps all of them ahead of every wave's weight loads;
+  //     an activation load queued behind weight loads (HBM misses, at the
+  //     start of a launch the whole chip's burst) would wait for them;
+  //  2. every wave issues its first kPre weight steps, in straight-line code
+  //     (a wave without tiles streams tile 0's and never uses them): behind a
+  //     branch the compiler cannot count the loads in flight and its wait for
+  //     the activations becomes a wait for everything;
+  //  3. the rows are normalised or copied into LDS; the staging ends at a
+  //     workgroup barrier, which a wave only reaches once its loads are
+  //     issued, so only kPre steps go before it (with the whole ring, the
+  //     late waves of a CU wait for the early waves' weights to come back
+  //     while the early waves idle at the barrier);
+  //  4. the rest of the ring is issued.
   // (bf16: x chunks per thread loaded ahead of the weights, 32 registers; the
   // float32 kernels keep their registers for the 4-fma dot products)
   constexpr bool kBf16 = sizeof(WT) == 2;
+  constexpr int kPre = U < kPreSteps ? U : kPreSteps;
   constexpr int XR = kBf16 ? 8 : 1;
   constexpr bool kEarlyNorm = kBf16 && M * NormRegs<NT, M>::CPT <= 10;  // 40 registers at most
-  __shared__ float red[NT / kWave][8];
+  __shared__ float red[kNormBlocks][8];
   NormRegs<NT, kEarlyNorm ? M : 1> nr;
   uint4 xr[XR];
   const int xkv = K / VE, xkpv = KP / VE, xtot = M * xkpv;
   const WT* xg = a.hn ? nullptr : static_cast<const WT*>(a.x) + static_cast<size_t>(slice) * K;
   if (a.hn) {
-    if constexpr (kEarlyNorm) norm_issue<NT, M>(a.hn, K, K, nr);
+    if constexpr (kEarlyNorm) norm_issue<NT, M>(a.hn, K, K, a.gain, nr);
   } else {
     // a wave issues only the chunks that hold rows (the issue slots of the
     // vector memory unit are what the start of a launch waits on)
@@ -265,19 +287,18 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE))) void 
       }
     }
   }
+  __builtin_amdgcn_s_barrier();
   uint4 wv[U][NW];
-  if (my_tiles > 0) {
-    set_rows(gw, cur);
+  set_rows(my_tiles > 0 ? gw : 0, cur);
 #pragma unroll
-    for (int u = 0; u < U; ++u) load_step(cur, u, wv[u]);
-  }
+  for (int u = 0; u < kPre; ++u) load_step(cur, u, wv[u]);
   if (a.hn) {
     // x = cvt(RMSNorm(h) * gain), made in LDS (one K slice: K = d); the
     // padding columns K .. KP-1 are zero
     if constexpr (kEarlyNorm) {
-      norm_commit<NT, M>(nr, K, a.gain, a.eps, xs, KP, red);
+      norm_commit<NT, M>(nr, K, a.eps, xs, KP, red);
     } else {
-      norm_rows<NT, M>(a.hn, K, K, a.gain, a.eps, xs, KP);
+      norm_rows<NT, M, WT>(a.hn, K, K, a.gain, a.eps, xs, KP);
     }
     for (int idx = threadIdx.x; idx < M * (KP - K); idx += NT) {
       const int m = idx / (KP - K);
@@ -291,11 +312,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE))) void 
     }
     for (int idx = threadIdx.x + XR * NT; idx < xtot; idx += NT) {
       const int m = idx / xkpv, v = idx - m * xkpv;
-      reinterpret_cast<uint4*>(xs)[idx] =
-          (v < xkv) ? reinterpret_cast<const uint4*>(xg + static_cast<size_t>(m) * a.ldx)[v] : make_uint4(0, 0, 0, 0);
+      uint4 val = make_uint4(0, 0, 0, 0);
+      if (v < xkv) val = reinterpret_cast<const uint4*>(xg + static_cast<size_t>(m) * a.ldx)[v];
+      reinterpret_cast<uint4*>(xs)[idx] = val;
     }
   }
   __syncthreads();
+#pragma unroll
+  for (int u = kPre; u < U; ++u) load_step(cur, u, wv[u]);
 
   float acc[NW][M];
   auto compute = [&](int st, const uint4 (&w)[NW]) {

@@ -125,6 +125,14 @@ hipError_t launch_ngram(int B, int n_min, int n_max, int gamma, const int32_t* p
 // len[b] = (src ? src[b] : len[b]) + add
 hipError_t launch_kv_len(int32_t* len, const int32_t* src, int add, int B, hipStream_t s);
 
+// Validation: *flag = 0; then flag |= 1 for an id outside [0, vocab) among
+// the first n_valid[r] (or per_row) of each row of ids [rows][per_row], and
+// flag |= 2 for a non-finite value among v[0 .. n).
+hipError_t launch_check_clear(int* flag, hipStream_t s);
+hipError_t launch_check_ids(const int32_t* ids, int rows, int per_row, const int32_t* n_valid, int vocab, int* flag,
+                            hipStream_t s);
+hipError_t launch_check_finite(const float* v, int64_t n, int* flag, hipStream_t s);
+
 // ---- sampler ----------------------------------------------------------------------
 int sampler_chunks(int vocab);
 // part[row][c] = (max, sum exp(l/T - max)) over chunk c of each row.

@@ -1,6 +1,8 @@
 // Small ops of the verify pass: the embedding gather (+ the RoPE angle table
 // of the pass), the residual sum + RMSNorm between linears, round and KV
 // length bookkeeping, and the n-gram prompt lookup.  They move kilobytes.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -52,7 +54,8 @@ __global__ __launch_bounds__(kThreads) void resid_norm_kernel(float* __restrict_
                                                               size_t pstride, int d, const float* __restrict__ gain,
                                                               float eps, OT* __restrict__ x) {
   constexpr int CPT = 4;  // 16-byte chunks per thread (d <= 16 * 256)
-  __shared__ float red[kThreads / kWave];
+  static_assert(CPT * kThreads / kWave == kNormBlocks, "one sum per block of the row");
+  __shared__ float red[kNormBlocks];
   const size_t r = blockIdx.x;
   const int d4 = d / 4;
   float4* hr = reinterpret_cast<float4*>(h + r * d);
@@ -64,7 +67,8 @@ __global__ __launch_bounds__(kThreads) void resid_norm_kernel(float* __restrict_
 #pragma unroll
     for (int k = 0; k < KS; ++k) pv[k][c] = reinterpret_cast<const float4*>(part + k * pstride + r * d)[e4];
   }
-  float ss = 0.f;
+  // sum of squares in the fixed block order of norm_commit (common.hpp)
+  const int wave = threadIdx.x / kWave, nblk = (d4 + kWave - 1) / kWave;
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
     float4 acc = pv[0][c];
@@ -79,32 +83,28 @@ __global__ __launch_bounds__(kThreads) void resid_norm_kernel(float* __restrict_
     v[c].y += acc.y;
     v[c].z += acc.z;
     v[c].w += acc.w;
-    if (static_cast<int>(threadIdx.x) + c * kThreads < d4) {
-      hr[threadIdx.x + c * kThreads] = v[c];
-      ss = fmaf(v[c].x, v[c].x, ss);
-      ss = fmaf(v[c].y, v[c].y, ss);
-      ss = fmaf(v[c].z, v[c].z, ss);
-      ss = fmaf(v[c].w, v[c].w, ss);
+    if (wave * kWave + c * kThreads < d4) {
+      float ss = 0.f;
+      if (static_cast<int>(threadIdx.x) + c * kThreads < d4) {
+        hr[threadIdx.x + c * kThreads] = v[c];
+        ss = fmaf(v[c].x, v[c].x, ss);
+        ss = fmaf(v[c].y, v[c].y, ss);
+        ss = fmaf(v[c].z, v[c].z, ss);
+        ss = fmaf(v[c].w, v[c].w, ss);
+      }
+      ss = wave_sum(ss);
+      if ((threadIdx.x & (kWave - 1)) == 0) red[c * (kThreads / kWave) + wave] = ss;
     }
   }
-  ss = wave_sum(ss);
-  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = ss;
   __syncthreads();
   float tot = red[0];
-#pragma unroll
-  for (int w = 1; w < kThreads / kWave; ++w) tot += red[w];
+  for (int b = 1; b < nblk; ++b) tot += red[b];
   const float scale = rsqrtf(tot / static_cast<float>(d) + eps);
   OT* o = x + r * d;
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {
     const int e4 = threadIdx.x + c * kThreads;
-    if (e4 < d4) {
-      const float4 g = reinterpret_cast<const float4*>(gain)[e4];
-      o[4 * e4 + 0] = Elt<OT>::from_f(v[c].x * scale * g.x);
-      o[4 * e4 + 1] = Elt<OT>::from_f(v[c].y * scale * g.y);
-      o[4 * e4 + 2] = Elt<OT>::from_f(v[c].z * scale * g.z);
-      o[4 * e4 + 3] = Elt<OT>::from_f(v[c].w * scale * g.w);
-    }
+    if (e4 < d4) store4<OT>(o + 4 * e4, v[c], scale, reinterpret_cast<const float4*>(gain)[e4]);
   }
 }
 
@@ -273,6 +273,50 @@ hipError_t launch_ngram(int B, int n_min, int n_max, int gamma, const int32_t* p
                         int32_t* drafts, int32_t* n_draft, int32_t* n_found, hipStream_t s) {
   hipLaunchKernelGGL(ngram_kernel, dim3(B), dim3(kNgramThreads), 0, s, n_min, n_max, gamma, prefix, prefix_len, P, out, out_len,
                      cap, fill_off, drafts, n_draft, n_found);
+  return hipGetLastError();
+}
+
+// ---- validation (SPEC_CHECK=1) ----------------------------------------------------
+// flag |= 1: a token id outside [0, vocab); flag |= 2: a non-finite value.
+__global__ void check_clear_kernel(int* flag) { *flag = 0; }
+
+__global__ void check_ids_kernel(const int32_t* __restrict__ ids, int rows, int per_row,
+                                 const int32_t* __restrict__ n_valid, int vocab, int* flag) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= static_cast<int64_t>(rows) * per_row) return;
+  const int r = static_cast<int>(i / per_row), c = static_cast<int>(i - static_cast<int64_t>(r) * per_row);
+  const int n = n_valid ? min(max(n_valid[r], 0), per_row) : per_row;
+  const int32_t t = ids[i];
+  if (c < n && (t < 0 || t >= vocab)) __hip_atomic_fetch_or(flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__global__ void check_finite_kernel(const float* __restrict__ v, int64_t n, int* flag) {
+  bool bad = false;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    bad |= !isfinite(v[i]);
+  if (__ballot(bad) && (threadIdx.x & (kWave - 1)) == 0)
+    __hip_atomic_fetch_or(flag, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+hipError_t launch_check_clear(int* flag, hipStream_t s) {
+  hipLaunchKernelGGL(check_clear_kernel, dim3(1), dim3(1), 0, s, flag);
+  return hipGetLastError();
+}
+
+hipError_t launch_check_ids(const int32_t* ids, int rows, int per_row, const int32_t* n_valid, int vocab, int* flag,
+                            hipStream_t s) {
+  const int64_t n = static_cast<int64_t>(rows) * per_row;
+  if (n <= 0 || !ids) return hipSuccess;
+  hipLaunchKernelGGL(check_ids_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, ids, rows,
+                     per_row, n_valid, vocab, flag);
+  return hipGetLastError();
+}
+
+hipError_t launch_check_finite(const float* v, int64_t n, int* flag, hipStream_t s) {
+  if (n <= 0 || !v) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(check_finite_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, v, n, flag);
   return hipGetLastError();
 }
 

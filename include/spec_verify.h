@@ -34,6 +34,15 @@
  *     KV row at or beyond max_ctx; its results are then undefined.
  *   - Uniforms are float32 values in [0, 1); the exact draw above assumes they
  *     are multiples of 2^-24 (any other value is truncated to that grid).
+ *   - Validation mode: with SPEC_CHECK=1 in the environment,
+ *     spec_verify_forward, spec_softmax_pq, spec_reject_sample and
+ *     spec_decode_step (and its _static form) also check their token ids
+ *     (input tokens, the last committed tokens, the first n_draft drafts:
+ *     inside [0, vocab)) and their float rows (logits, p and q rows: finite),
+ *     synchronise the stream and return SPEC_EDEVICE when a check fails; the
+ *     outputs are written either way.  In this mode a call blocks until its
+ *     work is done (it cannot be captured into a graph), and a decode step
+ *     keeps its logits in the workspace so that they can be checked.
  *
  * Data layout:
  *   - Weights are row-major [out][in] in the model dtype (float32 or bf16);
@@ -63,7 +72,7 @@ typedef enum spec_status {
   SPEC_ENOMEM = -2,        /* workspace smaller than the matching *_bytes() query */
   SPEC_EHIP = -3,          /* a HIP runtime call or a kernel launch failed */
   SPEC_EUNSUPPORTED = -4,  /* shape the kernels do not handle (see each call) */
-  SPEC_EDEVICE = -5        /* no usable gfx950 device */
+  SPEC_EDEVICE = -5        /* no usable gfx950 device; or (SPEC_CHECK=1) the inputs or logits failed validation */
 } spec_status;
 
 typedef enum spec_dtype { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
@@ -245,9 +254,16 @@ spec_status spec_decode_step_static(const spec_model* target, const spec_kv* kv,
  *                rows N..2N-1 (W is [2N][K]).
  *   W [N or 2N][K], x [M][K], y float32 [M][N] (epilogues 0, 1), z [M][N]
  *   (epilogue 2).  K a multiple of 16 bytes of the dtype; W and x 16-byte
- *   aligned.  Errors: SPEC_EINVAL, SPEC_EHIP. */
+ *   aligned.
+ *   hn, gain, eps  optional (hn NULL: x is the input): the input rows are
+ *   made from float32 residual rows hn [M][K] as RMSNorm(hn) * gain rounded
+ *   to the dtype while they are staged, the form the verify pass uses for
+ *   its QKV, gate/up and LM-head linears (x is then not read and may be
+ *   NULL).  Needs M <= 8, K <= 4096, gain [K] float32, eps >= 0.
+ * Errors: SPEC_EINVAL, SPEC_EHIP. */
 spec_status spec_linear(int32_t dtype, int32_t epilogue, const void* W, const void* x, int32_t M, int32_t N,
-                        int32_t K, float* y, void* z, hipStream_t stream);
+                        int32_t K, float* y, void* z, const float* hn, const float* gain, float eps,
+                        hipStream_t stream);
 
 /* Round bookkeeping on the device, so a whole generation can run as graph
  * replays with no host round trip per round (first page, Algorithm 1: a

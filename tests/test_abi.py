@@ -96,3 +96,21 @@ def test_missing_library_fails_loudly(tmp_path):
                        cwd=str(__import__("pathlib").Path(__file__).resolve().parents[1]))
     assert r.returncode != 0
     assert "is missing" in r.stderr and "no fallback" in r.stderr
+
+
+def test_check_mode_keeps_the_argument_checks(tmp_path):
+    """With SPEC_CHECK=1 the host-side argument checks still come first: bad
+    arguments are SPEC_EINVAL / SPEC_ENOMEM, never a validation result."""
+    import subprocess
+    import sys
+
+    code = ("import ctypes\nfrom draft_then_verify_amd import binding as bd\nlib = bd.load_library()\n"
+            "assert lib.spec_reject_sample(0, 4, 100, 1, None, 1, None, 1, 1, 1, 1, 1, 1 << 20, None) == -1\n"
+            "assert lib.spec_reject_sample(1, 2, 100, 1, None, 1, None, 1, 1, 1, 1, 1, 8, None) == -2\n"
+            "assert lib.spec_softmax_pq(None, 4, 100, 1.0, 1, 1, 1 << 20, None) == -1\n"
+            "kv = bd.spec_kv(1, 1, 1, 2, 16)\n"
+            "assert lib.spec_verify_forward(None, ctypes.byref(kv), 1, 1, 1, None, 1, 1 << 30, None) == -1\n"
+            "print('ok')\n")
+    env = dict(os.environ, SPEC_CHECK="1")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, cwd=ROOT)
+    assert r.returncode == 0 and "ok" in r.stdout, r.stderr[-2000:]

@@ -39,7 +39,8 @@ assert lib.spec_verify_forward(None, ctypes.byref(kv), 1, 1, 1, None, 1, 1 << 30
 assert lib.spec_workspace_bytes(None, 1, 1, 16) == 0
 assert lib.spec_commit_round(0, 4, 1, 1, 1, None, 1, 1, 8, 0, None, None, None, 0, None) == -1
 assert lib.spec_ngram_propose(1, 0, 3, 4, 1, None, 8, None, None, 0, None, 1, 1, None, None) == -1
-assert lib.spec_linear(7, 0, 1, 1, 1, 1, 1, 1, None, None) == -1
+assert lib.spec_linear(7, 0, 1, 1, 1, 1, 1, 1, None, None, None, 0.0, None) == -1
+assert lib.spec_linear(1, 0, 16, None, 1, 1, 8, 16, None, 16, None, 0.0, None) == -1  # hn without gain
 for _ in range(1000):  # the thread-local error string, rewritten many times
     lib.spec_kv_set_len(None, 1, None, 1, None)
     assert bd.spec_last_error()

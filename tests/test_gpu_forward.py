@@ -171,3 +171,33 @@ def test_8b_shape_two_layers_long_context(P):
     logits = torch.empty((1, 5, shape.vocab), dtype=torch.float32, device="cuda")
     recs.append(record_pass("verify", model, kv, 1, 5, i32(block), logits))
     check_passes(shape, w, recs, _tol(shape))
+
+
+@pytest.mark.parametrize("shape_name,n_layers,B,m", [
+    ("small", 3, 1, 5), ("small", 3, 2, 4), ("small", 3, 8, 1), ("qwen3_0p6b", 3, 1, 1), ("qwen3_8b", 2, 1, 5)])
+def test_traced_pass_matches_plain_pass(shape_name, n_layers, B, m):
+    """spec_verify_forward_trace (with nothing to capture) and
+    spec_verify_forward run the same launches: logits and the K/V rows written
+    are bitwise equal (ragged contexts across the batch)."""
+    shape = SHAPES[shape_name].with_(n_layers=n_layers)
+    seed = 131 + B * 10 + m
+    w = make_weights(shape, seed=seed, norm="random", device="cuda")
+    P = 40
+    max_ctx = P + m + 4
+    model = bd.SpecModel(shape, w)
+    kv = bd.KVCache(shape, n_layers, B, max_ctx)
+    prompt = make_prompt(B, P, shape.vocab, seed=seed)
+    gpu_prefill(model, kv, prompt)
+    kv.len.copy_(torch.as_tensor(np.array([P - 1 - 3 * (b % 3) for b in range(B)], np.int32)))
+    block = i32(make_prompt(B, m, shape.vocab, seed=seed + 1))
+    ws = bd.workspace(model.workspace_bytes(B, m, max_ctx))
+    plain = torch.empty((B, m, shape.vocab), dtype=torch.float32, device="cuda")
+    bd.spec_verify_forward(model, kv, B, m, block, plain, ws)
+    torch.cuda.synchronize()
+    k1, v1 = kv.k.clone(), kv.v.clone()
+    traced = torch.full_like(plain, float("nan"))
+    bd.spec_verify_forward_trace(model, kv, B, m, block, traced, {}, ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(plain).all()
+    assert torch.equal(plain, traced)
+    assert torch.equal(kv.k, k1) and torch.equal(kv.v, v1)

@@ -79,3 +79,39 @@ def test_linear_matrix_cores_large():
 def test_linear_float32():
     _check(704, 256, 5, 0, seed=3, dtype=torch.float32)
     _check(256, 704, 4, 1, seed=4, dtype=torch.float32)
+
+
+@pytest.mark.parametrize("epi,N", [(2, 12288), (0, 6144)])
+def test_linear_rmsnorm_staging(epi, N):
+    """The linear fed from float32 residual rows: the kernel makes its input
+    bf16(RMSNorm(h) * gain) while staging it (the form the verify pass uses
+    for QKV, gate/up and the LM head).  Against the oracle's RMSNorm, bf16
+    rounding and linear; an input element whose float32 norm lands on the
+    other side of a bf16 rounding boundary moves its term by at most one
+    bf16 spacing (2^-8 |x| |w|)."""
+    from oracle.model import rms_norm, silu
+
+    K, M = 4096, 5
+    g = torch.Generator(device="cuda").manual_seed(N + epi)
+    rows = 2 * N if epi == 2 else N
+    W = (torch.randn((rows, K), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    h = torch.randn((M, K), generator=g, device="cuda") * 3
+    gain = 1 + 0.1 * torch.randn(K, generator=g, device="cuda")
+    y = torch.empty((M, N), device="cuda")
+    z = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    bd.spec_linear(W, None, M, N, K, epilogue=epi, y=y if epi == 0 else None, z=z if epi == 2 else None,
+                   hn=h, gain=gain, eps=1e-6)
+    torch.cuda.synchronize()
+    Wc = W.float().cpu().numpy().astype(np.float64)
+    x = rms_norm(h.cpu().numpy().astype(np.float64), gain.cpu().numpy().astype(np.float64), 1e-6)
+    a = np.abs(x) @ np.abs(Wc).T  # sum |x||w| per output
+    ref = linear(x, Wc, True)
+    slack = 1e-4 * a + 2 ** -8 * a
+    if epi == 0:
+        assert (np.abs(y.cpu().numpy() - ref) <= slack + 1e-6).all()
+    else:
+        gate, up = ref[:, :N], ref[:, N:]
+        zr = silu(gate) * up
+        # |d silu / dg| <= 1.1
+        dz = np.abs(silu(gate)) * slack[:, N:] + 1.1 * np.abs(up) * slack[:, :N]
+        assert (np.abs(z.float().cpu().numpy() - zr) <= (np.abs(zr) + 1e-3) * 2 ** -7 + dz + 1e-6).all()

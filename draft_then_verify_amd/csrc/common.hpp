@@ -142,9 +142,32 @@ __device__ __forceinline__ unsigned long long block_sum_u64(unsigned long long v
 // whatever the workgroup size, so every RMSNorm of the library gives the
 // same bits for the same row: the row is cut into blocks of 64 16-byte
 // chunks (256 elements); in a block each lane adds the squares of its 4
-// elements (one fma chain), the wave adds its lanes by butterfly, and the
-// block sums are added in block order.
+// elements (one fma chain) and the wave adds its lanes by butterfly; the
+// (at most 16) block sums are added by a 16-lane butterfly, zeros standing
+// in for the blocks past the row (norm_scales).
 constexpr int kNormBlocks = 16;  // blocks of a row of at most 4096 elements
+
+// scale[g] = rsqrt(total_g / d + eps) in every lane, for rows g < G (<= 8),
+// from the block sums red[b][g] (b < nblk <= 16).  Lanes 16k .. 16k + 15
+// take the blocks of row g0 + k, four rows per pass: each wave computes a
+// row's total and scale once per 16 lanes, not once per thread (the
+// per-thread form kept the staging of a 5-row linear VALU-bound for ~3 us).
+template <int G>
+__device__ __forceinline__ void norm_scales(const float (*red)[8], int nblk, int d, float eps, float (&scale)[G]) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int b = lane & 15, k = lane >> 4;
+#pragma unroll
+  for (int g0 = 0; g0 < G; g0 += 4) {
+    const int g = g0 + k;
+    float v = (g < G && b < nblk) ? red[b][g < G ? g : 0] : 0.f;
+    v = group_sum<16>(v);
+    const float sc = rsqrtf(v / static_cast<float>(d) + eps);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      if (g0 + kk < G)
+        scale[g0 + kk] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc), 16 * kk));
+  }
+}
 template <int NT, int G> struct NormRegs {
   static constexpr int CPT = (4 * 256 + NT - 1) / NT;  // 16-byte chunks per thread and row (d <= 4096)
   float4 v[G][CPT];
@@ -216,16 +239,15 @@ __device__ __forceinline__ void norm_commit(const NormRegs<NT, G>& r, int d, flo
     }
   }
   __syncthreads();
+  float scale[G];
+  norm_scales<G>(red, nblk, d, eps, scale);
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    float ss = red[0][g];
-    for (int b = 1; b < nblk; ++b) ss += red[b][g];
-    const float scale = rsqrtf(ss / static_cast<float>(d) + eps);
     OT* o = out + static_cast<size_t>(g) * ldo;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int e4 = threadIdx.x + c * NT;
-      if (e4 < d4) store4<OT>(o + 4 * e4, r.v[g][c], scale, r.g[c]);
+      if (e4 < d4) store4<OT>(o + 4 * e4, r.v[g][c], scale[g], r.g[c]);
     }
   }
   __syncthreads();

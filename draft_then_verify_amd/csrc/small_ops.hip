@@ -55,7 +55,7 @@ __global__ __launch_bounds__(kThreads) void resid_norm_kernel(float* __restrict_
                                                               float eps, OT* __restrict__ x) {
   constexpr int CPT = 4;  // 16-byte chunks per thread (d <= 16 * 256)
   static_assert(CPT * kThreads / kWave == kNormBlocks, "one sum per block of the row");
-  __shared__ float red[kNormBlocks];
+  __shared__ float red[kNormBlocks][8];
   const size_t r = blockIdx.x;
   const int d4 = d / 4;
   float4* hr = reinterpret_cast<float4*>(h + r * d);
@@ -93,13 +93,13 @@ __global__ __launch_bounds__(kThreads) void resid_norm_kernel(float* __restrict_
         ss = fmaf(v[c].w, v[c].w, ss);
       }
       ss = wave_sum(ss);
-      if ((threadIdx.x & (kWave - 1)) == 0) red[c * (kThreads / kWave) + wave] = ss;
+      if ((threadIdx.x & (kWave - 1)) == 0) red[c * (kThreads / kWave) + wave][0] = ss;
     }
   }
   __syncthreads();
-  float tot = red[0];
-  for (int b = 1; b < nblk; ++b) tot += red[b];
-  const float scale = rsqrtf(tot / static_cast<float>(d) + eps);
+  float sc[1];
+  norm_scales<1>(red, nblk, d, eps, sc);
+  const float scale = sc[0];
   OT* o = x + r * d;
 #pragma unroll
   for (int c = 0; c < CPT; ++c) {

@@ -391,6 +391,7 @@ __global__ __launch_bounds__(NWV * kWave) __attribute__((amdgpu_waves_per_eu(NWV
   constexpr int CE = D::CE, CPR = D::CPR, RPI = D::RPI, NI = KTD / RPI, NT = NWV * kWave;
   static_assert(NI >= 1 && KTD % RPI == 0, "keys per tile");
   static_assert(CPR == 8 || CPR == 16, "K/V rows of 8 or 16 chunks");
+  static_assert(NWV <= 16, "the merge gives each wave one of 16 lanes");
   __shared__ float mo[NWV][RW][HD];
   __shared__ float2 ml[NWV][RW];
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
@@ -432,7 +433,10 @@ __global__ __launch_bounds__(NWV * kWave) __attribute__((amdgpu_waves_per_eu(NWV
   }
 
   for (int it = 0; it < trips; ++it) {
-    const int k0 = (it * NWV + wave) * KTD;  // this wave's tile (may lie past kend: all masked)
+    const int k0 = (it * NWV + wave) * KTD;  // this wave's tile
+    // a tile wholly past the keys would only load clamped rows and mask them
+    // all: skip it (the CU's vector memory pipe is what the waves share)
+    if (k0 >= kend) continue;
     const int klast = max(kend - 1, 0);
     v4u kr[NI], vr[NI];
 #pragma unroll
@@ -505,21 +509,42 @@ __global__ __launch_bounds__(NWV * kWave) __attribute__((amdgpu_waves_per_eu(NWV
     if (lane == 0) ml[wave][r] = make_float2(mrow[r], lrow[r]);
   }
   __syncthreads();
+  // The waves' weights exp(m_w - max) and the row's total weight l, once per
+  // row: lanes 16k .. 16k + 15 of wave 0 take row r0 + k, lane w its wave's
+  // partial (l summed by a 16-lane butterfly); then every output element is
+  // its waves' partials weighted in wave order.
+  __shared__ float wts[NWV][RW];
+  __shared__ float lsum[RW];
+  if (wave == 0) {
+    const int w = lane & 15, k = lane >> 4;
+#pragma unroll
+    for (int r0 = 0; r0 < RW; r0 += 4) {
+      const int r = r0 + k < RW ? r0 + k : RW - 1;
+      float Mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < NWV; ++j) Mx = fmaxf(Mx, ml[j][r].x);
+      float wt = 0.f, lw = 0.f;
+      if (w < NWV) {
+        const float2 v = ml[w][r];
+        wt = (v.x == -INFINITY) ? 0.f : expf(v.x - Mx);
+        lw = v.y * wt;
+      }
+      lw = group_sum<16>(lw);
+      if (r0 + k < RW) {
+        if (w < NWV) wts[w][r] = wt;
+        if (w == 0) lsum[r] = lw;
+      }
+    }
+  }
+  __syncthreads();
   ET* xo = static_cast<ET*>(a.xo);
   const int nr = max(0, min(RW, m - i0));
   for (int idx = threadIdx.x; idx < nr * HD; idx += NT) {
     const int r = idx / HD, dd = idx - r * HD;
-    float Mx = -INFINITY;
+    float acc = 0.f;
 #pragma unroll
-    for (int w = 0; w < NWV; ++w) Mx = fmaxf(Mx, ml[w][r].x);
-    float l = 0.f, acc = 0.f;
-#pragma unroll
-    for (int w = 0; w < NWV; ++w) {
-      const float2 v = ml[w][r];
-      const float wt = (v.x == -INFINITY) ? 0.f : expf(v.x - Mx);
-      l = fmaf(v.y, wt, l);
-      acc = fmaf(mo[w][r][dd], wt, acc);
-    }
+    for (int w = 0; w < NWV; ++w) acc = fmaf(mo[w][r][dd], wts[w][r], acc);
+    const float l = lsum[r];
     xo[static_cast<size_t>(b * m + i0 + r) * qld + h * HD + dd] = Elt<ET>::from_f(l > 0.f ? acc / l : 0.f);
   }
 }

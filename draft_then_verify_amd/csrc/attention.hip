@@ -396,16 +396,22 @@ __global__ __launch_bounds__(NWV * kWave) __attribute__((amdgpu_waves_per_eu(NWV
   __shared__ float2 ml[NWV][RW];
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
 
-  const int H = a.H, Hkv = a.Hkv, m = a.m;
-  const int rb = blockIdx.x % n_rb;
-  const int h = (blockIdx.x / n_rb) % H;
-  const int b = blockIdx.x / (n_rb * H);
+  const int H = a.H, Hkv = a.Hkv, m = a.m, S = a.dsplit;
+  const int sp = blockIdx.x % S;          // context split of this workgroup
+  const int unit = blockIdx.x / S;
+  const int rb = unit % n_rb;
+  const int h = (unit / n_rb) % H;
+  const int b = unit / (n_rb * H);
   const int i0 = rb * RW;                 // first query row of the block
   const int kvh = h / (H / Hkv);
   const int Lb = a.len[b];
-  // keys the block's rows may see: positions 0 .. Lb + i0 + RW - 1
+  // keys the block's rows may see: positions 0 .. Lb + i0 + RW - 1; split sp
+  // takes tiles [t_lo, t_hi) of them
   const int kend = max(0, min(min(Lb + m, Lb + i0 + RW), a.max_ctx));
-  const int ntiles = (kend + KTD - 1) / KTD;
+  const int ntiles_all = (kend + KTD - 1) / KTD;
+  const int tps = (ntiles_all + S - 1) / S;
+  const int t_lo = min(sp * tps, ntiles_all), t_hi = min(t_lo + tps, ntiles_all);
+  const int ntiles = t_hi - t_lo;
   const int trips = (ntiles + NWV - 1) / NWV;
   const int qld = H * HD;
   const ET* kc = static_cast<const ET*>(a.kc);
@@ -433,10 +439,11 @@ __global__ __launch_bounds__(NWV * kWave) __attribute__((amdgpu_waves_per_eu(NWV
   }
 
   for (int it = 0; it < trips; ++it) {
-    const int k0 = (it * NWV + wave) * KTD;  // this wave's tile
-    // a tile wholly past the keys would only load clamped rows and mask them
+    const int tile = it * NWV + wave;
+    const int k0 = (t_lo + tile) * KTD;  // this wave's tile
+    // a tile past the split's keys would only load clamped rows and mask them
     // all: skip it (the CU's vector memory pipe is what the waves share)
-    if (k0 >= kend) continue;
+    if (tile >= ntiles) continue;
     const int klast = max(kend - 1, 0);
     v4u kr[NI], vr[NI];
 #pragma unroll
@@ -545,8 +552,40 @@ __global__ __launch_bounds__(NWV * kWave) __attribute__((amdgpu_waves_per_eu(NWV
 #pragma unroll
     for (int w = 0; w < NWV; ++w) acc = fmaf(mo[w][r][dd], wts[w][r], acc);
     const float l = lsum[r];
-    xo[static_cast<size_t>(b * m + i0 + r) * qld + h * HD + dd] = Elt<ET>::from_f(l > 0.f ? acc / l : 0.f);
+    const int row = b * m + i0 + r;
+    if (S == 1) {
+      xo[static_cast<size_t>(row) * qld + h * HD + dd] = Elt<ET>::from_f(l > 0.f ? acc / l : 0.f);
+    } else {
+      // this split's partial: the unnormalised output, its max and weight
+      const size_t pi = (static_cast<size_t>(row) * H + h) * S + sp;
+      a.dpo[pi * HD + dd] = acc;
+      if (dd == 0) {
+        float Mx = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NWV; ++w) Mx = fmaxf(Mx, ml[w][r].x);
+        a.dpml[pi] = make_float2(Mx, l);
+      }
+    }
   }
+}
+
+// Output rows from the context splits' partials (a traced pass: the O linear
+// otherwise merges them while staging its input).  One workgroup per
+// (row, head); thread j takes VE consecutive head dimensions.
+template <typename ET, int HD>
+__global__ __launch_bounds__(HD) void attn_merge_kernel(AttnArgs a) {
+  constexpr int VE = 16 / static_cast<int>(sizeof(ET));
+  const int row = blockIdx.x / a.H, h = blockIdx.x % a.H;
+  const int dd0 = threadIdx.x * VE;
+  if (dd0 >= HD) return;
+  const size_t pi = (static_cast<size_t>(row) * a.H + h) * a.dsplit;
+  AttnPart<VE> part;
+  attn_part_load<VE>(a.dpo + pi * HD, a.dpml + pi, a.dsplit, HD, dd0, part);
+  float out[VE];
+  attn_part_merge<VE>(part, a.dsplit, out);
+  ET* xo = static_cast<ET*>(a.xo) + static_cast<size_t>(row) * a.H * HD + h * HD + dd0;
+#pragma unroll
+  for (int e = 0; e < VE; ++e) xo[e] = Elt<ET>::from_f(out[e]);
 }
 
 // Query rows per workgroup: split the m rows until B * H * blocks reaches
@@ -563,8 +602,9 @@ template <typename ET, int HD, int RW>
 hipError_t launch_decode_rw(const AttnArgs& a, int B, hipStream_t s) {
   const int n_rb = (a.m + RW - 1) / RW;
   constexpr int NWV = RW <= 2 ? 16 : kDecWaves, KTD = RW <= 2 ? 32 : KT;
-  hipLaunchKernelGGL((attn_decode_kernel<ET, HD, RW, NWV, KTD>), dim3(B * a.H * n_rb), dim3(NWV * kWave), 0, s, a,
-                     n_rb);
+  if (a.dsplit < 1 || a.dsplit > kMaxAttnSplits || (a.dsplit > 1 && (!a.dpo || !a.dpml))) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((attn_decode_kernel<ET, HD, RW, NWV, KTD>), dim3(B * a.H * n_rb * a.dsplit), dim3(NWV * kWave), 0,
+                     s, a, n_rb);
   return hipGetLastError();
 }
 
@@ -633,6 +673,27 @@ size_t attn_counters(int B, int H, int Hkv, int hd, int m) {
   return static_cast<size_t>(B) * Hkv * pl.nhb * pl.nqc;
 }
 
+int attn_decode_splits(bool bf16, int hd, int B, int H, int m, int max_ctx) {
+  if (!attn_decode_path(bf16, hd, m, max_ctx) || static_cast<long long>(B) * H * m >= kDecodeMaxUnits) return 1;
+  const int cpr = hd / (bf16 ? 8 : 4);  // 16-byte chunks per K/V row
+  const int rw = decode_rows_per_block(B, H, m, cpr == 16 ? 3 : 5);
+  const long long units = static_cast<long long>(B) * H * ((m + rw - 1) / rw);
+  return units >= 128 ? 1 : units >= 64 ? 2 : kMaxAttnSplits;
+}
+
+hipError_t launch_attn_merge(bool bf16, int hd, const AttnArgs& a, int rows, hipStream_t s) {
+  if (a.dsplit < 2 || rows <= 0) return hipSuccess;
+  const dim3 grid(rows * a.H);
+  if (bf16) {
+    if (hd == 128) hipLaunchKernelGGL((attn_merge_kernel<uint16_t, 128>), grid, dim3(128), 0, s, a);
+    else hipLaunchKernelGGL((attn_merge_kernel<uint16_t, 64>), grid, dim3(64), 0, s, a);
+  } else {
+    if (hd == 128) hipLaunchKernelGGL((attn_merge_kernel<float, 128>), grid, dim3(128), 0, s, a);
+    else hipLaunchKernelGGL((attn_merge_kernel<float, 64>), grid, dim3(64), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
 bool attn_decode_path(bool bf16, int hd, int m, int max_ctx) {
   if (m > 8 || max_ctx > kDecodeMaxCtx) return false;
   if (bf16) return hd == 128 ? decode_fits<uint16_t, 128>() : decode_fits<uint16_t, 64>();
@@ -642,7 +703,9 @@ bool attn_decode_path(bool bf16, int hd, int m, int max_ctx) {
 hipError_t launch_attention(bool bf16, int hd, const AttnArgs& a, int B, hipStream_t s) {
   if (B <= 0 || a.m <= 0) return hipSuccess;
   if (!attn_supported(a.H, a.Hkv, hd)) return hipErrorInvalidValue;
-  if (attn_decode_path(bf16, hd, a.m, a.max_ctx) && static_cast<long long>(B) * a.H * a.m < kDecodeMaxUnits) {
+  const bool decode = attn_decode_path(bf16, hd, a.m, a.max_ctx) && static_cast<long long>(B) * a.H * a.m < kDecodeMaxUnits;
+  if (a.dsplit != 1 && (!decode || (!bf16 && hd != 64))) return hipErrorInvalidValue;  // splits: short-pass kernel only
+  if (decode) {
     if (bf16) return hd == 128 ? launch_decode<uint16_t, 128>(a, B, s) : launch_decode<uint16_t, 64>(a, B, s);
     if (hd == 64) return launch_decode<float, 64>(a, B, s);
   }

@@ -48,8 +48,9 @@ size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 struct Layout {
-  size_t h, xn, xo, z, q, cs, po, pml, ctr, pt, logits, part, csum, tpart, lx, xsel, total;
+  size_t h, xn, xo, z, q, cs, po, pml, ctr, pt, logits, part, csum, tpart, lx, xsel, dpo, dpml, total;
   int n_split, n_qc, n_ctr, ks_o, ks_d;
+  int dsplit;  // context splits of the short-pass attention (1: none)
 };
 
 Layout make_layout(const spec_model_cfg& c, int B, int m, int max_ctx) {
@@ -85,6 +86,11 @@ Layout make_layout(const spec_model_cfg& c, int B, int m, int max_ctx) {
   L.tpart = take(rows * ((c.vocab + 127) / 128) * 8);  // LM-head tile statistics (fused step)
   L.lx = take(rows * 4);
   L.xsel = take(static_cast<size_t>(B) * c.d_model * elt);
+  // one-row passes (a drafter's step) split each head's context when the
+  // short-pass attention would run few workgroups
+  L.dsplit = rows == 1 ? sv::attn_decode_splits(c.dtype == SPEC_BF16, c.head_dim, B, c.n_heads, m, max_ctx) : 1;
+  L.dpo = take(rows * c.n_heads * L.dsplit * c.head_dim * 4);
+  L.dpml = take(rows * c.n_heads * L.dsplit * 8);
   L.total = off;
   return L;
 }
@@ -182,6 +188,9 @@ spec_status run_forward(const spec_model* M, const spec_kv* kv, int B, int m, co
   at.part_ml = reinterpret_cast<float2*>(ws + L.pml);
   at.counters = ctr;
   at.xo = ws + L.xo;
+  at.dsplit = L.dsplit;
+  at.dpo = reinterpret_cast<float*>(ws + L.dpo);
+  at.dpml = reinterpret_cast<float2*>(ws + L.dpml);
   float* pt = reinterpret_cast<float*>(ws + L.pt);
   const size_t pstride = static_cast<size_t>(rows) * d;
   sv::GemvArgs o;
@@ -220,11 +229,23 @@ spec_status run_forward(const spec_model* M, const spec_kv* kv, int B, int m, co
     HIP_TRY(snap(tr.q, l, qkv.q, static_cast<size_t>(H) * hd * sizeof(float)));
     at.layer = l;
     HIP_TRY(sv::launch_attention(bf16, hd, at, B, s));
+    // a split pass's O linear merges the partials while staging; a traced or
+    // K-sliced one gets them merged into xo first (the same arithmetic)
+    const bool merge_in_o = L.dsplit > 1 && o_direct && !trace;
+    if (L.dsplit > 1 && !merge_in_o) HIP_TRY(sv::launch_attn_merge(bf16, hd, at, rows, s));
     HIP_TRY(snap(tr.attn, l, at.xo, static_cast<size_t>(H) * hd * elt));
     o.W = M->wo[l];
     if (o_direct) {
       sv::GemvArgs od = o;
       od.y = h;
+      if (merge_in_o) {
+        od.x = nullptr;
+        od.apo = at.dpo;
+        od.apml = at.dpml;
+        od.asplit = L.dsplit;
+        od.ahd = hd;
+        od.aH = H;
+      }
       HIP_TRY(sv::launch_gemv(bf16, sv::EPI_RESID, od, rows, s));
       gu.hn = h;
       gu.gain = M->mlp_norm[l];

@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 namespace sv {
@@ -30,6 +31,72 @@ template <> struct Elt<uint16_t> {
   __device__ __forceinline__ static float to_f(uint16_t x) { return bf2f(x); }
   __device__ __forceinline__ static uint16_t from_f(float x) { return f2bf(x); }
 };
+
+// VE values (8 as bf16 or 4 as float32) as one 16-byte chunk.
+template <typename WT>
+__device__ __forceinline__ uint4 pack_chunk(const float (&v)[16 / sizeof(WT)]) {
+  if constexpr (sizeof(WT) == 2) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = static_cast<uint32_t>(f2bf(v[2 * i])) | (static_cast<uint32_t>(f2bf(v[2 * i + 1])) << 16);
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+    return make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3]));
+  }
+}
+
+// ---- attention context splits ---------------------------------------------------------
+// A head's context split over S workgroups leaves S partials: an unnormalised
+// output o_s (relative to the split's max m_s) and its weight l_s.  The
+// merged output is sum_s w_s o_s / sum_s w_s l_s with w_s = exp(m_s - max_s
+// m_s) (0 for an empty split), summed in split order.  attn_part_load issues
+// the loads of VE consecutive dimensions dd0 .. of one (row, head) (po and
+// pml point at its S partials), attn_part_merge does the arithmetic, so a
+// caller can issue other loads in between.
+constexpr int kMaxAttnSplits = 4;
+template <int VE> struct AttnPart {
+  float4 o[kMaxAttnSplits][VE / 4];
+  float2 ml[kMaxAttnSplits];
+};
+template <int VE>
+__device__ __forceinline__ void attn_part_load(const float* po, const float2* pml, int S, int hd, int dd0,
+                                               AttnPart<VE>& p) {
+#pragma unroll
+  for (int s = 0; s < kMaxAttnSplits; ++s) {
+    if (s < S) {
+      p.ml[s] = pml[s];
+#pragma unroll
+      for (int c = 0; c < VE / 4; ++c) p.o[s][c] = reinterpret_cast<const float4*>(po + s * hd + dd0)[c];
+    }
+  }
+}
+template <int VE>
+__device__ __forceinline__ void attn_part_merge(const AttnPart<VE>& p, int S, float (&out)[VE]) {
+  float M = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < kMaxAttnSplits; ++s)
+    if (s < S) M = fmaxf(M, p.ml[s].x);
+  float l = 0.f, acc[VE];
+#pragma unroll
+  for (int e = 0; e < VE; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int s = 0; s < kMaxAttnSplits; ++s) {
+    if (s < S) {
+      const float w = p.ml[s].x == -INFINITY ? 0.f : expf(p.ml[s].x - M);
+      l = fmaf(p.ml[s].y, w, l);
+#pragma unroll
+      for (int c = 0; c < VE / 4; ++c) {
+        acc[4 * c + 0] = fmaf(p.o[s][c].x, w, acc[4 * c + 0]);
+        acc[4 * c + 1] = fmaf(p.o[s][c].y, w, acc[4 * c + 1]);
+        acc[4 * c + 2] = fmaf(p.o[s][c].z, w, acc[4 * c + 2]);
+        acc[4 * c + 3] = fmaf(p.o[s][c].w, w, acc[4 * c + 3]);
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < VE; ++e) out[e] = l > 0.f ? acc[e] / l : 0.f;
+}
 
 // Reductions over the 64 lanes of a wave with DPP lane moves (no LDS
 // round trip): pairs, quads, mirrored halves and rows of 16 lanes, then the

@@ -271,9 +271,20 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE))) void 
   NormRegs<NT, kEarlyNorm ? M : 1> nr;
   uint4 xr[XR];
   const int xkv = K / VE, xkpv = KP / VE, xtot = M * xkpv;
-  const WT* xg = a.hn ? nullptr : static_cast<const WT*>(a.x) + static_cast<size_t>(slice) * K;
+  const WT* xg = (a.hn || a.apo) ? nullptr : static_cast<const WT*>(a.x) + static_cast<size_t>(slice) * K;
+  // one row merged from attention partials (the O linear of a split
+  // one-row pass): chunk j = threadIdx.x is loaded here, ahead of the weights
+  constexpr bool kApart = M == 1;
+  AttnPart<VE> ap;
+  auto apart_load = [&](int v) {
+    const int col = v * VE, hh = col / a.ahd;
+    const size_t pi = static_cast<size_t>(hh) * a.asplit;
+    attn_part_load<VE>(a.apo + pi * a.ahd, a.apml + pi, a.asplit, a.ahd, col - hh * a.ahd, ap);
+  };
   if (a.hn) {
     if constexpr (kEarlyNorm) norm_issue<NT, M>(a.hn, K, K, a.gain, nr);
+  } else if (kApart && a.apo) {
+    if (static_cast<int>(threadIdx.x) < xkv) apart_load(threadIdx.x);
   } else {
     // a wave issues only the chunks that hold rows (the issue slots of the
     // vector memory unit are what the start of a launch waits on)
@@ -303,6 +314,17 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE))) void 
     for (int idx = threadIdx.x; idx < M * (KP - K); idx += NT) {
       const int m = idx / (KP - K);
       xs[static_cast<size_t>(m) * KP + K + (idx - m * (KP - K))] = Elt<WT>::from_f(0.f);
+    }
+  } else if (kApart && a.apo) {
+    for (int v = threadIdx.x; v < xkpv; v += NT) {
+      uint4 val = make_uint4(0, 0, 0, 0);
+      if (v < xkv) {
+        if (v != static_cast<int>(threadIdx.x)) apart_load(v);
+        float out[VE];
+        attn_part_merge<VE>(ap, a.asplit, out);
+        val = pack_chunk<WT>(out);
+      }
+      reinterpret_cast<uint4*>(xs)[v] = val;
     }
   } else {
 #pragma unroll

@@ -147,6 +147,10 @@ hipError_t launch_all(const GemvArgs& a0, int M, hipStream_t s) {
   if (EPI == EPI_QKV && (b.N % 2 || b.hd % 2)) return hipErrorInvalidValue;
   // the normalising prologue reads whole residual rows: one K slice, GEMV path
   if (b.hn && (b.ksplit != 1 || M > 8 || b.K % 4)) return hipErrorInvalidValue;
+  // x merged from attention partials: one row, one K slice, whole heads of VE-element chunks
+  if (b.apo && (M != 1 || b.ksplit != 1 || b.hn || b.mfma || !b.apml || b.asplit < 1 ||
+                b.asplit > kMaxAttnSplits || b.ahd <= 0 || b.ahd % VE || b.aH * b.ahd != b.K))
+    return hipErrorInvalidValue;
   if (std::is_same<WT, uint16_t>::value && (M > 8 || b.mfma) && b.K % mfma::KB == 0 &&
       (EPI != EPI_QKV || b.hd == 128 || b.hd == 64))
     return launch_gemm<EPI>(b, M, s);

@@ -60,6 +60,11 @@ struct GemvArgs {
   const int32_t* draft = nullptr;
   float temp = 1.f;
   bool mfma = false;
+  // x from attention partials (AttnArgs::dpo/dpml of a split pass) instead of
+  // x: x[m][h * ahd + j] = the merge of the asplit partials of row m, head h
+  const float* apo = nullptr;
+  const float2* apml = nullptr;
+  int asplit = 1, ahd = 0, aH = 0;
 };
 hipError_t launch_gemv(bool bf16, int epi, const GemvArgs& a, int M, hipStream_t s);
 
@@ -98,6 +103,13 @@ struct AttnArgs {
   float2* part_ml = nullptr;   // [B][H][m][n_split]
   int* counters = nullptr;     // attn_counters(...) tickets, zero between launches
   void* xo = nullptr;          // [B*m][H*hd] output in the model dtype
+  // Short passes with few (sequence, head, row) units split each head's
+  // context over dsplit workgroups; each writes its partial (unnormalised
+  // output dpo [B*m][H][dsplit][hd], max and weight dpml [B*m][H][dsplit])
+  // instead of xo, and the O linear (or launch_attn_merge) merges them.
+  int dsplit = 1;
+  float* dpo = nullptr;
+  float2* dpml = nullptr;
 };
 // hd 64/128; G = H/Hkv divides the workgroup's waves (16 for hd 128, 8 for
 // hd 64) or is a multiple of them
@@ -111,6 +123,12 @@ hipError_t launch_attention(bool bf16, int hd, const AttnArgs& a, int B, hipStre
 // (sequence, query head), no context splits, so n_split, part_* and counters
 // are not used.
 bool attn_decode_path(bool bf16, int hd, int m, int max_ctx);
+// Context splits launch_attention gives a pass (1 unless the short-pass
+// kernel runs with few units).
+int attn_decode_splits(bool bf16, int hd, int B, int H, int m, int max_ctx);
+// xo from the partials of a split pass (rows = B*m), in the merge the O
+// linear applies while staging.
+hipError_t launch_attn_merge(bool bf16, int hd, const AttnArgs& a, int rows, hipStream_t s);
 
 // Round bookkeeping (see spec_commit_round).
 hipError_t launch_commit_round(int B, int gamma, const int32_t* n_acc, const int32_t* emitted, int32_t* tok2,

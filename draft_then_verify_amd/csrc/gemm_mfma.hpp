@@ -48,6 +48,12 @@ constexpr int KB = 64;     // K per LDS stage
 constexpr int LDK = KB + 8;  // LDS row stride in bf16 (16-byte pad spreads the banks)
 constexpr int NTH = 256;
 constexpr int kXcds = 8;
+// K blocks in flight through LDS (gemm_kernel2) for 128- and 64-row tiles;
+// 0: the register-staged gemm_kernel
+constexpr int kDmaStages = 2;
+constexpr int kDmaStages64 = 3;
+constexpr int kDmaKB = 64;    // K per LDS stage, 128-row tiles
+constexpr int kDmaKB64 = 64;  // 64-row tiles
 
 template <int EPI>
 __host__ __device__ inline int n_tiles(const GemvArgs& a) {
@@ -72,87 +78,14 @@ __device__ __forceinline__ int w_row(const GemvArgs& a, int nt, int lr) {
   }
 }
 
+// The epilogue of a workgroup's BMT x 128 tile (acc: the wave's MI x 4
+// 16 x 16 tiles).  Lane holds rows 4 (lane / 16) + r of each 16-row tile,
+// column lane % 16.
 template <int EPI, int BMT>
-__global__ __launch_bounds__(NTH) void gemm_kernel(GemvArgs a, int mtiles, int ntiles) {
-  constexpr int MI = BMT / 32;   // 16-row tiles per wave (a wave covers BMT / 2 rows)
-  constexpr int XL = BMT / 32;   // 16-byte X chunks per thread per K block
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][BMT][LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t ws[2][BN][LDK];
-  const int per = gridDim.x / kXcds;
-  const int tile = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
-  if (tile >= mtiles * ntiles) return;  // padding workgroups leave before any barrier
-  const int mt = tile % mtiles, nt = tile / mtiles;
-  const int M = a.M, K = a.K, slice = blockIdx.y;
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int wm = wave & 1, wn = wave >> 1;
-  const int m0 = mt * BMT;
-
-  // this thread's global chunks: X XL x 16 B, W 4 x 16 B per K block
-  const uint16_t* xp[XL];
-  const uint16_t* wp[4];
-  int xr[XL], xc[XL], wr[4], wc[4];
-#pragma unroll
-  for (int i = 0; i < XL; ++i) {
-    const int c = threadIdx.x + i * NTH;
-    xr[i] = c >> 3;
-    xc[i] = (c & 7) * 8;
-    xp[i] = static_cast<const uint16_t*>(a.x) + static_cast<size_t>(min(m0 + xr[i], M - 1)) * a.ldx +
-            static_cast<size_t>(slice) * K + xc[i];
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = threadIdx.x + i * NTH;
-    wr[i] = c >> 3;
-    wc[i] = (c & 7) * 8;
-    wp[i] = static_cast<const uint16_t*>(a.W) + static_cast<size_t>(w_row<EPI>(a, nt, wr[i])) * a.ldw +
-            static_cast<size_t>(slice) * K + wc[i];
-  }
-  v4u gx[XL], gw[4];
-  auto load = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < XL; ++i) gx[i] = *reinterpret_cast<const v4u*>(xp[i] + k0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) gw[i] = *reinterpret_cast<const v4u*>(wp[i] + k0);
-  };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < XL; ++i) *reinterpret_cast<v4u*>(&xs[buf][xr[i]][xc[i]]) = gx[i];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<v4u*>(&ws[buf][wr[i]][wc[i]]) = gw[i];
-  };
-
-  f32x4_t acc[MI][4];
-#pragma unroll
-  for (int i = 0; i < MI; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  const int nk = K / KB;
-  load(0);
-  store(0);
-  __syncthreads();
-  const int fr = lane & 15, fk = (lane >> 4) * 8;
-  for (int kb = 0; kb < nk; ++kb) {
-    const int buf = kb & 1;
-    if (kb + 1 < nk) load((kb + 1) * KB);
-#pragma unroll
-    for (int ks = 0; ks < KB; ks += 32) {
-      bf16x8_t af[MI], bfr[4];
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-        af[i] = *reinterpret_cast<const bf16x8_t*>(&xs[buf][wm * (BMT / 2) + i * 16 + fr][ks + fk]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bfr[j] = *reinterpret_cast<const bf16x8_t*>(&ws[buf][wn * 64 + j * 16 + fr][ks + fk]);
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (kb + 1 < nk) store(buf ^ 1);
-    __syncthreads();
-  }
-
-  // epilogue: lane holds rows 4 (lane / 16) + r of each 16-row tile, column lane % 16
+__device__ __forceinline__ void gemm_epilogue(const GemvArgs& a, f32x4_t (&acc)[BMT / 32][4], int mt, int nt,
+                                              int slice, int wm, int wn, int lane) {
+  constexpr int MI = BMT / 32;
+  const int M = a.M, m0 = mt * BMT;
   const int col = lane & 15, rb = (lane >> 4) * 4;
   if constexpr (EPI == EPI_LMSTAT) {
     // Row statistics of the 128-column tile in lmstat.hpp's order: this
@@ -310,6 +243,207 @@ __global__ __launch_bounds__(NTH) void gemm_kernel(GemvArgs a, int mtiles, int n
       }
     }
   }
+}
+
+template <int EPI, int BMT>
+__global__ __launch_bounds__(NTH) void gemm_kernel(GemvArgs a, int mtiles, int ntiles) {
+  constexpr int MI = BMT / 32;   // 16-row tiles per wave (a wave covers BMT / 2 rows)
+  constexpr int XL = BMT / 32;   // 16-byte X chunks per thread per K block
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][BMT][LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t ws[2][BN][LDK];
+  const int per = gridDim.x / kXcds;
+  const int tile = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
+  if (tile >= mtiles * ntiles) return;  // padding workgroups leave before any barrier
+  const int mt = tile % mtiles, nt = tile / mtiles;
+  const int M = a.M, K = a.K, slice = blockIdx.y;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int m0 = mt * BMT;
+
+  // this thread's global chunks: X XL x 16 B, W 4 x 16 B per K block
+  const uint16_t* xp[XL];
+  const uint16_t* wp[4];
+  int xr[XL], xc[XL], wr[4], wc[4];
+#pragma unroll
+  for (int i = 0; i < XL; ++i) {
+    const int c = threadIdx.x + i * NTH;
+    xr[i] = c >> 3;
+    xc[i] = (c & 7) * 8;
+    xp[i] = static_cast<const uint16_t*>(a.x) + static_cast<size_t>(min(m0 + xr[i], M - 1)) * a.ldx +
+            static_cast<size_t>(slice) * K + xc[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = threadIdx.x + i * NTH;
+    wr[i] = c >> 3;
+    wc[i] = (c & 7) * 8;
+    wp[i] = static_cast<const uint16_t*>(a.W) + static_cast<size_t>(w_row<EPI>(a, nt, wr[i])) * a.ldw +
+            static_cast<size_t>(slice) * K + wc[i];
+  }
+  v4u gx[XL], gw[4];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < XL; ++i) gx[i] = *reinterpret_cast<const v4u*>(xp[i] + k0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) gw[i] = *reinterpret_cast<const v4u*>(wp[i] + k0);
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < XL; ++i) *reinterpret_cast<v4u*>(&xs[buf][xr[i]][xc[i]]) = gx[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<v4u*>(&ws[buf][wr[i]][wc[i]]) = gw[i];
+  };
+
+  f32x4_t acc[MI][4];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = K / KB;
+  load(0);
+  store(0);
+  __syncthreads();
+  const int fr = lane & 15, fk = (lane >> 4) * 8;
+  for (int kb = 0; kb < nk; ++kb) {
+    const int buf = kb & 1;
+    if (kb + 1 < nk) load((kb + 1) * KB);
+#pragma unroll
+    for (int ks = 0; ks < KB; ks += 32) {
+      bf16x8_t af[MI], bfr[4];
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+        af[i] = *reinterpret_cast<const bf16x8_t*>(&xs[buf][wm * (BMT / 2) + i * 16 + fr][ks + fk]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bfr[j] = *reinterpret_cast<const bf16x8_t*>(&ws[buf][wn * 64 + j * 16 + fr][ks + fk]);
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    if (kb + 1 < nk) store(buf ^ 1);
+    __syncthreads();
+  }
+
+  gemm_epilogue<EPI, BMT>(a, acc, mt, nt, slice, wm, wn, lane);
+}
+
+// ---- the same tile with its K blocks moved global -> LDS directly -------------
+// global_load_lds_dwordx4 writes lane l's 16 bytes at the instruction's LDS
+// base + 16 l, so one instruction fills 64 / CPR tile rows of CPR chunks (one
+// K block of KBD bf16, CPR = KBD / 8) and no registers stage the loads: NS
+// blocks can be in flight, issued NS - 1 blocks ahead of the one being
+// multiplied.  Chunk c of tile row r sits in slot c ^ ((r >> SH) & (CPR - 1))
+// of its row (a lane picks the global chunk that belongs in its slot), so
+// the 16 rows of a fragment read fall in distinct LDS banks.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) void* gbl_ptr_t;
+
+template <int CPR>
+__device__ __forceinline__ int swz(int r, int c) {
+  constexpr int SH = CPR == 8 ? 1 : 2;
+  return r * CPR + (c ^ ((r >> SH) & (CPR - 1)));
+}
+
+// s_waitcnt vmcnt(n), expcnt and lgkmcnt not waited for (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+template <int EPI, int BMT, int NS, int KBD>
+__global__ __launch_bounds__(NTH) void gemm_kernel2(GemvArgs a, int mtiles, int ntiles) {
+  static_assert(KBD == 32 || KBD == 64, "K block");
+  constexpr int MI = BMT / 32;
+  constexpr int CPR = KBD / 8, RPI = kWave / CPR;  // chunks per row, rows per DMA instruction
+  constexpr int XI = BMT / (4 * RPI), WI = BN / (4 * RPI);  // DMA instructions per wave and block
+  constexpr int L = XI + WI;
+  constexpr int STAGE = (BMT + BN) * KBD;  // bf16 per stage
+  static_assert(NS >= 2 && NS <= 4 && (NS - 2) * L < 64, "stages");
+  __shared__ __attribute__((aligned(16))) uint16_t lds[NS * STAGE];
+  const int per = gridDim.x / kXcds;
+  const int tile = (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
+  if (tile >= mtiles * ntiles) return;  // padding workgroups leave before any barrier
+  const int mt = tile % mtiles, nt = tile / mtiles;
+  const int M = a.M, K = a.K, slice = blockIdx.y;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int m0 = mt * BMT;
+
+  // this lane's global chunk for each of its DMA instructions
+  const uint16_t* xp[XI];
+  const uint16_t* wp[WI];
+#pragma unroll
+  for (int i = 0; i < XI; ++i) {
+    const int r = (wave * XI + i) * RPI + lane / CPR;
+    const int c = swz<CPR>(r, lane % CPR) - r * CPR;  // the slot's chunk (the swizzle is its own inverse)
+    xp[i] = static_cast<const uint16_t*>(a.x) + static_cast<size_t>(min(m0 + r, M - 1)) * a.ldx +
+            static_cast<size_t>(slice) * K + c * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < WI; ++i) {
+    const int r = (wave * WI + i) * RPI + lane / CPR;
+    const int c = swz<CPR>(r, lane % CPR) - r * CPR;
+    wp[i] = static_cast<const uint16_t*>(a.W) + static_cast<size_t>(w_row<EPI>(a, nt, r)) * a.ldw +
+            static_cast<size_t>(slice) * K + c * 8;
+  }
+  auto issue = [&](int st, int k0) {
+    uint16_t* base = lds + st * STAGE;
+#pragma unroll
+    for (int i = 0; i < XI; ++i)
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(xp[i] + k0), (lds_ptr_t)(base + (wave * XI + i) * RPI * KBD), 16, 0,
+                                       0);
+#pragma unroll
+    for (int i = 0; i < WI; ++i)
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(wp[i] + k0),
+                                       (lds_ptr_t)(base + BMT * KBD + (wave * WI + i) * RPI * KBD), 16, 0, 0);
+  };
+
+  f32x4_t acc[MI][4];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = K / KBD;
+#pragma unroll
+  for (int st = 0; st < NS - 1; ++st)
+    if (st < nk) issue(st, st * KBD);
+  const int fr = lane & 15, fc = lane >> 4;
+  for (int kb = 0; kb < nk; ++kb) {
+    // this wave's block kb is in LDS once at most `later` later blocks are in flight
+    const int later = min(NS - 2, nk - 1 - kb);
+    if (later >= NS - 2) wait_vm<(NS - 2) * L>();
+    else if (later == 1) wait_vm<L>();
+    else wait_vm<0>();
+    // every wave's block kb is in; every wave is done with block kb - 1 (its
+    // LDS reads were consumed by its MFMAs).  A bare s_barrier: the fence of
+    // __syncthreads would wait for every block in flight.
+    __builtin_amdgcn_s_barrier();
+    if (kb + NS - 1 < nk) issue((kb + NS - 1) % NS, (kb + NS - 1) * KBD);
+    const uint16_t* xs = lds + (kb % NS) * STAGE;
+    const uint16_t* ws = xs + BMT * KBD;
+#pragma unroll
+    for (int ks = 0; ks < CPR; ks += 4) {  // 32 K per MFMA: chunks ks .. ks + 3
+      bf16x8_t af[MI], bfr[4];
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const int r = wm * (BMT / 2) + i * 16 + fr;
+        af[i] = *reinterpret_cast<const bf16x8_t*>(xs + swz<CPR>(r, ks + fc) * 8);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = wn * 64 + j * 16 + fr;
+        bfr[j] = *reinterpret_cast<const bf16x8_t*>(ws + swz<CPR>(r, ks + fc) * 8);
+      }
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+  }
+  gemm_epilogue<EPI, BMT>(a, acc, mt, nt, slice, wm, wn, lane);
 }
 
 }  // namespace mfma

@@ -119,7 +119,14 @@ hipError_t launch_gemm_t(const GemvArgs& a, hipStream_t s) {
   const int mt = (a.M + BMT - 1) / BMT, nt = mfma::n_tiles<EPI>(a);
   const int total = mt * nt;
   const int grid = (total + mfma::kXcds - 1) / mfma::kXcds * mfma::kXcds;
-  hipLaunchKernelGGL((mfma::gemm_kernel<EPI, BMT>), dim3(grid, a.ksplit), dim3(mfma::NTH), 0, s, a, mt, nt);
+  if constexpr (mfma::kDmaStages > 0) {
+    constexpr int NS = BMT == 128 ? mfma::kDmaStages : mfma::kDmaStages64;
+    constexpr int KBD = BMT == 128 ? mfma::kDmaKB : mfma::kDmaKB64;
+    hipLaunchKernelGGL((mfma::gemm_kernel2<EPI, BMT, NS, KBD>), dim3(grid, a.ksplit), dim3(mfma::NTH), 0, s, a, mt,
+                       nt);
+  } else {
+    hipLaunchKernelGGL((mfma::gemm_kernel<EPI, BMT>), dim3(grid, a.ksplit), dim3(mfma::NTH), 0, s, a, mt, nt);
+  }
   return hipGetLastError();
 }
 

@@ -488,6 +488,8 @@ def main():
     ap.add_argument("--new-tokens", type=int, default=256)
     ap.add_argument("--cpu-layers", type=int, default=36, help="target layers in the CPU-baseline sample")
     ap.add_argument("--cpu-prompt", type=int, default=32, help="prompt tokens before the CPU-baseline round")
+    ap.add_argument("--mfma-only", action="store_true",
+                    help="launch only the matrix-core linears at M = 1280 (for counter passes)")
     ap.add_argument("--kernel-only", action="store_true",
                     help="launch only the dominant kernel and a calibration copy (for counter passes)")
     ap.add_argument("--skip-generate", action="store_true", help="skip the emitted tok/s generations")
@@ -503,6 +505,13 @@ def main():
 
     if args.kernel_only:
         kernel_only(2)
+        return
+    if args.mfma_only:
+        from draft_then_verify_amd import binding as bd
+
+        bd.load_library()
+        for r in mfma_linears(reps=8):
+            log(f"mfma-only: {r['linear']} {r['us_per_launch']} us, {r['achieved']} TFLOP/s")
         return
 
     import torch

@@ -24,6 +24,9 @@ Qwen3-0.6B-shaped draft, B = 1, gamma = 4, a 256-token prompt, 256 new tokens.
 * ``batch_sweep``: speculative vs plain emitted tok/s for B in {1, 8, 64,
   256} on the second workload's target and 2-layer drafter (gamma = 4,
   256-token prompts).
+* ``batch_verify_step``: the verify step alone on the same target for B in
+  {1, 8, 64, 256} (5 to 1280 rows): ms, verified positions/s and algorithmic
+  GB/s.  ``--verify-batch B`` runs only one of them (for profiles).
 * ``division_check_gamma1``: the gamma = 1 division of the M1 Max page,
   predicted (1 + p) T_decode / (T_verify + T_draft) against the measured
   speculative/plain ratio, on the same shapes.
@@ -55,10 +58,11 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def verify_pass_bytes(shape, B: int, m: int, ctx_sum: int) -> int:
+def verify_pass_bytes(shape, B: int, m: int, ctx_sum: int, logits: bool = True) -> int:
     """Algorithmic bytes of one verify pass: every linear weight once, the
     gathered embedding rows, norm gains, the KV rows read (ctx_sum = sum over
-    sequences of the keys attended) and written, logits written and read once."""
+    sequences of the keys attended) and written, logits written and read once
+    (not when the step keeps them out of memory: logits False)."""
     e = 2 if shape.dtype == "bf16" else 4
     d, L, F, V = shape.d_model, shape.n_layers, shape.d_ff, shape.vocab
     hq = shape.n_heads * shape.head_dim
@@ -66,7 +70,7 @@ def verify_pass_bytes(shape, B: int, m: int, ctx_sum: int) -> int:
     norms = (2 * L + 1) * d * 4
     kv_tok = shape.kv_bytes_per_token()
     M = B * m
-    return weights + M * d * e + norms + ctx_sum * kv_tok + M * kv_tok + 2 * M * V * 4
+    return weights + M * d * e + norms + ctx_sum * kv_tok + M * kv_tok + (2 * M * V * 4 if logits else 0)
 
 
 GEMV_SOURCES = ("gemv_launch.hpp", "gemv_epi_swiglu.hip", "gemv_kernels.hpp", "common.hpp", "kernels.hpp")
@@ -251,6 +255,34 @@ def batch_sweep(n_new: int, batches=(1, 8, 64, 256), P: int = 256, g: int = 4) -
             f"{1e3 * rs['wall_s'] / rs['rounds']:.3f} ms), plain {rp['tok_s']:.0f} tok/s "
             f"({1e3 * rp['wall_s'] / rp['rounds']:.3f} ms per token), ratio {rs['tok_s'] / rp['tok_s']:.3f}, "
             f"MAL {rs['mean_acceptance_length']:.2f}")
+    return rows
+
+
+def batch_verify_steps(batches=(1, 8, 64, 256), P: int = 256, g: int = 4, steps: int = 20) -> list:
+    """The verify step alone (spec_decode_step, graph-replayed) of the second
+    workload's target at each batch size: ms per step, verified positions/s
+    and algorithmic GB/s."""
+    import torch
+
+    from draft_then_verify_amd import binding as bd
+    from synth import SHAPES, make_prompt, make_weights
+
+    sh = SHAPES["small"]
+    target = bd.SpecModel(sh, make_weights(sh, seed=21, device="cuda"))
+    rows = []
+    for B in batches:
+        prompt = make_prompt(B, P, sh.vocab, seed=22 + B)
+        ms, ctx_mean, note, _ = time_verify_step(target, sh, prompt, B, g, steps, 3, P + steps + 3 + 4 * (g + 1))
+        # with more than d_model / 4 rows the step's LM head writes softmax
+        # statistics instead of the logits (the library's rule for bf16)
+        fused = B * (g + 1) > sh.d_model // 4
+        nbytes = verify_pass_bytes(sh, B, g + 1, int(round(B * ctx_mean)), logits=not fused)
+        rows.append({"B": B, "rows": B * (g + 1), "ms": round(ms, 4),
+                     "verified_positions_per_s": round(B * (g + 1) / (ms / 1e3), 1),
+                     "GB_s": round(nbytes / (ms / 1e3) / 1e9, 1), "context": note})
+        log(f"verify step B={B} ({B * (g + 1)} rows): {ms:.4f} ms, {B * (g + 1) / (ms / 1e3):.0f} verified "
+            f"positions/s, {nbytes / (ms / 1e3) / 1e9:.0f} GB/s algorithmic, context {note}")
+        torch.cuda.empty_cache()
     return rows
 
 
@@ -498,6 +530,8 @@ def main():
                     help="skip the batch sweep, the gamma = 1 division check and the n-gram workload "
                          "(second workload's shapes)")
     ap.add_argument("--graph", type=int, default=1, help="time graph replays of the decode step (1) or eager calls (0)")
+    ap.add_argument("--verify-batch", type=int, default=0,
+                    help="time only the second workload's verify step at this batch size (for profiles)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this path has no multi-GPU mode (run with --gpus 1)", file=sys.stderr)
@@ -505,6 +539,12 @@ def main():
 
     if args.kernel_only:
         kernel_only(2)
+        return
+    if args.verify_batch:
+        from draft_then_verify_amd import binding as bd
+
+        bd.load_library()
+        batch_verify_steps(batches=(args.verify_batch,))
         return
     if args.mfma_only:
         from draft_then_verify_amd import binding as bd
@@ -599,9 +639,10 @@ def main():
                "generation": "graph-replayed rounds (drafter passes, verify step and bookkeeping on the device)"}
         del plain
 
-    sweep = division = ngram = mfma = None
+    sweep = division = ngram = mfma = vsteps = None
     if not args.skip_sweep:
         mfma = mfma_linears()
+        vsteps = batch_verify_steps()
         sweep = batch_sweep(args.new_tokens)
         division = division_check(args.new_tokens)
         ngram = ngram_workload(args.new_tokens)
@@ -629,6 +670,7 @@ def main():
                      "us_per_launch": round(k_us, 2), "bytes_per_launch": k_bytes},
         "cpu_baseline": cpu,
         "batch_sweep": sweep,
+        "batch_verify_step": vsteps,
         "division_check_gamma1": division,
         "ngram_workload": ngram,
         "mfma_linears": mfma,

@@ -8,14 +8,14 @@
 // real dense contraction and belongs on MFMA.  The GEMV kernel would stream
 // the weights once per 8 rows instead.
 //
-// Tiles: a workgroup computes BMT rows x 128 weight rows of Y with 4 waves in
-// a 2 x 2 arrangement; each wave owns BMT/2 x 64 = (BMT/32) x 4 tiles of
-// v_mfma_f32_16x16x32_bf16.  BMT is 128 when the launch still has a
-// workgroup per CU with it (each A fragment read from LDS then feeds 4 MFMAs
-// and each B fragment 4: 8 reads per 16 MFMAs against 6 per 8 at BMT = 64,
-// and the LDS reads are what bounds this kernel), else 64.  The K dimension advances 64 at a time through
-// two LDS buffers; the next block's 16-byte global loads are issued before
-// the current block is multiplied.  Fragment layouts (gfx950): A lane l holds
+// Tiles: a workgroup computes BMT rows x BNT weight rows of Y with 2 x
+// (BNT / 64) waves; each wave owns BMT/2 x 64 = (BMT/32) x 4 tiles of
+// v_mfma_f32_16x16x32_bf16.  The tile is 256 x 256 (8 waves, one workgroup
+// per CU) when the launch still has a workgroup per CU with it, else 128 x
+// 128 (4 waves, two workgroups per CU), else 64 x 128.  A CU's vector memory
+// path moves 64 bytes per clock: a 128 x 128 tile's K blocks take as many
+// clocks to load as its MFMAs take to run, a 256 x 256 tile's half as many.
+// The K dimension advances in blocks through a ring of LDS stages.  Fragment layouts (gfx950): A lane l holds
 // row l % 16, k = 8 (l / 16) .. +7; B lane l holds column l % 16, the same k;
 // D lane l holds rows 4 (l / 16) .. +3 of column l % 16.
 //
@@ -54,49 +54,60 @@ constexpr int kDmaStages = 2;
 constexpr int kDmaStages64 = 3;
 constexpr int kDmaKB = 64;    // K per LDS stage, 128-row tiles
 constexpr int kDmaKB64 = 64;  // 64-row tiles
+// 256 x 256 tiles (8 waves, one workgroup per CU); 0: not used
+constexpr int kDmaStages256 = 2;
+constexpr int kDmaKB256 = 64;
 
-template <int EPI>
+// Weight tiles of a launch whose workgroups hold BNT weight rows (128 or
+// 256; QKV only 128).
+template <int EPI, int BNT = BN>
 __host__ __device__ inline int n_tiles(const GemvArgs& a) {
-  if (EPI == EPI_SWIGLU) return (a.N + 63) / 64;
+  if (EPI == EPI_SWIGLU) return (a.N + BNT / 2 - 1) / (BNT / 2);
   if (EPI == EPI_QKV) return a.hd == 128 ? a.H + 2 * a.Hkv : (a.H + 2 * a.Hkv + 1) / 2;
-  return (a.N + BN - 1) / BN;
+  return (a.N + BNT - 1) / BNT;
 }
 
-// Weight row held in local tile row lr (0 .. 127) of weight tile nt.
-template <int EPI>
+// Weight row held in local tile row lr (0 .. BNT-1) of weight tile nt.  Each
+// 64 rows are one wave column's: for SwiGLU 32 gate rows, then the matching
+// 32 up rows.
+template <int EPI, int BNT>
 __device__ __forceinline__ int w_row(const GemvArgs& a, int nt, int lr) {
   const int wn = lr >> 6, c = lr & 63;
   if constexpr (EPI == EPI_SWIGLU) {
-    const int n = min(nt * 64 + wn * 32 + (c & 31), a.N - 1);
+    const int n = min(nt * (BNT / 2) + wn * 32 + (c & 31), a.N - 1);
     return c < 32 ? n : a.N + n;
   } else if constexpr (EPI == EPI_QKV) {
+    static_assert(BNT == 128, "QKV tiles are 128 rows");
     if (a.hd == 64) return min((2 * nt + wn) * 64 + c, a.N - 1);  // head 2 nt + wn, dim c
     const int dim = (c < 32) ? wn * 32 + c : 64 + wn * 32 + (c - 32);
     return nt * a.hd + dim;
   } else {
-    return min(nt * BN + lr, a.N - 1);
+    return min(nt * BNT + lr, a.N - 1);
   }
 }
 
-// The epilogue of a workgroup's BMT x 128 tile (acc: the wave's MI x 4
-// 16 x 16 tiles).  Lane holds rows 4 (lane / 16) + r of each 16-row tile,
-// column lane % 16.
-template <int EPI, int BMT>
+// The epilogue of a workgroup's BMT x BNT tile (acc: the wave's MI x 4
+// 16 x 16 tiles; wave column wn holds tile columns wn*64 .. +63).  Lane holds
+// rows 4 (lane / 16) + r of each 16-row tile, column lane % 16.
+template <int EPI, int BMT, int BNT>
 __device__ __forceinline__ void gemm_epilogue(const GemvArgs& a, f32x4_t (&acc)[BMT / 32][4], int mt, int nt,
                                               int slice, int wm, int wn, int lane) {
   constexpr int MI = BMT / 32;
+  constexpr int WN = BNT / 64;  // wave columns
   const int M = a.M, m0 = mt * BMT;
   const int col = lane & 15, rb = (lane >> 4) * 4;
   if constexpr (EPI == EPI_LMSTAT) {
-    // Row statistics of the 128-column tile in lmstat.hpp's order: this
-    // wave's 64 columns are half wn of the tile, column wn*64 + 16 j + col in
-    // slot j of lane col.  The two halves meet in LDS.
-    __shared__ float hmax[2][BMT];
-    __shared__ float hsum[2][BMT];
-    __shared__ int hidx[2][BMT];
+    // Row statistics of each 128-column tile in lmstat.hpp's order: wave
+    // column wn holds half wn & 1 of statistics tile nt * BNT / 128 + wn / 2,
+    // column 64 (wn & 1) + 16 j + col of it in slot j of lane col.  The two
+    // halves meet in LDS.
+    __shared__ float hmax[WN][BMT];
+    __shared__ float hsum[WN][BMT];
+    __shared__ int hidx[WN][BMT];
     const float T = a.temp;
     const int N = a.N, nts = (a.N + lmstat::kTile - 1) / lmstat::kTile;
-    const int n0 = nt * lmstat::kTile + wn * 64 + col;
+    const int n0 = nt * BNT + wn * 64 + col;
+    const int h0 = wn & ~1;  // the statistics tile's first half
     auto vals = [&](int i, int r, float (&v)[4]) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) v[j] = (n0 + j * 16 < N) ? __fdiv_rn(acc[i][j][r], T) : -INFINITY;
@@ -133,12 +144,13 @@ __device__ __forceinline__ void gemm_epilogue(const GemvArgs& a, f32x4_t (&acc)[
           const int lr = wm * (BMT / 2) + i * 16 + rb + r;
           float v[4];
           vals(i, r, v);
-          const float z = group_sum<16>(lmstat::slot_sum(v, fmaxf(hmax[0][lr], hmax[1][lr])));
+          const float z = group_sum<16>(lmstat::slot_sum(v, fmaxf(hmax[h0][lr], hmax[h0 + 1][lr])));
           if (col == 0) hsum[wn][lr] = z;
         }
       __syncthreads();
     }
-    if (wn == 0 && col == 0) {
+    const int stile = nt * (BNT / lmstat::kTile) + (wn >> 1);
+    if ((wn & 1) == 0 && col == 0 && stile < nts) {
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -148,14 +160,14 @@ __device__ __forceinline__ void gemm_epilogue(const GemvArgs& a, f32x4_t (&acc)[
           if (m >= M) continue;
           float2 st;
           if (T > 0.f) {
-            st = make_float2(fmaxf(hmax[0][lr], hmax[1][lr]), hsum[0][lr] + hsum[1][lr]);
+            st = make_float2(fmaxf(hmax[h0][lr], hmax[h0 + 1][lr]), hsum[h0][lr] + hsum[h0 + 1][lr]);
           } else {
-            float mx = hmax[0][lr];
-            int ix = hidx[0][lr];
-            lmstat::argmax_merge(mx, ix, hmax[1][lr], hidx[1][lr]);
+            float mx = hmax[h0][lr];
+            int ix = hidx[h0][lr];
+            lmstat::argmax_merge(mx, ix, hmax[h0 + 1][lr], hidx[h0 + 1][lr]);
             st = make_float2(mx, __int_as_float(ix));
           }
-          a.tpart[static_cast<size_t>(m) * nts + nt] = st;
+          a.tpart[static_cast<size_t>(m) * nts + stile] = st;
         }
     }
     // the logit at the drafted token of each row that scores one
@@ -186,13 +198,14 @@ __device__ __forceinline__ void gemm_epilogue(const GemvArgs& a, f32x4_t (&acc)[
       if constexpr (EPI == EPI_SWIGLU) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const int n = nt * 64 + wn * 32 + j * 16 + col;
+          const int n = nt * (BNT / 2) + wn * 32 + j * 16 + col;
           if (n < a.N) {
             const float g = acc[i][j][r], u = acc[i][j + 2][r];
             static_cast<uint16_t*>(a.z)[static_cast<size_t>(m) * a.ldz + n] = f2bf(g / (1.f + expf(-g)) * u);
           }
         }
       } else if constexpr (EPI == EPI_QKV) {
+        static_assert(BNT == 128, "QKV tiles are 128 rows");
         const int H = a.H, Hkv = a.Hkv, hd = a.hd, half = hd / 2;
         const bool two = hd == 64;  // two heads per workgroup
         const int hh = two ? 2 * nt + wn : nt;
@@ -233,7 +246,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemvArgs& a, f32x4_t (&acc)[
       } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int n = nt * BN + wn * 64 + j * 16 + col;
+          const int n = nt * BNT + wn * 64 + j * 16 + col;
           if (n < a.N) {
             float* dst = y + static_cast<size_t>(m) * a.ldy + n;
             if constexpr (EPI == EPI_RESID) *dst += acc[i][j][r];
@@ -277,7 +290,7 @@ __global__ __launch_bounds__(NTH) void gemm_kernel(GemvArgs a, int mtiles, int n
     const int c = threadIdx.x + i * NTH;
     wr[i] = c >> 3;
     wc[i] = (c & 7) * 8;
-    wp[i] = static_cast<const uint16_t*>(a.W) + static_cast<size_t>(w_row<EPI>(a, nt, wr[i])) * a.ldw +
+    wp[i] = static_cast<const uint16_t*>(a.W) + static_cast<size_t>(w_row<EPI, BN>(a, nt, wr[i])) * a.ldw +
             static_cast<size_t>(slice) * K + wc[i];
   }
   v4u gx[XL], gw[4];
@@ -325,7 +338,7 @@ __global__ __launch_bounds__(NTH) void gemm_kernel(GemvArgs a, int mtiles, int n
     __syncthreads();
   }
 
-  gemm_epilogue<EPI, BMT>(a, acc, mt, nt, slice, wm, wn, lane);
+  gemm_epilogue<EPI, BMT, BN>(a, acc, mt, nt, slice, wm, wn, lane);
 }
 
 // ---- the same tile with its K blocks moved global -> LDS directly -------------
@@ -352,14 +365,17 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
-template <int EPI, int BMT, int NS, int KBD>
-__global__ __launch_bounds__(NTH) void gemm_kernel2(GemvArgs a, int mtiles, int ntiles) {
+template <int EPI, int BMT, int BNT, int NS, int KBD>
+__global__ __launch_bounds__(2 * BNT) void gemm_kernel2(GemvArgs a, int mtiles, int ntiles) {
   static_assert(KBD == 32 || KBD == 64, "K block");
+  static_assert(BNT == 128 || BNT == 256, "weight tile");
   constexpr int MI = BMT / 32;
+  constexpr int NW = BNT / 32;  // waves: 2 rows x BNT / 64 columns of (BMT / 2) x 64 wave tiles
   constexpr int CPR = KBD / 8, RPI = kWave / CPR;  // chunks per row, rows per DMA instruction
-  constexpr int XI = BMT / (4 * RPI), WI = BN / (4 * RPI);  // DMA instructions per wave and block
+  constexpr int XI = BMT / (NW * RPI), WI = BNT / (NW * RPI);  // DMA instructions per wave and block
+  static_assert(XI * NW * RPI == BMT && WI * NW * RPI == BNT, "DMA rows");
   constexpr int L = XI + WI;
-  constexpr int STAGE = (BMT + BN) * KBD;  // bf16 per stage
+  constexpr int STAGE = (BMT + BNT) * KBD;  // bf16 per stage
   static_assert(NS >= 2 && NS <= 4 && (NS - 2) * L < 64, "stages");
   __shared__ __attribute__((aligned(16))) uint16_t lds[NS * STAGE];
   const int per = gridDim.x / kXcds;
@@ -385,7 +401,7 @@ __global__ __launch_bounds__(NTH) void gemm_kernel2(GemvArgs a, int mtiles, int 
   for (int i = 0; i < WI; ++i) {
     const int r = (wave * WI + i) * RPI + lane / CPR;
     const int c = swz<CPR>(r, lane % CPR) - r * CPR;
-    wp[i] = static_cast<const uint16_t*>(a.W) + static_cast<size_t>(w_row<EPI>(a, nt, r)) * a.ldw +
+    wp[i] = static_cast<const uint16_t*>(a.W) + static_cast<size_t>(w_row<EPI, BNT>(a, nt, r)) * a.ldw +
             static_cast<size_t>(slice) * K + c * 8;
   }
   auto issue = [&](int st, int k0) {
@@ -443,7 +459,7 @@ __global__ __launch_bounds__(NTH) void gemm_kernel2(GemvArgs a, int mtiles, int 
         for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
   }
-  gemm_epilogue<EPI, BMT>(a, acc, mt, nt, slice, wm, wn, lane);
+  gemm_epilogue<EPI, BMT, BNT>(a, acc, mt, nt, slice, wm, wn, lane);
 }
 
 }  // namespace mfma

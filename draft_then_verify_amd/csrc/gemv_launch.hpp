@@ -114,15 +114,18 @@ hipError_t launch_rows(const GemvArgs& a, int mb, hipStream_t s) {
   }
 }
 
-template <int EPI, int BMT>
+template <int EPI, int BMT, int BNT>
 hipError_t launch_gemm_t(const GemvArgs& a, hipStream_t s) {
-  const int mt = (a.M + BMT - 1) / BMT, nt = mfma::n_tiles<EPI>(a);
+  const int mt = (a.M + BMT - 1) / BMT, nt = mfma::n_tiles<EPI, BNT>(a);
   const int total = mt * nt;
   const int grid = (total + mfma::kXcds - 1) / mfma::kXcds * mfma::kXcds;
-  if constexpr (mfma::kDmaStages > 0) {
+  if constexpr (BNT == 256) {
+    hipLaunchKernelGGL((mfma::gemm_kernel2<EPI, BMT, BNT, mfma::kDmaStages256, mfma::kDmaKB256>), dim3(grid, a.ksplit),
+                       dim3(2 * BNT), 0, s, a, mt, nt);
+  } else if constexpr (mfma::kDmaStages > 0) {
     constexpr int NS = BMT == 128 ? mfma::kDmaStages : mfma::kDmaStages64;
     constexpr int KBD = BMT == 128 ? mfma::kDmaKB : mfma::kDmaKB64;
-    hipLaunchKernelGGL((mfma::gemm_kernel2<EPI, BMT, NS, KBD>), dim3(grid, a.ksplit), dim3(mfma::NTH), 0, s, a, mt,
+    hipLaunchKernelGGL((mfma::gemm_kernel2<EPI, BMT, BNT, NS, KBD>), dim3(grid, a.ksplit), dim3(2 * BNT), 0, s, a, mt,
                        nt);
   } else {
     hipLaunchKernelGGL((mfma::gemm_kernel<EPI, BMT>), dim3(grid, a.ksplit), dim3(mfma::NTH), 0, s, a, mt, nt);
@@ -134,10 +137,20 @@ template <int EPI>
 hipError_t launch_gemm(const GemvArgs& b, int M, hipStream_t s) {
   GemvArgs a = b;
   a.M = M;
-  // 128-row tiles while they still give every CU a workgroup (K slices count)
+  // The largest tile that still gives every CU a workgroup (K slices count):
+  // 256 x 256 (one workgroup of 8 waves per CU), else 128 x 128 (two of 4
+  // waves), else 64 x 128.  The LM head's statistics epilogue (exp of every
+  // logit, cross-wave merges) keeps 128 x 128: with one workgroup per CU
+  // nothing overlaps it.
+  if constexpr (EPI != EPI_QKV && EPI != EPI_LMSTAT) {
+    if constexpr (mfma::kDmaStages256 > 0) {
+      const long long tiles256 = static_cast<long long>((M + 255) / 256) * mfma::n_tiles<EPI, 256>(a) * a.ksplit;
+      if (tiles256 >= kCUs) return launch_gemm_t<EPI, 256, 256>(a, s);
+    }
+  }
   const long long tiles128 = static_cast<long long>((M + 127) / 128) * mfma::n_tiles<EPI>(a) * a.ksplit;
-  if (tiles128 >= kCUs) return launch_gemm_t<EPI, 128>(a, s);
-  return launch_gemm_t<EPI, 64>(a, s);
+  if (tiles128 >= kCUs) return launch_gemm_t<EPI, 128, 128>(a, s);
+  return launch_gemm_t<EPI, 64, 128>(a, s);
 }
 
 template <typename WT, int EPI>

@@ -76,6 +76,15 @@ def test_linear_matrix_cores_large():
     _check(151936, 4096, 40, 0, seed=303)   # 8B LM head, B = 8 verify rows
 
 
+@pytest.mark.parametrize("N,K,M,epi", [(40000, 1024, 257, 0),   # 2 x 157 tiles of 256 x 256, 1 row in the last
+                                       (13100, 1024, 1280, 1),  # 5 x 52, the last 44 columns wide
+                                       (8200, 2048, 1000, 2)])  # SwiGLU: 4 x 65 tiles of 128 outputs
+def test_linear_matrix_cores_wide_tiles(N, K, M, epi):
+    """Launches with at least one 256 x 256 tile per CU (8-wave workgroups),
+    ragged in rows and columns."""
+    _check(N, K, M, epi, seed=400 + epi)
+
+
 def test_linear_float32():
     _check(704, 256, 5, 0, seed=3, dtype=torch.float32)
     _check(256, 704, 4, 1, seed=4, dtype=torch.float32)

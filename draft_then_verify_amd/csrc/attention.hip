@@ -346,6 +346,359 @@ hipError_t launch_mq(const AttnArgs& a, int B, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---- matrix cores: bf16 K/V rows of head_dim 64 ---------------------------------
+// The split kernel's work with v_mfma_f32_16x16x32_bf16 instead of float32
+// FMAs.  With many query rows per KV head (G heads x the block's rows: 20 for
+// a gamma = 4 pass of a 4:1 GQA model) the FMA form is bound by issuing its
+// multiply-adds, not by the K/V bytes.
+//
+// Workgroup = (sequence b, KV head, context split, block of rows): its R = G x
+// mb query rows (R <= 32, padded to RT x 16) against the keys it sees.  Its
+// NW waves take 32-key blocks in turn (wave w: blocks w, w + NW, ...), each
+// with its own online softmax, and are merged at the end in wave order; no
+// wave waits for another inside the key loop.  Per block:
+//  * S^T = K . Q^T: A is K straight from the cache (lane l: key row l % 16,
+//    8 dims), B is the wave's queries (lane l: row l % 16, 8 dims), held in
+//    registers for the whole pass.  Key tile t's A row i is key
+//    8 (i / 4) + 4 t + i % 4 of the block, so that the result leaves lane l
+//    with keys 8 (l / 16) .. + 7 of row l % 16;
+//  * online softmax per row: the lane's 8 keys, then the 4 lanes of the row
+//    (xor 16, xor 32);
+//  * O^T += V^T . P^T: B is the lane's 8 probabilities as they are, A is V^T
+//    read from a per-wave LDS block where the wave has written the block's V
+//    rows transposed (dimension-major), and O^T leaves each row's output in
+//    the lanes that hold its softmax state, so rescaling needs no exchange.
+// The queries and probabilities enter as bf16 pairs x = hi + lo (hi the bf16
+// rounding of x, lo that of the remainder): the pair carries x to within
+// 2^-18 relative, and K and V are bf16 already, so the products are those of
+// the float32 form to within that, accumulated in float32.
+namespace mfa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+constexpr int NW = 2;        // waves per workgroup (1, 2, 4 and 8 measured; 2 fastest at B = 64 and 256)
+constexpr int KB = 32;       // keys per wave block
+constexpr int HD = 64;       // head_dim
+constexpr int VTS = KB + 8;  // bf16 per dimension row of a wave's V^T block (16-byte aligned)
+constexpr int RMAX = 32;     // query rows per workgroup
+
+// Row blocks of a pass: workgroups of at most 32 query rows (G heads x mb
+// rows), or of at most 16 when that still leaves fewer than two workgroups
+// per CU (more, narrower workgroups with fewer registers each, rather than
+// context splits and their merge).
+__host__ __device__ inline int row_blocks(int B, int Hkv, int G, int m) {
+  const int cap32 = RMAX / G > 1 ? RMAX / G : 1, cap16 = 16 / G > 1 ? 16 / G : 1;
+  const int n32 = (m + cap32 - 1) / cap32;
+  if (static_cast<long long>(B) * Hkv * n32 >= 512) return n32;
+  return (m + cap16 - 1) / cap16;
+}
+__host__ __device__ inline int rows_per_block(int m, int nqc) { return (m + nqc - 1) / nqc; }
+
+// e^x as 2^(x log2 e) with the hardware exponential (e^-inf = 0)
+__device__ __forceinline__ float exp_hw(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+
+__device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
+  hi = static_cast<__bf16>(x);
+  lo = static_cast<__bf16>(x - static_cast<float>(hi));
+}
+
+// bf16 e of a 16-byte chunk of 8
+__device__ __forceinline__ uint32_t half_of(const v4u& v, int e) {
+  return (e & 1) ? (v[e >> 1] >> 16) : (v[e >> 1] & 0xffffu);
+}
+
+template <int RT>
+__global__ __launch_bounds__(NW * kWave) void attn_mfma_kernel(AttnArgs a) {
+  constexpr int ROWS = RT * 16;
+  constexpr int VT_BYTES = NW * HD * VTS * 2;
+  constexpr int OB_BYTES = NW * ROWS * HD * 4;
+  constexpr int U_BYTES = VT_BYTES > OB_BYTES ? VT_BYTES : OB_BYTES;
+  __shared__ __attribute__((aligned(16))) unsigned char su[U_BYTES];  // V^T blocks, then the merge
+  __shared__ float2 sml[NW][ROWS];  // each wave's (max, weight) per row
+  __shared__ float2 sfin[ROWS];     // the workgroup's (max, weight) per row
+  __shared__ int last_sh;
+
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int g16 = lane >> 4, c16 = lane & 15;
+  const int H = a.H, Hkv = a.Hkv, m = a.m, G = H / Hkv;
+  const int mb = rows_per_block(m, a.n_qc);
+  const int kvh = blockIdx.x % Hkv, b = blockIdx.x / Hkv;
+  const int sp = blockIdx.y, qc = blockIdx.z, ns = a.n_split;
+  const int i_first = qc * mb;
+  const int R = G * mb;
+  const int Lb = a.len[b];
+  const int n_keys = max(0, min(Lb + m, a.max_ctx));
+  const int last_row = min(m, i_first + mb) - 1;
+  const int kvis = max(0, min(n_keys, Lb + last_row + 1));  // keys the block's last row sees
+  const int nblk = (kvis + KB - 1) / KB;
+  const int per = (nblk + ns - 1) / ns;  // blocks per split
+  const int kbeg = min(kvis, sp * per * KB);
+  const int kend = min(kvis, kbeg + per * KB);
+  const int qld = H * HD;
+  const uint16_t* kc = static_cast<const uint16_t*>(a.kc);
+  const uint16_t* vc = static_cast<const uint16_t*>(a.vc);
+  const size_t kvbase = ((static_cast<size_t>(a.layer) * a.kvB + b) * Hkv + kvh) * a.max_ctx;
+
+  // the wave's first block is in flight while the queries are set up
+  const int klast = max(kend - 1, 0);
+  const int vcq = lane & 7, vkq = lane >> 3;  // V staging: dims 8 vcq .., keys 4 vkq ..
+  v4u kf[2][2], vf[4];
+  auto load = [&](int kb) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int key = min(kb + 8 * (c16 >> 2) + 4 * kt + (c16 & 3), klast);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        kf[kt][ks] = *reinterpret_cast<const v4u*>(kc + (kvbase + key) * HD + ks * 32 + g16 * 8);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      vf[t] = *reinterpret_cast<const v4u*>(vc + (kvbase + min(kb + 4 * vkq + t, klast)) * HD + vcq * 8);
+  };
+  int kb = kbeg + wave * KB;
+  if (kb < kend) load(kb);
+
+  // this lane's query row in each row tile: r = 16 rt + c16 -> (head g, row i)
+  int lim[RT];  // last key the row sees (-1: a padding row or one past m)
+  bf16x8_t qh[RT][2], ql[RT][2];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int r = rt * 16 + c16;
+    const int g = r / mb, i = i_first + r % mb;
+    const bool valid = r < R && i < m;
+    lim[rt] = valid ? Lb + i : -1;
+    const float* qr = a.q + static_cast<size_t>(b * m + (valid ? i : 0)) * qld + (kvh * G + (valid ? g : 0)) * HD;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const float4 x0 = *reinterpret_cast<const float4*>(qr + ks * 32 + g16 * 8);
+      const float4 x1 = *reinterpret_cast<const float4*>(qr + ks * 32 + g16 * 8 + 4);
+      const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        __bf16 hi, lo;
+        split_bf16(valid ? xs[e] * 0.125f : 0.f, hi, lo);  // scaled by 1 / sqrt(64)
+        qh[rt][ks][e] = hi;
+        ql[rt][ks][e] = lo;
+      }
+    }
+  }
+
+  f32x4_t o[RT][4];  // O^T: dims 16 dt + 4 g16 + j of row 16 rt + c16
+  float mrow[RT], lrow[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    mrow[rt] = -INFINITY;
+    lrow[rt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) o[rt][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  unsigned char* vt = su + wave * (HD * VTS * 2);
+  for (; kb < kend; kb += NW * KB) {
+    // S^T for the block
+    f32x4_t sc[RT][2];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) sc[rt][0] = sc[rt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8_t ka = __builtin_bit_cast(bf16x8_t, kf[kt][ks]);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          sc[rt][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qh[rt][ks], sc[rt][kt], 0, 0, 0);
+          sc[rt][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, ql[rt][ks], sc[rt][kt], 0, 0, 0);
+        }
+      }
+    // the block's V rows into the wave's V^T block: dimension 8 vcq + e,
+    // keys 4 vkq .. + 3 as one 8-byte write
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      uint2 w;
+      w.x = half_of(vf[0], e) | (half_of(vf[1], e) << 16);
+      w.y = half_of(vf[2], e) | (half_of(vf[3], e) << 16);
+      *reinterpret_cast<uint2*>(vt + ((vcq * 8 + e) * VTS + 4 * vkq) * 2) = w;
+    }
+    const int kb_next = kb + NW * KB;
+    if (kb_next < kend) load(kb_next);
+    // online softmax; the lane's keys are kb + 8 g16 + 4 kt + j
+    bf16x8_t ph[RT], pq[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      float sv[8];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int key = kb + 8 * g16 + 4 * kt + j;
+          sv[4 * kt + j] = (key < kend && key <= lim[rt]) ? sc[rt][kt][j] : -INFINITY;
+        }
+      float tm = sv[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) tm = fmaxf(tm, sv[e]);
+      tm = fmaxf(tm, __shfl_xor(tm, 16, kWave));
+      tm = fmaxf(tm, __shfl_xor(tm, 32, kWave));
+      const float mnew = fmaxf(mrow[rt], tm);
+      const float mref = mnew == -INFINITY ? 0.f : mnew;  // no key seen yet: everything weighs 0
+      const float alpha = exp_hw(mrow[rt] - mref);
+      float ls = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = exp_hw(sv[e] - mref);
+        ls += p;
+        __bf16 hi, lo;
+        split_bf16(p, hi, lo);
+        ph[rt][e] = hi;
+        pq[rt][e] = lo;
+      }
+      lrow[rt] = lrow[rt] * alpha + ls;
+      mrow[rt] = mnew;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) o[rt][dt] *= alpha;
+    }
+    // O^T += V^T . P^T
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(vt + ((dt * 16 + c16) * VTS + 8 * g16) * 2);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, ph[rt], o[rt][dt], 0, 0, 0);
+        o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pq[rt], o[rt][dt], 0, 0, 0);
+      }
+    }
+  }
+
+  // merge the waves in wave order: (max, weight) per row through LDS, then
+  // each wave's rescaled output
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    float l = lrow[rt] + __shfl_xor(lrow[rt], 16, kWave);
+    l += __shfl_xor(l, 32, kWave);
+    if (g16 == 0) sml[wave][rt * 16 + c16] = make_float2(mrow[rt], l);
+  }
+  __syncthreads();  // also: every wave is done with its V^T block
+  float* ob = reinterpret_cast<float*>(su);
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int row = rt * 16 + c16;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sml[w][row].x);
+    const float Mref = M == -INFINITY ? 0.f : M;
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float2 ml = sml[w][row];
+      L = fmaf(ml.y, exp_hw(ml.x - Mref), L);
+    }
+    const float wown = exp_hw(mrow[rt] - Mref);
+    const float sc = ns == 1 ? (L > 0.f ? wown / L : 0.f) : wown;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+      *reinterpret_cast<float4*>(ob + (static_cast<size_t>(wave) * ROWS + row) * HD + dt * 16 + g16 * 4) =
+          make_float4(o[rt][dt][0] * sc, o[rt][dt][1] * sc, o[rt][dt][2] * sc, o[rt][dt][3] * sc);
+    if (wave == 0 && g16 == 0) sfin[row] = make_float2(M, L);
+  }
+  __syncthreads();
+  // rows summed over the waves in wave order: the output (one split) or this
+  // split's partial (unnormalised output, max, weight)
+  uint16_t* xo = static_cast<uint16_t*>(a.xo);
+  constexpr int Q4 = HD / 4;
+  for (int idx = threadIdx.x; idx < R * Q4; idx += NW * kWave) {
+    const int r = idx / Q4, d4 = idx - r * Q4;
+    const int g = r / mb, i = i_first + r % mb;
+    if (i >= m) continue;
+    float4 acc = *reinterpret_cast<const float4*>(ob + static_cast<size_t>(r) * HD + 4 * d4);
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+      const float4 v = *reinterpret_cast<const float4*>(ob + (static_cast<size_t>(w) * ROWS + r) * HD + 4 * d4);
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+    const int h = kvh * G + g;
+    if (ns == 1) {
+      uint2 pk;
+      pk.x = static_cast<uint32_t>(f2bf(acc.x)) | (static_cast<uint32_t>(f2bf(acc.y)) << 16);
+      pk.y = static_cast<uint32_t>(f2bf(acc.z)) | (static_cast<uint32_t>(f2bf(acc.w)) << 16);
+      *reinterpret_cast<uint2*>(xo + static_cast<size_t>(b * m + i) * qld + h * HD + 4 * d4) = pk;
+    } else {
+      const size_t prow = ((static_cast<size_t>(b) * H + h) * m + i) * ns + sp;
+      *reinterpret_cast<float4*>(a.part_o + prow * HD + 4 * d4) = acc;
+      if (d4 == 0) a.part_ml[prow] = sfin[r];
+    }
+  }
+  if (ns == 1) return;
+  if (!last_block(a.counters + static_cast<size_t>(blockIdx.x) * gridDim.z + qc, ns, &last_sh)) return;
+  // The last workgroup of the row block merges the splits.  A wave per row
+  // takes the splits' weights exp(m_s - max) (lane = split) and their sum;
+  // then each thread sums its 4 dimensions of a row over the splits in split
+  // order, 8 partial loads in flight at a time.
+  float* swt = ob;  // [ROWS][64] split weights (the merge area is free again)
+  for (int r = wave; r < R; r += NW) {
+    const int g = r / mb, i = i_first + r % mb;
+    if (i >= m) continue;
+    const size_t p0 = ((static_cast<size_t>(b) * H + kvh * G + g) * m + i) * ns;
+    const float2 ml = lane < ns ? a.part_ml[p0 + lane] : make_float2(-INFINITY, 0.f);
+    const float M = wave_max(ml.x);
+    const float w = exp_hw(ml.x - (M == -INFINITY ? 0.f : M));
+    const float L = wave_sum(ml.y * w);
+    swt[r * kWave + lane] = w;
+    if (lane == 0) sfin[r] = make_float2(M, L);
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < R * Q4; idx += NW * kWave) {
+    const int r = idx / Q4, d4 = idx - r * Q4;
+    const int g = r / mb, i = i_first + r % mb;
+    if (i >= m) continue;
+    const int h = kvh * G + g;
+    const size_t p0 = ((static_cast<size_t>(b) * H + h) * m + i) * ns;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int t0 = 0; t0 < ns; t0 += 8) {
+      float4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        v[u] = *reinterpret_cast<const float4*>(a.part_o + (p0 + min(t0 + u, ns - 1)) * HD + 4 * d4);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float w = t0 + u < ns ? swt[r * kWave + t0 + u] : 0.f;
+        acc.x = fmaf(v[u].x, w, acc.x);
+        acc.y = fmaf(v[u].y, w, acc.y);
+        acc.z = fmaf(v[u].z, w, acc.z);
+        acc.w = fmaf(v[u].w, w, acc.w);
+      }
+    }
+    const float L = sfin[r].y, inv = L > 0.f ? 1.f / L : 0.f;
+    uint2 pk;
+    pk.x = static_cast<uint32_t>(f2bf(acc.x * inv)) | (static_cast<uint32_t>(f2bf(acc.y * inv)) << 16);
+    pk.y = static_cast<uint32_t>(f2bf(acc.z * inv)) | (static_cast<uint32_t>(f2bf(acc.w * inv)) << 16);
+    *reinterpret_cast<uint2*>(xo + static_cast<size_t>(b * m + i) * qld + h * HD + 4 * d4) = pk;
+  }
+}
+
+template <int RT>
+hipError_t launch_rt(const AttnArgs& a, int B, hipStream_t s) {
+  hipLaunchKernelGGL((attn_mfma_kernel<RT>), dim3(B * a.Hkv, a.n_split, a.n_qc), dim3(NW * kWave), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch(const AttnArgs& a, int B, hipStream_t s) {
+  const int G = a.H / a.Hkv;
+  if (a.n_qc != row_blocks(B, a.Hkv, G, a.m) || a.n_split < 1 || a.n_split > kWave || !a.counters)
+    return hipErrorInvalidValue;
+  if (a.n_split > 1 && (!a.part_o || !a.part_ml)) return hipErrorInvalidValue;
+  const int R = G * rows_per_block(a.m, a.n_qc);
+  if (R > RMAX) return hipErrorInvalidValue;
+  return R <= 16 ? launch_rt<1>(a, B, s) : launch_rt<2>(a, B, s);
+}
+
+}  // namespace mfa
+
+// The matrix-core kernel takes the split path's bf16 passes of head_dim 64.
+bool mfma_attention(bool bf16, int H, int Hkv, int hd) {
+  return bf16 && hd == mfa::HD && Hkv > 0 && H % Hkv == 0 && H / Hkv <= mfa::RMAX;
+}
+
 // ---- short passes: m <= 8 query rows, contexts up to kDecodeMaxCtx -------------
 // One workgroup per (sequence, query head, block of RW query rows): with few
 // sequences the rows are split until there are enough workgroups to spread
@@ -656,11 +1009,22 @@ bool attn_supported(int H, int Hkv, int hd) {
   return G <= waves ? (waves % G == 0) : (G % waves == 0);
 }
 
-int attn_row_blocks(int H, int Hkv, int hd, int m) {
+int attn_row_blocks(bool bf16, int B, int H, int Hkv, int hd, int m) {
+  if (mfma_attention(bf16, H, Hkv, hd)) return mfa::row_blocks(B, Hkv, H / Hkv, m);
   return make_plan(H, Hkv, m, rows_per_wave(H, Hkv, hd, m), waves_for(hd)).nqc;
 }
 
-int attn_num_splits(int B, int H, int Hkv, int hd, int m, int max_ctx) {
+int attn_num_splits(bool bf16, int B, int H, int Hkv, int hd, int m, int max_ctx) {
+  if (mfma_attention(bf16, H, Hkv, hd)) {
+    // context splits only while the row blocks leave fewer workgroups than
+    // CUs: about one per CU, each split at least two blocks per wave (one
+    // block per wave measured slower on 2048-token contexts at B = 1)
+    const int units = B * Hkv * mfa::row_blocks(B, Hkv, H / Hkv, m);
+    if (units >= 256) return 1;
+    int n = (256 + units - 1) / units;
+    n = min(n, (max_ctx + 2 * mfa::NW * mfa::KB - 1) / (2 * mfa::NW * mfa::KB));
+    return max(1, min(n, kWave));
+  }
   const Plan pl = make_plan(H, Hkv, m, rows_per_wave(H, Hkv, hd, m), waves_for(hd));
   const int units = B * Hkv * pl.nhb * pl.nqc;  // workgroups per split
   int n = (512 + units - 1) / units;
@@ -668,7 +1032,8 @@ int attn_num_splits(int B, int H, int Hkv, int hd, int m, int max_ctx) {
   return max(1, min(n, kWave));
 }
 
-size_t attn_counters(int B, int H, int Hkv, int hd, int m) {
+size_t attn_counters(bool bf16, int B, int H, int Hkv, int hd, int m) {
+  if (mfma_attention(bf16, H, Hkv, hd)) return static_cast<size_t>(B) * Hkv * mfa::row_blocks(B, Hkv, H / Hkv, m);
   const Plan pl = make_plan(H, Hkv, m, rows_per_wave(H, Hkv, hd, m), waves_for(hd));
   return static_cast<size_t>(B) * Hkv * pl.nhb * pl.nqc;
 }
@@ -709,6 +1074,7 @@ hipError_t launch_attention(bool bf16, int hd, const AttnArgs& a, int B, hipStre
     if (bf16) return hd == 128 ? launch_decode<uint16_t, 128>(a, B, s) : launch_decode<uint16_t, 64>(a, B, s);
     if (hd == 64) return launch_decode<float, 64>(a, B, s);
   }
+  if (mfma_attention(bf16, a.H, a.Hkv, hd)) return mfa::launch(a, B, s);
   if (bf16) return hd == 128 ? launch_hd<uint16_t, 128>(a, B, s) : launch_hd<uint16_t, 64>(a, B, s);
   return hd == 128 ? launch_hd<float, 128>(a, B, s) : launch_hd<float, 64>(a, B, s);
 }

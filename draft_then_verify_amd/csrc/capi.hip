@@ -59,9 +59,10 @@ Layout make_layout(const spec_model_cfg& c, int B, int m, int max_ctx) {
   const size_t elt = c.dtype == SPEC_BF16 ? 2 : 4;
   const int hq = c.n_heads * c.head_dim;
   const int nch = sv::sampler_chunks(c.vocab);
-  L.n_qc = sv::attn_row_blocks(c.n_heads, c.n_kv_heads, c.head_dim, m);
-  L.n_split = sv::attn_num_splits(B, c.n_heads, c.n_kv_heads, c.head_dim, m, max_ctx);
-  L.n_ctr = static_cast<int>(sv::attn_counters(B, c.n_heads, c.n_kv_heads, c.head_dim, m));
+  const bool bf16 = c.dtype == SPEC_BF16;
+  L.n_qc = sv::attn_row_blocks(bf16, B, c.n_heads, c.n_kv_heads, c.head_dim, m);
+  L.n_split = sv::attn_num_splits(bf16, B, c.n_heads, c.n_kv_heads, c.head_dim, m, max_ctx);
+  L.n_ctr = static_cast<int>(sv::attn_counters(bf16, B, c.n_heads, c.n_kv_heads, c.head_dim, m));
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;

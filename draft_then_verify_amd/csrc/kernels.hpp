@@ -114,9 +114,11 @@ struct AttnArgs {
 // hd 64/128; G = H/Hkv divides the workgroup's waves (16 for hd 128, 8 for
 // hd 64) or is a multiple of them
 bool attn_supported(int H, int Hkv, int hd);
-int attn_row_blocks(int H, int Hkv, int hd, int m);  // n_qc
-int attn_num_splits(int B, int H, int Hkv, int hd, int m, int max_ctx);
-size_t attn_counters(int B, int H, int Hkv, int hd, int m);  // tickets the launch uses
+// The split path's plan (row blocks n_qc, context splits n_split, tickets);
+// bf16 passes of head_dim 64 take the matrix-core kernel, whose plan differs.
+int attn_row_blocks(bool bf16, int B, int H, int Hkv, int hd, int m);  // n_qc
+int attn_num_splits(bool bf16, int B, int H, int Hkv, int hd, int m, int max_ctx);
+size_t attn_counters(bool bf16, int B, int H, int Hkv, int hd, int m);  // tickets the launch uses
 hipError_t launch_attention(bool bf16, int hd, const AttnArgs& a, int B, hipStream_t s);
 // True when launch_attention takes the short-pass kernel (m <= 8 rows,
 // max_ctx <= 2048, a K/V row of at most 256 bytes): one workgroup per

@@ -149,6 +149,22 @@ def test_long_context_split_kernel():
     assert np.abs(got - ref).max() < 1e-4
 
 
+def test_matrix_core_attention_long_context_splits():
+    """bf16 K/V of head_dim 64 past 2048 cached positions: the matrix-core
+    attention kernel with many context splits merged by the last workgroup."""
+    shape = Shape("ctx3", 256, 1, 4, 1, 64, 512, 300, "bf16")
+    got, ref, *_ = _run(shape, B=1, P=2100, m=5, seed=115, max_ctx=2120)
+    assert np.abs(got - ref).max() < _tol(shape)
+
+
+def test_matrix_core_attention_many_rows():
+    """11 rows per sequence (a gamma = 10 pass) with 2 query heads per KV head
+    at B = 64, ragged contexts: 22-row workgroups on the matrix-core kernel."""
+    shape = Shape("h64g2", 512, 1, 8, 4, 64, 512, 400, "bf16")
+    got, ref, *_ = _run(shape, B=64, P=40, m=11, seed=116, lens_back=[i % 13 for i in range(64)])
+    assert np.abs(got - ref).max() < _tol(shape)
+
+
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("P", [520, 1030])
 def test_8b_shape_two_layers_long_context(P):

@@ -110,7 +110,8 @@ __device__ __forceinline__ void gemm_epilogue(const GemvArgs& a, f32x4_t (&acc)[
     const int h0 = wn & ~1;  // the statistics tile's first half
     auto vals = [&](int i, int r, float (&v)[4]) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = (n0 + j * 16 < N) ? __fdiv_rn(acc[i][j][r], T) : -INFINITY;
+      for (int j = 0; j < 4; ++j)  // x / 1 rounds to x: no division at T = 1
+        v[j] = (n0 + j * 16 < N) ? (T == 1.f ? acc[i][j][r] : __fdiv_rn(acc[i][j][r], T)) : -INFINITY;
     };
 #pragma unroll
     for (int i = 0; i < MI; ++i)

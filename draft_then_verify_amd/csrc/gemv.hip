@@ -22,14 +22,16 @@ using gemv::kMaxLds;
 
 int gemv_ksplit(bool bf16, int M, int N, int K) {
   if (bf16 && M > 8 && K % mfma::KB == 0) {
-    // matrix-core path: enough workgroups (about 2 per CU) from row blocks x
-    // weight tiles x K slices
+    // matrix-core path: enough workgroups (one per CU) from row blocks x
+    // weight tiles x K slices; each slice more is a partial of rows x N
+    // float32 that the residual-sum kernel reads back (two per CU: B = 256
+    // verify step 1.131 -> 1.165 ms)
     const int tiles = ((M + mfma::BM - 1) / mfma::BM) * ((N + mfma::BN - 1) / mfma::BN);
     int best = 1;
     for (int ks = 1; ks <= 8; ++ks) {
       if (K % (ks * mfma::KB)) continue;
       best = ks;
-      if (tiles * ks >= 2 * kCUs) break;
+      if (tiles * ks >= kCUs) break;
     }
     return best;
   }

@@ -172,7 +172,7 @@ __global__ __launch_bounds__(kThreads) void row_partials_kernel(const float* __r
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int idx = c0 + h * 64 + j * 16;
-        v[h][j] = idx < V ? __fdiv_rn(l[idx], T) : -INFINITY;
+        v[h][j] = idx < V ? (T == 1.f ? l[idx] : __fdiv_rn(l[idx], T)) : -INFINITY;  // x / 1 rounds to x
         mx = fmaxf(mx, v[h][j]);
       }
     mx = lmstat::group16_max(mx);

@@ -187,26 +187,49 @@ __global__ __launch_bounds__(kThreads) void row_partials_kernel(const float* __r
   }
 }
 
-// Chunk pairs from the LM head's tile statistics (EPI_LMSTAT), one thread
-// per (row, chunk): (M, Z) merged in tile order at T > 0, (max, lowest
-// argmax) at T = 0.
+// Chunk pairs from the LM head's tile statistics (EPI_LMSTAT): 32 lanes per
+// (row, chunk), lane k holding tile k.  At T = 0 the (max, lowest argmax)
+// pair is merged across the lanes (any order gives the same pair).  At T > 0
+// the maximum is taken across the lanes (exact in any order), each lane
+// weighs its tile by exp(M_t - M), and the chunk's weight sum Z_t x weight
+// runs in tile order with the fused multiply-adds of lmstat::merge_tiles, so
+// the pair is bitwise the one the materialised path builds.
 __global__ __launch_bounds__(kThreads) void tile_merge_kernel(int64_t rows, int V, int nch, int nts, bool greedy,
                                                               const float2* __restrict__ tpart,
                                                               float2* __restrict__ part) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  if (i >= rows * nch) return;
-  const int64_t row = i / nch;
-  const int c = static_cast<int>(i - row * nch);
-  const float2* t = tpart + row * nts + c * lmstat::kTilesPerChunk;
-  const int n = min(lmstat::kTilesPerChunk, nts - c * lmstat::kTilesPerChunk);
+  constexpr int kGroup = lmstat::kTilesPerChunk;  // lanes per (row, chunk)
+  static_assert(kGroup == 32 && kThreads % kGroup == 0, "two chunks per wave");
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * (kThreads / kGroup) + threadIdx.x / kGroup;
+  const int k = threadIdx.x % kGroup;
+  const bool live = i < rows * nch;  // every lane stays for the shuffles
+  const int64_t row = live ? i / nch : 0;
+  const int c = live ? static_cast<int>(i - row * nch) : 0;
+  const int n = min(kGroup, nts - c * kGroup);
+  const bool mine = live && k < n;
+  const float2 t = mine ? tpart[row * nts + c * kGroup + k] : make_float2(-INFINITY, 0.f);
   if (greedy) {
-    float m = -INFINITY;
-    int ix = V;
-    for (int k = 0; k < n; ++k) lmstat::argmax_merge(m, ix, t[k].x, __float_as_int(t[k].y));
-    part[i] = make_float2(m, __int_as_float(ix));
-  } else {
-    part[i] = lmstat::merge_tiles(t, n);
+    float m = t.x;
+    int ix = mine ? __float_as_int(t.y) : V;
+#pragma unroll
+    for (int off = kGroup / 2; off > 0; off >>= 1) {
+      const float m2 = __shfl_xor(m, off, kWave);
+      const int i2 = __shfl_xor(ix, off, kWave);
+      lmstat::argmax_merge(m, ix, m2, i2);
+    }
+    if (live && k == 0) part[i] = make_float2(m, __int_as_float(ix));
+    return;
   }
+  float M = t.x;
+#pragma unroll
+  for (int off = kGroup / 2; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, kWave));
+  const float w = t.y != 0.f ? expf(__fsub_rn(t.x, M)) : 0.f;
+  float Z = 0.f;
+#pragma unroll
+  for (int j = 0; j < kGroup; ++j) {
+    const float y = __shfl(t.y, j, kGroup), wj = __shfl(w, j, kGroup);
+    if (y != 0.f) Z = fmaf(y, wj, Z);  // lanes past n hold y = 0
+  }
+  if (live && k == 0) part[i] = make_float2(M, Z);
 }
 
 __global__ __launch_bounds__(kThreads) void softmax_write_kernel(const float* __restrict__ logits, int V, float T,
@@ -519,8 +542,9 @@ hipError_t launch_tile_merge(int64_t rows, int vocab, const float2* tpart, bool 
   const int nch = sampler_chunks(vocab);
   const int nts = (vocab + lmstat::kTile - 1) / lmstat::kTile;
   const int64_t n = rows * nch;
-  hipLaunchKernelGGL(tile_merge_kernel, dim3(static_cast<unsigned>((n + kThreads - 1) / kThreads)), dim3(kThreads), 0,
-                     s, rows, vocab, nch, nts, greedy, tpart, part);
+  constexpr int per = kThreads / lmstat::kTilesPerChunk;  // (row, chunk) pairs per workgroup
+  hipLaunchKernelGGL(tile_merge_kernel, dim3(static_cast<unsigned>((n + per - 1) / per)), dim3(kThreads), 0, s, rows,
+                     vocab, nch, nts, greedy, tpart, part);
   return hipGetLastError();
 }
 

@@ -165,6 +165,16 @@ def test_matrix_core_attention_many_rows():
     assert np.abs(got - ref).max() < _tol(shape)
 
 
+def test_matrix_core_attention_eight_heads_per_kv_head():
+    """8 query heads per KV head at B = 64 on the matrix-core kernel, ragged
+    contexts: the 11-row verify pass in 16-row workgroups (2 rows x 8 heads,
+    6 row blocks), the prefill's 29-row pass in 32-row workgroups (8 row
+    blocks of 4 rows)."""
+    shape = Shape("h64g8", 512, 1, 8, 1, 64, 512, 300, "bf16")
+    got, ref, *_ = _run(shape, B=64, P=30, m=11, seed=117, lens_back=[i % 5 for i in range(64)])
+    assert np.abs(got - ref).max() < _tol(shape)
+
+
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("P", [520, 1030])
 def test_8b_shape_two_layers_long_context(P):

@@ -189,9 +189,83 @@ __device__ __forceinline__ void gemm_epilogue(const GemvArgs& a, f32x4_t (&acc)[
       }
     return;
   }
+  if constexpr (EPI == EPI_QKV) {
+    // RoPE on query and key rows, then the stores: q rows (float32), and K/V
+    // rows into the cache at len[b] + i.  Every (cos, sin) pair and cache
+    // position this lane needs is loaded before the first store, so their
+    // latencies overlap instead of queueing behind the stores.
+    static_assert(BNT == 128, "QKV tiles are 128 rows");
+    const int H = a.H, Hkv = a.Hkv, hd = a.hd, half = hd / 2;
+    const bool two = hd == 64;  // two heads per workgroup
+    const int hh = two ? 2 * nt + wn : nt;
+    if (hh >= H + 2 * Hkv) return;  // an odd head count's empty half
+    const bool rope = hh < H + Hkv;
+    float2 cs[MI][4][2];
+    int pos[MI][4];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int rg = a.row0 + min(m0 + wm * (BMT / 2) + i * 16 + rb + r, M - 1);
+        const int b = rg / a.m_per_seq, ii = rg - b * a.m_per_seq;
+        pos[i][r] = hh >= H ? a.len[b] + ii : 0;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int d = two ? j * 16 + col : wn * 32 + j * 16 + col;  // 0 .. half-1; its pair is d + half
+          cs[i][r][j] = rope ? a.cs[static_cast<size_t>(rg) * half + d] : make_float2(0.f, 0.f);
+        }
+      }
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + wm * (BMT / 2) + i * 16 + rb + r;
+        if (m >= M) continue;
+        const int rg = a.row0 + m;
+        const int b = rg / a.m_per_seq;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int d = two ? j * 16 + col : wn * 32 + j * 16 + col;
+          const float x0 = acc[i][j][r], y0 = acc[i][j + 2][r];
+          if (rope) {
+            const float2 c = cs[i][r][j];
+            const float r0 = x0 * c.x - y0 * c.y, s0 = y0 * c.x + x0 * c.y;
+            if (hh < H) {
+              float* qr = a.q + static_cast<size_t>(rg) * (H * hd) + hh * hd;
+              qr[d] = r0;
+              qr[d + half] = s0;
+            } else if (pos[i][r] >= 0 && pos[i][r] < a.max_ctx) {
+              uint16_t* dst = static_cast<uint16_t*>(a.kc) +
+                              (((static_cast<size_t>(a.layer) * a.kvB + b) * Hkv + (hh - H)) * a.max_ctx + pos[i][r]) * hd;
+              dst[d] = f2bf(r0);
+              dst[d + half] = f2bf(s0);
+            }
+          } else if (pos[i][r] >= 0 && pos[i][r] < a.max_ctx) {
+            uint16_t* dst = static_cast<uint16_t*>(a.vc) +
+                            (((static_cast<size_t>(a.layer) * a.kvB + b) * Hkv + (hh - H - Hkv)) * a.max_ctx + pos[i][r]) * hd;
+            dst[d] = f2bf(x0);
+            dst[d + half] = f2bf(y0);
+          }
+        }
+      }
+    return;
+  }
   float* y = a.y ? a.y + static_cast<size_t>(slice) * a.ysplit : nullptr;
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
+    // residual add: the 16-row tile's values added to, loaded before its
+    // first store
+    float yv[4][4];
+    if constexpr (EPI == EPI_RESID) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int m = min(m0 + wm * (BMT / 2) + i * 16 + rb + r, M - 1);
+          const int n = min(nt * BNT + wn * 64 + j * 16 + col, a.N - 1);
+          yv[r][j] = y[static_cast<size_t>(m) * a.ldy + n];
+        }
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = m0 + wm * (BMT / 2) + i * 16 + rb + r;
@@ -205,52 +279,13 @@ __device__ __forceinline__ void gemm_epilogue(const GemvArgs& a, f32x4_t (&acc)[
             static_cast<uint16_t*>(a.z)[static_cast<size_t>(m) * a.ldz + n] = f2bf(g / (1.f + expf(-g)) * u);
           }
         }
-      } else if constexpr (EPI == EPI_QKV) {
-        static_assert(BNT == 128, "QKV tiles are 128 rows");
-        const int H = a.H, Hkv = a.Hkv, hd = a.hd, half = hd / 2;
-        const bool two = hd == 64;  // two heads per workgroup
-        const int hh = two ? 2 * nt + wn : nt;
-        if (hh >= H + 2 * Hkv) continue;  // an odd head count's empty half
-        const int rg = a.row0 + m;
-        const int b = rg / a.m_per_seq, ii = rg - b * a.m_per_seq;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          // 0 .. half-1; its pair is d + half
-          const int d = two ? j * 16 + col : wn * 32 + j * 16 + col;
-          const float x0 = acc[i][j][r], y0 = acc[i][j + 2][r];
-          if (hh < H + Hkv) {
-            const float2 c = a.cs[static_cast<size_t>(rg) * half + d];
-            const float r0 = x0 * c.x - y0 * c.y, s0 = y0 * c.x + x0 * c.y;
-            if (hh < H) {
-              float* qr = a.q + static_cast<size_t>(rg) * (H * hd) + hh * hd;
-              qr[d] = r0;
-              qr[d + half] = s0;
-            } else {
-              const int pos = a.len[b] + ii;
-              if (pos >= 0 && pos < a.max_ctx) {
-                uint16_t* dst = static_cast<uint16_t*>(a.kc) +
-                                (((static_cast<size_t>(a.layer) * a.kvB + b) * Hkv + (hh - H)) * a.max_ctx + pos) * hd;
-                dst[d] = f2bf(r0);
-                dst[d + half] = f2bf(s0);
-              }
-            }
-          } else {
-            const int pos = a.len[b] + ii;
-            if (pos >= 0 && pos < a.max_ctx) {
-              uint16_t* dst = static_cast<uint16_t*>(a.vc) +
-                              (((static_cast<size_t>(a.layer) * a.kvB + b) * Hkv + (hh - H - Hkv)) * a.max_ctx + pos) * hd;
-              dst[d] = f2bf(x0);
-              dst[d + half] = f2bf(y0);
-            }
-          }
-        }
       } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int n = nt * BNT + wn * 64 + j * 16 + col;
           if (n < a.N) {
             float* dst = y + static_cast<size_t>(m) * a.ldy + n;
-            if constexpr (EPI == EPI_RESID) *dst += acc[i][j][r];
+            if constexpr (EPI == EPI_RESID) *dst = yv[r][j] + acc[i][j][r];
             else *dst = acc[i][j][r];
           }
         }

@@ -108,6 +108,19 @@ __device__ __forceinline__ void gemm_epilogue(const GemvArgs& a, f32x4_t (&acc)[
     const int N = a.N, nts = (a.N + lmstat::kTile - 1) / lmstat::kTile;
     const int n0 = nt * BNT + wn * 64 + col;
     const int h0 = wn & ~1;  // the statistics tile's first half
+    // the drafted token each of this lane's rows scores (-1: none), loaded
+    // before the first store
+    const int mps = a.m_per_seq;
+    int xdr[MI][4];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + wm * (BMT / 2) + i * 16 + rb + r;
+        const int rg = a.row0 + min(m, M - 1);
+        const int b = rg / mps, ii = rg - b * mps;
+        xdr[i][r] = (a.lx && m < M && ii < mps - 1) ? a.draft[b * (mps - 1) + ii] : -1;
+      }
     auto vals = [&](int i, int r, float (&v)[4]) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)  // x / 1 rounds to x: no division at T = 1
@@ -172,17 +185,13 @@ __device__ __forceinline__ void gemm_epilogue(const GemvArgs& a, f32x4_t (&acc)[
         }
     }
     // the logit at the drafted token of each row that scores one
-    const int mps = a.m_per_seq;
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = m0 + wm * (BMT / 2) + i * 16 + rb + r;
-        if (m >= M || !a.lx) continue;
-        const int rg = a.row0 + m;
-        const int b = rg / mps, ii = rg - b * mps;
-        if (ii >= mps - 1) continue;
-        const int x = a.draft[b * (mps - 1) + ii];
+        const int x = xdr[i][r];
+        if (x < 0) continue;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           if (n0 + j * 16 == x && x < N) a.lx[m] = acc[i][j][r];

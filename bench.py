@@ -335,8 +335,10 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
 def mfma_linears(M: int = 1280, reps: int = 20) -> list:
     """The matrix-core linear at the second workload's weight shapes with
     M = 1280 rows (a B = 256, gamma = 4 verify pass): TFLOP/s per launch from
-    HIP events on the launching stream, against the dense bf16 peak.  Each
-    shape cycles through 8 weight copies so the weights come from HBM."""
+    HIP events around a graph replay of `reps` launches (so the host's
+    per-call cost does not show in launches shorter than it), against the
+    dense bf16 peak.  Each shape cycles through 8 weight copies so the weights
+    come from HBM."""
     import torch
 
     from draft_then_verify_amd import binding as bd
@@ -362,13 +364,19 @@ def mfma_linears(M: int = 1280, reps: int = 20) -> list:
         for W in Ws:
             go(W)
         torch.cuda.synchronize()
+        cg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(cg):
+            for r in range(reps):
+                go(Ws[r % len(Ws)])
+        cg.replay()
+        torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        for r in range(reps):
-            go(Ws[r % len(Ws)])
+        cg.replay()
         e1.record()
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / reps
+        del cg
         tflops = 2.0 * M * rows * K / (us * 1e-6) / 1e12
         out.append({"linear": name, "M": M, "N": rows, "K": K, "us_per_launch": round(us, 2),
                     "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

@@ -25,8 +25,10 @@ Qwen3-0.6B-shaped draft, B = 1, gamma = 4, a 256-token prompt, 256 new tokens.
   256} on the second workload's target and 2-layer drafter (gamma = 4,
   256-token prompts).
 * ``batch_verify_step``: the verify step alone on the same target for B in
-  {1, 8, 64, 256} (5 to 1280 rows): ms, verified positions/s and algorithmic
-  GB/s.  ``--verify-batch B`` runs only one of them (for profiles).
+  {1, 8, 64, 256} (5 to 1280 rows): ms, verified positions/s, effective GB/s
+  (the target's weights fit the last-level cache) and algorithmic TFLOP/s
+  against the bf16 peak.  ``--verify-batch B`` runs only one of them (for
+  profiles).
 * ``division_check_gamma1``: the gamma = 1 division of the M1 Max page,
   predicted (1 + p) T_decode / (T_verify + T_draft) against the measured
   speculative/plain ratio, on the same shapes.
@@ -258,10 +260,22 @@ def batch_sweep(n_new: int, batches=(1, 8, 64, 256), P: int = 256, g: int = 4) -
     return rows
 
 
+def verify_pass_flops(shape, B: int, m: int, ctx_mean: float) -> float:
+    """Algorithmic FLOPs of one verify pass: 2 per linear weight and row, and
+    4 per query head, head dimension, row and key attended (scores and P.V),
+    each row attending ctx_mean keys on average."""
+    d, L, F, V = shape.d_model, shape.n_layers, shape.d_ff, shape.vocab
+    hq = shape.n_heads * shape.head_dim
+    params = L * (shape.qkv_rows * d + d * hq + 2 * F * d + d * F) + V * d
+    M = B * m
+    return 2.0 * params * M + 4.0 * shape.n_heads * shape.head_dim * M * ctx_mean * L
+
+
 def batch_verify_steps(batches=(1, 8, 64, 256), P: int = 256, g: int = 4, steps: int = 20) -> list:
     """The verify step alone (spec_decode_step, graph-replayed) of the second
-    workload's target at each batch size: ms per step, verified positions/s
-    and algorithmic GB/s."""
+    workload's target at each batch size: ms per step, verified positions/s,
+    algorithmic GB/s and TFLOP/s.  The target's 246 MB of weights fit the
+    256 MB last-level cache, so the GB/s are effective rates, not HBM's."""
     import torch
 
     from draft_then_verify_amd import binding as bd
@@ -277,11 +291,13 @@ def batch_verify_steps(batches=(1, 8, 64, 256), P: int = 256, g: int = 4, steps:
         # statistics instead of the logits (the library's rule for bf16)
         fused = B * (g + 1) > sh.d_model // 4
         nbytes = verify_pass_bytes(sh, B, g + 1, int(round(B * ctx_mean)), logits=not fused)
+        tflops = verify_pass_flops(sh, B, g + 1, ctx_mean) / (ms / 1e3) / 1e12
         rows.append({"B": B, "rows": B * (g + 1), "ms": round(ms, 4),
                      "verified_positions_per_s": round(B * (g + 1) / (ms / 1e3), 1),
-                     "GB_s": round(nbytes / (ms / 1e3) / 1e9, 1), "context": note})
+                     "GB_s_effective": round(nbytes / (ms / 1e3) / 1e9, 1), "TFLOP_s": round(tflops, 1),
+                     "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4), "context": note})
         log(f"verify step B={B} ({B * (g + 1)} rows): {ms:.4f} ms, {B * (g + 1) / (ms / 1e3):.0f} verified "
-            f"positions/s, {nbytes / (ms / 1e3) / 1e9:.0f} GB/s algorithmic, context {note}")
+            f"positions/s, {nbytes / (ms / 1e3) / 1e9:.0f} GB/s effective, {tflops:.0f} TFLOP/s, context {note}")
         torch.cuda.empty_cache()
     return rows
 

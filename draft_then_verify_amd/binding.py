@@ -22,6 +22,7 @@ STATUS = {0: "SPEC_OK", -1: "SPEC_EINVAL", -2: "SPEC_ENOMEM", -3: "SPEC_EHIP", -
 # Every symbol the C header declares.
 EXPORTS = ("spec_model_create", "spec_model_destroy", "spec_workspace_bytes", "spec_sampler_workspace_bytes",
            "spec_verify_forward", "spec_verify_forward_trace", "spec_softmax_pq", "spec_reject_sample",
+           "spec_draft_sample",
            "spec_decode_step", "spec_decode_step_static", "spec_linear",
            "spec_kv_set_len", "spec_last_error", "spec_commit_round", "spec_ngram_propose")
 
@@ -80,6 +81,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                             vp, sz, vp]),
         "spec_softmax_pq": (i32, [vp, i64, i32, f32, vp, vp, sz, vp]),
         "spec_reject_sample": (i32, [i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "spec_draft_sample": (i32, [vp, i64, i32, i32, f32, vp, vp, i64, vp, i32, vp, sz, vp]),
         "spec_decode_step": (i32, [vp, ctypes.POINTER(spec_kv), i32, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                    sz, vp]),
         "spec_decode_step_static": (i32, [vp, ctypes.POINTER(spec_kv), i32, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp,
@@ -226,6 +228,27 @@ def spec_reject_sample(B: int, gamma: int, vocab: int, p, q, draft, n_draft, u_a
     _check(load_library().spec_reject_sample(B, gamma, vocab, _ptr(p), _ptr(q), _ptr(draft), _ptr(n_draft),
                                              _ptr(u_acc), _ptr(u_res), _ptr(n_accepted), _ptr(emitted), _ptr(ws),
                                              _nbytes(ws), _stream(stream)))
+
+
+def _strided_ptr(t, off: int, rows: int, ld: int, width: int) -> int:
+    """Address of element `off` of a contiguous tensor whose rows
+    off + r * ld .. + width - 1 (r < rows) the call will touch."""
+    if not isinstance(t, torch.Tensor) or not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    if off < 0 or ld < width or off + (rows - 1) * ld + width > t.numel():
+        raise ValueError(f"strided rows (offset {off}, {rows} x {ld}, width {width}) outside {t.numel()} elements")
+    return t.data_ptr() + off * t.element_size()
+
+
+def spec_draft_sample(logits, ld_logits: int, B: int, vocab: int, temperature: float, u, q, ld_q: int, tokens,
+                      ld_tokens: int, ws, stream=None, logits_off: int = 0, q_off: int = 0, tokens_off: int = 0):
+    """The drafter's sampling step over B rows strided through larger buffers:
+    row b of the logits at logits_off + b * ld_logits, of q at
+    q_off + b * ld_q, its token at tokens_off + b * ld_tokens (elements)."""
+    _check(load_library().spec_draft_sample(_strided_ptr(logits, logits_off, B, ld_logits, vocab), ld_logits, B, vocab,
+                                            temperature, _ptr(u), _strided_ptr(q, q_off, B, ld_q, vocab), ld_q,
+                                            _strided_ptr(tokens, tokens_off, B, ld_tokens, 1), ld_tokens, _ptr(ws),
+                                            _nbytes(ws), _stream(stream)))
 
 
 def spec_decode_step(target: SpecModel, kv: KVCache, B: int, gamma: int, temperature: float, last_tok, draft, n_draft,

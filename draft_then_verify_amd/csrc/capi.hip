@@ -515,6 +515,45 @@ SPEC_API spec_status spec_reject_sample(int32_t B, int32_t gamma, int32_t vocab,
   return check_end(flag, stream, "spec_reject_sample");
 }
 
+SPEC_API spec_status spec_draft_sample(const float* logits, int64_t ld_logits, int32_t B, int32_t vocab,
+                                       float temperature, const float* u, float* q, int64_t ld_q, int32_t* tokens,
+                                       int32_t ld_tokens, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!logits || !q || !tokens) return fail(SPEC_EINVAL, "NULL logits/q/tokens");
+  if (B <= 0 || B > 65535) return fail(SPEC_EINVAL, "B=%d (1..65535)", B);
+  if (vocab <= 0 || vocab > 64 * 4096) return fail(SPEC_EINVAL, "vocab=%d (1..262144)", vocab);
+  if (ld_logits < vocab || ld_q < vocab || ld_tokens < 1)
+    return fail(SPEC_EINVAL, "row strides %lld/%lld/%d below vocab/vocab/1", (long long)ld_logits, (long long)ld_q,
+                ld_tokens);
+  if (!valid_temperature(temperature)) return fail(SPEC_EINVAL, "temperature must be finite and >= 0");
+  if (temperature > 0.f && !u) return fail(SPEC_EINVAL, "u is NULL");
+  const size_t need = spec_sampler_workspace_bytes(B, B, vocab);
+  if (!ws || ws_bytes < need) return fail(SPEC_ENOMEM, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  const int nch = sv::sampler_chunks(vocab);
+  float2* part = static_cast<float2*>(ws);
+  auto* csum = reinterpret_cast<unsigned long long*>(static_cast<char*>(ws) + up(static_cast<size_t>(B) * nch * 8));
+  if (temperature == 0.f) {
+    HIP_TRY(sv::launch_row_argmax(logits, B, vocab, part, stream, ld_logits));
+    HIP_TRY(sv::launch_onehot_write(B, vocab, part, q, stream, ld_q));
+    HIP_TRY(sv::launch_greedy(B, 0, vocab, part, nullptr, nullptr, nullptr, tokens, nullptr, stream, ld_tokens));
+  } else {
+    HIP_TRY(sv::launch_row_partials(logits, B, vocab, temperature, part, stream, ld_logits));
+    HIP_TRY(sv::launch_softmax_write(logits, B, vocab, temperature, part, q, stream, ld_logits, ld_q));
+    sv::RejectRows rr;
+    rr.logits = logits;
+    rr.part = part;
+    rr.temperature = temperature;
+    rr.ld = ld_logits;
+    HIP_TRY(sv::launch_reject(rr, B, 0, vocab, nullptr, nullptr, nullptr, nullptr, u, nullptr, tokens, nullptr, csum,
+                              stream, ld_tokens));
+  }
+  if (!check_mode()) return SPEC_OK;
+  int* flag = nullptr;
+  spec_status st;
+  if ((st = check_begin(&flag, stream)) != SPEC_OK) return st;
+  for (int b = 0; b < B; ++b) HIP_TRY(sv::launch_check_finite(logits + static_cast<int64_t>(b) * ld_logits, vocab, flag, stream));
+  return check_end(flag, stream, "spec_draft_sample");
+}
+
 SPEC_API spec_status spec_decode_step(const spec_model* target, const spec_kv* kv, int32_t B, int32_t gamma,
                                       float temperature, const int32_t* last_tok, const int32_t* draft,
                                       const int32_t* n_draft, const float* q, const float* u_acc, const float* u_res,

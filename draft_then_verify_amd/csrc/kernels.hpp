@@ -156,19 +156,22 @@ hipError_t launch_check_finite(const float* v, int64_t n, int* flag, hipStream_t
 // ---- sampler ----------------------------------------------------------------------
 int sampler_chunks(int vocab);
 // part[row][c] = (max, sum exp(l/T - max)) over chunk c of each row.
+// ld: floats between logit rows (0: vocab).
 hipError_t launch_row_partials(const float* logits, int64_t rows, int vocab, float temperature, float2* part,
-                               hipStream_t s);
+                               hipStream_t s, int64_t ld = 0);
 // probs = exp(l/T - m) / Z with the row statistics combined from part.
 hipError_t launch_softmax_write(const float* logits, int64_t rows, int vocab, float temperature,
-                                const float2* part, float* probs, hipStream_t s);
+                                const float2* part, float* probs, hipStream_t s, int64_t ld_in = 0, int64_t ld_out = 0);
 // Temperature 0: part[row][c] = (chunk max, its lowest index as int bits);
 // one-hot rows at the row argmax; greedy accept (x_i == argmax_i) with the
 // argmax of row n emitted after the accepted drafts.
-hipError_t launch_row_argmax(const float* logits, int64_t rows, int vocab, float2* part, hipStream_t s);
-hipError_t launch_onehot_write(int64_t rows, int vocab, const float2* part, float* probs, hipStream_t s);
+hipError_t launch_row_argmax(const float* logits, int64_t rows, int vocab, float2* part, hipStream_t s,
+                             int64_t ld = 0);
+hipError_t launch_onehot_write(int64_t rows, int vocab, const float2* part, float* probs, hipStream_t s,
+                               int64_t ld_out = 0);
 hipError_t launch_greedy(int B, int gamma, int vocab, const float2* part, const int32_t* draft,
                          const int32_t* n_draft, int32_t* n_accepted, int32_t* emitted, int32_t* len_commit,
-                         hipStream_t s);
+                         hipStream_t s, int ld_em = 0);
 // Where the sampler's rows come from: materialised probabilities p, or
 // logits + chunk statistics part; for passes whose logits were not written,
 // lx (the logit at each row's drafted token) and sel ([B][vocab], the
@@ -180,11 +183,13 @@ struct RejectRows {
   float temperature = 1.f;
   const float* lx = nullptr;
   const float* sel = nullptr;
+  int64_t ld = 0;  // floats between rows of p or logits (0: vocab)
 };
 // Accept / resample / bonus.  csum is [B][chunks] scratch (2 x uint64 each).
 hipError_t launch_reject(const RejectRows& rr, int B, int gamma, int vocab, const float* q, const int32_t* draft,
                          const int32_t* n_draft, const float* u_acc, const float* u_res, int32_t* n_accepted,
-                         int32_t* emitted, int32_t* len_commit, unsigned long long* csum, hipStream_t s);
+                         int32_t* emitted, int32_t* len_commit, unsigned long long* csum, hipStream_t s,
+                         int ld_em = 0);  // ints between sequences' emitted rows (0: gamma + 1)
 // Chunk statistics part [rows][chunks] from the LM head's tile statistics
 // tpart [rows][ceil(vocab/128)] (EPI_LMSTAT).
 hipError_t launch_tile_merge(int64_t rows, int vocab, const float2* tpart, bool greedy, float2* part, hipStream_t s);

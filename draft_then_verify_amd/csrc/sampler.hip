@@ -70,6 +70,7 @@ struct RowSrc {
   const float* lx;
   const float* sel;
   int m;
+  int64_t ld = 0;  // floats between rows of p or logits (0: V)
   // called by a whole wave
   __device__ __forceinline__ float2 stats(int64_t row) const {
     return p ? make_float2(0.f, 1.f) : wave_stats(part + row * nch, nch);
@@ -79,8 +80,9 @@ struct RowSrc {
   }
   // p(v) of the row a sequence samples from (the only full row read)
   __device__ __forceinline__ float prob(int64_t row, int v, float2 st) const {
-    if (p) return p[row * V + v];
-    const float* l = sel ? sel + (row / m) * V : logits + row * V;
+    const int64_t rs = ld > 0 ? ld : V;
+    if (p) return p[row * rs + v];
+    const float* l = sel ? sel + (row / m) * V : logits + row * rs;
     return from_logit(l[v], st);
   }
   // p(x) at the drafted token x the row scores
@@ -155,12 +157,12 @@ __device__ __forceinline__ float sample_mass(float pv, bool use_p, const float* 
 // (max, sum exp) of chunk c of a row from materialised logits: 16-lane
 // groups take the chunk's 32 tiles (two each) in lmstat.hpp's order, and
 // thread 0 merges the tiles in order.
-__global__ __launch_bounds__(kThreads) void row_partials_kernel(const float* __restrict__ logits, int V, float T,
-                                                                int nch, float2* __restrict__ part) {
+__global__ __launch_bounds__(kThreads) void row_partials_kernel(const float* __restrict__ logits, int64_t ld, int V,
+                                                                float T, int nch, float2* __restrict__ part) {
   __shared__ float2 tst[lmstat::kTilesPerChunk];
   const int64_t row = blockIdx.y;
   const int c = blockIdx.x;
-  const float* l = logits + row * V;
+  const float* l = logits + row * ld;
   const int col = threadIdx.x & 15, grp = threadIdx.x >> 4;
   constexpr int kGroups = kThreads / 16;
   for (int t = grp; t < lmstat::kTilesPerChunk; t += kGroups) {
@@ -232,9 +234,10 @@ __global__ __launch_bounds__(kThreads) void tile_merge_kernel(int64_t rows, int 
   if (live && k == 0) part[i] = make_float2(M, Z);
 }
 
-__global__ __launch_bounds__(kThreads) void softmax_write_kernel(const float* __restrict__ logits, int V, float T,
-                                                                 int nch, const float2* __restrict__ part,
-                                                                 float* __restrict__ probs) {
+__global__ __launch_bounds__(kThreads) void softmax_write_kernel(const float* __restrict__ logits, int64_t ld_in,
+                                                                 int V, float T, int nch,
+                                                                 const float2* __restrict__ part,
+                                                                 float* __restrict__ probs, int64_t ld_out) {
   __shared__ float2 st_sh;
   const int64_t row = blockIdx.y;
   const int c = blockIdx.x;
@@ -244,11 +247,11 @@ __global__ __launch_bounds__(kThreads) void softmax_write_kernel(const float* __
   }
   __syncthreads();
   const float2 st = st_sh;
-  RowSrc src{nullptr, logits, part, T, nch, V};
+  RowSrc src{nullptr, logits, part, T, nch, V, nullptr, nullptr, 1, ld_in};
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
     const int v = c * kChunk + e * kThreads + threadIdx.x;
-    if (v < V) probs[row * V + v] = src.prob(row, v, st);
+    if (v < V) probs[row * ld_out + v] = src.prob(row, v, st);
   }
 }
 
@@ -264,6 +267,7 @@ struct RejectArgs {
   int32_t* emitted;
   int32_t* len_commit;
   unsigned long long* csum;  // [B][nch][2]: residual sum, p sum
+  int ld_em;                 // ints between sequences' emitted rows (0: gamma + 1)
 };
 
 __global__ __launch_bounds__(kThreads) void reject_chunks_kernel(RejectArgs a) {
@@ -371,9 +375,10 @@ __global__ __launch_bounds__(kThreads) void reject_final_kernel(RejectArgs a) {
   if (threadIdx.x == 0) {
     int tok = tok_sh;
     if (tok < 0) tok = 0;  // unreachable when S > 0 and k < 2^24
-    a.n_accepted[b] = n;
+    if (a.n_accepted) a.n_accepted[b] = n;
+    const int lde = a.ld_em > 0 ? a.ld_em : a.gamma + 1;
     for (int j = 0; j <= a.gamma; ++j)
-      a.emitted[b * (a.gamma + 1) + j] = j < n ? a.draft[b * a.gamma + j] : (j == n ? tok : -1);
+      a.emitted[b * lde + j] = j < n ? a.draft[b * a.gamma + j] : (j == n ? tok : -1);
     if (a.len_commit) a.len_commit[b] += n + 1;
   }
 }
@@ -423,13 +428,13 @@ __device__ __forceinline__ int wave_row_argmax(const float2* pr, int nch, int V)
 }
 
 // part[row][c] = (max of chunk c, its lowest index as int bits).
-__global__ __launch_bounds__(kThreads) void row_argmax_kernel(const float* __restrict__ logits, int V, int nch,
-                                                              float2* __restrict__ part) {
+__global__ __launch_bounds__(kThreads) void row_argmax_kernel(const float* __restrict__ logits, int64_t ld, int V,
+                                                              int nch, float2* __restrict__ part) {
   __shared__ float mred[kThreads / kWave];
   __shared__ int ired[kThreads / kWave];
   const int64_t row = blockIdx.y;
   const int c = blockIdx.x;
-  const float* l = logits + row * V;
+  const float* l = logits + row * ld;
   float m = -INFINITY;
   int i = V;
 #pragma unroll
@@ -452,7 +457,7 @@ __global__ __launch_bounds__(kThreads) void row_argmax_kernel(const float* __res
 
 // probs[row][v] = (v == argmax) ? 1 : 0.
 __global__ __launch_bounds__(kThreads) void onehot_write_kernel(int V, int nch, const float2* __restrict__ part,
-                                                                float* __restrict__ probs) {
+                                                                float* __restrict__ probs, int64_t ld_out) {
   __shared__ int a_sh;
   const int64_t row = blockIdx.y;
   const int c = blockIdx.x;
@@ -465,7 +470,7 @@ __global__ __launch_bounds__(kThreads) void onehot_write_kernel(int V, int nch, 
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
     const int v = c * kChunk + e * kThreads + threadIdx.x;
-    if (v < V) probs[row * V + v] = (v == a) ? 1.f : 0.f;
+    if (v < V) probs[row * ld_out + v] = (v == a) ? 1.f : 0.f;
   }
 }
 
@@ -476,7 +481,7 @@ __global__ __launch_bounds__(kThreads) void greedy_kernel(int V, int nch, int ga
                                                           const int32_t* __restrict__ n_draft,
                                                           int32_t* __restrict__ n_accepted,
                                                           int32_t* __restrict__ emitted,
-                                                          int32_t* __restrict__ len_commit) {
+                                                          int32_t* __restrict__ len_commit, int ld_em) {
   __shared__ int amax[kMaxRows];
   const int b = blockIdx.x;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
@@ -489,52 +494,54 @@ __global__ __launch_bounds__(kThreads) void greedy_kernel(int V, int nch, int ga
   if (threadIdx.x == 0) {
     int n = 0;
     while (n < nd && draft[b * gamma + n] == amax[n]) ++n;
-    n_accepted[b] = n;
+    if (n_accepted) n_accepted[b] = n;
+    const int lde = ld_em > 0 ? ld_em : gamma + 1;
     for (int j = 0; j <= gamma; ++j)
-      emitted[b * (gamma + 1) + j] = j < n ? draft[b * gamma + j] : (j == n ? amax[n] : -1);
+      emitted[b * lde + j] = j < n ? draft[b * gamma + j] : (j == n ? amax[n] : -1);
     if (len_commit) len_commit[b] += n + 1;
   }
 }
 
 }  // namespace
 
-hipError_t launch_row_argmax(const float* logits, int64_t rows, int vocab, float2* part, hipStream_t s) {
+hipError_t launch_row_argmax(const float* logits, int64_t rows, int vocab, float2* part, hipStream_t s, int64_t ld) {
   const int nch = sampler_chunks(vocab);
-  hipLaunchKernelGGL(row_argmax_kernel, dim3(nch, static_cast<unsigned>(rows)), dim3(kThreads), 0, s, logits, vocab,
-                     nch, part);
+  hipLaunchKernelGGL(row_argmax_kernel, dim3(nch, static_cast<unsigned>(rows)), dim3(kThreads), 0, s, logits,
+                     ld > 0 ? ld : vocab, vocab, nch, part);
   return hipGetLastError();
 }
 
-hipError_t launch_onehot_write(int64_t rows, int vocab, const float2* part, float* probs, hipStream_t s) {
+hipError_t launch_onehot_write(int64_t rows, int vocab, const float2* part, float* probs, hipStream_t s,
+                               int64_t ld_out) {
   const int nch = sampler_chunks(vocab);
   hipLaunchKernelGGL(onehot_write_kernel, dim3(nch, static_cast<unsigned>(rows)), dim3(kThreads), 0, s, vocab, nch,
-                     part, probs);
+                     part, probs, ld_out > 0 ? ld_out : vocab);
   return hipGetLastError();
 }
 
 hipError_t launch_greedy(int B, int gamma, int vocab, const float2* part, const int32_t* draft,
                          const int32_t* n_draft, int32_t* n_accepted, int32_t* emitted, int32_t* len_commit,
-                         hipStream_t s) {
+                         hipStream_t s, int ld_em) {
   hipLaunchKernelGGL(greedy_kernel, dim3(B), dim3(kThreads), 0, s, vocab, sampler_chunks(vocab), gamma, part, draft,
-                     n_draft, n_accepted, emitted, len_commit);
+                     n_draft, n_accepted, emitted, len_commit, ld_em);
   return hipGetLastError();
 }
 
 int sampler_chunks(int vocab) { return (vocab + kChunk - 1) / kChunk; }
 
 hipError_t launch_row_partials(const float* logits, int64_t rows, int vocab, float temperature, float2* part,
-                               hipStream_t s) {
+                               hipStream_t s, int64_t ld) {
   const int nch = sampler_chunks(vocab);
-  hipLaunchKernelGGL(row_partials_kernel, dim3(nch, static_cast<unsigned>(rows)), dim3(kThreads), 0, s, logits, vocab,
-                     temperature, nch, part);
+  hipLaunchKernelGGL(row_partials_kernel, dim3(nch, static_cast<unsigned>(rows)), dim3(kThreads), 0, s, logits,
+                     ld > 0 ? ld : vocab, vocab, temperature, nch, part);
   return hipGetLastError();
 }
 
 hipError_t launch_softmax_write(const float* logits, int64_t rows, int vocab, float temperature, const float2* part,
-                                float* probs, hipStream_t s) {
+                                float* probs, hipStream_t s, int64_t ld_in, int64_t ld_out) {
   const int nch = sampler_chunks(vocab);
   hipLaunchKernelGGL(softmax_write_kernel, dim3(nch, static_cast<unsigned>(rows)), dim3(kThreads), 0, s, logits,
-                     vocab, temperature, nch, part, probs);
+                     ld_in > 0 ? ld_in : vocab, vocab, temperature, nch, part, probs, ld_out > 0 ? ld_out : vocab);
   return hipGetLastError();
 }
 
@@ -553,8 +560,8 @@ RejectArgs reject_args(const RejectRows& rr, int B, int gamma, int vocab, const 
                        const int32_t* n_draft, const float* u_acc, const float* u_res, int32_t* n_accepted,
                        int32_t* emitted, int32_t* len_commit, unsigned long long* csum) {
   const int nch = sampler_chunks(vocab);
-  return RejectArgs{RowSrc{rr.p, rr.logits, rr.part, rr.temperature, nch, vocab, rr.lx, rr.sel, gamma + 1},
-                    gamma, q, draft, n_draft, u_acc, u_res, n_accepted, emitted, len_commit, csum};
+  return RejectArgs{RowSrc{rr.p, rr.logits, rr.part, rr.temperature, nch, vocab, rr.lx, rr.sel, gamma + 1, rr.ld},
+                    gamma, q, draft, n_draft, u_acc, u_res, n_accepted, emitted, len_commit, csum, 0};
 }
 }  // namespace
 
@@ -569,10 +576,12 @@ hipError_t launch_select_rows(const RejectRows& rr, int B, int gamma, int vocab,
 
 hipError_t launch_reject(const RejectRows& rr, int B, int gamma, int vocab, const float* q, const int32_t* draft,
                          const int32_t* n_draft, const float* u_acc, const float* u_res, int32_t* n_accepted,
-                         int32_t* emitted, int32_t* len_commit, unsigned long long* csum, hipStream_t s) {
+                         int32_t* emitted, int32_t* len_commit, unsigned long long* csum, hipStream_t s,
+                         int ld_em) {
   const int nch = sampler_chunks(vocab);
   RejectArgs a = reject_args(rr, B, gamma, vocab, q, draft, n_draft, u_acc, u_res, n_accepted, emitted, len_commit,
                              csum);
+  a.ld_em = ld_em;
   hipLaunchKernelGGL(reject_chunks_kernel, dim3(nch, B), dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -91,15 +91,12 @@ class ModelDrafter:
         self.kv = bd.KVCache(model.shape, model.n_layers, B, max_ctx)
         self.ws2 = bd.workspace(model.workspace_bytes(B, 2, max_ctx))
         self.ws1 = bd.workspace(model.workspace_bytes(B, 1, max_ctx))
-        self.sws = bd.workspace(bd.spec_sampler_workspace_bytes(2 * B, B, V))
+        self.sws = bd.workspace(bd.spec_sampler_workspace_bytes(B, B, V))
         self.logits2 = torch.empty((B, 2, V), dtype=torch.float32, device="cuda")
-        self.probs2 = torch.empty_like(self.logits2)
         self.logits1 = torch.empty((B, 1, V), dtype=torch.float32, device="cuda")
-        self.qtmp = torch.empty((B, 1, V), dtype=torch.float32, device="cuda")
         self.q = torch.empty((B, gamma, V), dtype=torch.float32, device="cuda")
         self.drafts = torch.empty((B, gamma), dtype=torch.int32, device="cuda")
-        self.x = torch.empty((B, 1), dtype=torch.int32, device="cuda")
-        self.n_tmp = torch.empty(B, dtype=torch.int32, device="cuda")
+        self.drafts_t = torch.empty((gamma, B), dtype=torch.int32, device="cuda")  # position-major
 
     def prefill(self, prompt: np.ndarray):
         B, P = prompt.shape
@@ -110,36 +107,28 @@ class ModelDrafter:
 
     def draft(self, tok2: torch.Tensor, target_len: torch.Tensor, u_draft: torch.Tensor):
         """tok2 [B, 2] = (previous, last) committed tokens; u_draft [gamma, B].
-        Returns (drafts [B, gamma] int32, q [B, gamma, V] float32, n_draft None)."""
-        B, V = self.B, self.model.shape.vocab
+        Returns (drafts [B, gamma] int32, q [B, gamma, V] float32, n_draft None).
+        Each position's sampling step writes its q rows straight into column i
+        of q and its tokens into row i of the position-major drafts_t, which
+        the next pass reads as its input; one transpose per round gives the
+        [B, gamma] drafts (none when B = 1)."""
+        B, V, g = self.B, self.model.shape.vocab, self.gamma
         bd.spec_kv_set_len(self.kv, B, target_len, -1)
         bd.spec_verify_forward(self.model, self.kv, B, 2, tok2, self.logits2, self.ws2)
         bd.spec_kv_set_len(self.kv, B, None, 2)
-        if B == 1:
-            # one sequence: the q rows, the drawn tokens and the second
-            # logits row are contiguous slices, so the kernels write them in
-            # place (no copies, and the first softmax covers one row)
-            bd.spec_softmax_pq(self.logits2[:, 1], 1, V, self.T, self.q[:, 0], self.sws)
-            for i in range(self.gamma):
-                if i > 0:
-                    bd.spec_verify_forward(self.model, self.kv, 1, 1, self.drafts[:, i - 1:i], self.logits1,
-                                           self.ws1)
-                    bd.spec_kv_set_len(self.kv, 1, None, 1)
-                    bd.spec_softmax_pq(self.logits1, 1, V, self.T, self.q[:, i], self.sws)
-                bd.spec_reject_sample(1, 0, V, self.q[:, i], None, None, None, None, u_draft[i], self.n_tmp,
-                                      self.drafts[:, i:i + 1], self.sws)
-            return self.drafts, self.q, None
-        bd.spec_softmax_pq(self.logits2, 2 * B, V, self.T, self.probs2, self.sws)
-        self.qtmp.copy_(self.probs2[:, 1:2])
-        for i in range(self.gamma):
+        tok = self.drafts if B == 1 else self.drafts_t  # [1, gamma] and [gamma, 1] coincide
+        for i in range(g):
             if i > 0:
-                bd.spec_verify_forward(self.model, self.kv, B, 1, self.x, self.logits1, self.ws1)
+                bd.spec_verify_forward(self.model, self.kv, B, 1, tok[i - 1] if B > 1 else self.drafts[:, i - 1:i],
+                                       self.logits1, self.ws1)
                 bd.spec_kv_set_len(self.kv, B, None, 1)
-                bd.spec_softmax_pq(self.logits1, B, V, self.T, self.qtmp, self.sws)
-            bd.spec_reject_sample(B, 0, V, self.qtmp, None, None, None, None, u_draft[i], self.n_tmp, self.x,
-                                  self.sws)
-            self.q[:, i].copy_(self.qtmp[:, 0])
-            self.drafts[:, i].copy_(self.x[:, 0])
+                logits, ld, off = self.logits1, V, 0
+            else:
+                logits, ld, off = self.logits2, 2 * V, V  # the last committed token's row of each sequence
+            bd.spec_draft_sample(logits, ld, B, V, self.T, u_draft[i], self.q, g * V, tok, 1 if B > 1 else g,
+                                 self.sws, logits_off=off, q_off=i * V, tokens_off=i * B if B > 1 else i)
+        if B > 1:
+            self.drafts.copy_(self.drafts_t.t())
         return self.drafts, self.q, None
 
 

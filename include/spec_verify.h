@@ -35,8 +35,9 @@
  *   - Uniforms are float32 values in [0, 1); the exact draw above assumes they
  *     are multiples of 2^-24 (any other value is truncated to that grid).
  *   - Validation mode: with SPEC_CHECK=1 in the environment,
- *     spec_verify_forward, spec_softmax_pq, spec_reject_sample and
- *     spec_decode_step (and its _static form) also check their token ids
+ *     spec_verify_forward, spec_softmax_pq, spec_reject_sample,
+ *     spec_draft_sample and spec_decode_step (and its _static form) also
+ *     check their token ids
  *     (input tokens, the last committed tokens, the first n_draft drafts:
  *     inside [0, vocab)) and their float rows (logits, p and q rows: finite),
  *     synchronise the stream and return SPEC_EDEVICE when a check fails; the
@@ -186,6 +187,28 @@ spec_status spec_verify_forward_trace(const spec_model* model, const spec_kv* kv
  * Errors: SPEC_EINVAL, SPEC_ENOMEM, SPEC_EHIP. */
 spec_status spec_softmax_pq(const float* logits, int64_t rows, int32_t vocab, float temperature,
                             float* probs, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* The drafter's sampling step (the last page's draft.sample: a token and the
+ * probability row it was drawn from; first page, Algorithm 1: x_i ~ q_i).
+ * For b < B, with logit row l_b = logits + b * ld_logits [vocab]:
+ *   q + b * ld_q [vocab]   out: q_b = softmax(l_b / temperature), written as
+ *                          spec_softmax_pq writes it (one-hot at the lowest
+ *                          argmax when temperature = 0);
+ *   tokens[b * ld_tokens]  out: a draw from q_b with the uniform u[b], by the
+ *                          rule spec_reject_sample applies with gamma = 0
+ *                          (the same token for the same row and uniform), or
+ *                          the argmax when temperature = 0 (u may be NULL).
+ * The strides let one call per draft position write column i of the
+ * [B][gamma][vocab] draft rows and [B][gamma] drafts that spec_decode_step
+ * reads (q + i * vocab with ld_q = gamma * vocab; tokens + i with
+ * ld_tokens = gamma), and read one row per sequence of a multi-row pass's
+ * logits (ld_logits = m * vocab).  ld_logits, ld_q >= vocab, ld_tokens >= 1;
+ * q must not overlap logits.
+ * ws: spec_sampler_workspace_bytes(B, B, vocab) bytes.
+ * Errors: SPEC_EINVAL, SPEC_ENOMEM, SPEC_EHIP. */
+spec_status spec_draft_sample(const float* logits, int64_t ld_logits, int32_t B, int32_t vocab, float temperature,
+                              const float* u, float* q, int64_t ld_q, int32_t* tokens, int32_t ld_tokens, void* ws,
+                              size_t ws_bytes, hipStream_t stream);
 
 /* The accept / resample / bonus rule on materialised rows (first page,
  * Algorithm 1: the accepted-prefix count, the residual resample and the

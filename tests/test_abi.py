@@ -27,7 +27,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(lib):
     names = header_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(bd.EXPORTS) == names
@@ -64,6 +64,17 @@ def test_host_checks_reject_before_launch(lib):
         assert lib.spec_softmax_pq(1, 4, 100, bad_t, 1, 1, 1 << 20, None) == -1
     st = lib.spec_reject_sample(1, 2, 100, 1, None, 1, None, None, 1, 1, 1, 1, 1 << 20, None)
     assert st == -1  # u_acc NULL with gamma > 0
+    # draft sampling: buffers present, B and vocab in range, strides at least a row, u for T > 0, workspace
+    #   spec_draft_sample(logits, ld_logits, B, vocab, T, u, q, ld_q, tokens, ld_tokens, ws, ws_bytes, stream)
+    assert lib.spec_draft_sample(None, 100, 1, 100, 1.0, 1, 1, 100, 1, 1, 1, 1 << 20, None) == -1
+    assert lib.spec_draft_sample(1, 100, 0, 100, 1.0, 1, 1, 100, 1, 1, 1, 1 << 20, None) == -1  # B = 0
+    assert lib.spec_draft_sample(1, 100, 1, 1 << 23, 1.0, 1, 1, 1 << 23, 1, 1, 1, 1 << 30, None) == -1
+    assert lib.spec_draft_sample(1, 99, 1, 100, 1.0, 1, 1, 100, 1, 1, 1, 1 << 20, None) == -1  # ld_logits < vocab
+    assert lib.spec_draft_sample(1, 100, 2, 100, 1.0, 1, 1, 50, 1, 1, 1, 1 << 20, None) == -1  # ld_q < vocab
+    assert lib.spec_draft_sample(1, 100, 2, 100, 1.0, 1, 1, 100, 1, 0, 1, 1 << 20, None) == -1  # ld_tokens 0
+    assert lib.spec_draft_sample(1, 100, 1, 100, 1.0, None, 1, 100, 1, 1, 1, 1 << 20, None) == -1  # u NULL, T > 0
+    assert lib.spec_draft_sample(1, 100, 1, 100, float("nan"), 1, 1, 100, 1, 1, 1, 1 << 20, None) == -1
+    assert lib.spec_draft_sample(1, 100, 4, 100, 1.0, 1, 1, 100, 1, 1, 1, 8, None) == -2  # workspace too small
     assert lib.spec_kv_set_len(None, 1, None, 1, None) == -1
     kv = bd.spec_kv(1, 1, 1, 2, 16)
     assert lib.spec_kv_set_len(ctypes.byref(kv), 3, None, 1, None) == -1

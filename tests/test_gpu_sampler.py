@@ -138,3 +138,33 @@ def test_softmax_temperature_zero_one_hot(V):
     p = gpu_softmax(f32(logits), V, 0.0).cpu().numpy()
     ref = S.softmax(logits, 0.0)
     assert np.array_equal(p, ref.astype(np.float32))
+
+
+@pytest.mark.parametrize("B,g,V,T", [(1, 4, 151936, 1.0), (5, 4, 32000, 1.0), (64, 10, 4097, 0.7), (7, 3, 32000, 0.0)])
+def test_draft_sample_matches_softmax_then_sample(B, g, V, T):
+    """spec_draft_sample over strided rows (row 1 of a two-row pass, written
+    into column i of the [B][gamma][V] draft rows and the [gamma][B] tokens)
+    is bitwise spec_softmax_pq followed by spec_reject_sample with gamma = 0
+    on contiguous copies: the same q rows and the same tokens."""
+    rng = np.random.default_rng(SEED + B + g + V)
+    logits2 = f32(_rows(rng, 2 * B, V, 3.0).reshape(B, 2, V))
+    u = torch.as_tensor(make_uniforms((B,), SEED, B, g)).cuda()
+    i = g - 1  # the last column: strides and offsets both non-trivial
+    q = torch.full((B, g, V), -1.0, device="cuda")
+    toks = torch.full((g, B), -7, dtype=torch.int32, device="cuda")
+    ws = bd.workspace(bd.spec_sampler_workspace_bytes(B, B, V))
+    bd.spec_draft_sample(logits2, 2 * V, B, V, T, u if T > 0 else None, q, g * V, toks, 1, ws,
+                         logits_off=V, q_off=i * V, tokens_off=i * B)
+    # reference: the two calls on a contiguous copy of the rows
+    rows = logits2[:, 1].contiguous()
+    p = torch.empty_like(rows)
+    ws2 = bd.workspace(bd.spec_sampler_workspace_bytes(B, B, V))
+    bd.spec_softmax_pq(rows, B, V, T, p, ws2)
+    n = torch.empty(B, dtype=torch.int32, device="cuda")
+    em = torch.empty((B, 1), dtype=torch.int32, device="cuda")
+    bd.spec_reject_sample(B, 0, V, p, None, None, None, None, u, n, em, ws2)
+    torch.cuda.synchronize()
+    assert torch.equal(q[:, i], p)
+    assert torch.equal(toks[i], em[:, 0])
+    # nothing outside the target column and row was written
+    assert bool((q[:, :i] == -1.0).all()) and bool((toks[:i] == -7).all())

@@ -536,15 +536,17 @@ SPEC_API spec_status spec_draft_sample(const float* logits, int64_t ld_logits, i
     HIP_TRY(sv::launch_onehot_write(B, vocab, part, q, stream, ld_q));
     HIP_TRY(sv::launch_greedy(B, 0, vocab, part, nullptr, nullptr, nullptr, tokens, nullptr, stream, ld_tokens));
   } else {
+    // the softmax pass also leaves each chunk's weight sums, so the draw is
+    // one workgroup per sequence over its chosen chunk
     HIP_TRY(sv::launch_row_partials(logits, B, vocab, temperature, part, stream, ld_logits));
-    HIP_TRY(sv::launch_softmax_write(logits, B, vocab, temperature, part, q, stream, ld_logits, ld_q));
+    HIP_TRY(sv::launch_softmax_write(logits, B, vocab, temperature, part, q, stream, ld_logits, ld_q, csum));
     sv::RejectRows rr;
     rr.logits = logits;
     rr.part = part;
     rr.temperature = temperature;
     rr.ld = ld_logits;
     HIP_TRY(sv::launch_reject(rr, B, 0, vocab, nullptr, nullptr, nullptr, nullptr, u, nullptr, tokens, nullptr, csum,
-                              stream, ld_tokens));
+                              stream, ld_tokens, true));
   }
   if (!check_mode()) return SPEC_OK;
   int* flag = nullptr;

@@ -159,9 +159,12 @@ int sampler_chunks(int vocab);
 // ld: floats between logit rows (0: vocab).
 hipError_t launch_row_partials(const float* logits, int64_t rows, int vocab, float temperature, float2* part,
                                hipStream_t s, int64_t ld = 0);
-// probs = exp(l/T - m) / Z with the row statistics combined from part.
+// probs = exp(l/T - m) / Z with the row statistics combined from part; with
+// csum, also each chunk's fixed-point weight sums for a gamma = 0 draw from
+// the rows (launch_reject then with have_chunks).
 hipError_t launch_softmax_write(const float* logits, int64_t rows, int vocab, float temperature,
-                                const float2* part, float* probs, hipStream_t s, int64_t ld_in = 0, int64_t ld_out = 0);
+                                const float2* part, float* probs, hipStream_t s, int64_t ld_in = 0, int64_t ld_out = 0,
+                                unsigned long long* csum = nullptr);
 // Temperature 0: part[row][c] = (chunk max, its lowest index as int bits);
 // one-hot rows at the row argmax; greedy accept (x_i == argmax_i) with the
 // argmax of row n emitted after the accepted drafts.
@@ -189,7 +192,8 @@ struct RejectRows {
 hipError_t launch_reject(const RejectRows& rr, int B, int gamma, int vocab, const float* q, const int32_t* draft,
                          const int32_t* n_draft, const float* u_acc, const float* u_res, int32_t* n_accepted,
                          int32_t* emitted, int32_t* len_commit, unsigned long long* csum, hipStream_t s,
-                         int ld_em = 0);  // ints between sequences' emitted rows (0: gamma + 1)
+                         int ld_em = 0,               // ints between sequences' emitted rows (0: gamma + 1)
+                         bool have_chunks = false);   // csum already holds the chunk sums (gamma = 0)
 // Chunk statistics part [rows][chunks] from the LM head's tile statistics
 // tpart [rows][ceil(vocab/128)] (EPI_LMSTAT).
 hipError_t launch_tile_merge(int64_t rows, int vocab, const float2* tpart, bool greedy, float2* part, hipStream_t s);

@@ -234,11 +234,18 @@ __global__ __launch_bounds__(kThreads) void tile_merge_kernel(int64_t rows, int 
   if (live && k == 0) part[i] = make_float2(M, Z);
 }
 
+// probs[row][v] = p(v) over chunk c of the row.  With csum (a row drawn from
+// as a bonus row, gamma = 0) it also writes the chunk's fixed-point weight
+// sum twice, as reject_chunks_kernel does for such a row, so the draw needs
+// only reject_final_kernel.
+template <bool SUMS>
 __global__ __launch_bounds__(kThreads) void softmax_write_kernel(const float* __restrict__ logits, int64_t ld_in,
                                                                  int V, float T, int nch,
                                                                  const float2* __restrict__ part,
-                                                                 float* __restrict__ probs, int64_t ld_out) {
+                                                                 float* __restrict__ probs, int64_t ld_out,
+                                                                 unsigned long long* __restrict__ csum) {
   __shared__ float2 st_sh;
+  __shared__ unsigned long long red[kThreads / kWave];
   const int64_t row = blockIdx.y;
   const int c = blockIdx.x;
   if (threadIdx.x < kWave) {
@@ -248,10 +255,22 @@ __global__ __launch_bounds__(kThreads) void softmax_write_kernel(const float* __
   __syncthreads();
   const float2 st = st_sh;
   RowSrc src{nullptr, logits, part, T, nch, V, nullptr, nullptr, 1, ld_in};
+  unsigned long long wp = 0;
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
     const int v = c * kChunk + e * kThreads + threadIdx.x;
-    if (v < V) probs[row * ld_out + v] = src.prob(row, v, st);
+    if (v < V) {
+      const float pv = src.prob(row, v, st);
+      probs[row * ld_out + v] = pv;
+      if (SUMS) wp += fixed_weight(pv);
+    }
+  }
+  if (SUMS) {
+    wp = block_sum_u64<kThreads>(wp, red);
+    if (threadIdx.x == 0) {
+      csum[(row * nch + c) * 2 + 0] = wp;
+      csum[(row * nch + c) * 2 + 1] = wp;
+    }
   }
 }
 
@@ -538,10 +557,15 @@ hipError_t launch_row_partials(const float* logits, int64_t rows, int vocab, flo
 }
 
 hipError_t launch_softmax_write(const float* logits, int64_t rows, int vocab, float temperature, const float2* part,
-                                float* probs, hipStream_t s, int64_t ld_in, int64_t ld_out) {
+                                float* probs, hipStream_t s, int64_t ld_in, int64_t ld_out, unsigned long long* csum) {
   const int nch = sampler_chunks(vocab);
-  hipLaunchKernelGGL(softmax_write_kernel, dim3(nch, static_cast<unsigned>(rows)), dim3(kThreads), 0, s, logits,
-                     ld_in > 0 ? ld_in : vocab, vocab, temperature, nch, part, probs, ld_out > 0 ? ld_out : vocab);
+  const dim3 grid(nch, static_cast<unsigned>(rows));
+  if (csum)
+    hipLaunchKernelGGL(softmax_write_kernel<true>, grid, dim3(kThreads), 0, s, logits, ld_in > 0 ? ld_in : vocab,
+                       vocab, temperature, nch, part, probs, ld_out > 0 ? ld_out : vocab, csum);
+  else
+    hipLaunchKernelGGL(softmax_write_kernel<false>, grid, dim3(kThreads), 0, s, logits, ld_in > 0 ? ld_in : vocab,
+                       vocab, temperature, nch, part, probs, ld_out > 0 ? ld_out : vocab, csum);
   return hipGetLastError();
 }
 
@@ -577,14 +601,16 @@ hipError_t launch_select_rows(const RejectRows& rr, int B, int gamma, int vocab,
 hipError_t launch_reject(const RejectRows& rr, int B, int gamma, int vocab, const float* q, const int32_t* draft,
                          const int32_t* n_draft, const float* u_acc, const float* u_res, int32_t* n_accepted,
                          int32_t* emitted, int32_t* len_commit, unsigned long long* csum, hipStream_t s,
-                         int ld_em) {
+                         int ld_em, bool have_chunks) {
   const int nch = sampler_chunks(vocab);
   RejectArgs a = reject_args(rr, B, gamma, vocab, q, draft, n_draft, u_acc, u_res, n_accepted, emitted, len_commit,
                              csum);
   a.ld_em = ld_em;
-  hipLaunchKernelGGL(reject_chunks_kernel, dim3(nch, B), dim3(kThreads), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (!have_chunks) {
+    hipLaunchKernelGGL(reject_chunks_kernel, dim3(nch, B), dim3(kThreads), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(reject_final_kernel, dim3(B), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }

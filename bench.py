@@ -352,8 +352,8 @@ def mfma_linears(M: int = 1280, reps: int = 20) -> list:
     """The matrix-core linear at the second workload's weight shapes with
     M = 1280 rows (a B = 256, gamma = 4 verify pass): TFLOP/s per launch from
     HIP events around a graph replay of `reps` launches (so the host's
-    per-call cost does not show in launches shorter than it), against the
-    dense bf16 peak.  Each shape cycles through 8 weight copies so the weights
+    per-call cost does not show in launches shorter than it; the median of 5
+    replays), against the dense bf16 peak.  Each shape cycles through 8 weight copies so the weights
     come from HBM."""
     import torch
 
@@ -387,11 +387,14 @@ def mfma_linears(M: int = 1280, reps: int = 20) -> list:
         cg.replay()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        cg.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / reps
+        times = []
+        for _ in range(5):
+            e0.record()
+            cg.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e3 / reps)
+        us = sorted(times)[2]  # the median of 5 replays
         del cg
         tflops = 2.0 * M * rows * K / (us * 1e-6) / 1e12
         out.append({"linear": name, "M": M, "N": rows, "K": K, "us_per_launch": round(us, 2),

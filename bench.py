@@ -643,6 +643,11 @@ def main():
         drafter = ModelDrafter(draft, B, g, max_ctx)
         spec = SpecDecoder(target, B, g, max_ctx, drafter=drafter, seed=11)
         spec.prefill(prompt)
+        # the drafter's part of a round on its own (its gamma passes, the
+        # first over two rows, softmax and draws); the round's first pass
+        # rewrites the KV rows this touches
+        t_draft = time_draft(drafter, spec.kv.len, B, g)
+        log(f"drafter round: {t_draft:.3f} ms ({g} passes of the 0.6B-shaped drafter with softmax and draws)")
         rs = spec.generate_graph(args.new_tokens)
         log(f"speculative: {rs['tok_s']:.1f} tok/s, MAL {rs['mean_acceptance_length']:.2f}, rounds {rs['rounds']}")
         del spec, drafter
@@ -663,6 +668,7 @@ def main():
                "round_ms_mean": round(1e3 * rs["wall_s"] / rs["rounds"], 3),
                "round_ms_p50": round(rs["round_ms_p50"], 3), "round_ms_p99": round(rs["round_ms_p99"], 3),
                "plain_round_ms_p50": round(rp["round_ms_p50"], 3), "plain_round_ms_p99": round(rp["round_ms_p99"], 3),
+               "draft_round_ms": round(t_draft, 4), "draft_pass_ms_mean": round(t_draft / g, 4),
                "generation": "graph-replayed rounds (drafter passes, verify step and bookkeeping on the device)"}
         del plain
 

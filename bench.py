@@ -200,6 +200,13 @@ def time_verify_step(target, shape, prompt, B: int, g: int, steps: int, warmup: 
         with torch.cuda.graph(cg):
             step()
         torch.cuda.synchronize()
+        # the host's submission of one replay (the first replay's falls
+        # inside the timed region; the later ones overlap the device's work)
+        th = time.perf_counter()
+        cg.replay()
+        th = time.perf_counter() - th
+        torch.cuda.synchronize()
+        log(f"graph replay submitted by the host in {1e3 * th:.3f} ms (B={B}, {B * (g + 1)} rows)")
     len0 = int(dec.kv.len[0])
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -213,10 +220,24 @@ def time_verify_step(target, shape, prompt, B: int, g: int, steps: int, warmup: 
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / steps
     len1 = int(dec.kv.len[0])
+    if int(dec.kv.len.max().item()) > max_ctx:
+        raise RuntimeError(f"the timed steps ran past max_ctx = {max_ctx}: size the cache for g + 1 tokens per step")
     # keys attended per step: len + m at each step; len grows by n + 1 per step
     ctx_mean = (len0 + len1) / 2.0 + g + 1 - 0.5 * (len1 - len0) / steps
     del dec
     return ms, ctx_mean, f"{len0}->{len1} (warmup from {len_before_warm})", cg is not None
+
+
+def warm_up(make, prompt, g: int) -> None:
+    """A short untimed generation on a decoder of the same shapes, so that the
+    timed generation's first round (run eagerly, and timed) pays none of the
+    process's one-time kernel set-up: the first launch of a kernel instance
+    loads its code, and the first workloads to use an instance would carry
+    that cost (on the copy-heavy workload, ~110 ms against ~170 ms of rounds)."""
+    dec = make()
+    dec.prefill(prompt)
+    dec.generate_graph(g + 2)
+    del dec
 
 
 def batch_sweep(n_new: int, batches=(1, 8, 64, 256), P: int = 256, g: int = 4) -> list:
@@ -239,11 +260,15 @@ def batch_sweep(n_new: int, batches=(1, 8, 64, 256), P: int = 256, g: int = 4) -
     for B in batches:
         prompt = make_prompt(B, P, sh.vocab, seed=22 + B)
         max_ctx = P + n_new + 2 * g + 4
-        spec = SpecDecoder(target, B, g, max_ctx, drafter=ModelDrafter(draft, B, g, max_ctx), seed=23)
+        make_spec = lambda: SpecDecoder(target, B, g, max_ctx, drafter=ModelDrafter(draft, B, g, max_ctx), seed=23)
+        make_plain = lambda: SpecDecoder(target, B, 0, max_ctx, seed=24)
+        warm_up(make_spec, prompt, g)
+        spec = make_spec()
         spec.prefill(prompt)
         rs = spec.generate_graph(n_new)
         del spec
-        plain = SpecDecoder(target, B, 0, max_ctx, seed=24)
+        warm_up(make_plain, prompt, 0)
+        plain = make_plain()
         plain.prefill(prompt)
         rp = plain.generate_graph(n_new)
         del plain
@@ -286,7 +311,9 @@ def batch_verify_steps(batches=(1, 8, 64, 256), P: int = 256, g: int = 4, steps:
     rows = []
     for B in batches:
         prompt = make_prompt(B, P, sh.vocab, seed=22 + B)
-        ms, ctx_mean, note, _ = time_verify_step(target, sh, prompt, B, g, steps, 3, P + steps + 3 + 4 * (g + 1))
+        # a step commits up to g + 1 tokens: room for every step (warm-up,
+        # the capture stream's eager call, the host-timing replay, the timed ones)
+        ms, ctx_mean, note, _ = time_verify_step(target, sh, prompt, B, g, steps, 3, P + (g + 1) * (steps + 3 + 3) + 8)
         # with more than d_model / 4 rows the step's LM head writes softmax
         # statistics instead of the logits (the library's rule for bf16)
         fused = B * (g + 1) > sh.d_model // 4
@@ -324,11 +351,16 @@ def ngram_workload(n_new: int, batches=(1, 64), P: int = 2048, g: int = 10) -> l
         prompt = markov_prompt(B, P, table, seed=33 + B).astype(np.int64)
         offs = np.random.default_rng(34 + B).integers(0, P - g - 1, size=B)
         max_ctx = P + n_new + 2 * g + 4
-        spec = SpecDecoder(target, B, g, max_ctx, drafter=DeviceNgramDrafter(B, g, n=3, fill_off=offs), seed=35)
+        make_spec = lambda: SpecDecoder(target, B, g, max_ctx, drafter=DeviceNgramDrafter(B, g, n=3, fill_off=offs),
+                                        seed=35)
+        make_plain = lambda: SpecDecoder(target, B, 0, max_ctx, seed=36)
+        warm_up(make_spec, prompt, g)
+        spec = make_spec()
         spec.prefill(prompt)
         rs = spec.generate_graph(n_new)
         del spec
-        plain = SpecDecoder(target, B, 0, max_ctx, seed=36)
+        warm_up(make_plain, prompt, 0)
+        plain = make_plain()
         plain.prefill(prompt)
         rp = plain.generate_graph(n_new)
         del plain
@@ -338,8 +370,11 @@ def ngram_workload(n_new: int, batches=(1, 64), P: int = 2048, g: int = 10) -> l
                      "mean_acceptance_length": round(rs["mean_acceptance_length"], 3),
                      "ngram_hit_rate": round(rs["ngram_hit_rate"], 4),
                      "ngram_found_tokens_per_round": round(rs["ngram_found_tokens_per_round"], 3),
+                     "spec_rounds": rs["rounds"], "spec_round_ms_p50": round(rs.get("round_ms_p50", 0.0), 4),
+                     "spec_wall_ms": round(1e3 * rs["wall_s"], 2), "plain_wall_ms": round(1e3 * rp["wall_s"], 2),
                      "note": "random-init target: a one-hot draft is accepted with probability p(x) ~ 1/V, "
                              "so this measures the cost of verifying gamma + 1 = 11 rows per emitted token"})
+        log(f"n-gram B={B}: {rs['rounds']} rounds, p50 {rs.get('round_ms_p50', 0.0):.3f} ms, wall {1e3 * rs['wall_s']:.1f} ms")
         log(f"n-gram B={B}: speculative {rs['tok_s']:.0f} tok/s, plain {rp['tok_s']:.0f} tok/s, "
             f"ratio {rs['tok_s'] / rp['tok_s']:.3f}, MAL {rs['mean_acceptance_length']:.2f}")
     return rows
@@ -351,9 +386,9 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
 def mfma_linears(M: int = 1280, reps: int = 20) -> list:
     """The matrix-core linear at the second workload's weight shapes with
     M = 1280 rows (a B = 256, gamma = 4 verify pass): TFLOP/s per launch from
-    HIP events around a graph replay of `reps` launches (so the host's
-    per-call cost does not show in launches shorter than it; the median of 5
-    replays), against the dense bf16 peak.  Each shape cycles through 8 weight copies so the weights
+    HIP events around 5 back-to-back replays of a graph of `reps` launches
+    (so neither the host's per-call cost nor the submission of the first
+    replay shows much in launches this short), against the dense bf16 peak.  Each shape cycles through 8 weight copies so the weights
     come from HBM."""
     import torch
 
@@ -387,14 +422,12 @@ def mfma_linears(M: int = 1280, reps: int = 20) -> list:
         cg.replay()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        times = []
+        e0.record()
         for _ in range(5):
-            e0.record()
             cg.replay()
-            e1.record()
-            torch.cuda.synchronize()
-            times.append(e0.elapsed_time(e1) * 1e3 / reps)
-        us = sorted(times)[2]  # the median of 5 replays
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (5 * reps)
         del cg
         tflops = 2.0 * M * rows * K / (us * 1e-6) / 1e12
         out.append({"linear": name, "M": M, "N": rows, "K": K, "us_per_launch": round(us, 2),
@@ -406,7 +439,7 @@ def mfma_linears(M: int = 1280, reps: int = 20) -> list:
     return out
 
 
-def time_draft(drafter, kv_len, B: int, g: int, steps: int = 20) -> float:
+def time_draft(drafter, kv_len, B: int, g: int, steps: int = 100) -> float:
     """Mean time of the drafter's work for one round (its passes, softmax
     and draws), graph-replayed; the drafter rewinds to kv_len - 1 each time."""
     import torch
@@ -482,16 +515,18 @@ def division_check(n_new: int, P: int = 256) -> dict:
     B, g = 1, 1
     prompt = make_prompt(B, P, sh.vocab, seed=32)
     max_ctx = P + n_new + 64
+    warm_up(lambda: SpecDecoder(target, B, g, max_ctx, drafter=ModelDrafter(draft, B, g, max_ctx), seed=33), prompt, g)
     drafter = ModelDrafter(draft, B, g, max_ctx)
     spec = SpecDecoder(target, B, g, max_ctx, drafter=drafter, seed=33)
     spec.prefill(prompt)
     t_draft = time_draft(drafter, spec.kv.len, B, g)
     rs = spec.generate_graph(n_new)
+    warm_up(lambda: SpecDecoder(target, B, 0, max_ctx, seed=34), prompt, 0)
     plain = SpecDecoder(target, B, 0, max_ctx, seed=34)
     plain.prefill(prompt)
     rp = plain.generate_graph(n_new)
     t_decode = 1e3 * rp["wall_s"] / rp["rounds"]
-    t_verify, _, _, _ = time_verify_step(target, sh, prompt, B, g, 20, 5, max_ctx)
+    t_verify, _, _, _ = time_verify_step(target, sh, prompt, B, g, 100, 5, max_ctx)
     t_book = time_bookkeeping(B, g, n_new + g + 1)
     p = rs["acceptance_rate"]
     predicted = (1 + p) * t_decode / (t_verify + t_draft)
@@ -542,7 +577,7 @@ def kernel_only(reps: int) -> None:
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--new-tokens", type=int, default=256)
     ap.add_argument("--cpu-layers", type=int, default=36, help="target layers in the CPU-baseline sample")
@@ -592,7 +627,8 @@ def main():
     torch.cuda.set_device(dev)
     tshape, dshape = SHAPES["qwen3_8b"], SHAPES["qwen3_0p6b"]
     B, g, P = 1, 4, 256
-    max_ctx = P + args.new_tokens + 2 * g + args.steps + args.warmup + 8
+    # room for the generations and for every verify step committing g + 1 tokens
+    max_ctx = P + max(args.new_tokens + 2 * g, (g + 1) * (args.steps + args.warmup + 3)) + 8
     t0 = time.perf_counter()
     wt = make_weights(tshape, seed=3, device="cuda")
     wd = make_weights(dshape, seed=4, device="cuda")
@@ -623,15 +659,23 @@ def main():
 
     for layer in range(tshape.n_layers):
         gate_up(layer)
-    reps = 3
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # one pass over the 36 layers' weights as a graph, replayed back to back,
+    # so that the host's per-call cost (ctypes, launch) cannot starve the device
     torch.cuda.synchronize()
-    e0.record()
-    for _ in range(reps):
+    kg = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(kg):
         for layer in range(tshape.n_layers):
             gate_up(layer)
+    kg.replay()
+    torch.cuda.synchronize()
+    reps = 3
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        kg.replay()
     e1.record()
     torch.cuda.synchronize()
+    del kg
     k_us = e0.elapsed_time(e1) * 1e3 / (reps * tshape.n_layers)
     k_bytes = 2 * F * d * 2 + M * d * 4 + d * 4 + M * F * 2
     k_gbs = k_bytes / (k_us / 1e6) / 1e9
@@ -640,6 +684,8 @@ def main():
     # ---- emitted tokens/s: speculative vs plain ---------------------------------------
     gen = {}
     if not args.skip_generate:
+        warm_up(lambda: SpecDecoder(target, B, g, max_ctx, drafter=ModelDrafter(draft, B, g, max_ctx), seed=11),
+                prompt, g)
         drafter = ModelDrafter(draft, B, g, max_ctx)
         spec = SpecDecoder(target, B, g, max_ctx, drafter=drafter, seed=11)
         spec.prefill(prompt)
@@ -651,6 +697,7 @@ def main():
         rs = spec.generate_graph(args.new_tokens)
         log(f"speculative: {rs['tok_s']:.1f} tok/s, MAL {rs['mean_acceptance_length']:.2f}, rounds {rs['rounds']}")
         del spec, drafter
+        warm_up(lambda: SpecDecoder(target, B, 0, max_ctx, seed=12), prompt, 0)
         plain = SpecDecoder(target, B, 0, max_ctx, seed=12)
         plain.prefill(prompt)
         rp = plain.generate_graph(args.new_tokens)

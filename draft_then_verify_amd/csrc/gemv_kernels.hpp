@@ -35,9 +35,16 @@ namespace gemv {
 
 constexpr int kMaxLds = 159 * 1024;  // dynamic LDS; 1 KiB is left for static arrays
 // Weight steps a wave issues before the activation staging (see the
-// prologue of gemv_kernel); the rest of the ring follows it.  Measured on the
-// 8B-shaped 5-row step: 1, 2, 4 steps -> 3.479, 3.416, 3.433 ms.
-constexpr int kPreSteps = 2;
+// prologue of gemv_kernel); the rest of the ring follows it.  Per epilogue,
+// from the 8B-shaped 5-row step and the 0.6B-shaped drafter round (3 runs of
+// each, graph-replayed): the same 2 steps everywhere gave 3.292 ms and 2.906
+// ms; the whole ring of 4 for the residual linears (O, down: a short bf16
+// copy stages their input) 3.243 and 2.850; with 3 for QKV and gate/up (an
+// RMSNorm of float32 rows stages theirs) 3.227 and 2.850.  One step for the
+// residual linears, or 4 for QKV, was slower.
+template <int EPI> constexpr int pre_steps() {
+  return EPI == EPI_RESID ? 4 : (EPI == EPI_QKV || EPI == EPI_SWIGLU) ? 3 : 2;
+}
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) const u32x4 global_u32x4;
@@ -257,14 +264,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE))) void 
   //     the activations becomes a wait for everything;
   //  3. the rows are normalised or copied into LDS; the staging ends at a
   //     workgroup barrier, which a wave only reaches once its loads are
-  //     issued, so only kPre steps go before it (with the whole ring, the
-  //     late waves of a CU wait for the early waves' weights to come back
-  //     while the early waves idle at the barrier);
+  //     issued, so kPre steps go before it: the whole ring where a short
+  //     copy stages the rows, one step less after a normalising staging
+  //     (there, with the whole ring, the late waves of a CU wait for the
+  //     early waves' weights to come back while the early waves idle at the
+  //     barrier; pre_steps has the measurements);
   //  4. the rest of the ring is issued.
   // (bf16: x chunks per thread loaded ahead of the weights, 32 registers; the
   // float32 kernels keep their registers for the 4-fma dot products)
   constexpr bool kBf16 = sizeof(WT) == 2;
-  constexpr int kPre = U < kPreSteps ? U : kPreSteps;
+  constexpr int kPre = U < pre_steps<EPI>() ? U : pre_steps<EPI>();
   constexpr int XR = kBf16 ? 8 : 1;
   constexpr bool kEarlyNorm = kBf16 && M * NormRegs<NT, M>::CPT <= 10;  // 40 registers at most
   __shared__ float red[kNormBlocks][8];

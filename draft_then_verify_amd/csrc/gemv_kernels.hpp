@@ -39,11 +39,13 @@ constexpr int kMaxLds = 159 * 1024;  // dynamic LDS; 1 KiB is left for static ar
 // from the 8B-shaped 5-row step and the 0.6B-shaped drafter round (3 runs of
 // each, graph-replayed): the same 2 steps everywhere gave 3.292 ms and 2.906
 // ms; the whole ring of 4 for the residual linears (O, down: a short bf16
-// copy stages their input) 3.243 and 2.850; with 3 for QKV and gate/up (an
-// RMSNorm of float32 rows stages theirs) 3.227 and 2.850.  One step for the
-// residual linears, or 4 for QKV, was slower.
+// copy stages their input) 3.243 and 2.850; with 3 for QKV as well (an
+// RMSNorm of float32 rows stages its input) 3.249 and 2.851.  One step for
+// the residual linears, or 4 for QKV, was slower.  Gate/up keeps 2: with 3
+// the step gained ~0.015 ms, but back-to-back gate/up launches (the
+// dominant kernel timed on its own) ran 4% slower than inside the step.
 template <int EPI> constexpr int pre_steps() {
-  return EPI == EPI_RESID ? 4 : (EPI == EPI_QKV || EPI == EPI_SWIGLU) ? 3 : 2;
+  return EPI == EPI_RESID ? 4 : EPI == EPI_QKV ? 3 : 2;
 }
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -265,9 +267,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(WPE))) void 
   //  3. the rows are normalised or copied into LDS; the staging ends at a
   //     workgroup barrier, which a wave only reaches once its loads are
   //     issued, so kPre steps go before it: the whole ring where a short
-  //     copy stages the rows, one step less after a normalising staging
-  //     (there, with the whole ring, the late waves of a CU wait for the
-  //     early waves' weights to come back while the early waves idle at the
+  //     copy stages the rows, fewer before a normalising staging (there,
+  //     with the whole ring, the late waves of a CU wait for the early
+  //     waves' weights to come back while the early waves idle at the
   //     barrier; pre_steps has the measurements);
   //  4. the rest of the ring is issued.
   // (bf16: x chunks per thread loaded ahead of the weights, 32 registers; the

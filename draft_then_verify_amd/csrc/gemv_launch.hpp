@@ -94,6 +94,11 @@ hipError_t launch_m(const GemvArgs& a, hipStream_t s) {
   constexpr int STEP = step_elems<WT>();
   constexpr int U0 = Cfg<EPI>::U;
   const int S = (a.K + STEP - 1) / STEP;
+  // residual linears of 6 steps per row (the 0.6B-shaped drafter's down
+  // linear, K = 3072): the whole row in flight, not 2 steps of it
+  if constexpr (EPI == EPI_RESID) {
+    if (S == 6) return launch_mu<WT, M, 6, EPI>(a, s);
+  }
   if (U0 >= 8 && S % 8 == 0) return launch_mu<WT, M, (U0 >= 8 ? 8 : U0), EPI>(a, s);
   if (U0 >= 4 && S % 4 == 0) return launch_mu<WT, M, (U0 >= 4 ? 4 : U0), EPI>(a, s);
   if (U0 >= 2 && S % 2 == 0) return launch_mu<WT, M, (U0 >= 2 ? 2 : U0), EPI>(a, s);

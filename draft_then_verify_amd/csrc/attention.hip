@@ -956,6 +956,19 @@ hipError_t launch_decode_rw(const AttnArgs& a, int B, hipStream_t s) {
   const int n_rb = (a.m + RW - 1) / RW;
   constexpr int NWV = RW <= 2 ? 16 : kDecWaves, KTD = RW <= 2 ? 32 : KT;
   if (a.dsplit < 1 || a.dsplit > kMaxAttnSplits || (a.dsplit > 1 && (!a.dpo || !a.dpml))) return hipErrorInvalidValue;
+  // A split one-row pass gives each workgroup a quarter or half of the
+  // context (≈ 75-150 keys at 300): 4 waves of 32-key tiles, where 16 left
+  // most waves idle and lengthened the merge (0.6B-shaped drafter round
+  // 2.779 -> 2.766 ms, the second workload's 2-layer drafter round 0.3224 ->
+  // 0.3201 ms; 8 waves in between).
+  if constexpr (RW == 1) {
+    if (a.dsplit > 1) {
+      constexpr int SW = 4;
+      hipLaunchKernelGGL((attn_decode_kernel<ET, HD, RW, SW, KTD>), dim3(B * a.H * n_rb * a.dsplit), dim3(SW * kWave),
+                         0, s, a, n_rb);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((attn_decode_kernel<ET, HD, RW, NWV, KTD>), dim3(B * a.H * n_rb * a.dsplit), dim3(NWV * kWave), 0,
                      s, a, n_rb);
   return hipGetLastError();

@@ -44,8 +44,11 @@ constexpr int kMaxLds = 159 * 1024;  // dynamic LDS; 1 KiB is left for static ar
 // the residual linears, or 4 for QKV, was slower.  Gate/up keeps 2: with 3
 // the step gained ~0.015 ms, but back-to-back gate/up launches (the
 // dominant kernel timed on its own) ran 4% slower than inside the step.
+// The residual linears issue their whole ring, whatever its depth (8 caps
+// it): with a ring of 6 (rows of 6 steps), 6 rather than 4 took the second
+// workload's B = 1 verify step from 0.304 to 0.301 ms.
 template <int EPI> constexpr int pre_steps() {
-  return EPI == EPI_RESID ? 4 : EPI == EPI_QKV ? 3 : 2;
+  return EPI == EPI_RESID ? 8 : EPI == EPI_QKV ? 3 : 2;
 }
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
